@@ -1,0 +1,153 @@
+/*
+ * qmm.h -- C ABI of the split-K W4A16 group-128 quantized matmul for MI355X (gfx950).
+ *
+ * The library computes
+ *
+ *     C[M,N] = A[M,K] . dequant(W)[N,K]^T,   dequant(W)[n,k] = scale[n,k/128] * q[n,k] + bias[n,k/128]
+ *
+ * with bf16 activations A, 4-bit unsigned weights q packed eight per 32-bit word
+ * along K, per-(row, 128-group) bf16 scale and bias, fp32 accumulation and a bf16
+ * result (tiny-llm "Week 2 Day 7: Split-K Prefill": the W4A16 g128 kernel it
+ * starts from, and the split of the reduction dimension it adds).
+ *
+ * When the unsplit output grid under-fills the GPU, an occupancy policy cuts the
+ * reduction into s equal partitions on 128-value group boundaries; each
+ * partition writes its own bf16 partial plane without atomics, and a second
+ * kernel sums the planes in fp32 and casts once to bf16 (same page, Tasks 2-4).
+ * When the grid is already full the policy returns s = 1 and the unsplit kernel
+ * runs unchanged. A dense bf16 split-K variant with fp32 partials is exported
+ * beside it (gpu-kernels-explained "Split-K, streams and overlap", Concept).
+ *
+ * Layouts (all row-major, contiguous, no strides):
+ *   A      bf16   [M][K]
+ *   Wq     uint32 [N][K/8]   nibble i (bits 4i..4i+3) of word j holds q[n, 8j+i]
+ *   scale  bf16   [N][K/128]
+ *   bias   bf16   [N][K/128]
+ *   C      bf16   [M][N]
+ *   partials      [s][M][N]  bf16 (W4A16) or fp32 (dense)
+ *   dense  A bf16 [M][K], B bf16 [N][K], C = A . B^T
+ *
+ * Ownership and execution: every pointer except those of qmm_splitk_plan is a
+ * device pointer owned by the caller, including the workspace. The library
+ * never allocates, frees or synchronises; it enqueues its kernels on `stream`
+ * (a hipStream_t; NULL is the default stream) and returns. Results are defined
+ * once the stream reaches that point. C must not overlap any input or the
+ * workspace. Calls are thread-safe; the library holds no state.
+ *
+ * Errors: every entry point returns QMM_OK (0) or a negative QMM_ERR_* code.
+ * All argument checks happen on the host before any launch, so a call that
+ * returns an error has enqueued nothing and touched no memory. QMM_ERR_HIP
+ * reports a launch failure from the HIP runtime.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QMM_OK = 0,
+    QMM_ERR_ARG = -1,       /* NULL pointer, non-positive size, unknown dtype, group size != 128 */
+    QMM_ERR_SHAPE = -2,     /* K not a multiple of 128 (32 for dense), split not allowed for the shape */
+    QMM_ERR_ALIGN = -3,     /* A / Wq / B / workspace not 16-byte aligned, or an element misaligned */
+    QMM_ERR_WORKSPACE = -4, /* split requested and workspace NULL or smaller than needed */
+    QMM_ERR_HIP = -5,       /* a kernel launch failed (hipGetLastError) */
+    QMM_ERR_SIZE = -6       /* a size would overflow the library's 32-bit row/column indexing */
+};
+
+/* Partial-plane element types for qmm_splitk_reduce. */
+enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
+
+/*
+ * Occupancy policy (tiny-llm "Week 2 Day 7: Split-K Prefill", Task 3):
+ *     base = ceil(M / tile_m) * ceil(N / tile_n)
+ *     s    = min(cap, floor(target_blocks / base), floor(K / min_k_per_split), K/128)
+ *     while s > 1 and (K/128) % s != 0: s -= 1
+ *     s <= 1 -> the unsplit kernel
+ * tile_m / tile_n = 0 mean "the block tile of the kernel this library launches
+ * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
+ */
+typedef struct qmm_policy {
+    int tile_m;
+    int tile_n;
+    int target_blocks;
+    int cap;
+    int min_k_per_split;
+} qmm_policy;
+
+/* Result of qmm_splitk_plan. */
+typedef struct qmm_plan {
+    int s;                  /* chosen split count, >= 1; 1 = unsplit kernel, no workspace, no reduce */
+    int base_tiles;         /* ceil(M/tile_m) * ceil(N/tile_n) under the policy's tile */
+    int tile_m, tile_n;     /* tile the occupancy count used */
+    int grid_x, grid_y, grid_z; /* grid of the matmul kernel this library launches for (M,N,K,s) */
+    int block_m, block_n;   /* output tile of one workgroup of that kernel */
+    size_t workspace_bytes; /* 2*s*M*N for s > 1, else 0 */
+} qmm_plan;
+
+/* The page's rule: 32 x 32 tiles, 320 target blocks, cap 16, one group per partition. */
+extern const qmm_policy QMM_POLICY_PAGE;
+/* The rule re-tuned for MI355X (256 CUs); used when s = 0 is passed to qmm_w4a16_g128. */
+extern const qmm_policy QMM_POLICY_MI355X;
+
+/*
+ * qmm_splitk_plan -- pick the split count for an (M, N, K) W4A16 g128 matmul.
+ * Host only, pure: touches no device, allocates nothing.
+ *   group_size must be 128. policy NULL selects QMM_POLICY_MI355X.
+ *   Returns QMM_OK and fills *out, or QMM_ERR_ARG / QMM_ERR_SHAPE / QMM_ERR_SIZE.
+ */
+int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *policy, qmm_plan *out);
+
+/*
+ * qmm_w4a16_g128 -- C = A . dequant(W)^T (tiny-llm "Week 2 Day 7", the public
+ * matmul whose dispatcher picks the split and runs the partition and reduce kernels).
+ *   s = 0  : the split comes from qmm_splitk_plan(M, N, K, 128, NULL)
+ *   s = 1  : the unsplit kernel (the control; also what the policy falls back to)
+ *   s > 1  : explicit split; must divide K/128. Launches the split kernel, writing
+ *            bf16 partial planes [s][M][N] into `workspace`, then the reduce into C.
+ *   workspace / workspace_bytes: needed only when the effective s > 1; at least
+ *   2*s*M*N bytes, 16-byte aligned. May be NULL otherwise.
+ *   Alignment: A and Wq 16-byte aligned; scale, bias and C 2-byte aligned.
+ *   The effective s = 1 path is the same launch however it was reached, so its
+ *   result is bitwise identical for s = 0 (when the policy picks 1) and s = 1.
+ */
+int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                   int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qmm_splitk_reduce -- C[i] = bf16_rne( sum over p = 0..s-1, in this order, in fp32,
+ * of partials[p][i] ) for i < M*N (tiny-llm "Week 2 Day 7", Task 4: one output
+ * element per thread, FP32 sum, one cast to the model dtype).
+ *   partial_dtype: QMM_PARTIAL_BF16 or QMM_PARTIAL_F32. partials holds s planes of
+ *   M*N elements back to back, aligned to its element size. s >= 1.
+ */
+int qmm_splitk_reduce(const void *partials, int partial_dtype, int s, int M, int N, void *C,
+                      void *stream);
+
+/*
+ * qmm_bf16_splitk -- dense C = A . B^T with bf16 A[M][K], B[N][K], fp32 accumulation
+ * (gpu-kernels-explained "Split-K, streams and overlap", Concept: a small output
+ * with a long k cut into s slices, partial sums added by a second pass).
+ *   K must be a multiple of 32. The reduction is cut into s near-equal partitions of
+ *   32-value granules: partition p covers granules [floor(p*U/s), floor((p+1)*U/s)),
+ *   U = K/32, so any 1 <= s <= U is allowed.
+ *   s = 0 picks s with the MI355X occupancy rule over this kernel's tile.
+ *   s = 1 writes C directly; s > 1 writes fp32 partial planes [s][M][N] to the
+ *   workspace (>= 4*s*M*N bytes, 16-byte aligned), then reduces them into C.
+ *   A and B 16-byte aligned; C 2-byte aligned.
+ */
+int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int N, int K, int s,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *qmm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,171 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+They load libqmm.so, check that it exports every symbol include/qmm.h declares,
+exercise the host-only split plan against the oracle's statement of the page's
+rule, and check that every invalid call returns its error code before any
+launch. No call here reaches a kernel launch: each one fails validation first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import qmm_synth as syn
+import weight_only_quantized_qmm_amd as q
+from oracle import policy as opolicy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+# Fake, never-dereferenced device addresses for validation-only calls.
+ADDR = 0x7f0000000000
+ADDR2 = 0x7f0010000000
+ADDR3 = 0x7f0020000000
+
+
+def header_symbols():
+    text = open(HEADER).read()
+    funcs = set(re.findall(r"^\s*(?:int|const char \*)\s*(qmm_\w+)\s*\(", text, re.M))
+    data = set(re.findall(r"^extern const qmm_policy (\w+);", text, re.M))
+    return funcs, data
+
+
+def test_library_exports_every_declared_symbol():
+    funcs, data = header_symbols()
+    assert funcs == set(q.EXPORTED_FUNCTIONS)
+    assert data == set(q.EXPORTED_DATA)
+    L = q.lib()
+    for f in funcs:
+        assert hasattr(L, f), f
+    for d in data:
+        ctypes.c_int.in_dll(L, d)  # resolves the data symbol
+
+
+def test_status_strings():
+    for code in (q.QMM_OK, q.QMM_ERR_ARG, q.QMM_ERR_SHAPE, q.QMM_ERR_ALIGN, q.QMM_ERR_WORKSPACE,
+                 q.QMM_ERR_HIP, q.QMM_ERR_SIZE):
+        assert q.qmm_status_string(code).startswith("QMM")
+    assert "unknown" in q.qmm_status_string(12345)
+
+
+def test_page_preset_values():
+    assert q.policy_preset("QMM_POLICY_PAGE").as_dict() == dict(
+        tile_m=32, tile_n=32, target_blocks=320, cap=16, min_k_per_split=128)
+
+
+def _page_split_oracle(M, N, K, **kw):
+    r = dict(opolicy.PAGE_PRESET)
+    r.update(kw)
+    return opolicy.split_count(M, N, K, **r)
+
+
+ALL_SHAPES = ([(32, 1024, 2560), (48, 1000, 2560), (512, 512, 16384)]
+              + [(M, N, K) for _, M, N, K, _ in syn.projection_sweep()]
+              + [(M, N, K) for _, M, N, K, _ in syn.decode_sweep()]
+              + [(1, 1, 128), (3, 17, 256), (129, 4096, 9728), (7, 100000, 128)])
+
+
+@pytest.mark.parametrize("M,N,K", ALL_SHAPES)
+def test_plan_page_preset_matches_oracle_rule(M, N, K):
+    pol = q.policy_preset("QMM_POLICY_PAGE")
+    plan = q.qmm_splitk_plan(M, N, K, policy=pol)
+    assert plan.s == _page_split_oracle(M, N, K)
+    assert plan.base_tiles == opolicy.base_tiles(M, N, 32, 32)
+    assert plan.workspace_bytes == (2 * plan.s * M * N if plan.s > 1 else 0)
+
+
+def test_plan_tunables_follow_oracle_rule():
+    for target in (64, 320, 512, 1024, 4096):
+        for cap in (1, 4, 16, 32):
+            for min_k in (128, 256, 512, 1024):
+                pol = q.qmm_policy(16, 64, target, cap, min_k)
+                for M, N, K in ALL_SHAPES:
+                    got = q.qmm_splitk_plan(M, N, K, policy=pol).s
+                    assert got == opolicy.split_count(M, N, K, tile_m=16, tile_n=64, target=target, cap=cap,
+                                                      min_k_per_split=min_k), (M, N, K, target, cap, min_k)
+
+
+@pytest.mark.parametrize("M,N,K", ALL_SHAPES)
+def test_plan_mi355x_preset_is_valid(M, N, K):
+    pol = q.policy_preset("QMM_POLICY_MI355X")
+    plan = q.qmm_splitk_plan(M, N, K)
+    G = K // 128
+    assert 1 <= plan.s <= min(pol.cap, G) and G % plan.s == 0
+    assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
+    assert plan.tile_m == plan.block_m and plan.tile_n == plan.block_n
+    assert plan.base_tiles == -(-M // plan.block_m) * -(-N // plan.block_n)
+    assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.block_n,
+                                         target=pol.target_blocks, cap=pol.cap,
+                                         min_k_per_split=pol.min_k_per_split)
+    assert plan.grid_z == plan.s
+    assert plan.grid_x * plan.block_n >= N and plan.grid_y * plan.block_m >= M
+
+
+def test_plan_rejects_bad_arguments():
+    for args, code in [((0, 8, 128), q.QMM_ERR_ARG), ((8, 0, 128), q.QMM_ERR_ARG), ((8, 8, 0), q.QMM_ERR_ARG),
+                       ((8, 8, 200), q.QMM_ERR_SHAPE)]:
+        with pytest.raises(q.QmmError) as e:
+            q.qmm_splitk_plan(*args)
+        assert e.value.status == code
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_splitk_plan(8, 8, 128, group_size=64)
+    assert e.value.status == q.QMM_ERR_ARG
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_splitk_plan(8, 8, 128, policy=q.qmm_policy(32, 32, 320, 0, 128))
+    assert e.value.status == q.QMM_ERR_ARG
+
+
+def _w4(**kw):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=32, N=1024, K=2560, s=1,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    return q.qmm_w4a16_g128(a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"], a["s"],
+                            a["workspace"], a["workspace_bytes"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(Wq=None), q.QMM_ERR_ARG), (dict(scale=None), q.QMM_ERR_ARG),
+    (dict(bias=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG),
+    (dict(M=0), q.QMM_ERR_ARG), (dict(N=-1), q.QMM_ERR_ARG), (dict(K=0), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG),
+    (dict(K=2500), q.QMM_ERR_SHAPE), (dict(s=3), q.QMM_ERR_SHAPE), (dict(s=40), q.QMM_ERR_SHAPE),
+    (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(Wq=ADDR2 + 4), q.QMM_ERR_ALIGN), (dict(C=ADDR + 1), q.QMM_ERR_ALIGN),
+    (dict(scale=ADDR3 + 1), q.QMM_ERR_ALIGN),
+    (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024 - 2), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x200008, workspace_bytes=2 * 4 * 32 * 1024), q.QMM_ERR_ALIGN),
+    (dict(M=1 << 30, N=1 << 30), q.QMM_ERR_SIZE),
+])
+def test_w4a16_rejects_before_launch(kw, code):
+    assert _w4(**kw) == code
+
+
+def test_w4a16_policy_split_needs_workspace():
+    # s = 0 resolves through the MI355X plan; where it splits, no workspace is an error
+    M, N, K = 16, 1024, 2560
+    if q.qmm_splitk_plan(M, N, K).s > 1:
+        assert _w4(M=M, N=N, K=K, s=0) == q.QMM_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 0, 2, 4, 4, ADDR), q.QMM_ERR_ARG), ((ADDR, 0, 2, 4, 4, None), q.QMM_ERR_ARG),
+    ((ADDR, 2, 2, 4, 4, ADDR2), q.QMM_ERR_ARG), ((ADDR, 0, 0, 4, 4, ADDR2), q.QMM_ERR_ARG),
+    ((ADDR, 0, 2, 0, 4, ADDR2), q.QMM_ERR_ARG), ((ADDR + 1, 0, 2, 4, 4, ADDR2), q.QMM_ERR_ALIGN),
+    ((ADDR + 2, 1, 2, 4, 4, ADDR2), q.QMM_ERR_ALIGN), ((ADDR, 0, 2, 4, 4, ADDR2 + 1), q.QMM_ERR_ALIGN),
+])
+def test_reduce_rejects_before_launch(args, code):
+    assert q.qmm_splitk_reduce(*args, stream=0, check=False) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(B=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG),
+    (dict(K=100), q.QMM_ERR_SHAPE), (dict(s=513), q.QMM_ERR_SHAPE), (dict(M=-2), q.QMM_ERR_ARG),
+    (dict(A=ADDR + 4), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR3, workspace_bytes=4 * 4 * 512 * 512 - 4), q.QMM_ERR_WORKSPACE),
+])
+def test_dense_rejects_before_launch(kw, code):
+    a = dict(A=ADDR, B=ADDR2, C=ADDR + 0x100000, M=512, N=512, K=16384, s=1, workspace=None, workspace_bytes=0)
+    a.update(kw)
+    rc = q.qmm_bf16_splitk(a["A"], a["B"], a["C"], a["M"], a["N"], a["K"], a["s"], a["workspace"],
+                           a["workspace_bytes"], stream=0, check=False)
+    assert rc == code

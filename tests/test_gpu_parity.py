@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case uses the seeded inputs of qmm_synth, runs the library through its
+ctypes binding on the current torch stream, and compares with the oracle:
+  * split and unsplit W4A16 results within |gpu-ref| <= 0.02|ref| + 0.02 rms(ref);
+  * the s = 1 fallback bitwise equal to the explicit unsplit kernel;
+  * the reduce kernel bitwise equal to the oracle's fp32 sum + one bf16 cast;
+  * closed forms that are exact in bf16 (zero weights, one-hot rows) bitwise;
+  * determinism and untouched guard bands around C and the workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qmm_synth as syn
+import weight_only_quantized_qmm_amd as q
+from gpu_util import (check_tolerance, dev_bf16, dev_u32, host_bits, host_f64, sample_points,
+                      w4a16_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_w4a16(dv, M, N, K, s, guard=0):
+    """Run the library; returns C (bf16 device tensor). guard > 0 wraps C and the workspace
+    in canary regions of that many elements and checks them afterwards."""
+    s_eff = q.effective_split(M, N, K, s)
+    Cbuf = torch.full((M * N + 2 * guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    C = Cbuf[guard:guard + M * N].view(M, N)
+    ws = None
+    wbuf = None
+    if s_eff > 1:
+        nws = s_eff * M * N
+        gw = ((guard + 7) // 8) * 8  # keep the workspace 16-byte aligned
+        wbuf = torch.full((nws + 2 * gw,), -777.0, dtype=torch.bfloat16, device="cuda")
+        ws = wbuf[gw:gw + nws]
+    q.qmm_w4a16_g128(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws)
+    torch.cuda.synchronize()
+    if guard:
+        g = host_bits(Cbuf)
+        canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+        assert np.all(g[:guard] == canary) and np.all(g[guard + M * N:] == canary), "C guard band written"
+        if wbuf is not None:
+            w = host_bits(wbuf)
+            wc = host_bits(torch.tensor([-777.0], dtype=torch.bfloat16))[0]
+            assert np.all(w[:gw] == wc) and np.all(w[gw + s_eff * M * N:] == wc), "workspace guard written"
+    return C
+
+
+# ------------------------------------------------------------------ config 0 / 1
+
+@pytest.fixture(scope="module")
+def cfg0():
+    M, N, K = 32, 1024, 2560
+    d = syn.w4a16_inputs(M, N, K, seed=0)
+    return M, N, K, d, oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+
+
+@pytest.mark.parametrize("s", [1, 4, 0])
+def test_cfg0_k_projection(cfg0, s):
+    M, N, K, d, ref = cfg0
+    say("cfg0 M=%d N=%d K=%d s=%d" % (M, N, K, s))
+    C = run_w4a16(w4a16_device(d), M, N, K, s, guard=64)
+    check_tolerance(host_f64(C), ref, what="cfg0 s=%d" % s)
+
+
+@pytest.fixture(scope="module")
+def cfg1():
+    M, N, K = 48, 1000, 2560
+    d = syn.w4a16_inputs(M, N, K, seed=1000)
+    return M, N, K, d, oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+
+
+@pytest.mark.parametrize("s", [1, 2, 4, 5, 10, 20])
+def test_cfg1_partial_tile_split_sweep(cfg1, s):
+    M, N, K, d, ref = cfg1
+    say("cfg1 M=%d N=%d K=%d s=%d" % (M, N, K, s))
+    C = run_w4a16(w4a16_device(d), M, N, K, s, guard=64)
+    check_tolerance(host_f64(C), ref, what="cfg1 s=%d" % s)
+
+
+def test_cfg1_unsplit_equals_policy_when_policy_is_one(cfg1):
+    M, N, K, d, _ = cfg1
+    dv = w4a16_device(d)
+    a = host_bits(run_w4a16(dv, M, N, K, 1))
+    b = host_bits(run_w4a16(dv, M, N, K, 1))
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------- config 2 (sweep)
+
+SWEEP = syn.projection_sweep()
+
+
+@pytest.mark.parametrize("name,M,N,K,idx", SWEEP, ids=["%s-M%d" % (n, m) for n, m, _, _, _ in SWEEP])
+def test_cfg2_projection_sweep(name, M, N, K, idx):
+    seed = 2000 + idx
+    d = syn.w4a16_inputs(M, N, K, seed=seed)
+    dv = w4a16_device(d)
+    s_pol = q.effective_split(M, N, K, 0)
+    say("cfg2 %s M=%d N=%d K=%d policy s=%d" % (name, M, N, K, s_pol))
+    C = run_w4a16(dv, M, N, K, 0)
+    C1 = run_w4a16(dv, M, N, K, 1)
+    got, got1 = host_f64(C), host_f64(C1)
+    if M <= 32:
+        ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+        check_tolerance(got, ref, what="%s M=%d policy" % (name, M))
+        check_tolerance(got1, ref, what="%s M=%d unsplit" % (name, M))
+    else:
+        ms, ns = sample_points(M, N, seed)
+        ref = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+        check_tolerance(got[ms, ns], ref, what="%s M=%d policy (sampled)" % (name, M))
+        check_tolerance(got1[ms, ns], ref, what="%s M=%d unsplit (sampled)" % (name, M))
+    if s_pol == 1:
+        # the policy's fallback is the unsplit kernel, bit for bit
+        assert np.array_equal(host_bits(C), host_bits(C1))
+
+
+# ----------------------------------------------------------- config 3 (dense)
+
+@pytest.fixture(scope="module")
+def cfg3():
+    M, N, K = 512, 512, 16384
+    d = syn.dense_inputs(M, N, K, seed=3000)
+    return M, N, K, d, oracle.qmm_dense(d["A"], d["B"], M, N, K)
+
+
+@pytest.mark.parametrize("s", [1, 2, 4, 6, 8, 12, 16, 32])
+def test_cfg3_dense_split_sweep(cfg3, s):
+    M, N, K, d, ref = cfg3
+    say("cfg3 dense M=%d N=%d K=%d s=%d" % (M, N, K, s))
+    A, B = dev_bf16(d["A"]), dev_bf16(d["B"])
+    C = q.bf16_splitk(A, B, s=s)
+    torch.cuda.synchronize()
+    check_tolerance(host_f64(C), ref, what="dense s=%d" % s)
+
+
+def test_dense_ragged_and_reduce_fp32():
+    M, N, K = 37, 45, 32 * 70
+    d = syn.dense_inputs(M, N, K, seed=3001)
+    ref = oracle.qmm_dense(d["A"], d["B"], M, N, K)
+    A, B = dev_bf16(d["A"]), dev_bf16(d["B"])
+    for s in (1, 3, 7, 70):
+        say("dense ragged M=%d N=%d K=%d s=%d" % (M, N, K, s))
+        C = q.bf16_splitk(A, B, s=s)
+        torch.cuda.synchronize()
+        check_tolerance(host_f64(C), ref, what="dense ragged s=%d" % s)
+
+
+# ----------------------------------------------------------- config 4 (decode)
+
+DECODE = syn.decode_sweep()
+
+
+@pytest.mark.parametrize("name,M,N,K,idx", DECODE, ids=["%s-M%d" % (n, m) for n, m, _, _, _ in DECODE])
+def test_cfg4_decode(name, M, N, K, idx):
+    d = syn.w4a16_inputs(M, N, K, seed=4000 + idx)
+    dv = w4a16_device(d)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    G = K // 128
+    valid = [s for s in range(1, G + 1) if G % s == 0 and K // s >= 512]
+    for s in valid + [0]:
+        say("cfg4 %s M=%d N=%d K=%d s=%d" % (name, M, N, K, s))
+        C = run_w4a16(dv, M, N, K, s, guard=32)
+        check_tolerance(host_f64(C), ref, what="%s M=%d s=%d" % (name, M, s))
+
+
+# ---------------------------------------------------------------- reduce
+
+@pytest.mark.parametrize("s,M,N", [(1, 16, 1024), (2, 32, 1024), (5, 48, 1000), (20, 7, 33), (32, 1, 9),
+                                   (10, 128, 2560), (3, 2048, 1024)])
+def test_reduce_bf16_bitexact(s, M, N):
+    say("reduce bf16 s=%d M=%d N=%d" % (s, M, N))
+    planes = syn.bf16_planes(s, M, N, seed=5000 + s + M + N, sigma=3.0)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    q.qmm_splitk_reduce(dev_bf16(planes), q.QMM_PARTIAL_BF16, s, M, N, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out).ravel(), oracle.reduce_bf16(planes, s, M * N))
+
+
+@pytest.mark.parametrize("s,M,N", [(1, 8, 8), (6, 512, 512), (32, 5, 7), (12, 3, 1001)])
+def test_reduce_f32_bitexact(s, M, N):
+    say("reduce f32 s=%d M=%d N=%d" % (s, M, N))
+    planes = syn.f32_planes(s, M, N, seed=5100 + s, sigma=40.0)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    q.qmm_splitk_reduce(torch.from_numpy(planes).cuda(), q.QMM_PARTIAL_F32, s, M, N, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out).ravel(), oracle.reduce_f32(planes, s, M * N))
+
+
+# ---------------------------------------------------------- exact closed forms
+
+@pytest.mark.parametrize("s", [1, 2, 4, 5, 10, 20])
+def test_zero_weights_give_exact_zero(s):
+    M, N, K = 24, 200, 2560
+    d = syn.w4a16_inputs(M, N, K, seed=6000)
+    d["Wq"] = np.full_like(d["Wq"], 0x88888888)  # q == 8, bias = -8*scale -> w == 0
+    say("zero weights s=%d" % s)
+    C = run_w4a16(w4a16_device(d), M, N, K, s)
+    bits = host_bits(C)
+    assert np.all((bits == 0) | (bits == 0x8000))
+
+
+@pytest.mark.parametrize("s", [1, 2, 4, 5, 10, 20])
+def test_one_hot_rows_give_exact_weights(s):
+    """A[m, k_m] = 1: C[m, n] = w[n, k_m] exactly (one nonzero partial; bf16 of an exact
+    fp32 value). Pins the nibble order, scale/bias indexing and the partition bounds."""
+    M, N, K = 40, 130, 2560
+    d = syn.w4a16_inputs(M, N, K, seed=6001)
+    rng = np.random.default_rng(6001)
+    ks = rng.choice(K, size=M, replace=False)
+    ks[:8] = [0, 7, 8, 127, 128, 1279, 1280, 2559]
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), ks] = 0x3F80
+    d["A"] = A
+    say("one-hot s=%d" % s)
+    C = run_w4a16(w4a16_device(d), M, N, K, s, guard=16)
+    w = oracle.dequant_w4a16(d["Wq"], d["scale"], d["bias"], N, K)
+    expect = oracle.bf16_round_array(w[:, ks].T)
+    got = host_bits(C).copy()
+    got[got == 0x8000] = 0  # the sign of an exact zero is not part of the definition
+    expect[expect == 0x8000] = 0
+    assert np.array_equal(got, expect)
+
+
+def test_determinism_two_runs():
+    M, N, K = 16, 9728, 2560
+    d = syn.w4a16_inputs(M, N, K, seed=6002)
+    dv = w4a16_device(d)
+    for s in (1, 4, 10):
+        say("determinism s=%d" % s)
+        a = host_bits(run_w4a16(dv, M, N, K, s))
+        b = host_bits(run_w4a16(dv, M, N, K, s))
+        assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------- edge shapes
+
+EDGE = [(1, 1, 128, 1), (1, 17, 256, 2), (3, 33, 384, 3), (15, 100, 512, 4), (17, 64, 1024, 8),
+        (129, 70, 256, 2), (130, 1001, 640, 5), (2048, 16, 128, 1), (8, 4100, 1280, 10)]
+
+
+@pytest.mark.parametrize("M,N,K,s", EDGE)
+def test_edge_shapes(M, N, K, s):
+    d = syn.w4a16_inputs(M, N, K, seed=7000 + M + N + K)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for ss in sorted({1, s, 0}):
+        say("edge M=%d N=%d K=%d s=%d" % (M, N, K, ss))
+        C = run_w4a16(dv, M, N, K, ss, guard=40)
+        check_tolerance(host_f64(C), ref, what="edge %dx%dx%d s=%d" % (M, N, K, ss))
+
+
+def test_error_leaves_output_untouched():
+    M, N, K = 16, 64, 256
+    d = syn.w4a16_inputs(M, N, K, seed=7100)
+    dv = w4a16_device(d)
+    C = torch.full((M, N), 3.0, dtype=torch.bfloat16, device="cuda")
+    rc = q.qmm_w4a16_g128(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, 2, None, check=False)
+    assert rc == q.QMM_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(C == 3.0)

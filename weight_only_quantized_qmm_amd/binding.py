@@ -1,0 +1,190 @@
+"""ctypes binding of libqmm.so (include/qmm.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors are passed as device pointers and
+torch's current HIP stream is passed as the stream; every step of the matmul
+runs in the library's kernels. PyTorch is used for device memory and streams.
+The library must be built (``python -m weight_only_quantized_qmm_amd.build``);
+if it is missing, every call raises -- there is no fallback implementation.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmm.so")
+
+QMM_OK = 0
+QMM_ERR_ARG = -1
+QMM_ERR_SHAPE = -2
+QMM_ERR_ALIGN = -3
+QMM_ERR_WORKSPACE = -4
+QMM_ERR_HIP = -5
+QMM_ERR_SIZE = -6
+QMM_PARTIAL_BF16 = 0
+QMM_PARTIAL_F32 = 1
+
+# Every symbol include/qmm.h declares.
+EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
+                      "qmm_status_string")
+EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s returned %d (%s)" % (where, status, qmm_status_string(status)))
+
+
+class qmm_policy(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("target_blocks", ctypes.c_int),
+                ("cap", ctypes.c_int), ("min_k_per_split", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class qmm_plan(ctypes.Structure):
+    _fields_ = [("s", ctypes.c_int), ("base_tiles", ctypes.c_int), ("tile_m", ctypes.c_int),
+                ("tile_n", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
+                ("grid_z", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded libqmm.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libqmm.so is not built (%s); run python -m weight_only_quantized_qmm_amd.build"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        I, P, S = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.qmm_splitk_plan.argtypes = [I, I, I, I, ctypes.POINTER(qmm_policy), ctypes.POINTER(qmm_plan)]
+        L.qmm_splitk_plan.restype = I
+        L.qmm_w4a16_g128.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.qmm_w4a16_g128.restype = I
+        L.qmm_splitk_reduce.argtypes = [P, I, I, I, I, P, P]
+        L.qmm_splitk_reduce.restype = I
+        L.qmm_bf16_splitk.argtypes = [P, P, P, I, I, I, I, P, S, P]
+        L.qmm_bf16_splitk.restype = I
+        L.qmm_status_string.argtypes = [I]
+        L.qmm_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def qmm_status_string(status):
+    return lib().qmm_status_string(int(status)).decode()
+
+
+def policy_preset(name):
+    """QMM_POLICY_PAGE or QMM_POLICY_MI355X as a qmm_policy value."""
+    if name not in EXPORTED_DATA:
+        raise KeyError(name)
+    p = qmm_policy.in_dll(lib(), name)
+    return qmm_policy(p.tile_m, p.tile_n, p.target_blocks, p.cap, p.min_k_per_split)
+
+
+def qmm_splitk_plan(M, N, K, group_size=128, policy=None):
+    """Host-only plan (no device); returns a qmm_plan, raises QmmError on a bad shape."""
+    out = qmm_plan()
+    pol = ctypes.byref(policy) if policy is not None else None
+    rc = lib().qmm_splitk_plan(int(M), int(N), int(K), int(group_size), pol, ctypes.byref(out))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_splitk_plan")
+    return out
+
+
+def _ptr(x):
+    """Device pointer of a tensor (or an int address / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t):
+    if t is None:
+        return 0
+    return t.numel() * t.element_size()
+
+
+def qmm_w4a16_g128(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
+                   stream=None, check=True):
+    """C = A . dequant(W)^T on `stream` (torch's current stream by default); returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_w4a16_g128(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                              int(s), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_g128")
+    return rc
+
+
+def qmm_splitk_reduce(partials, partial_dtype, s, M, N, C, stream=None, check=True):
+    rc = lib().qmm_splitk_reduce(_ptr(partials), int(partial_dtype), int(s), int(M), int(N), _ptr(C),
+                                 _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_splitk_reduce")
+    return rc
+
+
+def qmm_bf16_splitk(A, B, C, M, N, K, s=0, workspace=None, workspace_bytes=None, stream=None, check=True):
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_bf16_splitk(_ptr(A), _ptr(B), _ptr(C), int(M), int(N), int(K), int(s), _ptr(workspace),
+                               int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_bf16_splitk")
+    return rc
+
+
+# ---------------------------------------------------------------- conveniences
+
+def w4a16_workspace_bytes(M, N, s):
+    return 2 * s * M * N if s > 1 else 0
+
+
+def effective_split(M, N, K, s=0):
+    return qmm_splitk_plan(M, N, K).s if s == 0 else s
+
+
+def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None):
+    """Allocating wrapper: A bf16[M,K], Wq int32/uint32[N,K/8], scale/bias bf16[N,K/128] -> C bf16[M,N]."""
+    import torch
+    M, K = A.shape
+    N = Wq.shape[0]
+    s_eff = effective_split(M, N, K, s)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if s_eff > 1 and workspace is None:
+        workspace = torch.empty(w4a16_workspace_bytes(M, N, s_eff), dtype=torch.uint8, device=A.device)
+    qmm_w4a16_g128(A, Wq, scale, bias, out, M, N, K, s_eff, workspace)
+    return out
+
+
+def bf16_splitk(A, B, s=1, out=None, workspace=None):
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if s > 1 and workspace is None:
+        workspace = torch.empty(4 * s * M * N, dtype=torch.uint8, device=A.device)
+    qmm_bf16_splitk(A, B, out, M, N, K, s, workspace)
+    return out

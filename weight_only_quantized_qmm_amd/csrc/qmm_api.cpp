@@ -1,0 +1,201 @@
+// qmm_api.cpp -- the C ABI declared in include/qmm.h: argument checks, the split
+// policy, and the dispatch of the gfx950 kernels.
+//
+// tiny-llm "Week 2 Day 7: Split-K Prefill", Task 3 and Task 4: the dispatcher
+// picks the partition count from occupancy, dispatches the partition kernel and
+// then the reduction, and uses the unsplit kernel unchanged when the count is 1.
+// Every check below runs on the host before any launch, so an error return has
+// no device side effect.
+#include "qmm.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "qmm_launch.h"
+
+using qmm_impl::DenseTile;
+using qmm_impl::W4A16Tile;
+
+extern "C" {
+const qmm_policy QMM_POLICY_PAGE = {32, 32, 320, 16, 128};
+const qmm_policy QMM_POLICY_MI355X = {0, 0, 512, 16, 512};
+}
+
+namespace {
+
+constexpr int kGroup = 128;
+constexpr int kGranule = 32;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+// Block tile of the W4A16 kernel used for an M-row problem: the whole M (up to
+// 128 rows) in one block row, so each weight is dequantised once per block.
+W4A16Tile w4a16_tile(int M, int /*N*/) {
+    W4A16Tile t;
+    t.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    t.ns = 2;
+    return t;
+}
+
+DenseTile dense_tile(int /*M*/, int /*N*/) {
+    DenseTile t;
+    t.mt = 4;
+    t.ns = 4;
+    return t;
+}
+
+// Sizes the kernels index with 32-bit row/column counters and 64-bit offsets.
+bool sizes_ok(int M, int N, int K) {
+    if ((long long)M * (long long)N > (long long)INT_MAX * 64) return false;
+    if ((long long)N * (long long)K > (long long)INT_MAX * 64) return false;
+    if ((long long)M * (long long)K > (long long)INT_MAX * 64) return false;
+    return true;
+}
+
+int split_rule(long long base, int G, int K, const qmm_policy &pol) {
+    long long s = pol.cap;
+    const long long by_target = pol.target_blocks / base;
+    if (by_target < s) s = by_target;
+    const long long by_k = K / pol.min_k_per_split;
+    if (by_k < s) s = by_k;
+    if (G < s) s = G;
+    while (s > 1 && G % s != 0) --s;
+    return s < 1 ? 1 : (int)s;
+}
+
+bool policy_ok(const qmm_policy &p) {
+    return p.tile_m >= 0 && p.tile_n >= 0 && p.target_blocks >= 0 && p.cap >= 1 && p.min_k_per_split >= 1;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *policy,
+                               qmm_plan *out)
+{
+    if (!out || M <= 0 || N <= 0 || K <= 0 || group_size != kGroup) return QMM_ERR_ARG;
+    if (K % kGroup != 0) return QMM_ERR_SHAPE;
+    if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
+    const qmm_policy pol = policy ? *policy : QMM_POLICY_MI355X;
+    if (!policy_ok(pol)) return QMM_ERR_ARG;
+    const W4A16Tile tile = w4a16_tile(M, N);
+    const int tm = pol.tile_m > 0 ? pol.tile_m : tile.block_m();
+    const int tn = pol.tile_n > 0 ? pol.tile_n : tile.block_n();
+    const long long base = ceil_div(M, tm) * ceil_div(N, tn);
+    const int G = K / kGroup;
+    const int s = split_rule(base, G, K, pol);
+    out->s = s;
+    out->base_tiles = base > INT_MAX ? INT_MAX : (int)base;
+    out->tile_m = tm;
+    out->tile_n = tn;
+    out->grid_x = (int)ceil_div(N, tile.block_n());
+    out->grid_y = (int)ceil_div(M, tile.block_m());
+    out->grid_z = s;
+    out->block_m = tile.block_m();
+    out->block_n = tile.block_n();
+    out->workspace_bytes = s > 1 ? (size_t)2 * (size_t)s * (size_t)M * (size_t)N : 0;
+    return QMM_OK;
+}
+
+extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void *bias,
+                              void *C, int M, int N, int K, int s, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (!A || !Wq || !scale || !bias || !C) return QMM_ERR_ARG;
+    if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
+    if (K % kGroup != 0) return QMM_ERR_SHAPE;
+    if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
+    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
+        return QMM_ERR_ALIGN;
+    const int G = K / kGroup;
+    if (s == 0) {
+        qmm_plan plan;
+        const int rc = qmm_splitk_plan(M, N, K, kGroup, nullptr, &plan);
+        if (rc != QMM_OK) return rc;
+        s = plan.s;
+    } else if (s > G || G % s != 0) {
+        return QMM_ERR_SHAPE;
+    }
+    const size_t MN = (size_t)M * (size_t)N;
+    if (s > 1) {
+        if (!workspace || workspace_bytes < 2 * (size_t)s * MN) return QMM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+    }
+    const W4A16Tile tile = w4a16_tile(M, N);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s == 1) {
+        const bool vec = (N % 4 == 0) && aligned(C, 8);
+        return hip_status(qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, C, M, N, K, 1, vec, st));
+    }
+    const bool vec_ws = (N % 4 == 0);
+    int rc = hip_status(qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
+    if (rc != QMM_OK) return rc;
+    const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
+    return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
+}
+
+extern "C" int qmm_splitk_reduce(const void *partials, int partial_dtype, int s, int M, int N, void *C,
+                                 void *stream)
+{
+    if (!partials || !C || s < 1 || M <= 0 || N <= 0) return QMM_ERR_ARG;
+    if (partial_dtype != QMM_PARTIAL_BF16 && partial_dtype != QMM_PARTIAL_F32) return QMM_ERR_ARG;
+    if ((long long)M * (long long)N > (long long)INT_MAX * 64) return QMM_ERR_SIZE;
+    const bool f32 = partial_dtype == QMM_PARTIAL_F32;
+    if (!aligned(partials, f32 ? 4 : 2) || !aligned(C, 2)) return QMM_ERR_ALIGN;
+    const size_t MN = (size_t)M * (size_t)N;
+    const bool vec = (MN % 8 == 0) && aligned(partials, 16) && aligned(C, 16);
+    return hip_status(qmm_impl::launch_reduce(partials, f32, s, MN, C, vec, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int N, int K, int s,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!A || !B || !C) return QMM_ERR_ARG;
+    if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
+    if (K % kGranule != 0) return QMM_ERR_SHAPE;
+    if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 2)) return QMM_ERR_ALIGN;
+    const int U = K / kGranule;
+    const DenseTile tile = dense_tile(M, N);
+    if (s == 0) {
+        // The occupancy rule over this kernel's tile: fill one wave of workgroups.
+        const long long base = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n());
+        long long t = 256 / base;
+        if (t > 32) t = 32;
+        if (t > U) t = U;
+        s = t < 1 ? 1 : (int)t;
+    } else if (s > U) {
+        return QMM_ERR_SHAPE;
+    }
+    const size_t MN = (size_t)M * (size_t)N;
+    if (s > 1) {
+        if (!workspace || workspace_bytes < 4 * (size_t)s * MN) return QMM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s == 1) {
+        const bool vec = (N % 4 == 0) && aligned(C, 8);
+        return hip_status(qmm_impl::launch_dense(tile, A, B, C, false, M, N, K, 1, vec, st));
+    }
+    int rc = hip_status(qmm_impl::launch_dense(tile, A, B, workspace, true, M, N, K, s, N % 4 == 0, st));
+    if (rc != QMM_OK) return rc;
+    const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
+    return hip_status(qmm_impl::launch_reduce(workspace, true, s, MN, C, vec_red, st));
+}
+
+extern "C" const char *qmm_status_string(int status)
+{
+    switch (status) {
+    case QMM_OK: return "QMM_OK";
+    case QMM_ERR_ARG: return "QMM_ERR_ARG: null pointer, non-positive size or bad argument";
+    case QMM_ERR_SHAPE: return "QMM_ERR_SHAPE: K not a multiple of the group/granule, or split not allowed";
+    case QMM_ERR_ALIGN: return "QMM_ERR_ALIGN: pointer not aligned as required";
+    case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or too small for the split";
+    case QMM_ERR_HIP: return "QMM_ERR_HIP: kernel launch failed";
+    case QMM_ERR_SIZE: return "QMM_ERR_SIZE: problem too large for the library's indexing";
+    default: return "QMM: unknown status";
+    }
+}

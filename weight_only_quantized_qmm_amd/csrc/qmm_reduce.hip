@@ -1,0 +1,101 @@
+// qmm_reduce.hip -- the split-K merge pass for gfx950.
+//
+// C[i] = bf16( ((P[0][i] + P[1][i]) + ...) + P[s-1][i] ), every addition in fp32,
+// one round-to-nearest-even cast at the end (tiny-llm "Week 2 Day 7: Split-K
+// Prefill", Task 4: one output element per thread, FP32 sum of all partitions,
+// a single cast to the model dtype). The planes are s contiguous arrays of
+// M*N elements; the sum runs in ascending partition order so that the result
+// is reproducible bit for bit.
+//
+// MI355X layout: the op is a pure stream (reads s*M*N partial elements, writes
+// M*N outputs), so each lane owns eight consecutive outputs and moves them with
+// 128-bit loads and stores (one 16-byte load per bf16 plane, two per fp32 plane).
+// The scalar variant handles element counts or pointers that are not 16-byte
+// multiples, one output per lane.
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+using namespace qmm_dev;
+
+namespace {
+
+__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
+    const uint4 x = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ void load8(const float *p, float v[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load1(const float *p) { return *p; }
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+reduce_vec8(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_t MN)
+{
+    const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i >= MN) return;  // MN is a multiple of 8 on this path
+    float acc[8];
+    load8(part + i, acc);
+    for (int p = 1; p < s; ++p) {
+        float v[8];
+        load8(part + (size_t)p * MN + i, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4 *>(C + i) = o;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+reduce_scalar(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_t MN)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= MN) return;
+    float acc = load1(part + i);
+    for (int p = 1; p < s; ++p) acc = acc + load1(part + (size_t)p * MN + i);
+    C[i] = (uint16_t)f32_to_bf16(acc);
+}
+
+template <typename T>
+hipError_t launch_t(const T *part, int s, size_t MN, uint16_t *C, bool vec, hipStream_t stream)
+{
+    const size_t per_thread = vec ? 8 : 1;
+    const size_t threads = (MN + per_thread - 1) / per_thread;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    (void)hipGetLastError();
+    if (vec)
+        hipLaunchKernelGGL((reduce_vec8<T>), grid, dim3(256), 0, stream, part, C, s, MN);
+    else
+        hipLaunchKernelGGL((reduce_scalar<T>), grid, dim3(256), 0, stream, part, C, s, MN);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace qmm_impl {
+
+hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t MN, void *C,
+                         bool vec, hipStream_t stream)
+{
+    if (f32_partials)
+        return launch_t(static_cast<const float *>(partials), s, MN, static_cast<uint16_t *>(C), vec, stream);
+    return launch_t(static_cast<const uint16_t *>(partials), s, MN, static_cast<uint16_t *>(C), vec, stream);
+}
+
+}  // namespace qmm_impl

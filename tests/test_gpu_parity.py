@@ -264,3 +264,46 @@ def test_error_leaves_output_untouched():
     assert rc == q.QMM_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(C == 3.0)
+
+
+# ------------------------------------------------------------ graph capture
+
+def test_graph_capture_replays_match_eager():
+    """The library enqueues only kernels (no memsets, no allocation), so a HIP graph of
+    its calls replays to the eager result bit for bit, replay after replay."""
+    cases = [(16, 1024, 2560, 5), (32, 9728, 2560, 1), (48, 1000, 2560, 4)]
+    bufs = []
+    for i, (M, N, K, s) in enumerate(cases):
+        d = syn.w4a16_inputs(M, N, K, seed=8000 + i)
+        dv = w4a16_device(d)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(2 * s * M * N, 16), dtype=torch.uint8, device="cuda")
+        bufs.append((M, N, K, s, dv, C, ws))
+
+    def step():
+        for M, N, K, s, dv, C, ws in bufs:
+            q.qmm_w4a16_g128(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws if s > 1 else None)
+
+    say("graph: eager reference")
+    step()
+    torch.cuda.synchronize()
+    eager = [host_bits(b[5]).copy() for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for b in bufs:
+            b[5].fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        say("graph: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for b, e in zip(bufs, eager):
+            assert np.array_equal(host_bits(b[5]), e), "replay %d differs" % rep

@@ -99,7 +99,7 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
                                          target=pol.target_blocks, cap=pol.cap,
                                          min_k_per_split=pol.min_k_per_split)
     assert plan.grid_z == plan.s
-    assert plan.grid_x * plan.block_n >= N and plan.grid_y * plan.block_m >= M
+    assert plan.grid_x * plan.grid_y == -(-M // plan.block_m) * -(-N // plan.block_n)
 
 
 def test_plan_rejects_bad_arguments():

@@ -34,9 +34,28 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // 128 rows) in one block row, so each weight is dequantised once per block.
 W4A16Tile w4a16_tile(int M, int /*N*/) {
     W4A16Tile t;
-    t.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+    if (M <= 64) {
+        t.kind = qmm_impl::W4A16_SKINNY;
+        t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    } else if (M <= 128) {
+        t.kind = qmm_impl::W4A16_NARROW;
+        t.mt = 8;
+    } else {
+        t.kind = qmm_impl::W4A16_WIDE;
+        t.mt = 16;
+    }
     t.ns = 2;
     return t;
+}
+
+hipError_t dispatch_w4a16(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
+                        void *out, int M, int N, int K, int s, bool vec, hipStream_t st) {
+    if (tile.kind == qmm_impl::W4A16_WIDE) return qmm_impl::launch_w4a16_wide(A, Wq, scale, bias, out, M, N, K, s, vec, st);
+    if (tile.kind == qmm_impl::W4A16_SKINNY) {
+        const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, (K / kGroup) / s);
+        return qmm_impl::launch_w4a16_skinny(tile.mt, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s, vec, st);
+    }
+    return qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, out, M, N, K, s, vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {
@@ -91,8 +110,13 @@ extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_po
     out->base_tiles = base > INT_MAX ? INT_MAX : (int)base;
     out->tile_m = tm;
     out->tile_n = tn;
-    out->grid_x = (int)ceil_div(N, tile.block_n());
-    out->grid_y = (int)ceil_div(M, tile.block_m());
+    if (tile.kind == qmm_impl::W4A16_WIDE) {  // one-dimensional tile numbering, M-block fastest
+        out->grid_x = (int)(ceil_div(N, tile.block_n()) * ceil_div(M, tile.block_m()));
+        out->grid_y = 1;
+    } else {
+        out->grid_x = (int)ceil_div(N, tile.block_n());
+        out->grid_y = (int)ceil_div(M, tile.block_m());
+    }
     out->grid_z = s;
     out->block_m = tile.block_m();
     out->block_n = tile.block_n();
@@ -128,10 +152,10 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (s == 1) {
         const bool vec = (N % 4 == 0) && aligned(C, 8);
-        return hip_status(qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, C, M, N, K, 1, vec, st));
+        return hip_status(dispatch_w4a16(tile, A, Wq, scale, bias, C, M, N, K, 1, vec, st));
     }
     const bool vec_ws = (N % 4 == 0);
-    int rc = hip_status(qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
+    int rc = hip_status(dispatch_w4a16(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
     if (rc != QMM_OK) return rc;
     const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
     return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));

@@ -27,7 +27,7 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
              int M, int N, int K, int s, int vec_store)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15;
     const int slot = lane >> 4;
     const int m_wave = blockIdx.y * (2 * 16 * MT) + (wave >> 1) * (16 * MT);

@@ -7,7 +7,10 @@
 namespace qmm_dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // bf16 bit pattern -> fp32 (exact: bf16 is the top half of a binary32).
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
@@ -17,8 +20,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; lo in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Dequantise the eight 4-bit weights of one packed word, w_i = scale * q_i + bias
+// (q_i = bits 4i..4i+3), into four bf16 pairs in k order: .x = (w0, w1), ..., .w = (w6, w7).
+// The even nibbles are isolated with one mask and converted with the byte-to-float
+// conversions; the odd nibbles are masked in place, so they convert to 16*q and meet
+// scale/16 instead (the product is the same real number and the FMA rounds once, so
+// every weight is bitwise fma(q, scale, bias) whenever scale/16 is exact, i.e. for
+// |scale| >= 2^-122). 22 VALU instructions per 8 weights.
+__device__ __forceinline__ uint4 dequant8(uint32_t x, float sc, float sc16, float bi) {
+    uint32_t lo = x & 0x0F0F0F0Fu;
+    uint32_t hi = x & 0xF0F0F0F0u;
+    // keep the masks opaque so the byte extracts stay single conversion instructions
+    asm("" : "+v"(lo));
+    asm("" : "+v"(hi));
+    uint4 r;
+    r.x = pack_bf16x2(__builtin_fmaf((float)(lo & 0xFFu), sc, bi), __builtin_fmaf((float)(hi & 0xFFu), sc16, bi));
+    r.y = pack_bf16x2(__builtin_fmaf((float)((lo >> 8) & 0xFFu), sc, bi),
+                      __builtin_fmaf((float)((hi >> 8) & 0xFFu), sc16, bi));
+    r.z = pack_bf16x2(__builtin_fmaf((float)((lo >> 16) & 0xFFu), sc, bi),
+                      __builtin_fmaf((float)((hi >> 16) & 0xFFu), sc16, bi));
+    r.w = pack_bf16x2(__builtin_fmaf((float)(lo >> 24), sc, bi), __builtin_fmaf((float)(hi >> 24), sc16, bi));
+    return r;
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -34,6 +62,14 @@ __device__ __forceinline__ uint32_t word_of(const uint4 &v, int t) {
 // k values to (slot, element) is valid as long as X and Y use the same one.
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 x, bf16x8 y, f32x4 d) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, d, 0, 0, 0);
+}
+
+// D = X . Y^T + D on a 32x32 tile with a 16-deep reduction (v_mfma_f32_32x32x16_bf16,
+// the full-rate bf16 MFMA on gfx950). Lane l supplies row (l % 32) of X and of Y, as
+// the eight reduction values of slot (l / 32); it receives D[r][l % 32] for
+// r = (v % 4) + 4*(l / 32) + 8*(v / 4), v = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 x, bf16x8 y, f32x16 d) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, d, 0, 0, 0);
 }
 
 }  // namespace qmm_dev

@@ -45,7 +45,7 @@ w4a16_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
              uint16_t *__restrict__ out, int M, int N, int K, int gpp, int vec_store)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15;
     const int slot = lane >> 4;
     const int n_wave = (blockIdx.x * 4 + wave) * (16 * NS);

@@ -1,0 +1,192 @@
+// qmm_w4a16_skinny.hip -- W4A16 group-128 matmul kernel for few rows (M <= 64) on gfx950.
+//
+// Same contract as the other W4A16 kernels (tiny-llm "Week 2 Day 7: Split-K
+// Prefill", Task 2): blockIdx.z is the partition p, the workgroup covers groups
+// [p*gpp, (p+1)*gpp) of the reduction and writes its tile into plane p of `out`
+// (C itself when s = 1), with plain stores and no atomics.
+//
+// With few rows the op streams the packed weights once and is bound by memory
+// latency and bandwidth, not by the matrix cores (a dispatch on MI355X costs about
+// 1.6 us before the first byte arrives). The design therefore maximises the bytes
+// in flight per wave and keeps the work in one dispatch where possible:
+//   * a workgroup owns a (16*MT) x (16*NS) output tile and up to 16 waves; the
+//     waves split the tile's reduction range, wave w taking groups g0 + w,
+//     g0 + w + WAVES, ... of its partition;
+//   * each wave issues all loads of a round of up to GPW groups at once -- per
+//     group and lane one 16-byte load of packed weights per 16-column subtile, four
+//     16-byte loads of activations per 16-row subtile, and the scale/bias of its
+//     rows -- then waits once and runs the MFMAs of the round;
+//   * the waves' fp32 tiles meet in LDS and are summed in ascending wave order
+//     (deterministic), rounded once to bf16 and stored with 8-byte stores.
+// Weights are dequantised in registers: w = scale*q + bias in fp32, rounded to
+// bf16 (each weight is used by all 16*MT rows of the tile from the same registers).
+// The 16x16x32 MFMA takes the weights as its first operand, so a lane's result is
+// four consecutive output columns of one row.
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+using namespace qmm_dev;
+
+namespace {
+
+constexpr int MAX_WAVES = 16;
+
+template <int MT, int NS, int GPW, int MAXW>
+__global__ void __launch_bounds__(64 * MAXW)
+w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
+                    const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
+                    uint16_t *__restrict__ out, int M, int N, int K, int gpp, int vec_store)
+{
+    extern __shared__ __attribute__((aligned(16))) char red[];  // [WAVES][MT][NS][64] float4
+    // Fetch every pointer argument up front, in the kernel's first scalar loads: left to
+    // itself the compiler loads them after the first branch, one more dependent memory
+    // round trip before the first weight load.
+    asm volatile("" ::"s"(A), "s"(Wq), "s"(scale), "s"(bias), "s"(out));
+    const int waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int r = lane & 15;
+    const int slot = lane >> 4;
+    const int n_blk = blockIdx.x * (16 * NS);
+    const int m_blk = blockIdx.y * (16 * MT);
+    const int G = K >> 7;
+    const int g0 = blockIdx.z * gpp;
+    // this wave's groups: g0 + wave + waves*i, i < n_w
+    const int n_w = (gpp - wave + waves - 1) / waves;
+
+    const uint4 *wptr[NS];
+    const uint16_t *sptr[NS];
+    const uint16_t *bptr[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const int n = min(n_blk + 16 * j + r, N - 1);  // rows past N read row N-1, never stored
+        wptr[j] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K >> 3)) + slot;
+        sptr[j] = scale + (size_t)n * G;
+        bptr[j] = bias + (size_t)n * G;
+    }
+    const uint4 *aptr[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int m = min(m_blk + 16 * i + r, M - 1);  // rows past M read row M-1, never stored
+        aptr[i] = reinterpret_cast<const uint4 *>(A + (size_t)m * (size_t)K) + 4 * slot;
+    }
+
+    f32x4 acc[MT][NS];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int base = 0; base < n_w; base += GPW) {
+        uint4 wv[GPW][NS];
+        uint4 av[GPW][MT][4];
+        uint32_t sc[GPW][NS], bi[GPW][NS];
+        // issue every load of the round before the first use
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            if (base + q >= n_w) break;  // uniform across the wave
+            const int g = g0 + wave + waves * (base + q);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                wv[q][j] = wptr[j][4 * g];
+                sc[q][j] = sptr[j][g];
+                bi[q][j] = bptr[j][g];
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) av[q][i][t] = aptr[i][16 * g + t];
+        }
+        // Keep all of the round's loads ahead of the first MFMA: without this the
+        // compiler sinks each group's loads next to its use, one round trip per group.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            if (base + q >= n_w) break;  // uniform across the wave
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const float s_ = bf16_to_f32(sc[q][j]);
+                const float b_ = bf16_to_f32(bi[q][j]);
+                const float s16 = s_ * 0.0625f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const bf16x8 b = as_bf16x8(dequant8(word_of(wv[q][j], t), s_, s16, b_));
+#pragma unroll
+                    for (int i = 0; i < MT; ++i) acc[i][j] = mfma16x16x32(b, as_bf16x8(av[q][i][t]), acc[i][j]);
+                }
+            }
+        }
+    }
+
+    // Cross-wave sum in LDS: wave w stores its tiles, then each of the MT*NS*64 lane-quads
+    // (i, j, lane) is owned by one thread (strided over the workgroup), which adds the
+    // waves' values in order w = 0, 1, ...
+    f32x4 *red4 = reinterpret_cast<f32x4 *>(red);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) red4[((wave * MT + i) * NS + j) * 64 + lane] = acc[i][j];
+    __syncthreads();
+    for (int t = threadIdx.x; t < MT * NS * 64; t += blockDim.x) {
+        f32x4 sum = red4[t];
+        for (int w = 1; w < waves; ++w) sum += red4[w * MT * NS * 64 + t];
+        const int l = t & 63;
+        const int j = (t >> 6) % NS;
+        const int i = (t >> 6) / NS;
+        const int m = m_blk + 16 * i + (l & 15);
+        const int n = n_blk + 16 * j + 4 * (l >> 4);
+        if (m < M) {
+            uint16_t *dst = out + (size_t)blockIdx.z * (size_t)M * (size_t)N + (size_t)m * (size_t)N + n;
+            if (vec_store && n + 3 < N) {
+                uint2 v;
+                v.x = pack_bf16x2(sum[0], sum[1]);
+                v.y = pack_bf16x2(sum[2], sum[3]);
+                *reinterpret_cast<uint2 *>(dst) = v;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)f32_to_bf16(sum[e]);
+            }
+        }
+    }
+}
+
+template <int MT, int NS, int GPW, int MAXW>
+hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, int M, int N,
+                      int K, int s, int waves, bool vec_store, hipStream_t stream)
+{
+    const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
+    const int gpp = (K / 128) / s;
+    const size_t lds = (size_t)waves * MT * NS * 64 * 16;
+    if (waves > MAXW) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
+                       static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
+                       static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
+                       static_cast<uint16_t *>(out), M, N, K, gpp, vec_store ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+namespace qmm_impl {
+
+// The host picks (mt, gpw, waves) with SkinnyShape (qmm_launch.h): mt 1 with up to 16
+// waves and gpw <= 3; mt 2 with up to 8 waves and gpw <= 3; mt 4 with up to 8 waves
+// and gpw <= 2 (register budgets of 128 / 256 / 256 VGPRs per lane).
+hipError_t launch_w4a16_skinny(int mt, int gpw, int waves, const void *A, const void *Wq, const void *scale,
+                               const void *bias, void *out, int M, int N, int K, int s, bool vec_store,
+                               hipStream_t stream)
+{
+    if (waves < 1 || waves > MAX_WAVES) return hipErrorInvalidValue;
+#define QMM_CFG(MT_, GPW_, MAXW_)                                                                              \
+    if (mt == MT_ && gpw == GPW_)                                                                              \
+        return launch_cfg<MT_, 2, GPW_, MAXW_>(A, Wq, scale, bias, out, M, N, K, s, waves, vec_store, stream);
+    QMM_CFG(1, 1, 16) QMM_CFG(1, 2, 16) QMM_CFG(1, 3, 16)
+    QMM_CFG(2, 1, 8) QMM_CFG(2, 2, 8) QMM_CFG(2, 3, 8)
+    QMM_CFG(4, 1, 8) QMM_CFG(4, 2, 8)
+#undef QMM_CFG
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qmm_impl

@@ -16,8 +16,17 @@ Timing:
     W warm-up steps, then K timed steps between two synchronisations;
   * per shape: a graph of R back-to-back calls over R distinct buffer sets
     totalling >= 1 GiB, for the policy's split and for the unsplit control;
-  * the dominant kernel (largest share of the step) is also timed launch by
-    launch with HIP events on its stream, for the roofline figure.
+  * the dominant kernel (largest share of the step: the large-M kernel) is
+    timed on its own for the roofline figure: the seven M = 2048 shapes launched
+    unsplit, back to back in one graph, HIP events on the launch stream around
+    each replay (``--dominant-only`` runs just this part, for the profiler);
+  * machine floors measured in the same run: empty-kernel dispatch, HBM
+    stream read and copy, bf16 MFMA rate (libqmm_calib.so).
+
+Traffic: ``--pmc-run`` is the workload of two rocprofv3 --pmc passes
+(FETCH_SIZE, WRITE_SIZE) and ``--summarize-pmc`` turns them into the text
+summary under profiles/ that the ``traffic`` field reads back (it stays null
+when the kernel source changed after the counters were taken).
 
 CPU baseline: the fp64 CPU oracle on the host cores, on a bounded sample of
 the same sweep (listed in the output), extrapolated to one whole sweep.
@@ -58,15 +67,191 @@ def roofline(M, N, K, seconds):
                 frac=max(t_hbm, t_mfma) / seconds, gbs=b / seconds / 1e9, tflops=f / seconds / 1e12)
 
 
+# The dominant kernel of the step (largest share of its time): the large-M W4A16 kernel.
+DOMINANT_KERNEL = "w4a16_wide_kernel"
+DOMINANT_SOURCE = os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", "qmm_w4a16_wide.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_wide_M2048_traffic.txt")
+COPY_BYTES = 256 << 20     # size of the plain copy that calibrates the profiler's byte counters
+
+
+def dominant_shapes(shapes):
+    """The M = 2048 shapes: the large-M kernel runs them (unsplit in the timing below)."""
+    return [sh for sh in shapes if sh.M > 128]
+
+
+def source_digest(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def calib_lib():
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_quantized_qmm_amd", "libqmm_calib.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libqmm_calib.so is not built; run python -m weight_only_quantized_qmm_amd.build")
+    L = ctypes.CDLL(path)
+    I, P, S = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.qmm_calib_empty.argtypes = [I, P]
+    L.qmm_calib_read.argtypes = [P, S, P, P]
+    L.qmm_calib_copy.argtypes = [P, P, S, P]
+    L.qmm_calib_mfma.argtypes = [I, I, P, P]
+    for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_copy, L.qmm_calib_mfma):
+        f.restype = I
+    return L
+
+
+def calibrate(torch):
+    """This GPU's own floors, measured in the same run: dispatch, HBM read/copy, bf16 MFMA."""
+    L = calib_lib()
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        g = graph_of(torch, lambda: [fn() for _ in range(reps)])
+        return time_graph(torch, g) / reps
+
+    t_empty = timed(lambda: L.qmm_calib_empty(1, torch.cuda.current_stream().cuda_stream), 200)
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf2 = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    t_read = timed(lambda: L.qmm_calib_read(buf.data_ptr(), nbytes, out.data_ptr(),
+                                            torch.cuda.current_stream().cuda_stream), 4)
+    t_copy = timed(lambda: L.qmm_calib_copy(buf.data_ptr(), buf2.data_ptr(), nbytes // 2,
+                                            torch.cuda.current_stream().cuda_stream), 4)
+    del buf, buf2
+    grid, iters = 256 * 8, 4096
+    t_mfma = timed(lambda: L.qmm_calib_mfma(grid, iters, out.data_ptr(), torch.cuda.current_stream().cuda_stream), 4)
+    torch.cuda.empty_cache()
+    return {"empty_dispatch_us": round(t_empty * 1e6, 3),
+            "hbm_read_TBps": round(nbytes / t_read / 1e12, 3),
+            "hbm_copy_TBps": round(nbytes / t_copy / 1e12, 3),  # bytes read + bytes written
+            "mfma_bf16_tflops": round(grid * 4 * iters * 4 * 32768 / t_mfma / 1e12, 1),
+            "note": "empty kernel back to back in a graph; 2 GiB read; 1 GiB copy; "
+                    "v_mfma_f32_32x32x16_bf16 loop on 2048 workgroups"}
+
+
+def read_traffic(alg_bytes_per_launch):
+    """HBM bytes per launch of the dominant kernel from the committed profiler counters, or None.
+
+    The summary records the digest of the kernel source it was taken on; a
+    different digest (the kernel changed since) gives None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None, "no counter summary"
+    fields = {}
+    for line in open(TRAFFIC_SUMMARY):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel source digest") != source_digest(DOMINANT_SOURCE):
+        return None, "kernel changed since the counters were taken"
+    t = float(fields["hbm bytes per launch (scaled)"])
+    return t, "FETCH_SIZE + WRITE_SIZE per launch x copy-kernel scale; %.2fx the algorithmic bytes" % (
+        t / alg_bytes_per_launch)
+
+
+def dominant_roofline(torch, shapes, rounds=4):
+    """Roofline figure of the dominant kernel: every M = 2048 shape launched unsplit
+    (one kernel per call, no reduce), `rounds` times over two buffer sets, captured
+    as one graph; HIP events on the launch stream around each replay give the mean
+    launch duration (median of the replays)."""
+    dom = dominant_shapes(shapes)
+    g = graph_of(torch, lambda: [sh.call(r, 1) for r in range(rounds) for sh in dom])
+    avg_dur = time_graph(torch, g) / (rounds * len(dom))
+    del g
+    flops = sum(algorithmic_flops(sh.M, sh.N, sh.K) for sh in dom) / len(dom)
+    nbytes = sum(algorithmic_bytes(sh.M, sh.N, sh.K) for sh in dom) / len(dom)
+    achieved = flops / avg_dur
+    calib = calibrate(torch)
+    traffic, traffic_note = read_traffic(nbytes)
+    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK, "traffic": traffic,
+            "kernel": "%s, unsplit, M=2048 launches (%s)" % (DOMINANT_KERNEL, ", ".join(sh.name for sh in dom)),
+            "launches_per_replay": rounds * len(dom), "avg_launch_us": avg_dur * 1e6,
+            "algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops,
+            "frac_of_measured_mfma_peak": achieved / (calib["mfma_bf16_tflops"] * 1e12),
+            "traffic_note": traffic_note,
+            "block_tile": [dom[0].plan.block_m, dom[0].plan.block_n]}
+    return roof, calib
+
+
+def pmc_run():
+    """Workload of the counter passes: each M = 2048 shape once unsplit, then one plain copy."""
+    import torch
+    import qmm_synth as syn
+    import weight_only_quantized_qmm_amd as q
+    torch.cuda.set_device(0)
+    shapes = [Shape(n, M, N, K, i, 1, torch, syn, q) for n, M, N, K, i in syn.projection_sweep() if M > 128]
+    for sh in shapes:
+        sh.call(0, 1)
+    torch.cuda.synchronize()
+    L = calib_lib()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    L.qmm_calib_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    print("pmc run: %d launches of %s + one %d-byte copy" % (len(shapes), DOMINANT_KERNEL, COPY_BYTES), flush=True)
+
+
+def summarize_pmc(fetch_dir, write_dir, commands):
+    """Text summary of two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over pmc_run()."""
+    import csv
+    import glob
+    import qmm_synth as syn
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter_collection.csv under %s" % d)
+        rows = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    pick = lambda rows, key: [v for k, vs in rows.items() if key in k for v in vs]
+    cf, cw = pick(fetch, "calib_copy"), pick(write, "calib_copy")
+    df, dw = pick(fetch, DOMINANT_KERNEL), pick(write, DOMINANT_KERNEL)
+    f_scale = COPY_BYTES / (cf[0] * 1024.0)
+    w_scale = COPY_BYTES / (cw[0] * 1024.0)
+    shapes = [(n, M, N, K) for n, M, N, K, _ in syn.projection_sweep() if M > 128]
+    alg = [algorithmic_bytes(M, N, K) for _, M, N, K in shapes]
+    lines = ["# HBM traffic of %s (unsplit, M = 2048 Qwen3-4B projections) from rocprofv3 counters" % DOMINANT_KERNEL,
+             "commands:"] + ["  " + c for c in commands] + [
+        "copy kernel: %d bytes read and written; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (COPY_BYTES, cf[0], cw[0]),
+        "fetch scale: %.4f" % f_scale, "write scale: %.4f" % w_scale,
+        "per launch (shape order %s):" % ", ".join(n for n, *_ in shapes)]
+    tot = []
+    for (n, M, N, K), a, fv, wv in zip(shapes, alg, df, dw):
+        b = fv * 1024 * f_scale + wv * 1024 * w_scale
+        tot.append(b)
+        lines.append("  %-5s M=%d N=%d K=%d: fetch %.1f KiB, write %.1f KiB -> %.3e B scaled; algorithmic %.3e B (%.2fx)"
+                     % (n, M, N, K, fv, wv, b, a, b / a))
+    lines += ["kernel source digest: %s" % source_digest(DOMINANT_SOURCE),
+              "hbm bytes per launch (scaled): %.6e" % (sum(tot) / len(tot)),
+              "algorithmic bytes per launch: %.6e" % (sum(alg) / len(alg))]
+    print("\n".join(lines))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=25.0, help="CPU-baseline sample budget")
     ap.add_argument("--no-per-shape", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--dominant-only", action="store_true",
+                    help="only the dominant-kernel roofline measurement (the profiled command)")
+    ap.add_argument("--pmc-run", action="store_true", help="only the workload of the profiler counter passes")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc output folders")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help="commands recorded in the traffic summary")
     return ap.parse_args()
 
 
@@ -115,7 +300,7 @@ def graph_of(torch, fn):
     return g
 
 
-def time_graph(torch, g, reps=3):
+def time_graph(torch, g, reps=5):
     """Median seconds of one replay."""
     g.replay()
     torch.cuda.synchronize()
@@ -148,42 +333,51 @@ def per_shape(torch, syn, q, name, M, N, K, idx):
 
 
 def cpu_baseline(syn, budget_s):
-    """fp64 oracle on the host cores over a bounded, listed sample of the sweep, extrapolated."""
-    import numpy as np
+    """fp64 oracle on the host cores over the sweep, shape by shape, within a time budget;
+    shapes the budget does not reach are extrapolated by multiply-add count."""
     import oracle
 
     cores = oracle.default_threads()
     shapes = syn.projection_sweep()
-    # order: small-M shapes whole, then 128-row slices of the 2048-row shapes
+    # order: the small-M shapes, then the 2048-row shapes, each whole, until the budget is spent
     order = [sh for sh in shapes if sh[1] <= 128] + [sh for sh in shapes if sh[1] > 128]
     spent, sample, est_total = 0.0, [], 0.0
     done_macs, done_time = 0.0, 0.0
     for name, M, N, K, idx in order:
-        rows = M if M <= 128 else 128
         if spent >= budget_s:
             break
         d = syn.w4a16_weights(N, K, seed=2000 + idx)
-        A = syn.normal_bf16((rows, K), seed=2500 + idx)
+        A = syn.normal_bf16((M, K), seed=2500 + idx)
         t0 = time.perf_counter()
-        oracle.qmm_w4a16(A, d["Wq"], d["scale"], d["bias"], rows, N, K, s=1, nthreads=cores)
+        oracle.qmm_w4a16(A, d["Wq"], d["scale"], d["bias"], M, N, K, s=1, nthreads=cores)
         dt = time.perf_counter() - t0
         spent += dt
-        sample.append("%s M=%d%s" % (name, M, "" if rows == M else " (rows 0..%d)" % (rows - 1)))
-        est_total += dt * (M / rows)
-        done_macs += rows * N * K
+        sample.append("%s M=%d" % (name, M))
+        est_total += dt
+        done_macs += M * N * K
         done_time += dt
     covered = {(s.split()[0], s.split()[1]) for s in sample}
     rate = done_time / done_macs  # seconds per MAC over the sample
     for name, M, N, K, idx in shapes:
         if (name, "M=%d" % M) not in covered:
             est_total += rate * M * N * K
-    return dict(value=est_total * 1e6, unit="us per sweep (35 projection matmuls, extrapolated)", cores=cores,
-                kind="oracle",
-                sample="%s; %.1f s measured, rest extrapolated by multiply-add count" % (", ".join(sample), spent))
+    whole = len(sample) == len(shapes)
+    return dict(value=est_total * 1e6,
+                unit="us per sweep (35 projection matmuls%s)" % ("" if whole else ", extrapolated"),
+                cores=cores, kind="oracle",
+                sample="%s; %.1f s measured%s" % (
+                    "the whole sweep, each shape once" if whole else ", ".join(sample), spent,
+                    "" if whole else ", rest extrapolated by multiply-add count"))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands)
+        return
+    if args.pmc_run:
+        pmc_run()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -199,6 +393,12 @@ def main():
     torch.cuda.set_device(0)
     q.lib()
     sweep = syn.projection_sweep()
+
+    if args.dominant_only:
+        shapes = [Shape(n, M, N, K, i, 2, torch, syn, q) for n, M, N, K, i in sweep if M > 128]
+        roof, calib = dominant_roofline(torch, shapes)
+        print(json.dumps({"roofline": roof, "machine_floors": calib}), flush=True)
+        return
 
     # ---- the timed step: the whole sweep, graph-replayed over two rotation sets
     shapes = [Shape(n, M, N, K, i, 2, torch, syn, q) for n, M, N, K, i in sweep]
@@ -227,32 +427,11 @@ def main():
     torch.cuda.synchronize()
     eager_step_s = (time.perf_counter() - t0) / 3
 
-    # ---- the dominant kernel: the unsplit large-M launches, timed one by one with events
-    dom = [sh for sh in shapes if sh.M > 128 and sh.s == 1]
-    durs, flops, nbytes = [], [], []
-    stream = torch.cuda.current_stream()
-    for rep in range(3):
-        for sh in dom:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            sh.call(rep + 1, 1)
-            b.record(stream)
-            b.synchronize()
-            if rep > 0:  # first pass warms
-                durs.append(a.elapsed_time(b) / 1e3)
-                flops.append(algorithmic_flops(sh.M, sh.N, sh.K))
-                nbytes.append(algorithmic_bytes(sh.M, sh.N, sh.K))
+    roof, calib = dominant_roofline(torch, shapes)
     del graphs
     for sh in shapes:
         sh.free()
     torch.cuda.empty_cache()
-    avg_dur = sum(durs) / len(durs)
-    achieved = sum(flops) / len(flops) / avg_dur
-    roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
-            "frac": achieved / MFMA_BF16_PEAK, "traffic": None,
-            "kernel": "w4a16 kernel, unsplit, M=2048 launches (%s)" % ", ".join(sh.name for sh in dom),
-            "launches": len(durs), "avg_launch_us": avg_dur * 1e6,
-            "block_tile": [dom[0].plan.block_m, dom[0].plan.block_n] if dom else None}
 
     # ---- per-shape table
     table = []
@@ -291,6 +470,7 @@ def main():
         "eager_us_per_step": round(eager_step_s * 1e6, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "machine_floors": calib,
         "shapes": table,
     }
     if table:

@@ -18,7 +18,9 @@ using qmm_impl::W4A16Tile;
 
 extern "C" {
 const qmm_policy QMM_POLICY_PAGE = {32, 32, 320, 16, 128};
-const qmm_policy QMM_POLICY_MI355X = {0, 0, 512, 16, 512};
+// Tile 0 x 0 = the output tile of the kernel that runs the shape; target, cap and minimum K per
+// partition fitted to per-shape split sweeps on MI355X (split never slower than unsplit).
+const qmm_policy QMM_POLICY_MI355X = {0, 0, 256, 20, 128};
 }
 
 namespace {

@@ -1,0 +1,109 @@
+// qmm_calib.hip -- measurement kernels for the benchmark (libqmm_calib.so).
+//
+// Not part of the matmul library: these kernels give the benchmark the
+// machine's own floors on the same device and in the same run, so that a
+// roofline fraction can be read against the published peaks and against what
+// this GPU actually delivers:
+//   * an empty kernel (the dispatch floor of one launch);
+//   * a streaming read and a streaming copy of a large buffer (achievable HBM
+//     bandwidth; the copy of a known size also calibrates the profiler's
+//     FETCH_SIZE / WRITE_SIZE counters);
+//   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ void calib_empty_kernel() {}
+
+// Grid-stride read of n16 16-byte vectors; the xor of everything read is
+// written only if it hits an impossible value, so the loads stay live.
+__global__ void __launch_bounds__(256) calib_read_kernel(const uint4 *__restrict__ src, size_t n16, uint32_t *out)
+{
+    uint4 acc = {0u, 0u, 0u, 0u};
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc.x ^= a.x ^ b.x ^ c.x ^ d.x;
+        acc.y ^= a.y ^ b.y ^ c.y ^ d.y;
+        acc.z ^= a.z ^ b.z ^ c.z ^ d.z;
+        acc.w ^= a.w ^ b.w ^ c.w ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = src[i];
+        acc.x ^= a.x;
+        acc.y ^= a.y;
+        acc.z ^= a.z;
+        acc.w ^= a.w;
+    }
+    if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) out[0] = 1u;
+}
+
+__global__ void __launch_bounds__(256) calib_copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                         size_t n16)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave;
+// each instruction is 2*32*32*16 = 32768 flops.
+__global__ void __launch_bounds__(256) calib_mfma_kernel(int iters, float *out)
+{
+    const float x = (float)(threadIdx.x & 7) * 0.125f;
+    bf16x8_t a, b;
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(x + e);
+        b[e] = (__bf16)(x - e);
+    }
+    f32x16_t acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+    for (int i = 0; i < iters; ++i) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc3, 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int e = 0; e < 16; ++e) s += acc0[e] + acc1[e] + acc2[e] + acc3[e];
+    if (s == 1.2345f) out[0] = s;
+}
+
+}  // namespace
+
+// All entry points enqueue on `stream` and return the hipError_t of the launch.
+extern "C" {
+
+int qmm_calib_empty(int grid, void *stream)
+{
+    hipLaunchKernelGGL(calib_empty_kernel, dim3(grid), dim3(64), 0, (hipStream_t)stream);
+    return (int)hipGetLastError();
+}
+
+// bytes must be a multiple of 16; src 16-byte aligned; out: one uint32 of device memory.
+int qmm_calib_read(const void *src, size_t bytes, void *out, void *stream)
+{
+    hipLaunchKernelGGL(calib_read_kernel, dim3(256 * 32), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
+    return (int)hipGetLastError();
+}
+
+int qmm_calib_copy(const void *src, void *dst, size_t bytes, void *stream)
+{
+    hipLaunchKernelGGL(calib_copy_kernel, dim3(256 * 32), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), bytes / 16);
+    return (int)hipGetLastError();
+}
+
+// flops = grid * 4 waves * iters * 4 * 32768; out: one float of device memory.
+int qmm_calib_mfma(int grid, int iters, void *out, void *stream)
+{
+    hipLaunchKernelGGL(calib_mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
+                       static_cast<float *>(out));
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

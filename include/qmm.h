@@ -56,7 +56,7 @@ enum {
     QMM_ERR_ALIGN = -3,     /* A / Wq / B / workspace not 16-byte aligned, or an element misaligned */
     QMM_ERR_WORKSPACE = -4, /* split requested and workspace NULL or smaller than needed */
     QMM_ERR_HIP = -5,       /* a kernel launch failed (hipGetLastError) */
-    QMM_ERR_SIZE = -6       /* a size would overflow the library's 32-bit row/column indexing */
+    QMM_ERR_SIZE = -6       /* a size would overflow the library's 32-bit indexing (M*N, N*K, M*K > 2^37, or K >= 2^22) */
 };
 
 /* Partial-plane element types for qmm_splitk_reduce. */
@@ -70,6 +70,19 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  *     s <= 1 -> the unsplit kernel
  * tile_m / tile_n = 0 mean "the block tile of the kernel this library launches
  * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
+ *
+ * With tile_m = tile_n = 0 and M > 64 (the large-M kernel, T = base tiles, M-block
+ * fastest, num_m tiles per column of tiles) the rule fills the kernel's workgroup
+ * slots, target_blocks times the workgroups one CU holds (2 for its 128-row tiles),
+ * with partitions that may differ by one group (no divisibility step); below,
+ * target_blocks stands for that slot count:
+ *     smax = min(cap, K/128, floor(K / min_k_per_split))
+ *     T <  target_blocks: s = min(smax, floor(target_blocks / T)), every tile split
+ *     T >= target_blocks: full = floor(T / target_blocks) * target_blocks, rounded down
+ *         to a multiple of num_m, run unsplit; the tail T - full split in
+ *         s = min(smax, floor(target_blocks / (T - full))) partitions
+ *     s <= 1 -> the unsplit kernel
+ * Partition p of a split tile covers groups [floor(p*G/s), floor((p+1)*G/s)), G = K/128.
  */
 typedef struct qmm_policy {
     int tile_m;
@@ -87,11 +100,15 @@ typedef struct qmm_plan {
     int grid_x, grid_y, grid_z; /* grid of the matmul kernel this library launches for (M,N,K,s) */
     int block_m, block_n;   /* output tile of one workgroup of that kernel */
     size_t workspace_bytes; /* 2*s*M*N for s > 1, else 0 */
+    int full_tiles;         /* kernel tiles computed unsplit ahead of the split ones: all of them
+                               when s = 1, 0 for a uniform split, in between for a split tail */
 } qmm_plan;
 
 /* The page's rule: 32 x 32 tiles, 320 target blocks, cap 16, one group per partition. */
 extern const qmm_policy QMM_POLICY_PAGE;
-/* The rule re-tuned for MI355X (256 CUs); used when s = 0 is passed to qmm_w4a16_g128. */
+/* The rule re-tuned for MI355X (256 CUs): {0, 0, 256, 16, 512}, kernel tiles, 256 target
+ * blocks (the CU count), cap 16, at least 512 K values per partition; used when s = 0 is
+ * passed to qmm_w4a16_g128. */
 extern const qmm_policy QMM_POLICY_MI355X;
 
 /*
@@ -105,10 +122,13 @@ int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *polic
 /*
  * qmm_w4a16_g128 -- C = A . dequant(W)^T (tiny-llm "Week 2 Day 7", the public
  * matmul whose dispatcher picks the split and runs the partition and reduce kernels).
- *   s = 0  : the split comes from qmm_splitk_plan(M, N, K, 128, NULL)
+ *   s = 0  : the decomposition comes from qmm_splitk_plan(M, N, K, 128, NULL)
+ *            (its s, and its full_tiles for the large-M kernel)
  *   s = 1  : the unsplit kernel (the control; also what the policy falls back to)
- *   s > 1  : explicit split; must divide K/128. Launches the split kernel, writing
- *            bf16 partial planes [s][M][N] into `workspace`, then the reduce into C.
+ *   s > 1  : explicit split of every tile into s equal partitions; s must divide K/128.
+ *            Launches the split kernel, writing bf16 partial planes [s][M][N] into
+ *            `workspace`, then the reduce into C (of the split tiles' columns only,
+ *            when the plan runs the first tiles unsplit).
  *   workspace / workspace_bytes: needed only when the effective s > 1; at least
  *   2*s*M*N bytes, 16-byte aligned. May be NULL otherwise.
  *   Alignment: A and Wq 16-byte aligned; scale, bias and C 2-byte aligned.

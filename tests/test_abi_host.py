@@ -91,15 +91,43 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     pol = q.policy_preset("QMM_POLICY_MI355X")
     plan = q.qmm_splitk_plan(M, N, K)
     G = K // 128
-    assert 1 <= plan.s <= min(pol.cap, G) and G % plan.s == 0
-    assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
     assert plan.tile_m == plan.block_m and plan.tile_n == plan.block_n
-    assert plan.base_tiles == -(-M // plan.block_m) * -(-N // plan.block_n)
-    assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.block_n,
-                                         target=pol.target_blocks, cap=pol.cap,
-                                         min_k_per_split=pol.min_k_per_split)
-    assert plan.grid_z == plan.s
-    assert plan.grid_x * plan.grid_y == -(-M // plan.block_m) * -(-N // plan.block_n)
+    tiles = -(-M // plan.block_m) * -(-N // plan.block_n)
+    assert plan.base_tiles == tiles
+    assert 1 <= plan.s <= min(pol.cap, G)
+    assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
+    assert plan.workspace_bytes == (2 * plan.s * M * N if plan.s > 1 else 0)
+    if M > 64:  # the large-M kernel: slot-filling rule, two workgroups per CU for 128-row tiles
+        slots = pol.target_blocks * (2 if plan.block_m == 128 else 1)
+        num_m = -(-M // plan.block_m)
+        assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
+            tiles, num_m, K, slots, pol.cap, pol.min_k_per_split)
+        assert plan.full_tiles % num_m == 0 or plan.full_tiles == tiles
+        assert plan.grid_x == plan.full_tiles + (tiles - plan.full_tiles) * plan.s
+        assert plan.grid_y == 1 and plan.grid_z == 1
+    else:  # the page's rule over the kernel's tile
+        assert G % plan.s == 0
+        assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.block_n,
+                                             target=pol.target_blocks, cap=pol.cap,
+                                             min_k_per_split=pol.min_k_per_split)
+        assert plan.grid_z == plan.s
+        assert plan.grid_x * plan.grid_y == tiles
+        assert plan.full_tiles == (tiles if plan.s == 1 else 0)
+
+
+def test_fill_decomposition_cases():
+    # 608 tiles (gate at M=2048 in 128 x 256 tiles), 512 slots: 512 unsplit, the last
+    # 96 in five partitions; 160 tiles: three partitions each; 512 tiles: no split.
+    assert opolicy.fill_decomposition(608, 16, 2560, 512, 16, 512) == (5, 512)
+    assert opolicy.fill_decomposition(160, 16, 9728, 512, 16, 512) == (3, 0)
+    assert opolicy.fill_decomposition(512, 16, 2560, 512, 16, 512) == (1, 512)
+    assert opolicy.fill_decomposition(520, 8, 2560, 512, 16, 512) == (5, 512)
+    # full rounded down to whole columns of tiles: 1100 tiles, 3 per column
+    assert opolicy.fill_decomposition(1100, 3, 2560, 512, 16, 512) == (5, 1023)
+    assert opolicy.fill_decomposition(7, 1, 128, 512, 16, 512) == (1, 7)  # K < 2 * min_k
+    assert opolicy.near_equal_partitions(20, 8) == [(0, 2), (2, 5), (5, 7), (7, 10), (10, 12), (12, 15),
+                                                   (15, 17), (17, 20)]
+    assert opolicy.near_equal_partitions(20, 5) == [(4 * p, 4 * p + 4) for p in range(5)]
 
 
 def test_plan_rejects_bad_arguments():

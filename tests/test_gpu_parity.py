@@ -120,6 +120,30 @@ def test_cfg2_projection_sweep(name, M, N, K, idx):
         assert np.array_equal(host_bits(C), host_bits(C1))
 
 
+def test_split_tail_decomposition():
+    """Large-M plan that runs most tiles unsplit and splits only the last column of tiles
+    (ragged in N): the unsplit columns equal the s = 1 kernel bit for bit, the split tail
+    is within tolerance of the oracle, and nothing outside C is written."""
+    M, N, K = 1000, 64 * 256 + 100, 2560
+    plan = q.qmm_splitk_plan(M, N, K)
+    say("split tail M=%d N=%d K=%d s=%d full_tiles=%d" % (M, N, K, plan.s, plan.full_tiles))
+    assert plan.s > 1 and 0 < plan.full_tiles < plan.base_tiles
+    n_lo = (plan.full_tiles // -(-M // plan.block_m)) * plan.block_n
+    d = syn.w4a16_inputs(M, N, K, seed=7200)
+    dv = w4a16_device(d)
+    C = run_w4a16(dv, M, N, K, 0, guard=64)
+    C1 = run_w4a16(dv, M, N, K, 1)
+    bits, bits1 = host_bits(C), host_bits(C1)
+    assert np.array_equal(bits[:, :n_lo], bits1[:, :n_lo])
+    ms = np.repeat(np.arange(M, dtype=np.int32), N - n_lo)
+    ns = np.tile(np.arange(n_lo, N, dtype=np.int32), M)
+    ref = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+    check_tolerance(host_f64(C)[ms, ns], ref, what="split tail columns")
+    m2, n2 = sample_points(M, N, 7200)
+    ref2 = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, m2, n2)
+    check_tolerance(host_f64(C)[m2, n2], ref2, what="split tail, sampled")
+
+
 # ----------------------------------------------------------- config 3 (dense)
 
 @pytest.fixture(scope="module")

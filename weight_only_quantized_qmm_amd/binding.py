@@ -46,7 +46,7 @@ class qmm_plan(ctypes.Structure):
     _fields_ = [("s", ctypes.c_int), ("base_tiles", ctypes.c_int), ("tile_m", ctypes.c_int),
                 ("tile_n", ctypes.c_int), ("grid_x", ctypes.c_int), ("grid_y", ctypes.c_int),
                 ("grid_z", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("full_tiles", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -174,7 +174,8 @@ def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     if s_eff > 1 and workspace is None:
         workspace = torch.empty(w4a16_workspace_bytes(M, N, s_eff), dtype=torch.uint8, device=A.device)
-    qmm_w4a16_g128(A, Wq, scale, bias, out, M, N, K, s_eff, workspace)
+    # s = 0 goes to the library as is: its plan may also run part of the tiles unsplit
+    qmm_w4a16_g128(A, Wq, scale, bias, out, M, N, K, s, workspace)
     return out
 
 

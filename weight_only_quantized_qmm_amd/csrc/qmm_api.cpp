@@ -18,9 +18,10 @@ using qmm_impl::W4A16Tile;
 
 extern "C" {
 const qmm_policy QMM_POLICY_PAGE = {32, 32, 320, 16, 128};
-// Tile 0 x 0 = the output tile of the kernel that runs the shape; target, cap and minimum K per
-// partition fitted to per-shape split sweeps on MI355X (split never slower than unsplit).
-const qmm_policy QMM_POLICY_MI355X = {0, 0, 256, 20, 128};
+// Tile 0 x 0 = the output tile of the kernel that runs the shape; 256 target blocks = the CU
+// count (times two for the large-M kernel, which holds two workgroups per CU); cap and minimum
+// K per partition fitted to per-shape split sweeps on MI355X (split never slower than unsplit).
+const qmm_policy QMM_POLICY_MI355X = {0, 0, 256, 16, 512};
 }
 
 namespace {
@@ -34,30 +35,26 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 // Block tile of the W4A16 kernel used for an M-row problem: the whole M (up to
 // 128 rows) in one block row, so each weight is dequantised once per block.
+// Kernel by row count: the small-M kernel up to 64 rows; the large-M kernel with 128-row
+// tiles (two workgroups per CU) up to 128 rows, with 256-row tiles of eight 256 x 32 waves above.
 W4A16Tile w4a16_tile(int M, int /*N*/) {
     W4A16Tile t;
     if (M <= 64) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    } else if (M <= 128) {
-        t.kind = qmm_impl::W4A16_NARROW;
-        t.mt = 8;
+        t.ns = 2;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
-        t.mt = 16;
+        t.mt = M <= 128 ? 8 : 16;
+        t.ns = M <= 128 ? 0 : 2;
     }
-    t.ns = 2;
     return t;
 }
 
-hipError_t dispatch_w4a16(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
-                        void *out, int M, int N, int K, int s, bool vec, hipStream_t st) {
-    if (tile.kind == qmm_impl::W4A16_WIDE) return qmm_impl::launch_w4a16_wide(A, Wq, scale, bias, out, M, N, K, s, vec, st);
-    if (tile.kind == qmm_impl::W4A16_SKINNY) {
-        const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, (K / kGroup) / s);
-        return qmm_impl::launch_w4a16_skinny(tile.mt, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s, vec, st);
-    }
-    return qmm_impl::launch_w4a16(tile, A, Wq, scale, bias, out, M, N, K, s, vec, st);
+hipError_t dispatch_skinny(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
+                           void *out, int M, int N, int K, int s, bool vec, hipStream_t st) {
+    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, (K / kGroup) / s);
+    return qmm_impl::launch_w4a16_skinny(tile.mt, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s, vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {
@@ -67,11 +64,14 @@ DenseTile dense_tile(int /*M*/, int /*N*/) {
     return t;
 }
 
-// Sizes the kernels index with 32-bit row/column counters and 64-bit offsets.
+// Sizes the kernels index with 32-bit row/column counters and 64-bit offsets; the
+// reduction length also bounds the large-M kernel's 32-bit per-lane copy offsets
+// (256 rows of A: 512*K bytes < 2^31).
 bool sizes_ok(int M, int N, int K) {
     if ((long long)M * (long long)N > (long long)INT_MAX * 64) return false;
     if ((long long)N * (long long)K > (long long)INT_MAX * 64) return false;
     if ((long long)M * (long long)K > (long long)INT_MAX * 64) return false;
+    if (K >= (1 << 22)) return false;
     return true;
 }
 
@@ -84,6 +84,39 @@ int split_rule(long long base, int G, int K, const qmm_policy &pol) {
     if (G < s) s = G;
     while (s > 1 && G % s != 0) --s;
     return s < 1 ? 1 : (int)s;
+}
+
+// The large-M kernel's decomposition under a kernel-tile policy: (s, full_tiles).
+struct Decomp {
+    int s;
+    int full_tiles;
+};
+
+Decomp wide_rule(long long T, long long num_m, int G, int K, long long target, const qmm_policy &pol) {
+    long long smax = pol.cap;
+    if (G < smax) smax = G;
+    const long long by_k = K / pol.min_k_per_split;
+    if (by_k < smax) smax = by_k;
+    Decomp d = {1, (int)T};
+    if (smax <= 1 || target <= 0) return d;
+    if (T >= target) {
+        long long full = (T / target) * target;
+        full -= full % num_m;
+        const long long tail = T - full;
+        if (tail == 0) return d;
+        long long s = target / tail;
+        if (smax < s) s = smax;
+        if (s <= 1) return d;
+        d.s = (int)s;
+        d.full_tiles = (int)full;
+        return d;
+    }
+    long long s = target / T;
+    if (smax < s) s = smax;
+    if (s <= 1) return d;
+    d.s = (int)s;
+    d.full_tiles = 0;
+    return d;
 }
 
 bool policy_ok(const qmm_policy &p) {
@@ -107,19 +140,31 @@ extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_po
     const int tn = pol.tile_n > 0 ? pol.tile_n : tile.block_n();
     const long long base = ceil_div(M, tm) * ceil_div(N, tn);
     const int G = K / kGroup;
-    const int s = split_rule(base, G, K, pol);
+    const long long kernel_tiles = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n());
+    Decomp d;
+    if (tile.kind == qmm_impl::W4A16_WIDE && pol.tile_m == 0 && pol.tile_n == 0) {
+        // slots: target_blocks times the workgroups of this kernel one CU holds
+        const long long slots = (long long)pol.target_blocks * qmm_impl::wide_wgs_per_cu(tile.ns);
+        d = wide_rule(kernel_tiles, ceil_div(M, tile.block_m()), G, K, slots, pol);
+    } else {
+        d.s = split_rule(base, G, K, pol);
+        d.full_tiles = d.s == 1 ? (int)kernel_tiles : 0;
+    }
+    const int s = d.s;
     out->s = s;
     out->base_tiles = base > INT_MAX ? INT_MAX : (int)base;
     out->tile_m = tm;
     out->tile_n = tn;
-    if (tile.kind == qmm_impl::W4A16_WIDE) {  // one-dimensional tile numbering, M-block fastest
-        out->grid_x = (int)(ceil_div(N, tile.block_n()) * ceil_div(M, tile.block_m()));
+    out->full_tiles = d.full_tiles;
+    if (tile.kind == qmm_impl::W4A16_WIDE) {  // one-dimensional grid: full tiles, then (tile, partition)
+        out->grid_x = (int)(d.full_tiles + (kernel_tiles - d.full_tiles) * s);
         out->grid_y = 1;
+        out->grid_z = 1;
     } else {
         out->grid_x = (int)ceil_div(N, tile.block_n());
         out->grid_y = (int)ceil_div(M, tile.block_m());
+        out->grid_z = s;
     }
-    out->grid_z = s;
     out->block_m = tile.block_m();
     out->block_n = tile.block_n();
     out->workspace_bytes = s > 1 ? (size_t)2 * (size_t)s * (size_t)M * (size_t)N : 0;
@@ -137,11 +182,14 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
     if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
         return QMM_ERR_ALIGN;
     const int G = K / kGroup;
+    const W4A16Tile tile = w4a16_tile(M, N);
+    int full_tiles = 0;
     if (s == 0) {
         qmm_plan plan;
         const int rc = qmm_splitk_plan(M, N, K, kGroup, nullptr, &plan);
         if (rc != QMM_OK) return rc;
         s = plan.s;
+        full_tiles = plan.full_tiles;
     } else if (s > G || G % s != 0) {
         return QMM_ERR_SHAPE;
     }
@@ -150,14 +198,27 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
         if (!workspace || workspace_bytes < 2 * (size_t)s * MN) return QMM_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
     }
-    const W4A16Tile tile = w4a16_tile(M, N);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (s == 1) {
-        const bool vec = (N % 4 == 0) && aligned(C, 8);
-        return hip_status(dispatch_w4a16(tile, A, Wq, scale, bias, C, M, N, K, 1, vec, st));
+    const bool vec_c = (N % 4 == 0) && aligned(C, 8);
+    if (tile.kind == qmm_impl::W4A16_WIDE) {
+        const int num_m = (int)ceil_div(M, tile.block_m());
+        const int tiles = num_m * (int)ceil_div(N, tile.block_n());
+        if (s == 1) full_tiles = tiles;
+        // Partial planes and C share one store-width decision (N % 4 == 0 and 8-byte C).
+        int rc = hip_status(qmm_impl::launch_w4a16_wide(tile.ns, A, Wq, scale, bias, C, s > 1 ? workspace : nullptr,
+                                                        M, N, K, full_tiles, s, vec_c, st));
+        if (rc != QMM_OK || s == 1) return rc;
+        if (full_tiles == 0) {
+            const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
+            return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
+        }
+        const int n_lo = (full_tiles / num_m) * tile.block_n();
+        const bool vec_red = (N % 8 == 0) && aligned(C, 16);
+        return hip_status(qmm_impl::launch_reduce_cols(workspace, s, M, N, n_lo, C, vec_red, st));
     }
+    if (s == 1) return hip_status(dispatch_skinny(tile, A, Wq, scale, bias, C, M, N, K, 1, vec_c, st));
     const bool vec_ws = (N % 4 == 0);
-    int rc = hip_status(dispatch_w4a16(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
+    int rc = hip_status(dispatch_skinny(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
     if (rc != QMM_OK) return rc;
     const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
     return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));

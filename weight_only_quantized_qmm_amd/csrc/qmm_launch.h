@@ -8,17 +8,16 @@
 namespace qmm_impl {
 
 // Which W4A16 kernel runs an M-row problem, and the output tile of one workgroup.
-//   SKINNY (M <= 64) : a (16*mt) x 32 tile, up to 16 waves splitting its reduction;
-//   NARROW (M <= 128): 4 waves side by side along N, each 16*ns columns x 16*mt rows;
-//   WIDE   (M > 128) : a 256 x 128 tile.
-enum W4A16Kind { W4A16_SKINNY = 0, W4A16_NARROW = 1, W4A16_WIDE = 2 };
+//   SKINNY (M <= 64): a (16*mt) x 32 tile, up to 16 waves splitting its reduction;
+//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variants 1-3).
+enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
 
 struct W4A16Tile {
     W4A16Kind kind;
-    int mt;  // 16-row MFMA subtiles per block (SKINNY: 1, 2, 4; NARROW: 8)
-    int ns;  // 16-column MFMA subtiles per wave (NARROW) or per block (SKINNY: 2)
-    int block_m() const { return kind == W4A16_WIDE ? 256 : 16 * mt; }
-    int block_n() const { return kind == W4A16_WIDE ? 128 : kind == W4A16_SKINNY ? 16 * ns : 4 * 16 * ns; }
+    int mt;  // 16-row MFMA subtiles per block (SKINNY: 1, 2, 4; WIDE: 8, 16)
+    int ns;  // SKINNY: 16-column MFMA subtiles per block (2); WIDE: kernel variant
+    int block_m() const { return 16 * mt; }
+    int block_n() const { return kind == W4A16_WIDE ? 256 : 16 * ns; }
 };
 
 // Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups.
@@ -46,19 +45,31 @@ struct DenseTile {
     int block_n() const { return 2 * 16 * ns; }
 };
 
-hipError_t launch_w4a16(W4A16Tile tile, const void *A, const void *Wq, const void *scale,
-                        const void *bias, void *out, int M, int N, int K, int s, bool vec_store,
-                        hipStream_t stream);
-
 hipError_t launch_w4a16_skinny(int mt, int gpw, int waves, const void *A, const void *Wq, const void *scale,
                                const void *bias, void *out, int M, int N, int K, int s, bool vec_store,
                                hipStream_t stream);
 
-hipError_t launch_w4a16_wide(const void *A, const void *Wq, const void *scale, const void *bias, void *out,
-                             int M, int N, int K, int s, bool vec_store, hipStream_t stream);
+// Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves (two workgroups per CU);
+// 1, 2, 3 = 256 x 256 tiles (one per CU) of 8 waves of 128 x 64, 8 waves of 256 x 32,
+// 4 waves of 256 x 64. Rows per tile, and workgroups one CU holds (LDS: 76 KB for 128
+// rows, 124 KB for 256).
+inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
+inline int wide_wgs_per_cu(int variant) { return variant == 0 ? 2 : 1; }
+constexpr int kWideCols = 256;
+
+// Large-M kernel: the first full_tiles tiles (M-block fastest) unsplit into C, the
+// remaining ones in `split` near-equal group partitions into the planes of `part`
+// ([split][M][N] bf16; unused when split = 1).
+hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
+                             void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
+                             hipStream_t stream);
 
 hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t MN, void *C,
                          bool vec, hipStream_t stream);
+
+// The same merge restricted to columns [n_lo, N) of bf16 planes [s][M][N].
+hipError_t launch_reduce_cols(const void *partials, int s, int M, int N, int n_lo, void *C, bool vec,
+                              hipStream_t stream);
 
 hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out, bool f32_out,
                         int M, int N, int K, int s, bool vec_store, hipStream_t stream);

@@ -72,6 +72,42 @@ reduce_scalar(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_
     C[i] = (uint16_t)f32_to_bf16(acc);
 }
 
+// Columns [n_lo, N) of bf16 planes [s][M][N]: W = N - n_lo columns per row; eight
+// consecutive columns per lane when W, N and n_lo are multiples of 8, else one.
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+reduce_cols(const uint16_t *__restrict__ part, uint16_t *__restrict__ C, int s, int M, int N, int n_lo)
+{
+    const int W = N - n_lo;
+    const int per = VEC ? 8 : 1;
+    const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * per;
+    if (i >= (size_t)M * (size_t)W) return;
+    const int m = (int)(i / (size_t)W);
+    const int n = n_lo + (int)(i % (size_t)W);
+    const size_t off = (size_t)m * (size_t)N + n;
+    const size_t MN = (size_t)M * (size_t)N;
+    if (VEC) {
+        float acc[8];
+        load8(part + off, acc);
+        for (int p = 1; p < s; ++p) {
+            float v[8];
+            load8(part + (size_t)p * MN + off, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4 *>(C + off) = o;
+    } else {
+        float acc = load1(part + off);
+        for (int p = 1; p < s; ++p) acc = acc + load1(part + (size_t)p * MN + off);
+        C[off] = (uint16_t)f32_to_bf16(acc);
+    }
+}
+
 template <typename T>
 hipError_t launch_t(const T *part, int s, size_t MN, uint16_t *C, bool vec, hipStream_t stream)
 {
@@ -96,6 +132,24 @@ hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t 
     if (f32_partials)
         return launch_t(static_cast<const float *>(partials), s, MN, static_cast<uint16_t *>(C), vec, stream);
     return launch_t(static_cast<const uint16_t *>(partials), s, MN, static_cast<uint16_t *>(C), vec, stream);
+}
+
+hipError_t launch_reduce_cols(const void *partials, int s, int M, int N, int n_lo, void *C, bool vec,
+                              hipStream_t stream)
+{
+    if (n_lo < 0 || n_lo >= N) return hipErrorInvalidValue;
+    const size_t elems = (size_t)M * (size_t)(N - n_lo);
+    const size_t per_thread = vec ? 8 : 1;
+    const size_t threads = (elems + per_thread - 1) / per_thread;
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    const uint16_t *p = static_cast<const uint16_t *>(partials);
+    uint16_t *c = static_cast<uint16_t *>(C);
+    (void)hipGetLastError();
+    if (vec)
+        hipLaunchKernelGGL((reduce_cols<true>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
+    else
+        hipLaunchKernelGGL((reduce_cols<false>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
+    return hipGetLastError();
 }
 
 }  // namespace qmm_impl

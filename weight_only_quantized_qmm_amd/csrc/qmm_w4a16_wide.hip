@@ -1,40 +1,48 @@
 // qmm_w4a16_wide.hip -- W4A16 group-128 matmul kernel for many rows (M > 128) on gfx950.
 //
-// Same contract as the small-M kernel (tiny-llm "Week 2 Day 7: Split-K Prefill",
-// Task 2): blockIdx.z is the partition p, the block covers groups
-// [p*gpp, (p+1)*gpp) of the reduction and writes plane p of `out` (C itself when
-// s = 1), with plain stores and no atomics.
+// Split contract of tiny-llm "Week 2 Day 7: Split-K Prefill", Task 2: a workgroup
+// computes one output tile over one group-aligned partition of the reduction and
+// writes its bf16 result into that partition's plane (C itself when unsplit), with
+// plain stores and no atomics. Beyond the page's uniform split, the grid may run the
+// first tiles unsplit and split only the remaining ones, and the partitions may differ
+// by one group (see the work decomposition above the kernel): on 256 CUs this fills
+// the last wave of workgroups instead of leaving it mostly idle.
 //
-// This regime is bound by the bf16 matrix cores, so the design maximises MFMA
-// issue: a 256 x 128 output tile per workgroup of 4 wave64s (2 x 2, each wave a
-// 128 x 64 tile of 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators), the reduction
-// walked in stages of 32 values.
+// This regime is bound by the bf16 matrix cores. A workgroup of 8 wave64s owns a
+// 256 x 256 output tile (2 x 4 waves, each a 128 x 64 tile of 4 x 2
+// v_mfma_f32_32x32x16_bf16 accumulators) and walks its partition in stages of 64
+// reduction values. The square tile halves the re-reads of A against a 256 x 128
+// tile, and 64-value stages make every row of A a whole 128-byte line.
 //
-// Data movement per stage:
-//   A: 256 rows x 32 k of bf16 (16 KB), copied global -> LDS by the direct
-//      load-to-LDS instruction (global_load_lds_dwordx4: lane i of an
-//      instruction lands at LDS base + 16*i), three stages ahead of its use;
-//   W: 128 rows x 32 k of packed nibbles (2 KB) plus the group's scale and bias,
-//      loaded into registers four stages ahead, dequantised ONCE per workgroup
-//      (w = scale*q + bias in fp32, rounded to bf16) into a bf16 LDS tile (8 KB)
-//      one stage ahead of its use.
-// LDS holds a ring of four A slots (16 KB each) and two dequantised-W buffers
-// (8 KB each): 80 KB per workgroup, two workgroups per CU. The matrix cores work
-// on stage i while stage i+1 is dequantised, A of stages i+2, i+3 is in flight
-// and W of stages i+2 .. i+5 is in flight in a four-set register ring.
+// Data movement: every global read of the kernel is a direct global -> LDS copy
+// (global_load_lds_*), two stages ahead of its use, into rings of three slots:
+//   A:  256 rows x 64 bf16 (32 KB per stage), four 1 KB copies per wave;
+//   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage), one copy per wave;
+//   scale/bias: the group's 256 + 256 bf16 values, one 2-byte copy per lane
+//       (zero-extended into a dword), once per group, in a ring of two.
+// The compiler neither sees nor waits for these copies; the kernel retires them
+// itself: at the end of stage i each wave waits (s_waitcnt vmcnt) until the copies
+// it issued for stage i+1 have landed, and the barrier that follows publishes them
+// to the whole workgroup. No other vector-memory instruction is issued in the loop,
+// so the counter arithmetic is exact.
 //
-// The compiler does not track the LDS writes of the load-to-LDS instruction, so
-// the kernel waits for them itself: before the barrier that ends stage i, each
-// wave waits (s_waitcnt vmcnt) until the copies it issued for stage i+1 have
-// landed; the barrier then publishes them to the whole workgroup.
+// Dequantisation: each wave turns its 64 columns' packed words straight into MFMA
+// operands (w = scale*q + bias in fp32, rounded to bf16). One packed 32-bit word is
+// eight consecutive reduction values, i.e. one lane's operand of one
+// 32x32x16 MFMA. For reduction step t of a stage, lane l (half h = l / 32) takes word
+// 4h + t of its row, so one 16-byte LDS read gives a lane its words for all four
+// steps; its A operand is the matching 8 values (16-byte chunk 4h + t of the row).
+// The MFMA takes the weights as its first operand, so a lane's results are four
+// consecutive output columns of one row (8-byte stores).
 //
-// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row r is stored at
-// chunk c ^ ((r >> 2) & 3), which keeps the 16-byte fragment reads (rows r..r+15
-// at one chunk) and the tile writes free of bank conflicts.
+// LDS layouts: A rows are 128 bytes (eight 16-byte chunks), chunk c of row r stored
+// at chunk c ^ ((r >> 1) & 7); W rows are 32 bytes, chunk h of row r at
+// h ^ ((r >> 3) & 1). Both keep the 16-lane phases of the 16-byte reads on distinct
+// banks.
 //
-// Block order: tiles are numbered with the M-block fastest, so with 8 M-blocks
-// (M = 2048) the workgroups that the round-robin dispatch sends to one XCD share
-// the same 256 rows of A, which then stay in that XCD's L2.
+// Block order: tiles are numbered with the M-block fastest, so with 8 M-blocks the
+// workgroups that the round-robin dispatch sends to one XCD share the same 256 rows
+// of A in that XCD's L2.
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -42,270 +50,306 @@ using namespace qmm_dev;
 
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 128;
-constexpr int BK = 32;
-constexpr int A_BYTES = BM * BK * 2;        // 16 KB per A slot, 4 slots
-constexpr int B_BYTES = BN * BK * 2;        // 8 KB per dequantised W buffer, 2 buffers
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int W_SLOT = BN * BK / 2;  // 8 KB
+constexpr int SB_SLOT = BN * 4 * 2;  // 2 KB: 256 scale dwords, then 256 bias dwords
+constexpr int ROT_GROUPS = 8;        // k-start spread of the workgroups sharing A rows
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// Tile geometry of a variant: 128*WM rows x 256 columns per workgroup, each wave a
+// (32*MI) x (32*NJ) block of 32x32 MFMA tiles, waves side by side along N first.
+template <int WM_, int MI_, int NJ_>
+struct Cfg {
+    static constexpr int WM = WM_, MI = MI_, NJ = NJ_;
+    static constexpr int BM = 128 * WM;             // rows per tile
+    static constexpr int NWN = 8 / NJ;              // waves along N (256 columns)
+    static constexpr int NWM = BM / (32 * MI);      // waves along M
+    static constexpr int NW = NWM * NWN;            // waves per workgroup
+    static constexpr int A_SLOT = BM * BK * 2;      // 16 or 32 KB
+    static constexpr int AC = (BM / 8) / NW;        // A copies (1 KB each) per wave per stage
+    static constexpr int WC = 8 / NW;               // W copies (and scale/bias copies) per wave
+    static constexpr int N_EVEN = AC + 2 * WC;      // copies a wave issues in an even stage
+    static constexpr int N_ODD = AC + WC;           // ... in an odd stage
+    static constexpr int OCC = WM == 1 ? 2 : 1;     // workgroups one CU holds (LDS)
+};
+
+// LDS of one workgroup: three A slots, three W slots, two scale/bias slots.
+template <int WM>
+struct Lds {
+    char a[3 * 128 * WM * BK * 2];
+    char w[3 * W_SLOT];
+    char sb[2 * SB_SLOT];
+};
 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64; the count's
 // low four bits sit in bits 3:0 of the immediate, its high two bits in bits 15:14).
 #define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
 
-struct WRegs {
-    u32x2 w;          // 16 packed weights of row n = tid/2, k half tid%2
-    uint32_t sc, bi;  // bf16 bits of the group's scale and bias for row n
-};
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_void *)p; }
 
-struct Ctx {
-    int rot, nst;  // k-stage rotation of this workgroup, stages in its partition
-    const uint16_t *A;
-    const uint32_t *Wq;
-    const uint16_t *scale;
-    const uint16_t *bias;
-    int M, N, K, G;
-    int m0, n0, k_begin;
-    int tid, lane, wave, wm, wn;
-};
-
-// LDS: four A slots (a ring, stage st in slot st % 4) and two dequantised-W buffers
-// (stage st in buffer st % 2): 80 KB per workgroup, two workgroups per CU.
-__shared__ __attribute__((aligned(1024))) char lds_a[4][A_BYTES];
-__shared__ __attribute__((aligned(1024))) char lds_b[2][B_BYTES];
-
-template <int S>
-__device__ __forceinline__ char *a_slot() { return lds_a[S]; }
-template <int S>
-__device__ __forceinline__ char *b_buf() { return lds_b[S]; }
-
-// W and the group's scale/bias for stage st: 3 vector-memory instructions.
-// Reduction offset of pipeline stage st: the workgroup walks its partition's stages
-// starting at a per-workgroup rotation (see the kernel), wrapping around.
-__device__ __forceinline__ int stage_k(const Ctx &c, int st) { return c.k_begin + ((st + c.rot) % c.nst) * BK; }
-
-__device__ __forceinline__ WRegs load_w(const Ctx &c, int st)
-{
-    WRegs R;
-    const int k0 = stage_k(c, st);
-    const int n = min(c.n0 + (c.tid >> 1), c.N - 1);
-    const int h = c.tid & 1;
-    R.w = *reinterpret_cast<const u32x2 *>(c.Wq + (size_t)n * (size_t)(c.K >> 3) + (k0 >> 3) + 2 * h);
-    const int g = k0 >> 7;
-    R.sc = c.scale[(size_t)n * c.G + g];
-    R.bi = c.bias[(size_t)n * c.G + g];
-    return R;
-}
-
-// One 16-byte global -> LDS copy per lane: lane i's bytes land at LDS byte
-// address lds_off + 16*i (lds_off is wave-uniform, passed in M0). Issued as inline
-// assembly so that the compiler neither tracks nor waits for it: the kernel orders
-// these copies itself with explicit s_waitcnt vmcnt and workgroup barriers.
-__device__ __forceinline__ void copy16_to_lds(const void *gsrc, uint32_t lds_off)
-{
+// Global -> LDS copies (global_load_lds_*, address = scalar base + 32-bit lane offset).
+// Lane i's data lands at LDS byte lds_off + 16*i (dwordx4) or lds_off + 4*i (ushort,
+// zero-extended to a dword); lds_off is wave-uniform and travels in M0. Inline assembly,
+// so that the compiler neither tracks nor waits for them.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(gsrc) : "memory", "m0");
+__device__ __forceinline__ void copy16(uint32_t lds_off, uint32_t voff, const void *sbase)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy2(uint32_t lds_off, uint32_t voff, const void *sbase)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds_off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+template <class CF>
+struct Ctx {
+    const char *A;      // A + m0*K (bytes), wave-uniform
+    const char *Wq;     // Wq + n0*K/8 words (bytes)
+    const char *sb[CF::WC];  // scale/bias source of this wave's copies (scale or bias, + n0*G)
+    int gpp, rot, g_begin;
+    uint32_t a_off[CF::AC];    // per-lane byte offsets of the A copies (stage k excluded)
+    uint32_t w_off[CF::WC];    // per-lane byte offsets of the W copies
+    uint32_t sb_off[CF::WC];   // per-lane byte offsets of the scale/bias copies
+    uint32_t a_lds, w_lds, sb_lds;  // this wave's destinations inside slot 0
+    uint32_t a_rd[4];   // per-lane LDS byte offsets of the A operand reads, step t
+    uint32_t w_rd, sb_rd;
+};
+
+// Group of stage x (two stages per group), rotated per workgroup.
+template <class CF>
+__device__ __forceinline__ int stage_group(const Ctx<CF> &c, int x)
+{
+    int g = (x >> 1) + c.rot;
+    if (g >= c.gpp) g -= c.gpp;
+    return c.g_begin + g;
 }
 
-template <int S>
-__device__ __forceinline__ uint32_t a_slot_lds_offset() { return (uint32_t)(uintptr_t)(lds_void *)a_slot<S>(); }
-
-// A tile of stage st into LDS slot S: 4 copy instructions per wave.
-// Instruction q = 4*wave + j fills LDS bytes [1024q, 1024q + 1024) of the A region,
-// i.e. rows 16q .. 16q+15; lane i carries LDS 16-byte position 64q + i, which is
-// row r = 16q + i/4, stored chunk i%4, so it fetches logical chunk (i%4) ^ ((r>>2)&3).
-template <int S>
-__device__ __forceinline__ void dma_a(const Ctx &c, int st)
+// The copies of stage x into A/W slot `slot3` (and its group's scale/bias into
+// slot `sbslot` when WITH_SB): AC + WC (+ WC) vector-memory instructions per wave.
+template <class CF, bool WITH_SB>
+__device__ __forceinline__ void issue(const Ctx<CF> &c, int x, int slot3, int sbslot)
 {
-    const int k0 = stage_k(c, st);
-    const uint32_t base = a_slot_lds_offset<S>() + 4096u * (uint32_t)__builtin_amdgcn_readfirstlane(c.wave);
+    typedef CF GE;
+    const int g = __builtin_amdgcn_readfirstlane(stage_group(c, x));
+    const int k0 = g * 128 + (x & 1) * BK;
+    const char *Ab = c.A + 2 * (size_t)k0;
+    const uint32_t a_dst = c.a_lds + (uint32_t)slot3 * GE::A_SLOT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = 4 * c.wave + j;
-        const int r = 16 * q + (c.lane >> 2);
-        const int chunk = (c.lane & 3) ^ ((r >> 2) & 3);
-        const int m = min(c.m0 + r, c.M - 1);
-        copy16_to_lds(c.A + (size_t)m * (size_t)c.K + k0 + 8 * chunk, base + 1024u * j);
+    for (int j = 0; j < GE::AC; ++j) copy16(a_dst + 1024u * j, c.a_off[j], Ab);
+    const uint32_t w_dst = c.w_lds + (uint32_t)slot3 * W_SLOT;
+#pragma unroll
+    for (int j = 0; j < GE::WC; ++j) copy16(w_dst + 1024u * j, c.w_off[j], c.Wq + (size_t)(k0 >> 1));
+    if (WITH_SB) {
+        const uint32_t sb_dst = c.sb_lds + (uint32_t)sbslot * SB_SLOT;
+#pragma unroll
+        for (int j = 0; j < GE::WC; ++j) copy2(sb_dst + 256u * j, c.sb_off[j], c.sb[j] + 2 * (size_t)g);
     }
 }
 
-// Dequantise stage registers into dequantised-W buffer S (row n = tid/2, chunks 2h
-// and 2h+1 of its 64-byte row).
-template <int S>
-__device__ __forceinline__ void dequant_w(const Ctx &c, const WRegs &R)
+// The 32 MFMAs of one stage for this wave, operands from A/W slot `slot3` and
+// scale/bias slot `sbslot`.
+template <class CF>
+__device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF::WM> &L, int slot3, int sbslot,
+                                        f32x16 (&acc)[CF::MI][CF::NJ])
 {
-    char *Bs = b_buf<S>();
-    const int n = c.tid >> 1;
-    const int h = c.tid & 1;
-    const float sc = bf16_to_f32(R.sc);
-    const float bi = bf16_to_f32(R.bi);
-    const float sc16 = sc * 0.0625f;
-    *reinterpret_cast<uint4 *>(Bs + swz(n, 2 * h)) = dequant8(R.w[0], sc, sc16, bi);
-    *reinterpret_cast<uint4 *>(Bs + swz(n, 2 * h + 1)) = dequant8(R.w[1], sc, sc16, bi);
-}
-
-// sched_group_barrier masks (instruction classes the scheduler may place in a group)
-constexpr int SG_VALU = 0x002;
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DS_READ = 0x100;
-
-// The MFMAs of one stage (2 x 8 per wave) with the dequantisation of the next stage's
-// W (2 x 22 VALU instructions) and the second half's LDS reads woven between them,
-// so the vector ALU work runs in the shadow of the matrix cores instead of before them.
-template <int SA, int SB>
-__device__ __forceinline__ void compute_and_dequant(const Ctx &c, f32x16 (&acc)[4][2], const WRegs &wn,
-                                                    uint4 &d0, uint4 &d1)
-{
-    const char *As = a_slot<SA>();
-    const char *Bs = b_buf<SB>();
-    const int r = c.lane & 31;
-    const int sl = c.lane >> 5;
-    const float sc = bf16_to_f32(wn.sc);
-    const float bi = bf16_to_f32(wn.bi);
-    const float sc16 = sc * 0.0625f;
-    bf16x8 af[2][4], bfr[2][2];
+    constexpr int MI = CF::MI, NJ = CF::NJ;
+    const char *As = L.a + slot3 * CF::A_SLOT;
+    const char *Ws = L.w + slot3 * W_SLOT;
+    const char *Ss = L.sb + sbslot * SB_SLOT;
+    uint4 wpk[NJ];
+    float sc[NJ], sc16[NJ], bi[NJ];
 #pragma unroll
-    for (int k16 = 0; k16 < 2; ++k16) {
-        const int chunk = 2 * k16 + sl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[k16][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + swz(c.wm * 128 + i * 32 + r, chunk)));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bfr[k16][j] = as_bf16x8(*reinterpret_cast<const uint4 *>(Bs + swz(c.wn * 64 + j * 32 + r, chunk)));
+    for (int j = 0; j < NJ; ++j) {
+        wpk[j] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd + 1024 * j);
+        sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd + 128 * j));
+        bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 + c.sb_rd + 128 * j));
+        sc16[j] = sc[j] * 0.0625f;
     }
-    d0 = dequant8(wn.w[0], sc, sc16, bi);
-    d1 = dequant8(wn.w[1], sc, sc16, bi);
+    // Software pipeline over the four reduction steps: the A operands and dequantised
+    // weights of step t+1 are produced while the MFMAs of step t run. The scheduling
+    // fences keep the compiler from sinking the next step's LDS reads down to their
+    // use, which would expose the LDS latency before every MFMA.
+    bf16x8 af[2][MI], bfr[2][NJ];
 #pragma unroll
-    for (int k16 = 0; k16 < 2; ++k16)
+    for (int i = 0; i < MI; ++i) af[0][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[0] + 4096 * i));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NJ; ++j) bfr[0][j] = as_bf16x8(dequant8(wpk[j].x, sc[j], sc16[j], bi[j]));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(bfr[k16][j], af[k16][i], acc[i][j]);
-    // Schedule: the first half's 6 LDS reads, then 8 MFMAs each followed by 3 VALU,
-    // with the second half's 6 reads issued after the second MFMA; then 8 more MFMAs
-    // each followed by 3 VALU.
-    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+    for (int t = 0; t < 4; ++t) {
+        const int cur = t & 1, nxt = cur ^ 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < 3) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
-        if (q == 1) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+            for (int i = 0; i < MI; ++i)
+                af[nxt][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t + 1] + 4096 * i));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                bfr[nxt][j] = as_bf16x8(dequant8(word_of(wpk[j], t + 1), sc[j], sc16[j], bi[j]));
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bfr[cur][j], af[cur][i], acc[i][j]);
     }
-}
-
-// One stage: st is computed from A slot CUR = st % 4 and W buffer st % 2, while the
-// W registers `wr` (stage st+1) are dequantised into buffer (st+1) % 2 and then
-// refilled with stage st+5. The body is branch-free: past the last stage the
-// indices are clamped, so the extra loads only touch slots and buffers that are
-// never read again, and every stage issues exactly 7 vector-memory instructions
-// (A: 4 copies first, W: 3 loads last).
-template <int CUR>
-__device__ __forceinline__ void stage(const Ctx &c, int st, int nst, WRegs &wr, f32x16 (&acc)[4][2])
-{
-    dma_a<(CUR + 3) % 4>(c, min(st + 3, nst - 1));
-    uint4 d0, d1;
-    compute_and_dequant<CUR, CUR % 2>(c, acc, wr, d0, d1);
-    {
-        char *Bs = b_buf<(CUR + 1) % 2>();
-        const int n = c.tid >> 1;
-        const int h = c.tid & 1;
-        *reinterpret_cast<uint4 *>(Bs + swz(n, 2 * h)) = d0;
-        *reinterpret_cast<uint4 *>(Bs + swz(n, 2 * h + 1)) = d1;
-    }
-    wr = load_w(c, min(st + 5, nst - 1));
-    // The A copies of stage st+1 were the first 4 instructions of stage st-2; issued
-    // after them: 3 + 7 + 7 = 17. Waiting until at most 17 are outstanding retires
-    // them, whatever order the instructions have within a stage.
-    QMM_WAIT_VMCNT(17);
-    __syncthreads();
-    // Keep the next stage's instructions below the barrier.
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ void __launch_bounds__(256, 2)
+// Work decomposition (one-dimensional grid of full_tiles + tail_tiles * split
+// workgroups): workgroup b < full_tiles computes tile b over the whole reduction and
+// writes C; the others compute tile full_tiles + q % tail_tiles (q = b - full_tiles)
+// over partition p = q / tail_tiles, the groups [floor(p*G/split), floor((p+1)*G/split)),
+// and write plane p of `part` (C itself when split = 1). With full_tiles = 0 this is the
+// plain split into `split` partitions (equal ones when split divides G).
+template <class CF>
+__global__ void __launch_bounds__(64 * CF::NW, CF::OCC)
 w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                   const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                  uint16_t *__restrict__ out, int M, int N, int K, int gpp, int vec_store)
+                  uint16_t *__restrict__ C, uint16_t *__restrict__ part, int M, int N, int K,
+                  int full_tiles, int tail_tiles, int split, int vec_store)
 {
-    Ctx c;
-    c.A = A;
-    c.Wq = Wq;
-    c.scale = scale;
-    c.bias = bias;
-    c.M = M;
-    c.N = N;
-    c.K = K;
-    c.G = K >> 7;
-    c.tid = threadIdx.x;
-    c.lane = c.tid & 63;
-    c.wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);  // wave-uniform
-    c.wm = c.wave >> 1;
-    c.wn = c.wave & 1;
-    const int num_m = (M + BM - 1) / BM;
-    c.m0 = (blockIdx.x % num_m) * BM;
-    c.n0 = (blockIdx.x / num_m) * BN;
-    c.k_begin = blockIdx.z * gpp * 128;
-    const int nst = gpp * (128 / BK);  // a multiple of 4, at least 4
-    // Workgroups that run side by side on one XCD share rows of A; starting each at a
-    // different group (4 stages) of the partition spreads their simultaneous reads of
-    // A over more L2 channels. The order of the fp32 sums depends only on the tile.
-    c.nst = nst;
-    c.rot = ((blockIdx.x / num_m) * 4) % nst;
-    uint16_t *dst = out + (size_t)blockIdx.z * (size_t)M * (size_t)N;
+    typedef CF GE;
+    constexpr int MI = CF::MI, NJ = CF::NJ;
+    __shared__ __attribute__((aligned(1024))) Lds<CF::WM> L;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wm = wave / CF::NWN;  // row block of the wave (32*MI rows)
+    const int wn = wave % CF::NWN;  // column block of the wave (32*NJ columns)
+    const int G = K >> 7;
+    const int b = blockIdx.x;
+    int tile, p, nparts;
+    if (b < full_tiles) {
+        tile = b;
+        p = 0;
+        nparts = 1;
+    } else {
+        const int q = b - full_tiles;
+        tile = full_tiles + q % tail_tiles;
+        p = q / tail_tiles;
+        nparts = split;
+    }
+    const int g_lo = (int)(((long long)p * G) / nparts);
+    const int g_hi = (int)(((long long)(p + 1) * G) / nparts);
+    const int gpp = g_hi - g_lo;  // >= 1: nparts <= G
+    uint16_t *dst = nparts > 1 ? part + (size_t)p * (size_t)M * (size_t)N : C;
+    const int num_m = (M + GE::BM - 1) / GE::BM;
+    const int m_idx = tile % num_m;
+    const int n_idx = tile / num_m;
+    const int m0 = m_idx * GE::BM;
+    const int n0 = n_idx * BN;
 
-    f32x16 acc[4][2];
+    Ctx<CF> c;
+    c.gpp = gpp;
+    c.g_begin = g_lo;
+    // Workgroups that run side by side on one XCD share rows of A; starting them at
+    // different groups (within a window of ROT_GROUPS) spreads their simultaneous
+    // reads of A over more L2 channels. The fp32 sums' order depends only on the tile
+    // and the partition.
+    c.rot = (n_idx % ROT_GROUPS) % gpp;
+    c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
+    c.Wq = reinterpret_cast<const char *>(Wq) + (size_t)n0 * (size_t)(K >> 1);
+
+    // Copy lanes. A: copy j of wave w fills LDS rows 8q .. 8q+7, q = AC*w + j; lane i
+    // lands at row r = 8q + i/8, stored chunk i%8, so it fetches logical chunk
+    // (i%8) ^ ((r>>1)&7). Rows past M re-read row M-1 (never stored).
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < GE::AC; ++j) {
+        const int r = 8 * (GE::AC * wave + j) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        const int rr = min(m0 + r, M - 1) - m0;
+        c.a_off[j] = 2u * ((uint32_t)rr * (uint32_t)K + 8u * (uint32_t)chunk);
+    }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < GE::WC; ++j) {
+        // W: copy q = w*WC + j fills rows 32q .. 32q+31 (32 bytes each); lane i -> row
+        // 32q + i/2, stored chunk i%2, logical chunk (i%2) ^ ((r>>3)&1). Rows past N
+        // re-read N-1.
+        const int q = wave * GE::WC + j;
+        const int r = 32 * q + (lane >> 1);
+        const int h = (lane & 1) ^ ((r >> 3) & 1);
+        const int rr = min(n0 + r, N - 1) - n0;
+        c.w_off[j] = (uint32_t)(rr * (K >> 1) + 16 * h);
+        // scale (copies 0..3) / bias (copies 4..7): lane i -> row 64*(q%4) + i.
+        const int rs = min(n0 + 64 * (q & 3) + lane, N - 1) - n0;
+        c.sb_off[j] = (uint32_t)(2 * rs * G);
+        c.sb[j] = reinterpret_cast<const char *>(q < 4 ? scale : bias) + 2 * (size_t)n0 * (size_t)G;
+    }
+    c.a_lds = lds_addr(L.a) + 1024u * (uint32_t)(GE::AC * wave);
+    c.w_lds = lds_addr(L.w) + 1024u * (uint32_t)(wave * GE::WC);
+    c.sb_lds = lds_addr(L.sb) + 256u * (uint32_t)(wave * GE::WC);
+    // Operand reads: lane (r32 = lane % 32, half h = lane / 32).
+    {
+        const int r32 = lane & 31;
+        const int h = lane >> 5;
+        const int arow = wm * 32 * MI + r32;  // + 32 i (leaves the swizzle bits unchanged)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) c.a_rd[t] = (uint32_t)(arow * 128 + 16 * ((4 * h + t) ^ ((arow >> 1) & 7)));
+        const int nrow = wn * 32 * NJ + r32;  // + 32 j (likewise)
+        c.w_rd = (uint32_t)(nrow * 32 + 16 * (h ^ ((nrow >> 3) & 1)));
+        c.sb_rd = (uint32_t)(4 * nrow);
+    }
+
+    f32x16 acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // Prologue: W of stages 0..3 into the register ring, A of stages 0..2 into
-    // slots 0..2, W of stage 0 dequantised into buffer 0, W of stage 4 loaded.
-    dma_a<0>(c, 0);
-    WRegs w0 = load_w(c, 0);
-    dma_a<1>(c, 1);
-    WRegs w1 = load_w(c, 1);
-    dma_a<2>(c, 2);
-    WRegs w2 = load_w(c, 2);
-    WRegs w3 = load_w(c, 3);
-    dequant_w<0>(c, w0);
-    w0 = load_w(c, min(4, nst - 1));
-    // A of stage 0 landed: issued after it are W0 (3), A1 (4), W1 (3), A2 (4), W2, W3, W4 (9) = 23;
-    // the A copies of stages 1 and 2 are then retired by the waits of stages 0 and 1.
-    QMM_WAIT_VMCNT(23);
+    const int nst = 2 * gpp;  // stages in the partition, even
+    // Prologue: stage 0 (A, W, group 0's scale/bias) and stage 1 (A, W); wait for stage 0.
+    issue<CF, true>(c, 0, 0, 0);
+    issue<CF, false>(c, 1, 1, 0);
+    QMM_WAIT_VMCNT(GE::N_ODD);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Stage st uses A slot st % 4, W buffer st % 2 and W register set st % 4
-    // (w0 holds stages 0, 4, 8, ...; w1 holds 1, 5, ...). nst is a multiple of 4.
-    for (int st = 0; st < nst; st += 4) {
-        stage<0>(c, st, nst, w1, acc);
-        stage<1>(c, st + 1, nst, w2, acc);
-        stage<2>(c, st + 2, nst, w3, acc);
-        stage<3>(c, st + 3, nst, w0, acc);
+    // Stage x uses A/W slot x % 3 and scale/bias slot (x/2) % 2. Stage st (even)
+    // issues stage st+2 with its group's scale/bias (N_EVEN copies per wave), stage
+    // st+1 issues stage st+3 (N_ODD); past the last stage the copies repeat stage
+    // nst-1 into slots that are never read again, so every stage issues the same count.
+    int s3 = 0;  // st % 3
+    for (int st = 0; st < nst; st += 2) {
+        const int s3n = s3 == 2 ? 0 : s3 + 1;    // (st+1) % 3
+        const int s3p = s3 == 0 ? 2 : s3 - 1;    // (st+2) % 3
+        const int sbs = (st >> 1) & 1;
+        issue<CF, true>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
+        compute<CF>(c, L, s3, sbs, acc);
+        // stage st+1's copies (issued one stage earlier) are followed by this stage's
+        QMM_WAIT_VMCNT(GE::N_EVEN);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        issue<CF, false>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
+        compute<CF>(c, L, s3n, sbs, acc);
+        // stage st+2's copies (issued above) are followed by this stage's
+        QMM_WAIT_VMCNT(GE::N_ODD);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        s3 = s3p;
     }
+    // No copy may still be writing LDS when the workgroup ends.
+    QMM_WAIT_VMCNT(0);
 
-    // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*128 + 32i + (lane % 32)
-    // and n = n0 + wn*64 + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
-    const int r = c.lane & 31;
-    const int sl = c.lane >> 5;
+    // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*32*MI + 32i + (lane % 32)
+    // and n = n0 + wn*32*NJ + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
+    const int r = lane & 31;
+    const int sl = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = c.m0 + c.wm * 128 + 32 * i + r;
+    for (int i = 0; i < MI; ++i) {
+        const int m = m0 + wm * 32 * MI + 32 * i + r;
         const bool row_ok = m < M;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int vq = 0; vq < 4; ++vq) {
-                const int n = c.n0 + c.wn * 64 + 32 * j + 8 * vq + 4 * sl;
+                const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
                 uint16_t *p = dst + (size_t)m * (size_t)N + n;
                 const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
                 const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
@@ -327,20 +371,50 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
     }
 }
 
+typedef Cfg<1, 4, 2> CfgV0;  // 128 x 256 tile, 4 waves of 128 x 64, two workgroups per CU
+typedef Cfg<2, 4, 2> CfgV1;  // 256 x 256 tile, 8 waves of 128 x 64
+typedef Cfg<2, 8, 1> CfgV2;  // 256 x 256 tile, 8 waves of 256 x 32
+typedef Cfg<2, 8, 2> CfgV3;  // 256 x 256 tile, 4 waves of 256 x 64 (accumulators in AGPRs)
+
+template <class CF>
+void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
+                const uint16_t *bi, uint16_t *c, uint16_t *pt, int M, int N, int K, int full_tiles, int tail_tiles,
+                int split, int vec)
+{
+    hipLaunchKernelGGL((w4a16_wide_kernel<CF>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt, M, N, K,
+                       full_tiles, tail_tiles, split, vec);
+}
+
 }  // namespace
 
 namespace qmm_impl {
 
-hipError_t launch_w4a16_wide(const void *A, const void *Wq, const void *scale, const void *bias, void *out,
-                             int M, int N, int K, int s, bool vec_store, hipStream_t stream)
+// The per-lane copy offsets are 32-bit byte offsets within 256 rows of A: K < 2^22.
+hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
+                             void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
+                             hipStream_t stream)
 {
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    const int gpp = (K / 128) / s;
+    if (K >= (1 << 22) || variant < 0 || variant > 3) return hipErrorInvalidValue;
+    const int rows = wide_rows(variant);
+    const int tiles = ((M + rows - 1) / rows) * ((N + BN - 1) / BN);
+    if (full_tiles < 0 || full_tiles > tiles || split < 1 || split > K / 128) return hipErrorInvalidValue;
+    if (split > 1 && !part) return hipErrorInvalidValue;
+    const int tail_tiles = tiles - full_tiles;
+    const dim3 grid(full_tiles + tail_tiles * split);
+    const uint16_t *a = static_cast<const uint16_t *>(A);
+    const uint32_t *w = static_cast<const uint32_t *>(Wq);
+    const uint16_t *sc = static_cast<const uint16_t *>(scale);
+    const uint16_t *bi = static_cast<const uint16_t *>(bias);
+    uint16_t *c = static_cast<uint16_t *>(C);
+    uint16_t *pt = static_cast<uint16_t *>(part);
+    const int vec = vec_store ? 1 : 0;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(w4a16_wide_kernel, dim3(tiles, 1, s), dim3(256), 0, stream,
-                       static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
-                       static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       static_cast<uint16_t *>(out), M, N, K, gpp, vec_store ? 1 : 0);
+    switch (variant) {
+    case 0: launch_cfg<CfgV0>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    case 1: launch_cfg<CfgV1>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    case 2: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    default: launch_cfg<CfgV3>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    }
     return hipGetLastError();
 }
 

@@ -176,6 +176,51 @@ def dominant_roofline(torch, shapes, rounds=4):
     return roof, calib
 
 
+def dense_sweep(torch, syn, q):
+    """Dense bf16 split-K, A, B bf16 [512, 16384]: us per call for each s of the sweep and
+    for the library's own choice (s = 0), over >= 1 GiB of rotated inputs."""
+    M = N = 512
+    K = 16384
+    d = syn.dense_inputs(M, N, K, seed=3000)
+
+    def dev16(x):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    base = (dev16(d["A"]), dev16(d["B"]))
+    R = max(8, math.ceil(ROTATE_BYTES / (2 * (M + N) * K)))
+    sets = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(4 * 32 * M * N, dtype=torch.uint8, device="cuda")
+    out = {}
+    for s in (1, 2, 4, 6, 8, 12, 16, 32, 0):
+        def run(s=s):
+            for r in range(R):
+                A, B = sets[r]
+                q.qmm_bf16_splitk(A, B, C, M, N, K, s, ws if s != 1 else None, ws.numel() if s != 1 else 0)
+        g = graph_of(torch, run)
+        out["policy" if s == 0 else "s%d" % s] = round(time_graph(torch, g) / R * 1e6, 3)
+        del g
+    del sets, ws
+    torch.cuda.empty_cache()
+    byts, flops = 2 * (M + N) * K + 2 * M * N, 2 * M * N * K
+    t = out["policy"] * 1e-6
+    return {"shape": [M, N, K], "us": out, "roof_us": round(max(byts / HBM_PEAK, flops / MFMA_BF16_PEAK) * 1e6, 3),
+            "frac_policy": round(max(byts / HBM_PEAK, flops / MFMA_BF16_PEAK) / t, 4)}
+
+
+def decode_table(torch, syn, q):
+    """Decode shapes (down, gate at M = 1, 4, 8): the policy's split against the unsplit
+    control, with the weight-read rate (packed weights + scale/bias bytes / time)."""
+    rows = []
+    for name, M, N, K, idx in syn.decode_sweep():
+        sh, R, t = per_shape(torch, syn, q, name, M, N, K, idx + 100)
+        wbytes = N * K // 2 + N * (K // 128) * 4
+        rows.append(dict(name=name, M=M, N=N, K=K, s=sh.s, us=round(t[0] * 1e6, 3), us_unsplit=round(t[1] * 1e6, 3),
+                         weight_gbs=round(wbytes / t[0] / 1e9, 1), weight_frac_hbm=round(wbytes / t[0] / HBM_PEAK, 4)))
+    return rows
+
+
 def pmc_run():
     """Workload of the counter passes: each M = 2048 shape once unsplit, then one plain copy."""
     import torch
@@ -449,6 +494,11 @@ def main():
                               roof_us=round(r["t_roof_us"], 3), frac=round(r["frac"], 4), rotation_sets=R))
             print("# %s" % json.dumps(table[-1]), file=sys.stderr, flush=True)
 
+    dense = decode = None
+    if not args.no_per_shape:
+        dense = dense_sweep(torch, syn, q)
+        decode = decode_table(torch, syn, q)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(syn, args.cpu_seconds)
@@ -476,6 +526,8 @@ def main():
         "cpu_baseline": cpu,
         "machine_floors": calib,
         "shapes": table,
+        "dense_bf16_splitk": dense,
+        "decode": decode,
     }
     if table:
         small = [t for t in table if t["M"] <= 128]

@@ -1,19 +1,27 @@
 // qmm_dense.hip -- dense bf16 split-K matmul C = A . B^T for gfx950.
 //
-// gpu-kernels-explained "Split-K, streams and overlap", Concept: a small output
-// with a long reduction gives too few output tiles to fill the GPU; cutting k
-// into s slices multiplies the blocks by s, each block computes one tile over
-// one slice, and a second pass adds the s partial sums. Here the slices are
-// near-equal runs of 32-value granules (one MFMA depth): partition p covers
-// granules [floor(p*U/s), floor((p+1)*U/s)), U = K/32. Each partition writes
-// an fp32 partial plane (plain stores, no atomics); with s = 1 the block writes
-// the bf16 result directly.
+// gpu-kernels-explained "Split-K, streams and overlap", Concept and Maths: a small
+// output with a long reduction gives too few output tiles to fill the GPU; cutting k
+// into s slices multiplies the workgroups by s, each computes one tile over one slice,
+// and a second pass adds the s partial sums. Here the slices are near-equal runs of
+// 32-value granules: partition p covers granules [floor(p*U/s), floor((p+1)*U/s)),
+// U = K/32. Each partition writes an fp32 partial plane (plain stores, no atomics);
+// with s = 1 the workgroup writes the bf16 result directly.
 //
-// Work decomposition: a workgroup is 2 x 2 wave64s; each wave owns a
-// (16*MT) x (16*NS) output tile and streams its A rows and B rows straight from
-// global memory with 128-bit loads (lane l: row l%16 of a subtile, eight k
-// values of slot l/16 of the current 32-deep granule), prefetching the next
-// granule while the MFMAs of the current one run.
+// Structure (the same pipeline as the large-M W4A16 kernel, without the dequant):
+//   * a workgroup of 4 wave64s owns a 128 x 128 output tile (2 x 2 waves, each a
+//     64 x 64 block of 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators);
+//   * the partition is walked in stages of 64 reduction values; A and B rows of a stage
+//     (128 bytes each) are copied global -> LDS by global_load_lds_dwordx4, two stages
+//     ahead, into rings of three 16 KB slots each (96 KB); each wave waits for its own
+//     copies of the next stage (s_waitcnt vmcnt) before the barrier that ends a stage;
+//   * a partition with an odd number of granules ends with a half stage (32 values):
+//     its copies re-read the first half of the row instead of reading past it, and
+//     the two reduction steps of the missing half are skipped;
+//   * LDS rows are 128 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7);
+//   * B is the MFMA's first operand, so a lane's results are four consecutive output
+//     columns of one row (16-byte fp32 or 8-byte bf16 stores);
+//   * workgroups are ordered so that each XCD computes whole partitions (see below).
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -21,134 +29,228 @@ using namespace qmm_dev;
 
 namespace {
 
-template <int MT, int NS, bool F32_OUT>
-__global__ void __launch_bounds__(256)
+constexpr int TM = 128, TN = 128, SK = 64;
+constexpr int SLOT = TM * SK * 2;  // 16 KB per operand per stage
+constexpr int NCOPY = 8;           // copies per wave per stage: 4 of A, 4 of B
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+#define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(const lds_void *)p; }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One 16-byte global -> LDS copy per lane (lane i lands at lds_off + 16*i), scalar base
+// plus 32-bit lane offset; inline assembly so that the compiler does not wait for it.
+__device__ __forceinline__ void copy16(uint32_t lds_off, uint32_t voff, const void *sbase)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+constexpr int RING = 3;  // slots per operand: stage x in slot x % 3
+
+struct DenseLds {
+    char a[RING * SLOT];
+    char b[RING * SLOT];
+};
+
+struct DCtx {
+    const char *A, *B;     // A + m0*K, B + n0*K (bytes)
+    int k_begin, k_end;    // reduction range of the partition
+    uint32_t a_off[4][2];  // per-lane byte offsets of the A copies: full / half stage
+    uint32_t b_off[4][2];
+    uint32_t a_lds, b_lds; // this wave's copy destinations inside slot 0
+    uint32_t a_rd[4], b_rd[4];  // operand read offsets, reduction step t
+};
+
+// Copies of stage x (k0 = k_begin + 64x) into slot `slot`: 8 instructions per wave.
+__device__ __forceinline__ void issue(const DCtx &c, int x, int slot)
+{
+    const int k0 = c.k_begin + SK * x;
+    const int half = (c.k_end - k0) < SK ? 1 : 0;
+    const char *Ab = c.A + 2 * (size_t)k0;
+    const char *Bb = c.B + 2 * (size_t)k0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy16(c.a_lds + (uint32_t)slot * SLOT + 1024u * j, c.a_off[j][half], Ab);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) copy16(c.b_lds + (uint32_t)slot * SLOT + 1024u * j, c.b_off[j][half], Bb);
+}
+
+__device__ __forceinline__ void compute(const DCtx &c, const DenseLds &L, int slot, bool half, f32x16 (&acc)[2][2])
+{
+    const char *As = L.a + slot * SLOT;
+    const char *Bs = L.b + slot * SLOT;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if (half && t >= 2) break;  // uniform: the missing half of a half stage
+        bf16x8 af[2], bf[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t] + 4096 * i));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(Bs + c.b_rd[t] + 4096 * j));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(bf[j], af[i], acc[i][j]);
+    }
+}
+
+template <bool F32_OUT>
+__global__ void __launch_bounds__(256, 1)
 dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ out,
              int M, int N, int K, int s, int vec_store)
 {
+    __shared__ __attribute__((aligned(1024))) DenseLds L;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int r = lane & 15;
-    const int slot = lane >> 4;
-    const int m_wave = blockIdx.y * (2 * 16 * MT) + (wave >> 1) * (16 * MT);
-    const int n_wave = blockIdx.x * (2 * 16 * NS) + (wave & 1) * (16 * NS);
-    if (m_wave >= M || n_wave >= N) return;  // no block-wide synchronisation follows
-    const int p = blockIdx.z;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int num_m = (M + TM - 1) / TM;
+    const int tiles = num_m * ((N + TN - 1) / TN);
+    // XCD-aware order: the dispatcher sends workgroup b to XCD b % 8, so when the grid
+    // is a multiple of 8 XCD x gets the contiguous run [x*G/8, (x+1)*G/8) of the
+    // (partition, tile) list in partition-major order: whole partitions per XCD, whose
+    // A and B slices are then read into that XCD's L2 once instead of once per XCD.
+    const int total = tiles * s;
+    const int b = blockIdx.x;
+    const int L_idx = (total % 8 == 0) ? (b % 8) * (total / 8) + b / 8 : b;
+    const int tile = L_idx % tiles;
+    const int p = L_idx / tiles;
+    const int m0 = (tile % num_m) * TM;
+    const int n0 = (tile / num_m) * TN;
     const long long U = K >> 5;
-    const int u_begin = (int)(((long long)p * U) / s);
-    const int u_end = (int)(((long long)(p + 1) * U) / s);
+    const int u_lo = (int)(((long long)p * U) / s);
+    const int u_hi = (int)(((long long)(p + 1) * U) / s);
 
-    const uint4 *bptr[NS];
+    DCtx c;
+    c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
+    c.B = reinterpret_cast<const char *>(B) + 2 * (size_t)n0 * (size_t)K;
+    c.k_begin = 32 * u_lo;
+    c.k_end = 32 * u_hi;
+    // Copy j of wave w fills LDS rows 8q .. 8q+7, q = 4w + j; lane i -> row 8q + i/8,
+    // stored chunk i%8, logical chunk (i%8) ^ ((r>>1)&7); a half stage reads logical
+    // chunk & 3 (the stage's valid half). Rows past M (N) re-read the last row.
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        const int n = min(n_wave + 16 * j + r, N - 1);
-        bptr[j] = reinterpret_cast<const uint4 *>(B + (size_t)n * (size_t)K) + slot;
+    for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (4 * wave + j) + (lane >> 3);
+        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+        const int ra = min(m0 + r, M - 1) - m0;
+        const int rb = min(n0 + r, N - 1) - n0;
+        c.a_off[j][0] = 2u * ((uint32_t)ra * (uint32_t)K + 8u * (uint32_t)chunk);
+        c.a_off[j][1] = 2u * ((uint32_t)ra * (uint32_t)K + 8u * (uint32_t)(chunk & 3));
+        c.b_off[j][0] = 2u * ((uint32_t)rb * (uint32_t)K + 8u * (uint32_t)chunk);
+        c.b_off[j][1] = 2u * ((uint32_t)rb * (uint32_t)K + 8u * (uint32_t)(chunk & 3));
     }
-    const uint4 *aptr[MT];
+    c.a_lds = lds_addr(L.a) + 4096u * (uint32_t)wave;
+    c.b_lds = lds_addr(L.b) + 4096u * (uint32_t)wave;
+    {
+        // Reduction step t, lane half h: logical chunk 2t + h (eight values) of the row.
+        const int r32 = lane & 31, h = lane >> 5;
+        const int arow = wm * 64 + r32;  // + 32 i: same swizzle
+        const int brow = wn * 64 + r32;  // + 32 j
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = min(m_wave + 16 * i + r, M - 1);
-        aptr[i] = reinterpret_cast<const uint4 *>(A + (size_t)m * (size_t)K) + slot;
-    }
-
-    f32x4 acc[MT][NS];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    uint4 bn[NS], an[MT];
-    if (u_begin < u_end) {
-#pragma unroll
-        for (int j = 0; j < NS; ++j) bn[j] = bptr[j][4 * u_begin];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) an[i] = aptr[i][4 * u_begin];
-    }
-    for (int u = u_begin; u < u_end; ++u) {
-        uint4 bc[NS], ac[MT];
-#pragma unroll
-        for (int j = 0; j < NS; ++j) bc[j] = bn[j];
-#pragma unroll
-        for (int i = 0; i < MT; ++i) ac[i] = an[i];
-        if (u + 1 < u_end) {
-#pragma unroll
-            for (int j = 0; j < NS; ++j) bn[j] = bptr[j][4 * (u + 1)];
-#pragma unroll
-            for (int i = 0; i < MT; ++i) an[i] = aptr[i][4 * (u + 1)];
+        for (int t = 0; t < 4; ++t) {
+            c.a_rd[t] = (uint32_t)(arow * 128 + 16 * ((2 * t + h) ^ ((arow >> 1) & 7)));
+            c.b_rd[t] = (uint32_t)(brow * 128 + 16 * ((2 * t + h) ^ ((brow >> 1) & 7)));
         }
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-#pragma unroll
-            for (int i = 0; i < MT; ++i)
-                acc[i][j] = mfma16x16x32(as_bf16x8(bc[j]), as_bf16x8(ac[i]), acc[i][j]);
     }
 
-    // Lane holds C[m_wave + 16i + r][n_wave + 16j + 4*slot + e], e = 0..3.
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = m_wave + 16 * i + r;
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Stages of the partition (the last one may be a half stage); past the last stage
+    // the copies repeat it into a slot that is never read again, so every stage issues
+    // NCOPY copies and the waits below are exact.
+    const int nst = (c.k_end - c.k_begin + SK - 1) / SK;  // >= 1
+    issue(c, 0, 0);
+    issue(c, min(1, nst - 1), 1);
+    QMM_WAIT_VMCNT(NCOPY);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    int slot = 0;  // st % 3
+    for (int st = 0; st < nst; ++st) {
+        const int slot_issue = slot == 0 ? 2 : slot - 1;  // (st + 2) % 3: the slot stage st-1 used
+        issue(c, min(st + 2, nst - 1), slot_issue);
+        compute(c, L, slot, (c.k_end - (c.k_begin + SK * st)) < SK, acc);
+        QMM_WAIT_VMCNT(NCOPY);  // the copies of stage st+1 landed; this stage's 8 may remain
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        slot = slot == 2 ? 0 : slot + 1;
+    }
+    QMM_WAIT_VMCNT(0);  // no copy may still be writing LDS when the workgroup ends
+
+    // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*64 + 32i + (lane % 32)
+    // and n = n0 + wn*64 + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
+    const int r = lane & 31, sl = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + wm * 64 + 32 * i + r;
         if (m >= M) continue;
 #pragma unroll
-        for (int j = 0; j < NS; ++j) {
-            const int n0 = n_wave + 16 * j + 4 * slot;
-            const size_t off = (size_t)m * (size_t)N + n0;
-            if (F32_OUT) {
-                float *dst = static_cast<float *>(out) + (size_t)p * (size_t)M * (size_t)N + off;
-                if (vec_store && n0 + 3 < N) {
-                    *reinterpret_cast<float4 *>(dst) =
-                        make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-                } else {
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + e < N) dst[e] = acc[i][j][e];
-                }
-            } else {
-                uint16_t *dst = static_cast<uint16_t *>(out) + off;
-                if (vec_store && n0 + 3 < N) {
-                    uint2 v;
-                    v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-                    v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-                    *reinterpret_cast<uint2 *>(dst) = v;
+            for (int vq = 0; vq < 4; ++vq) {
+                const int n = n0 + wn * 64 + 32 * j + 8 * vq + 4 * sl;
+                const size_t off = (size_t)m * (size_t)N + n;
+                const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
+                const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
+                if (F32_OUT) {
+                    float *dst = static_cast<float *>(out) + (size_t)p * (size_t)M * (size_t)N + off;
+                    if (vec_store && n + 3 < N) {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+                    } else {
+                        if (n < N) dst[0] = v0;
+                        if (n + 1 < N) dst[1] = v1;
+                        if (n + 2 < N) dst[2] = v2;
+                        if (n + 3 < N) dst[3] = v3;
+                    }
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n0 + e < N) dst[e] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+                    uint16_t *dst = static_cast<uint16_t *>(out) + off;
+                    if (vec_store && n + 3 < N) {
+                        uint2 v;
+                        v.x = pack_bf16x2(v0, v1);
+                        v.y = pack_bf16x2(v2, v3);
+                        *reinterpret_cast<uint2 *>(dst) = v;
+                    } else {
+                        if (n < N) dst[0] = (uint16_t)f32_to_bf16(v0);
+                        if (n + 1 < N) dst[1] = (uint16_t)f32_to_bf16(v1);
+                        if (n + 2 < N) dst[2] = (uint16_t)f32_to_bf16(v2);
+                        if (n + 3 < N) dst[3] = (uint16_t)f32_to_bf16(v3);
+                    }
                 }
             }
         }
     }
 }
 
-template <int MT, int NS>
-hipError_t launch_tile(const void *A, const void *B, void *out, bool f32_out, int M, int N, int K,
-                       int s, bool vec_store, hipStream_t stream)
-{
-    const int block_m = 2 * 16 * MT, block_n = 2 * 16 * NS;
-    dim3 grid((N + block_n - 1) / block_n, (M + block_m - 1) / block_m, s);
-    (void)hipGetLastError();
-    if (f32_out)
-        hipLaunchKernelGGL((dense_kernel<MT, NS, true>), grid, dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), out,
-                           M, N, K, s, vec_store ? 1 : 0);
-    else
-        hipLaunchKernelGGL((dense_kernel<MT, NS, false>), grid, dim3(256), 0, stream,
-                           static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), out,
-                           M, N, K, s, vec_store ? 1 : 0);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 namespace qmm_impl {
 
+// K < 2^22 (32-bit copy offsets over 128 rows); s <= K/32. vec_store: N % 4 == 0 and
+// the output 16-byte (fp32 planes) or 8-byte (bf16 C) aligned.
 hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out, bool f32_out,
                         int M, int N, int K, int s, bool vec_store, hipStream_t stream)
 {
-    if (tile.mt == 4 && tile.ns == 4)
-        return launch_tile<4, 4>(A, B, out, f32_out, M, N, K, s, vec_store, stream);
-    if (tile.mt == 2 && tile.ns == 2)
-        return launch_tile<2, 2>(A, B, out, f32_out, M, N, K, s, vec_store, stream);
-    return hipErrorInvalidValue;
+    if (tile.block_m() != TM || tile.block_n() != TN) return hipErrorInvalidValue;
+    if (K >= (1 << 22) || s < 1 || s > K / 32) return hipErrorInvalidValue;
+    const int tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    const dim3 grid(tiles * s);
+    (void)hipGetLastError();
+    if (f32_out)
+        hipLaunchKernelGGL((dense_kernel<true>), grid, dim3(256), 0, stream, static_cast<const uint16_t *>(A),
+                           static_cast<const uint16_t *>(B), out, M, N, K, s, vec_store ? 1 : 0);
+    else
+        hipLaunchKernelGGL((dense_kernel<false>), grid, dim3(256), 0, stream, static_cast<const uint16_t *>(A),
+                           static_cast<const uint16_t *>(B), out, M, N, K, s, vec_store ? 1 : 0);
+    return hipGetLastError();
 }
 
 }  // namespace qmm_impl

@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kGroup = 128;
 constexpr int kGranule = 32;
+constexpr int kCUs = 256;  // MI355X compute units
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -37,12 +38,14 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // 128 rows) in one block row, so each weight is dequantised once per block.
 // Kernel by row count: the small-M kernel up to 64 rows; the large-M kernel with 128-row
 // tiles (two workgroups per CU) up to 128 rows, with 256-row tiles of eight 256 x 32 waves above.
-W4A16Tile w4a16_tile(int M, int /*N*/) {
+W4A16Tile w4a16_tile(int M, int N) {
     W4A16Tile t;
     if (M <= 64) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-        t.ns = 2;
+        // 64-column tiles when 32-column ones would need more than one workgroup per CU
+        // (one workgroup of the small-M kernel fills a CU's wave slots).
+        t.ns = ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs ? 4 : 2;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.mt = M <= 128 ? 8 : 16;
@@ -53,8 +56,9 @@ W4A16Tile w4a16_tile(int M, int /*N*/) {
 
 hipError_t dispatch_skinny(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
                            void *out, int M, int N, int K, int s, bool vec, hipStream_t st) {
-    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, (K / kGroup) / s);
-    return qmm_impl::launch_w4a16_skinny(tile.mt, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s, vec, st);
+    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s);
+    return qmm_impl::launch_w4a16_skinny(tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s,
+                                         vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {

@@ -8,14 +8,14 @@
 namespace qmm_impl {
 
 // Which W4A16 kernel runs an M-row problem, and the output tile of one workgroup.
-//   SKINNY (M <= 64): a (16*mt) x 32 tile, up to 16 waves splitting its reduction;
-//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variants 1-3).
+//   SKINNY (M <= 64): a (16*mt) x (16*ns) tile, ns 2 or 4, up to 16 waves splitting its reduction;
+//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variants 1, 2).
 enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
 
 struct W4A16Tile {
     W4A16Kind kind;
     int mt;  // 16-row MFMA subtiles per block (SKINNY: 1, 2, 4; WIDE: 8, 16)
-    int ns;  // SKINNY: 16-column MFMA subtiles per block (2); WIDE: kernel variant
+    int ns;  // SKINNY: 16-column MFMA subtiles per block (2 or 4); WIDE: kernel variant
     int block_m() const { return 16 * mt; }
     int block_n() const { return kind == W4A16_WIDE ? 256 : 16 * ns; }
 };
@@ -26,10 +26,10 @@ struct SkinnyShape {
     int gpw;    // groups whose loads one wave issues together
 };
 
-inline SkinnyShape skinny_shape(int mt, int gpp)
+inline SkinnyShape skinny_shape(int mt, int ns, int gpp)
 {
-    const int max_waves = mt == 1 ? 16 : 8;
-    const int max_gpw = mt == 4 ? 2 : 3;
+    const int max_waves = (mt == 1 && ns == 2) ? 16 : 8;
+    const int max_gpw = ns == 4 ? (mt == 1 ? 3 : mt == 2 ? 2 : 1) : (mt == 4 ? 2 : 3);
     SkinnyShape sh;
     sh.waves = gpp < max_waves ? gpp : max_waves;
     const int per_wave = (gpp + sh.waves - 1) / sh.waves;
@@ -45,14 +45,13 @@ struct DenseTile {
     int block_n() const { return 2 * 16 * ns; }
 };
 
-hipError_t launch_w4a16_skinny(int mt, int gpw, int waves, const void *A, const void *Wq, const void *scale,
-                               const void *bias, void *out, int M, int N, int K, int s, bool vec_store,
-                               hipStream_t stream);
+hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
+                               const void *scale, const void *bias, void *out, int M, int N, int K, int s,
+                               bool vec_store, hipStream_t stream);
 
 // Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves (two workgroups per CU);
-// 1, 2, 3 = 256 x 256 tiles (one per CU) of 8 waves of 128 x 64, 8 waves of 256 x 32,
-// 4 waves of 256 x 64. Rows per tile, and workgroups one CU holds (LDS: 76 KB for 128
-// rows, 124 KB for 256).
+// 1, 2 = 256 x 256 tiles (one per CU) of 8 waves of 128 x 64, 8 waves of 256 x 32.
+// Rows per tile, and workgroups one CU holds (LDS: 76 KB for 128 rows, 124 KB for 256).
 inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
 inline int wide_wgs_per_cu(int variant) { return variant == 0 ? 2 : 1; }
 constexpr int kWideCols = 256;

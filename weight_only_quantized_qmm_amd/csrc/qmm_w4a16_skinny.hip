@@ -171,20 +171,25 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
 
 namespace qmm_impl {
 
-// The host picks (mt, gpw, waves) with SkinnyShape (qmm_launch.h): mt 1 with up to 16
-// waves and gpw <= 3; mt 2 with up to 8 waves and gpw <= 3; mt 4 with up to 8 waves
-// and gpw <= 2 (register budgets of 128 / 256 / 256 VGPRs per lane).
-hipError_t launch_w4a16_skinny(int mt, int gpw, int waves, const void *A, const void *Wq, const void *scale,
-                               const void *bias, void *out, int M, int N, int K, int s, bool vec_store,
-                               hipStream_t stream)
+// The host picks (mt, ns, gpw, waves) with SkinnyShape (qmm_launch.h). 32-column tiles
+// (ns 2): mt 1 with up to 16 waves and gpw <= 3; mt 2 with up to 8 waves and gpw <= 3;
+// mt 4 with up to 8 waves and gpw <= 2. 64-column tiles (ns 4), used when the 32-column
+// grid would not fit on the GPU in one round: up to 8 waves, gpw <= 3, 2, 1 for mt 1, 2,
+// 4 (register budgets of 128 VGPRs per lane at 16 waves, 256 at 8).
+hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
+                               const void *scale, const void *bias, void *out, int M, int N, int K, int s,
+                               bool vec_store, hipStream_t stream)
 {
     if (waves < 1 || waves > MAX_WAVES) return hipErrorInvalidValue;
-#define QMM_CFG(MT_, GPW_, MAXW_)                                                                              \
-    if (mt == MT_ && gpw == GPW_)                                                                              \
-        return launch_cfg<MT_, 2, GPW_, MAXW_>(A, Wq, scale, bias, out, M, N, K, s, waves, vec_store, stream);
-    QMM_CFG(1, 1, 16) QMM_CFG(1, 2, 16) QMM_CFG(1, 3, 16)
-    QMM_CFG(2, 1, 8) QMM_CFG(2, 2, 8) QMM_CFG(2, 3, 8)
-    QMM_CFG(4, 1, 8) QMM_CFG(4, 2, 8)
+#define QMM_CFG(MT_, NS_, GPW_, MAXW_)                                                                         \
+    if (mt == MT_ && ns == NS_ && gpw == GPW_)                                                                 \
+        return launch_cfg<MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, M, N, K, s, waves, vec_store, stream);
+    QMM_CFG(1, 2, 1, 16) QMM_CFG(1, 2, 2, 16) QMM_CFG(1, 2, 3, 16)
+    QMM_CFG(2, 2, 1, 8) QMM_CFG(2, 2, 2, 8) QMM_CFG(2, 2, 3, 8)
+    QMM_CFG(4, 2, 1, 8) QMM_CFG(4, 2, 2, 8)
+    QMM_CFG(1, 4, 1, 8) QMM_CFG(1, 4, 2, 8) QMM_CFG(1, 4, 3, 8)
+    QMM_CFG(2, 4, 1, 8) QMM_CFG(2, 4, 2, 8)
+    QMM_CFG(4, 4, 1, 8)
 #undef QMM_CFG
     return hipErrorInvalidValue;
 }

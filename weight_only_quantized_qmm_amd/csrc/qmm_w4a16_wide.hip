@@ -374,7 +374,6 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 typedef Cfg<1, 4, 2> CfgV0;  // 128 x 256 tile, 4 waves of 128 x 64, two workgroups per CU
 typedef Cfg<2, 4, 2> CfgV1;  // 256 x 256 tile, 8 waves of 128 x 64
 typedef Cfg<2, 8, 1> CfgV2;  // 256 x 256 tile, 8 waves of 256 x 32
-typedef Cfg<2, 8, 2> CfgV3;  // 256 x 256 tile, 4 waves of 256 x 64 (accumulators in AGPRs)
 
 template <class CF>
 void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
@@ -394,7 +393,7 @@ hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const v
                              void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
                              hipStream_t stream)
 {
-    if (K >= (1 << 22) || variant < 0 || variant > 3) return hipErrorInvalidValue;
+    if (K >= (1 << 22) || variant < 0 || variant > 2) return hipErrorInvalidValue;
     const int rows = wide_rows(variant);
     const int tiles = ((M + rows - 1) / rows) * ((N + BN - 1) / BN);
     if (full_tiles < 0 || full_tiles > tiles || split < 1 || split > K / 128) return hipErrorInvalidValue;
@@ -412,8 +411,7 @@ hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const v
     switch (variant) {
     case 0: launch_cfg<CfgV0>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
     case 1: launch_cfg<CfgV1>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
-    case 2: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
-    default: launch_cfg<CfgV3>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    default: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
     }
     return hipGetLastError();
 }

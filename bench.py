@@ -210,14 +210,31 @@ def dense_sweep(torch, syn, q):
 
 
 def decode_table(torch, syn, q):
-    """Decode shapes (down, gate at M = 1, 4, 8): the policy's split against the unsplit
-    control, with the weight-read rate (packed weights + scale/bias bytes / time)."""
+    """Decode shapes (down, gate at M = 1, 4, 8): the matmul's policy split against its
+    unsplit control and against the decode matrix-vector kernel (qmm_w4a16_gemv, its own
+    split), with the weight-read rate (packed weights + scale/bias bytes / time)."""
     rows = []
     for name, M, N, K, idx in syn.decode_sweep():
         sh, R, t = per_shape(torch, syn, q, name, M, N, K, idx + 100)
         wbytes = N * K // 2 + N * (K // 128) * 4
+        # the matrix-vector kernel over the same rotation
+        gs = q.qmm_gemv_min_split(M, K)
+        sh2 = Shape(name, M, N, K, idx + 100, R, torch, syn, q)
+        ws = torch.empty(max(2 * gs * M * N, 256), dtype=torch.uint8, device="cuda")
+
+        def run():
+            for r in range(R):
+                A, W, S, B = sh2.sets[r]
+                q.qmm_w4a16_gemv(A, W, S, B, sh2.C, M, N, K, gs, ws if gs > 1 else None)
+        g = graph_of(torch, run)
+        t_gemv = time_graph(torch, g) / R
+        del g
+        sh2.free()
+        torch.cuda.empty_cache()
+        best = min(t[0], t_gemv)
         rows.append(dict(name=name, M=M, N=N, K=K, s=sh.s, us=round(t[0] * 1e6, 3), us_unsplit=round(t[1] * 1e6, 3),
-                         weight_gbs=round(wbytes / t[0] / 1e9, 1), weight_frac_hbm=round(wbytes / t[0] / HBM_PEAK, 4)))
+                         gemv_s=gs, gemv_us=round(t_gemv * 1e6, 3),
+                         weight_gbs=round(wbytes / best / 1e9, 1), weight_frac_hbm=round(wbytes / best / HBM_PEAK, 4)))
     return rows
 
 

@@ -139,6 +139,27 @@ int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void 
                    int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * qmm_w4a16_gemv -- the same product for decode-sized M (1 to 8 rows) on a matrix-vector
+ * kernel with no matrix-core padding (tiny-llm "Week 2 Day 7", Benchmark Analysis:
+ * decode runs on a separate matvec). Every packed weight is read once per call.
+ *   M in 1..8, else QMM_ERR_SHAPE. Same layouts, alignment, ownership and errors as
+ *   qmm_w4a16_g128.
+ *   s = 0  : qmm_gemv_min_split(M, K), the smallest split whose partitions fit the
+ *            kernel's staging of A in LDS;
+ *   s >= 1 : explicit; must divide K/128 and K/s must fit (QMM_ERR_SHAPE otherwise):
+ *            K/s <= 10240, m8*K/s <= 30720 and, for m8 = 8, K/s <= 4096, where m8 is M
+ *            rounded up to 1, 2, 4 or 8.
+ *   s > 1 writes bf16 planes [s][M][N] into `workspace` (at least 2*s*M*N bytes,
+ *   16-byte aligned) and merges them with the reduce of qmm_splitk_reduce.
+ */
+int qmm_w4a16_gemv(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                   int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The split qmm_w4a16_gemv uses for s = 0 (>= 1), or QMM_ERR_ARG / QMM_ERR_SHAPE /
+ * QMM_ERR_SIZE. Host only. */
+int qmm_gemv_min_split(int M, int K);
+
+/*
  * qmm_splitk_reduce -- C[i] = bf16_rne( sum over p = 0..s-1, in this order, in fp32,
  * of partials[p][i] ) for i < M*N (tiny-llm "Week 2 Day 7", Task 4: one output
  * element per thread, FP32 sum, one cast to the model dtype).

@@ -185,6 +185,52 @@ def test_reduce_rejects_before_launch(args, code):
     assert q.qmm_splitk_reduce(*args, stream=0, check=False) == code
 
 
+def _gemv_min_split_rule(M, K):
+    """The documented rule of qmm_gemv_min_split, restated."""
+    m8 = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+    G = K // 128
+    for s in range(1, G + 1):
+        kp = K // s
+        if G % s == 0 and kp <= 10240 and m8 * kp <= 30720 and (m8 < 8 or kp <= 4096):
+            return s
+    return None
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("K", [128, 2560, 4096, 9728, 12288, 30720, 65536])
+def test_gemv_min_split_rule(M, K):
+    want = _gemv_min_split_rule(M, K)
+    if want is None:
+        with pytest.raises(q.QmmError):
+            q.qmm_gemv_min_split(M, K)
+    else:
+        assert q.qmm_gemv_min_split(M, K) == want
+
+
+def test_gemv_min_split_cases():
+    # decode shapes: down (K 9728) and gate (K 2560) at M = 1, 4, 8
+    assert [q.qmm_gemv_min_split(M, 9728) for M in (1, 4, 8)] == [1, 2, 4]
+    assert [q.qmm_gemv_min_split(M, 2560) for M in (1, 4, 8)] == [1, 1, 1]
+    for args, code in [((0, 256), q.QMM_ERR_ARG), ((9, 256), q.QMM_ERR_SHAPE), ((1, 200), q.QMM_ERR_SHAPE)]:
+        assert q.lib().qmm_gemv_min_split(*args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG), (dict(M=0), q.QMM_ERR_ARG),
+    (dict(M=9), q.QMM_ERR_SHAPE), (dict(K=200), q.QMM_ERR_SHAPE), (dict(s=3), q.QMM_ERR_SHAPE),
+    (dict(M=8, K=9728, s=1), q.QMM_ERR_SHAPE),  # 9728 values do not fit for 8 rows
+    (dict(s=2), q.QMM_ERR_WORKSPACE), (dict(A=ADDR + 2), q.QMM_ERR_ALIGN),
+    (dict(s=2, workspace=ADDR3, workspace_bytes=2 * 2 * 4 * 1024 - 2), q.QMM_ERR_WORKSPACE),
+])
+def test_gemv_rejects_before_launch(kw, code):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=4, N=1024, K=2560, s=1,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    rc = q.qmm_w4a16_gemv(a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"], a["s"],
+                          a["workspace"], a["workspace_bytes"], stream=0, check=False)
+    assert rc == code
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(A=None), q.QMM_ERR_ARG), (dict(B=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG),
     (dict(K=100), q.QMM_ERR_SHAPE), (dict(s=513), q.QMM_ERR_SHAPE), (dict(M=-2), q.QMM_ERR_ARG),

@@ -193,6 +193,87 @@ def test_cfg4_decode(name, M, N, K, idx):
         check_tolerance(host_f64(C), ref, what="%s M=%d s=%d" % (name, M, s))
 
 
+# ------------------------------------------------------ decode matrix-vector kernel
+
+def run_gemv(dv, M, N, K, s, guard=0):
+    s_eff = s or q.qmm_gemv_min_split(M, K)
+    Cbuf = torch.full((M * N + 2 * guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    C = Cbuf[guard:guard + M * N].view(M, N)
+    ws = torch.empty(2 * s_eff * M * N + 16, dtype=torch.uint8, device="cuda") if s_eff > 1 else None
+    q.qmm_w4a16_gemv(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws)
+    torch.cuda.synchronize()
+    if guard:
+        g = host_bits(Cbuf)
+        canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+        assert np.all(g[:guard] == canary) and np.all(g[guard + M * N:] == canary), "C guard band written"
+    return C
+
+
+def gemv_splits(M, K):
+    """Every split the decode kernel accepts for (M, K)."""
+    G = K // 128
+    m8 = 1 if M <= 1 else 2 if M <= 2 else 4 if M <= 4 else 8
+    return [s for s in range(1, G + 1) if G % s == 0 and K // s <= 10240 and m8 * (K // s) <= 30720
+            and (m8 < 8 or K // s <= 4096)]
+
+
+@pytest.mark.parametrize("name,M,N,K,idx", DECODE, ids=["%s-M%d" % (n, m) for n, m, _, _, _ in DECODE])
+def test_gemv_decode_shapes(name, M, N, K, idx):
+    d = syn.w4a16_inputs(M, N, K, seed=4000 + idx)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for s in [0] + gemv_splits(M, K)[:4]:
+        say("gemv %s M=%d N=%d K=%d s=%d" % (name, M, N, K, s))
+        C = run_gemv(dv, M, N, K, s)
+        check_tolerance(host_f64(C), ref, what="gemv %s M=%d s=%d" % (name, M, s))
+
+
+GEMV_EDGE = [(1, 1, 128), (3, 17, 256), (5, 100, 384), (8, 33, 4096), (2, 1000, 10240), (7, 4100, 1280),
+             (4, 64, 7680), (6, 15, 3968)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_EDGE)
+def test_gemv_edge_shapes(M, N, K):
+    d = syn.w4a16_inputs(M, N, K, seed=4500 + M + N + K)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    splits = gemv_splits(M, K)
+    for s in sorted({0, splits[0], splits[-1]}):
+        say("gemv edge M=%d N=%d K=%d s=%d" % (M, N, K, s))
+        C = run_gemv(dv, M, N, K, s, guard=24)
+        check_tolerance(host_f64(C), ref, what="gemv edge %dx%dx%d s=%d" % (M, N, K, s))
+
+
+def test_gemv_closed_forms():
+    """Zero weights give zero up to the kernel's cancellation bound; one-hot rows of A
+    give the dequantised weight, rounded once to bf16; two runs agree bit for bit.
+
+    The kernel sums A*(128 + q) in fp32 and subtracts 128*sum(A) per chunk of 32 values
+    (the products are exact, the sums round), so with q = 8 and bias = -8*scale the
+    result is scale * (rounding residue), bounded by K fp32 additions of terms up to
+    136*max|A|: |C| <= K * 2^-24 * 136 * max|A| * max(scale) * 4 (generous factor 4)."""
+    M, N, K = 8, 96, 1024
+    d = syn.w4a16_inputs(M, N, K, seed=4600)
+    d["Wq"][:] = np.uint32(0x88888888)  # q = 8 and bias = -8*scale: w = 0
+    dv = w4a16_device(d)
+    C = run_gemv(dv, M, N, K, 0)
+    amax = float(np.max(np.abs(syn.bf16_bits_to_f32(d["A"]))))
+    smax = float(np.max(syn.bf16_bits_to_f32(d["scale"])))
+    bound = K * 2.0 ** -24 * 136 * amax * smax * 4
+    assert float(np.max(np.abs(host_f64(C)))) <= bound
+    d = syn.w4a16_inputs(M, N, K, seed=4601)
+    ks = np.random.default_rng(4601).integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), ks] = 0x3F80  # 1.0
+    d["A"] = A
+    dv = w4a16_device(d)
+    C = run_gemv(dv, M, N, K, 0)
+    w = oracle.dequant_w4a16(d["Wq"], d["scale"], d["bias"], N, K)  # [N][K], exact
+    want = oracle.bf16_round_array(w[:, ks].T)
+    assert np.array_equal(host_bits(C), want)
+    assert np.array_equal(host_bits(run_gemv(dv, M, N, K, 0)), host_bits(C))
+
+
 # ---------------------------------------------------------------- reduce
 
 @pytest.mark.parametrize("s,M,N", [(1, 16, 1024), (2, 32, 1024), (5, 48, 1000), (20, 7, 33), (32, 1, 9),

@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     EXPORTED_DATA, EXPORTED_FUNCTIONS, QMM_ERR_ALIGN, QMM_ERR_ARG, QMM_ERR_HIP, QMM_ERR_SHAPE,
     QMM_ERR_SIZE, QMM_ERR_WORKSPACE, QMM_OK, QMM_PARTIAL_BF16, QMM_PARTIAL_F32, QmmError,
     bf16_splitk, effective_split, lib, policy_preset, qmm_bf16_splitk, qmm_plan, qmm_policy,
-    qmm_splitk_plan, qmm_splitk_reduce, qmm_status_string, qmm_w4a16_g128, w4a16,
-    w4a16_workspace_bytes)
+    qmm_gemv_min_split, qmm_splitk_plan, qmm_splitk_reduce, qmm_status_string, qmm_w4a16_g128,
+    qmm_w4a16_gemv, w4a16, w4a16_workspace_bytes)

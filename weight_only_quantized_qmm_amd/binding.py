@@ -24,7 +24,7 @@ QMM_PARTIAL_F32 = 1
 
 # Every symbol include/qmm.h declares.
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
-                      "qmm_status_string")
+                      "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -72,6 +72,10 @@ def lib():
         L.qmm_splitk_reduce.restype = I
         L.qmm_bf16_splitk.argtypes = [P, P, P, I, I, I, I, P, S, P]
         L.qmm_bf16_splitk.restype = I
+        L.qmm_w4a16_gemv.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.qmm_w4a16_gemv.restype = I
+        L.qmm_gemv_min_split.argtypes = [I, I]
+        L.qmm_gemv_min_split.restype = I
         L.qmm_status_string.argtypes = [I]
         L.qmm_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -133,6 +137,26 @@ def qmm_w4a16_g128(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspac
                               int(s), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_w4a16_g128")
+    return rc
+
+
+def qmm_w4a16_gemv(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
+                   stream=None, check=True):
+    """C = A . dequant(W)^T for M <= 8 on the matrix-vector kernel; returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_w4a16_gemv(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                              int(s), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_gemv")
+    return rc
+
+
+def qmm_gemv_min_split(M, K):
+    """The split qmm_w4a16_gemv uses for s = 0; raises on an invalid shape."""
+    rc = lib().qmm_gemv_min_split(int(M), int(K))
+    if rc < 0:
+        raise QmmError(rc, "qmm_gemv_min_split")
     return rc
 
 

@@ -26,7 +26,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 
-SOURCES = ["qmm_w4a16_skinny.hip", "qmm_w4a16_wide.hip", "qmm_reduce.hip", "qmm_dense.hip", "qmm_api.cpp"]
+SOURCES = ["qmm_w4a16_skinny.hip", "qmm_w4a16_wide.hip", "qmm_gemv.hip", "qmm_reduce.hip", "qmm_dense.hip",
+           "qmm_api.cpp"]
 CALIB_SOURCES = ["qmm_calib.hip"]
 
 

@@ -228,6 +228,51 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
     return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
 }
 
+namespace {
+int gemv_m8(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+}  // namespace
+
+extern "C" int qmm_gemv_min_split(int M, int K)
+{
+    if (M < 1 || K <= 0) return QMM_ERR_ARG;
+    if (M > 8) return QMM_ERR_SHAPE;
+    if (K % kGroup != 0) return QMM_ERR_SHAPE;
+    if (!sizes_ok(1, 1, K)) return QMM_ERR_SIZE;
+    const int G = K / kGroup;
+    for (int s = 1; s <= G; ++s)
+        if (G % s == 0 && qmm_impl::gemv_split_fits(gemv_m8(M), K / s)) return s;
+    return QMM_ERR_SHAPE;
+}
+
+extern "C" int qmm_w4a16_gemv(const void *A, const void *Wq, const void *scale, const void *bias, void *C, int M,
+                              int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!A || !Wq || !scale || !bias || !C) return QMM_ERR_ARG;
+    if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
+    if (M > 8 || K % kGroup != 0) return QMM_ERR_SHAPE;
+    if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
+    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
+        return QMM_ERR_ALIGN;
+    const int G = K / kGroup;
+    if (s == 0) {
+        s = qmm_gemv_min_split(M, K);
+        if (s < 0) return s;
+    } else if (s > G || G % s != 0 || !qmm_impl::gemv_split_fits(gemv_m8(M), K / s)) {
+        return QMM_ERR_SHAPE;
+    }
+    const size_t MN = (size_t)M * (size_t)N;
+    if (s > 1) {
+        if (!workspace || workspace_bytes < 2 * (size_t)s * MN) return QMM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (s == 1) return hip_status(qmm_impl::launch_w4a16_gemv(A, Wq, scale, bias, C, M, N, K, 1, st));
+    int rc = hip_status(qmm_impl::launch_w4a16_gemv(A, Wq, scale, bias, workspace, M, N, K, s, st));
+    if (rc != QMM_OK) return rc;
+    const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
+    return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
+}
+
 extern "C" int qmm_splitk_reduce(const void *partials, int partial_dtype, int s, int M, int N, void *C,
                                  void *stream)
 {

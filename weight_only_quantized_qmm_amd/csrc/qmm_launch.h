@@ -63,6 +63,14 @@ hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const v
                              void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
                              hipStream_t stream);
 
+// Decode matrix-vector kernel (M <= 8): a partition of kp reduction values fits its A
+// staging when kp <= 10240 (at most 5 chunks of 32 per lane) and m8 * kp <= 30720
+// (m8 = M rounded up to 1, 2, 4 or 8; LDS), and for m8 = 8 kp <= 4096 as well.
+inline bool gemv_split_fits(int m8, int kp) { return kp <= 10240 && m8 * kp <= 30720 && (m8 < 8 || kp <= 4096); }
+
+hipError_t launch_w4a16_gemv(const void *A, const void *Wq, const void *scale, const void *bias, void *out, int M,
+                             int N, int K, int s, hipStream_t stream);
+
 hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t MN, void *C,
                          bool vec, hipStream_t stream);
 

@@ -24,7 +24,7 @@
  *   scale  bf16   [N][K/128]
  *   bias   bf16   [N][K/128]
  *   C      bf16   [M][N]
- *   partials      [s][M][N]  bf16 (W4A16) or fp32 (dense)
+ *   partials      [s][M][N]  bf16 (W4A16), fp32 (dense, and W4A16 through qmm_w4a16_g128_f32p)
  *   dense  A bf16 [M][K], B bf16 [N][K], C = A . B^T
  *
  * Ownership and execution: every pointer except those of qmm_splitk_plan is a
@@ -137,6 +137,20 @@ int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *polic
  */
 int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
                    int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * qmm_w4a16_g128_f32p -- qmm_w4a16_g128 with fp32 partial planes: each partition's
+ * fp32 accumulator is stored unrounded and the reduce sums fp32 values, so the split
+ * result differs from an fp32 sum over all of K only by summation order and the final
+ * cast (tiny-llm "Week 2 Day 7: Split-K Prefill", Task 2 and Task 4: the partials may
+ * be kept in FP32 at the cost of twice the workspace traffic).
+ *   Same arguments, layouts, decomposition and errors as qmm_w4a16_g128, except that
+ *   the workspace holds fp32 planes [s][M][N]: at least 4*s*M*N bytes when the
+ *   effective s > 1. The effective s = 1 path is the same launch as qmm_w4a16_g128's,
+ *   bitwise.
+ */
+int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                        int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * qmm_w4a16_gemv -- the same product for decode-sized M (1 to 8 rows) on a matrix-vector

@@ -63,6 +63,20 @@ def w4a16_inputs(M, N, K, seed, scale_lo=0.005, scale_hi=0.02):
     return dict(A=A, Wq=pack_nibbles(q), scale=scale, bias=bias, q=q)
 
 
+def w4a16_pow2_inputs(M, N, K, seed):
+    """Like w4a16_inputs, but every scale is a power of two (2^-7, 2^-6 or 2^-5) and
+    bias = -8*scale, so each dequantised weight (q - 8)*scale is exact in bf16 and each
+    product with A exact in fp32: a single-cast kernel then differs from the correctly
+    rounded result only through its fp32 accumulation."""
+    d = w4a16_inputs(M, N, K, seed)
+    rng = rng_for(seed + 0x5EED)
+    e = rng.integers(-7, -4, size=d["scale"].shape)
+    scale = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    d["scale"] = f32_to_bf16_bits(scale)
+    d["bias"] = f32_to_bf16_bits(np.float32(-8.0) * scale)
+    return d
+
+
 def w4a16_weights(N, K, seed, scale_lo=0.005, scale_hi=0.02):
     """Weights only (for shapes where several activation sets share one weight set)."""
     rng = rng_for(seed)

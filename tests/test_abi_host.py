@@ -168,6 +168,33 @@ def test_w4a16_rejects_before_launch(kw, code):
     assert _w4(**kw) == code
 
 
+def _w4f(**kw):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=32, N=1024, K=2560, s=1,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    return q.qmm_w4a16_g128_f32p(a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"], a["s"],
+                                 a["workspace"], a["workspace_bytes"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG), (dict(K=2500), q.QMM_ERR_SHAPE),
+    (dict(s=3), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    # fp32 planes: the bf16-sized workspace is too small by half
+    (dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=4 * 4 * 32 * 1024 - 4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x200008, workspace_bytes=4 * 4 * 32 * 1024), q.QMM_ERR_ALIGN),
+    (dict(M=1 << 30, N=1 << 30), q.QMM_ERR_SIZE),
+])
+def test_w4a16_f32p_rejects_before_launch(kw, code):
+    assert _w4f(**kw) == code
+
+
+def test_w4a16_workspace_sizes():
+    assert q.w4a16_workspace_bytes(32, 1024, 1) == 0
+    assert q.w4a16_workspace_bytes(32, 1024, 4) == 2 * 4 * 32 * 1024
+    assert q.w4a16_workspace_bytes(32, 1024, 4, f32_partials=True) == 4 * 4 * 32 * 1024
+
+
 def test_w4a16_policy_split_needs_workspace():
     # s = 0 resolves through the MI355X plan; where it splits, no workspace is an error
     M, N, K = 16, 1024, 2560

@@ -25,28 +25,31 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def run_w4a16(dv, M, N, K, s, guard=0):
-    """Run the library; returns C (bf16 device tensor). guard > 0 wraps C and the workspace
-    in canary regions of that many elements and checks them afterwards."""
+def run_w4a16(dv, M, N, K, s, guard=0, f32p=False):
+    """Run the library (qmm_w4a16_g128, or qmm_w4a16_g128_f32p when f32p); returns C (bf16
+    device tensor). guard > 0 wraps C and the workspace in canary regions of that many
+    elements and checks them afterwards."""
     s_eff = q.effective_split(M, N, K, s)
     Cbuf = torch.full((M * N + 2 * guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
     C = Cbuf[guard:guard + M * N].view(M, N)
     ws = None
     wbuf = None
+    wdt = torch.float32 if f32p else torch.bfloat16
     if s_eff > 1:
         nws = s_eff * M * N
         gw = ((guard + 7) // 8) * 8  # keep the workspace 16-byte aligned
-        wbuf = torch.full((nws + 2 * gw,), -777.0, dtype=torch.bfloat16, device="cuda")
+        wbuf = torch.full((nws + 2 * gw,), -777.0, dtype=wdt, device="cuda")
         ws = wbuf[gw:gw + nws]
-    q.qmm_w4a16_g128(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws)
+    fn = q.qmm_w4a16_g128_f32p if f32p else q.qmm_w4a16_g128
+    fn(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws)
     torch.cuda.synchronize()
     if guard:
         g = host_bits(Cbuf)
         canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
         assert np.all(g[:guard] == canary) and np.all(g[guard + M * N:] == canary), "C guard band written"
         if wbuf is not None:
-            w = host_bits(wbuf)
-            wc = host_bits(torch.tensor([-777.0], dtype=torch.bfloat16))[0]
+            w = wbuf.cpu().numpy() if f32p else host_bits(wbuf)
+            wc = (np.float32(-777.0) if f32p else host_bits(torch.tensor([-777.0], dtype=torch.bfloat16))[0])
             assert np.all(w[:gw] == wc) and np.all(w[gw + s_eff * M * N:] == wc), "workspace guard written"
     return C
 
@@ -142,6 +145,97 @@ def test_split_tail_decomposition():
     m2, n2 = sample_points(M, N, 7200)
     ref2 = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, m2, n2)
     check_tolerance(host_f64(C)[m2, n2], ref2, what="split tail, sampled")
+
+
+# --------------------------------------------------- fp32 partial planes (W4A16)
+
+def check_single_cast(bits, ref, min_equal, what):
+    """bits: bf16 result; ref: fp64 exact value. Every element lies within one bf16 spacing
+    of ref (the correctly rounded value or its neighbour across a nearby midpoint), plus
+    an absolute 1e-4*rms(ref) for the fp32 accumulation near zero (its typical size is
+    about sqrt(K)*2^-24*rms(ref), 3e-6*rms at K = 2560), and at least min_equal of them
+    are the correctly rounded value. Returns that fraction."""
+    got = syn.bf16_bits_to_f32(bits).astype(np.float64)
+    mag = np.maximum(np.abs(ref), np.abs(got))
+    spacing = np.exp2(np.floor(np.log2(np.maximum(mag, 1e-30))) - 7)
+    err = np.abs(got - ref)
+    bad = err > spacing + 1e-4 * float(np.sqrt(np.mean(ref * ref)))
+    assert not bad.any(), "%s: %d elements more than one bf16 spacing away; first got %s ref %s" % (
+        what, int(bad.sum()), got[bad][:4].tolist(), ref[bad][:4].tolist())
+    frac = float(np.mean(bits == oracle.bf16_round_array(ref)))
+    say("%s: correctly rounded fraction %.4f" % (what, frac))
+    assert frac >= min_equal, "%s: only %.4f correctly rounded" % (what, frac)
+    return frac
+
+
+F32P_CASES = [  # (M, N, K, explicit splits): small-M kernel, 128-row and 256-row large-M kernels
+    (48, 1000, 2560, (2, 5, 20)), (100, 1000, 2560, (4, 10)), (256, 520, 4096, (2, 8, 32))]
+
+
+@pytest.mark.parametrize("M,N,K,splits", F32P_CASES)
+def test_f32p_partials_round_once(M, N, K, splits):
+    """Power-of-two scales make every dequantised weight and product exact, so a result
+    rounded to bf16 once (unsplit, or fp32 planes) is correctly rounded but for fp32
+    accumulation; bf16 planes round each partition first (printed for contrast)."""
+    d = syn.w4a16_pow2_inputs(M, N, K, seed=9000 + M)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    say("f32p M=%d N=%d K=%d s=1" % (M, N, K))
+    c1 = host_bits(run_w4a16(dv, M, N, K, 1))
+    check_single_cast(c1, ref, 0.98, "unsplit %dx%dx%d" % (M, N, K))
+    c1f = host_bits(run_w4a16(dv, M, N, K, 1, f32p=True))
+    assert np.array_equal(c1, c1f), "f32p s=1 is not the unsplit launch"
+    for s in splits + (0,):
+        say("f32p M=%d N=%d K=%d s=%d" % (M, N, K, s))
+        C = run_w4a16(dv, M, N, K, s, guard=64, f32p=True)
+        check_tolerance(host_f64(C), ref, what="f32p s=%d" % s)
+        check_single_cast(host_bits(C), ref, 0.98, "f32p %dx%dx%d s=%d" % (M, N, K, s))
+    sb = max(splits)
+    fb = float(np.mean(host_bits(run_w4a16(dv, M, N, K, sb)) == oracle.bf16_round_array(ref)))
+    say("bf16 planes s=%d: correctly rounded fraction %.4f" % (sb, fb))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_gemv_unsplit_rounds_once(M):
+    N, K = 1000, 2560
+    d = syn.w4a16_pow2_inputs(M, N, K, seed=9050 + M)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    say("gemv single cast M=%d N=%d K=%d" % (M, N, K))
+    C = host_bits(run_gemv(w4a16_device(d), M, N, K, 1))
+    check_single_cast(C, ref, 0.98, "gemv %dx%dx%d s=1" % (M, N, K))
+
+
+def test_f32p_split_tail():
+    """The large-M plan with unsplit leading columns and a split tail, fp32 planes: leading
+    columns equal the unsplit kernel, tail columns round once (sampled by the oracle)."""
+    M, N, K = 1000, 64 * 256 + 100, 2560
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert plan.s > 1 and 0 < plan.full_tiles < plan.base_tiles
+    n_lo = (plan.full_tiles // -(-M // plan.block_m)) * plan.block_n
+    d = syn.w4a16_pow2_inputs(M, N, K, seed=9100)
+    dv = w4a16_device(d)
+    say("f32p split tail M=%d N=%d K=%d s=%d" % (M, N, K, plan.s))
+    C = host_bits(run_w4a16(dv, M, N, K, 0, guard=64, f32p=True))
+    C1 = host_bits(run_w4a16(dv, M, N, K, 1))
+    assert np.array_equal(C[:, :n_lo], C1[:, :n_lo])
+    rng = np.random.default_rng(9100)
+    ms = rng.integers(0, M, 20000).astype(np.int32)
+    ns = rng.integers(n_lo, N, 20000).astype(np.int32)
+    ref = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+    check_single_cast(C[ms, ns], ref, 0.98, "f32p split tail")
+
+
+def test_f32p_policy_fallback_is_unsplit():
+    # shapes where the plan picks s = 1: the f32p entry runs the unsplit launch unchanged
+    for M, N, K in [(2048, 9728, 2560), (64, 9728, 2560)]:
+        if q.qmm_splitk_plan(M, N, K).s != 1:
+            continue
+        d = syn.w4a16_inputs(M, N, K, seed=9200 + M)
+        dv = w4a16_device(d)
+        say("f32p fallback M=%d N=%d K=%d" % (M, N, K))
+        a = host_bits(run_w4a16(dv, M, N, K, 0, f32p=True))
+        b = host_bits(run_w4a16(dv, M, N, K, 1))
+        assert np.array_equal(a, b)
 
 
 # ----------------------------------------------------------- config 3 (dense)

@@ -24,7 +24,7 @@ QMM_PARTIAL_F32 = 1
 
 # Every symbol include/qmm.h declares.
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
-                      "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split")
+                      "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -68,6 +68,8 @@ def lib():
         L.qmm_splitk_plan.restype = I
         L.qmm_w4a16_g128.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_g128.restype = I
+        L.qmm_w4a16_g128_f32p.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.qmm_w4a16_g128_f32p.restype = I
         L.qmm_splitk_reduce.argtypes = [P, I, I, I, I, P, P]
         L.qmm_splitk_reduce.restype = I
         L.qmm_bf16_splitk.argtypes = [P, P, P, I, I, I, I, P, S, P]
@@ -140,6 +142,18 @@ def qmm_w4a16_g128(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspac
     return rc
 
 
+def qmm_w4a16_g128_f32p(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
+                        stream=None, check=True):
+    """qmm_w4a16_g128 with fp32 partial planes (workspace >= 4*s*M*N bytes); returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_w4a16_g128_f32p(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                                   int(s), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_g128_f32p")
+    return rc
+
+
 def qmm_w4a16_gemv(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
                    stream=None, check=True):
     """C = A . dequant(W)^T for M <= 8 on the matrix-vector kernel; returns the status."""
@@ -180,16 +194,18 @@ def qmm_bf16_splitk(A, B, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
 
 # ---------------------------------------------------------------- conveniences
 
-def w4a16_workspace_bytes(M, N, s):
-    return 2 * s * M * N if s > 1 else 0
+def w4a16_workspace_bytes(M, N, s, f32_partials=False):
+    return (4 if f32_partials else 2) * s * M * N if s > 1 else 0
 
 
 def effective_split(M, N, K, s=0):
     return qmm_splitk_plan(M, N, K).s if s == 0 else s
 
 
-def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None):
-    """Allocating wrapper: A bf16[M,K], Wq int32/uint32[N,K/8], scale/bias bf16[N,K/128] -> C bf16[M,N]."""
+def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None, f32_partials=False):
+    """Allocating wrapper: A bf16[M,K], Wq int32/uint32[N,K/8], scale/bias bf16[N,K/128] -> C bf16[M,N].
+
+    f32_partials selects qmm_w4a16_g128_f32p (fp32 partial planes)."""
     import torch
     M, K = A.shape
     N = Wq.shape[0]
@@ -197,9 +213,11 @@ def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     if s_eff > 1 and workspace is None:
-        workspace = torch.empty(w4a16_workspace_bytes(M, N, s_eff), dtype=torch.uint8, device=A.device)
+        workspace = torch.empty(w4a16_workspace_bytes(M, N, s_eff, f32_partials), dtype=torch.uint8,
+                                device=A.device)
     # s = 0 goes to the library as is: its plan may also run part of the tiles unsplit
-    qmm_w4a16_g128(A, Wq, scale, bias, out, M, N, K, s, workspace)
+    fn = qmm_w4a16_g128_f32p if f32_partials else qmm_w4a16_g128
+    fn(A, Wq, scale, bias, out, M, N, K, s, workspace)
     return out
 
 

@@ -55,10 +55,10 @@ W4A16Tile w4a16_tile(int M, int N) {
 }
 
 hipError_t dispatch_skinny(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
-                           void *out, int M, int N, int K, int s, bool vec, hipStream_t st) {
+                           void *out, bool f32_part, int M, int N, int K, int s, bool vec, hipStream_t st) {
     const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s);
-    return qmm_impl::launch_w4a16_skinny(tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, M, N, K, s,
-                                         vec, st);
+    return qmm_impl::launch_w4a16_skinny(tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part, M, N,
+                                         K, s, vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {
@@ -175,9 +175,11 @@ extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_po
     return QMM_OK;
 }
 
-extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void *bias,
-                              void *C, int M, int N, int K, int s, void *workspace,
-                              size_t workspace_bytes, void *stream)
+namespace {
+
+// The W4A16 matmul with partial planes of element size 2 (bf16) or 4 (fp32, f32_part).
+int w4a16_run(const void *A, const void *Wq, const void *scale, const void *bias, void *C, int M, int N, int K, int s,
+              void *workspace, size_t workspace_bytes, bool f32_part, void *stream)
 {
     if (!A || !Wq || !scale || !bias || !C) return QMM_ERR_ARG;
     if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
@@ -198,8 +200,9 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
         return QMM_ERR_SHAPE;
     }
     const size_t MN = (size_t)M * (size_t)N;
+    const size_t esz = f32_part ? 4 : 2;
     if (s > 1) {
-        if (!workspace || workspace_bytes < 2 * (size_t)s * MN) return QMM_ERR_WORKSPACE;
+        if (!workspace || workspace_bytes < esz * (size_t)s * MN) return QMM_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -210,22 +213,38 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
         if (s == 1) full_tiles = tiles;
         // Partial planes and C share one store-width decision (N % 4 == 0 and 8-byte C).
         int rc = hip_status(qmm_impl::launch_w4a16_wide(tile.ns, A, Wq, scale, bias, C, s > 1 ? workspace : nullptr,
-                                                        M, N, K, full_tiles, s, vec_c, st));
+                                                        f32_part, M, N, K, full_tiles, s, vec_c, st));
         if (rc != QMM_OK || s == 1) return rc;
         if (full_tiles == 0) {
             const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
-            return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
+            return hip_status(qmm_impl::launch_reduce(workspace, f32_part, s, MN, C, vec_red, st));
         }
         const int n_lo = (full_tiles / num_m) * tile.block_n();
         const bool vec_red = (N % 8 == 0) && aligned(C, 16);
-        return hip_status(qmm_impl::launch_reduce_cols(workspace, s, M, N, n_lo, C, vec_red, st));
+        return hip_status(qmm_impl::launch_reduce_cols(workspace, f32_part, s, M, N, n_lo, C, vec_red, st));
     }
-    if (s == 1) return hip_status(dispatch_skinny(tile, A, Wq, scale, bias, C, M, N, K, 1, vec_c, st));
+    if (s == 1) return hip_status(dispatch_skinny(tile, A, Wq, scale, bias, C, false, M, N, K, 1, vec_c, st));
     const bool vec_ws = (N % 4 == 0);
-    int rc = hip_status(dispatch_skinny(tile, A, Wq, scale, bias, workspace, M, N, K, s, vec_ws, st));
+    int rc = hip_status(dispatch_skinny(tile, A, Wq, scale, bias, workspace, f32_part, M, N, K, s, vec_ws, st));
     if (rc != QMM_OK) return rc;
     const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
-    return hip_status(qmm_impl::launch_reduce(workspace, false, s, MN, C, vec_red, st));
+    return hip_status(qmm_impl::launch_reduce(workspace, f32_part, s, MN, C, vec_red, st));
+}
+
+}  // namespace
+
+extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void *bias,
+                              void *C, int M, int N, int K, int s, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    return w4a16_run(A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias,
+                                   void *C, int M, int N, int K, int s, void *workspace,
+                                   size_t workspace_bytes, void *stream)
+{
+    return w4a16_run(A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, true, stream);
 }
 
 namespace {

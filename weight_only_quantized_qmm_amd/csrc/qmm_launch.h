@@ -45,9 +45,10 @@ struct DenseTile {
     int block_n() const { return 2 * 16 * ns; }
 };
 
+// out: C (bf16) when s = 1, else the partial planes [s][M][N], bf16 or (f32_part) fp32.
 hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
-                               const void *scale, const void *bias, void *out, int M, int N, int K, int s,
-                               bool vec_store, hipStream_t stream);
+                               const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
+                               int s, bool vec_store, hipStream_t stream);
 
 // Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves (two workgroups per CU);
 // 1, 2 = 256 x 256 tiles (one per CU) of 8 waves of 128 x 64, 8 waves of 256 x 32.
@@ -58,10 +59,10 @@ constexpr int kWideCols = 256;
 
 // Large-M kernel: the first full_tiles tiles (M-block fastest) unsplit into C, the
 // remaining ones in `split` near-equal group partitions into the planes of `part`
-// ([split][M][N] bf16; unused when split = 1).
+// ([split][M][N], bf16 or (f32_part) fp32; unused when split = 1).
 hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
-                             void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
-                             hipStream_t stream);
+                             void *C, void *part, bool f32_part, int M, int N, int K, int full_tiles, int split,
+                             bool vec_store, hipStream_t stream);
 
 // Decode matrix-vector kernel (M <= 8): a partition of kp reduction values fits its A
 // staging when kp <= 10240 (at most 5 chunks of 32 per lane) and m8 * kp <= 30720
@@ -74,9 +75,9 @@ hipError_t launch_w4a16_gemv(const void *A, const void *Wq, const void *scale, c
 hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t MN, void *C,
                          bool vec, hipStream_t stream);
 
-// The same merge restricted to columns [n_lo, N) of bf16 planes [s][M][N].
-hipError_t launch_reduce_cols(const void *partials, int s, int M, int N, int n_lo, void *C, bool vec,
-                              hipStream_t stream);
+// The same merge restricted to columns [n_lo, N) of planes [s][M][N] (bf16 or fp32).
+hipError_t launch_reduce_cols(const void *partials, bool f32_partials, int s, int M, int N, int n_lo, void *C,
+                              bool vec, hipStream_t stream);
 
 hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out, bool f32_out,
                         int M, int N, int K, int s, bool vec_store, hipStream_t stream);

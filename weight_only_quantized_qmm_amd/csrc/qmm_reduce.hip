@@ -72,11 +72,11 @@ reduce_scalar(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_
     C[i] = (uint16_t)f32_to_bf16(acc);
 }
 
-// Columns [n_lo, N) of bf16 planes [s][M][N]: W = N - n_lo columns per row; eight
+// Columns [n_lo, N) of planes [s][M][N]: W = N - n_lo columns per row; eight
 // consecutive columns per lane when W, N and n_lo are multiples of 8, else one.
-template <bool VEC>
+template <typename T, bool VEC>
 __global__ void __launch_bounds__(256)
-reduce_cols(const uint16_t *__restrict__ part, uint16_t *__restrict__ C, int s, int M, int N, int n_lo)
+reduce_cols(const T *__restrict__ part, uint16_t *__restrict__ C, int s, int M, int N, int n_lo)
 {
     const int W = N - n_lo;
     const int per = VEC ? 8 : 1;
@@ -134,22 +134,28 @@ hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t 
     return launch_t(static_cast<const uint16_t *>(partials), s, MN, static_cast<uint16_t *>(C), vec, stream);
 }
 
-hipError_t launch_reduce_cols(const void *partials, int s, int M, int N, int n_lo, void *C, bool vec,
-                              hipStream_t stream)
+template <typename T>
+hipError_t launch_cols_t(const T *p, int s, int M, int N, int n_lo, uint16_t *c, bool vec, hipStream_t stream)
 {
-    if (n_lo < 0 || n_lo >= N) return hipErrorInvalidValue;
     const size_t elems = (size_t)M * (size_t)(N - n_lo);
     const size_t per_thread = vec ? 8 : 1;
     const size_t threads = (elems + per_thread - 1) / per_thread;
     const dim3 grid((unsigned)((threads + 255) / 256));
-    const uint16_t *p = static_cast<const uint16_t *>(partials);
-    uint16_t *c = static_cast<uint16_t *>(C);
     (void)hipGetLastError();
     if (vec)
-        hipLaunchKernelGGL((reduce_cols<true>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
+        hipLaunchKernelGGL((reduce_cols<T, true>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
     else
-        hipLaunchKernelGGL((reduce_cols<false>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
+        hipLaunchKernelGGL((reduce_cols<T, false>), grid, dim3(256), 0, stream, p, c, s, M, N, n_lo);
     return hipGetLastError();
+}
+
+hipError_t launch_reduce_cols(const void *partials, bool f32_partials, int s, int M, int N, int n_lo, void *C,
+                              bool vec, hipStream_t stream)
+{
+    if (n_lo < 0 || n_lo >= N) return hipErrorInvalidValue;
+    uint16_t *c = static_cast<uint16_t *>(C);
+    if (f32_partials) return launch_cols_t(static_cast<const float *>(partials), s, M, N, n_lo, c, vec, stream);
+    return launch_cols_t(static_cast<const uint16_t *>(partials), s, M, N, n_lo, c, vec, stream);
 }
 
 }  // namespace qmm_impl

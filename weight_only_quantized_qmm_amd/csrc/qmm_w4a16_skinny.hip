@@ -35,7 +35,7 @@ template <int MT, int NS, int GPW, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                    uint16_t *__restrict__ out, int M, int N, int K, int gpp, int vec_store)
+                    void *__restrict__ out, int M, int N, int K, int gpp, int vec_store, int f32_part)
 {
     extern __shared__ __attribute__((aligned(16))) char red[];  // [WAVES][MT][NS][64] float4
     // Fetch every pointer argument up front, in the kernel's first scalar loads: left to
@@ -136,24 +136,37 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         const int m = m_blk + 16 * i + (l & 15);
         const int n = n_blk + 16 * j + 4 * (l >> 4);
         if (m < M) {
-            uint16_t *dst = out + (size_t)blockIdx.z * (size_t)M * (size_t)N + (size_t)m * (size_t)N + n;
-            if (vec_store && n + 3 < N) {
-                uint2 v;
-                v.x = pack_bf16x2(sum[0], sum[1]);
-                v.y = pack_bf16x2(sum[2], sum[3]);
-                *reinterpret_cast<uint2 *>(dst) = v;
-            } else {
+            // C (bf16) when unsplit, else plane blockIdx.z of bf16 or (f32_part) fp32 partials
+            const size_t e = (size_t)blockIdx.z * (size_t)M * (size_t)N + (size_t)m * (size_t)N + n;
+            if (f32_part && gridDim.z > 1) {
+                float *dst = static_cast<float *>(out) + e;
+                if (vec_store && n + 3 < N) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(sum[0], sum[1], sum[2], sum[3]);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N) dst[e] = (uint16_t)f32_to_bf16(sum[e]);
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        if (n + e2 < N) dst[e2] = sum[e2];
+                }
+            } else {
+                uint16_t *dst = static_cast<uint16_t *>(out) + e;
+                if (vec_store && n + 3 < N) {
+                    uint2 v;
+                    v.x = pack_bf16x2(sum[0], sum[1]);
+                    v.y = pack_bf16x2(sum[2], sum[3]);
+                    *reinterpret_cast<uint2 *>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        if (n + e2 < N) dst[e2] = (uint16_t)f32_to_bf16(sum[e2]);
+                }
             }
         }
     }
 }
 
 template <int MT, int NS, int GPW, int MAXW>
-hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, int M, int N,
-                      int K, int s, int waves, bool vec_store, hipStream_t stream)
+hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, bool f32_part,
+                      int M, int N, int K, int s, int waves, bool vec_store, hipStream_t stream)
 {
     const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
     const int gpp = (K / 128) / s;
@@ -163,7 +176,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
     hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       static_cast<uint16_t *>(out), M, N, K, gpp, vec_store ? 1 : 0);
+                       out, M, N, K, gpp, vec_store ? 1 : 0, f32_part ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -177,13 +190,14 @@ namespace qmm_impl {
 // grid would not fit on the GPU in one round: up to 8 waves, gpw <= 3, 2, 1 for mt 1, 2,
 // 4 (register budgets of 128 VGPRs per lane at 16 waves, 256 at 8).
 hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
-                               const void *scale, const void *bias, void *out, int M, int N, int K, int s,
-                               bool vec_store, hipStream_t stream)
+                               const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
+                               int s, bool vec_store, hipStream_t stream)
 {
     if (waves < 1 || waves > MAX_WAVES) return hipErrorInvalidValue;
 #define QMM_CFG(MT_, NS_, GPW_, MAXW_)                                                                         \
     if (mt == MT_ && ns == NS_ && gpw == GPW_)                                                                 \
-        return launch_cfg<MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, M, N, K, s, waves, vec_store, stream);
+        return launch_cfg<MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, s, waves, vec_store,   \
+                                                 stream);
     QMM_CFG(1, 2, 1, 16) QMM_CFG(1, 2, 2, 16) QMM_CFG(1, 2, 3, 16)
     QMM_CFG(2, 2, 1, 8) QMM_CFG(2, 2, 2, 8) QMM_CFG(2, 2, 3, 8)
     QMM_CFG(4, 2, 1, 8) QMM_CFG(4, 2, 2, 8)

@@ -200,6 +200,37 @@ __device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF::WM> &L, 
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Four consecutive outputs (columns n .. n+3 of one row, element offset e) as bf16 or
+// fp32: one 8- or 16-byte store when vec and n+3 < N, else element by element up to N.
+__device__ __forceinline__ void store4(char *base, bool f32, size_t e, int n, int N, int vec, float v0, float v1,
+                                       float v2, float v3)
+{
+    if (f32) {
+        float *q = reinterpret_cast<float *>(base) + e;
+        if (vec && n + 3 < N) {
+            *reinterpret_cast<float4 *>(q) = make_float4(v0, v1, v2, v3);
+        } else {
+            if (n < N) q[0] = v0;
+            if (n + 1 < N) q[1] = v1;
+            if (n + 2 < N) q[2] = v2;
+            if (n + 3 < N) q[3] = v3;
+        }
+    } else {
+        uint16_t *q = reinterpret_cast<uint16_t *>(base) + e;
+        if (vec && n + 3 < N) {
+            uint2 v;
+            v.x = pack_bf16x2(v0, v1);
+            v.y = pack_bf16x2(v2, v3);
+            *reinterpret_cast<uint2 *>(q) = v;
+        } else {
+            if (n < N) q[0] = (uint16_t)f32_to_bf16(v0);
+            if (n + 1 < N) q[1] = (uint16_t)f32_to_bf16(v1);
+            if (n + 2 < N) q[2] = (uint16_t)f32_to_bf16(v2);
+            if (n + 3 < N) q[3] = (uint16_t)f32_to_bf16(v3);
+        }
+    }
+}
+
 // Work decomposition (one-dimensional grid of full_tiles + tail_tiles * split
 // workgroups): workgroup b < full_tiles computes tile b over the whole reduction and
 // writes C; the others compute tile full_tiles + q % tail_tiles (q = b - full_tiles)
@@ -210,8 +241,8 @@ template <class CF>
 __global__ void __launch_bounds__(64 * CF::NW, CF::OCC)
 w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                   const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                  uint16_t *__restrict__ C, uint16_t *__restrict__ part, int M, int N, int K,
-                  int full_tiles, int tail_tiles, int split, int vec_store)
+                  uint16_t *__restrict__ C, void *__restrict__ part, int M, int N, int K,
+                  int full_tiles, int tail_tiles, int split, int vec_store, int f32_part)
 {
     typedef CF GE;
     constexpr int MI = CF::MI, NJ = CF::NJ;
@@ -237,7 +268,10 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
     const int g_lo = (int)(((long long)p * G) / nparts);
     const int g_hi = (int)(((long long)(p + 1) * G) / nparts);
     const int gpp = g_hi - g_lo;  // >= 1: nparts <= G
-    uint16_t *dst = nparts > 1 ? part + (size_t)p * (size_t)M * (size_t)N : C;
+    // Destination: C for an unsplit tile; else plane p of `part`, bf16 or (f32_part) fp32.
+    const bool to_f32 = nparts > 1 && f32_part;
+    char *dst = nparts > 1 ? static_cast<char *>(part) + (size_t)p * (size_t)M * (size_t)N * (f32_part ? 4 : 2)
+                           : reinterpret_cast<char *>(C);
     const int num_m = (M + GE::BM - 1) / GE::BM;
     const int m_idx = tile % num_m;
     const int n_idx = tile / num_m;
@@ -350,26 +384,14 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 #pragma unroll
             for (int vq = 0; vq < 4; ++vq) {
                 const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
-                uint16_t *p = dst + (size_t)m * (size_t)N + n;
                 const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
                 const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
-                if (vec_store && n + 3 < N) {
-                    if (row_ok) {
-                        uint2 v;
-                        v.x = pack_bf16x2(v0, v1);
-                        v.y = pack_bf16x2(v2, v3);
-                        *reinterpret_cast<uint2 *>(p) = v;
-                    }
-                } else if (row_ok) {
-                    if (n < N) p[0] = (uint16_t)f32_to_bf16(v0);
-                    if (n + 1 < N) p[1] = (uint16_t)f32_to_bf16(v1);
-                    if (n + 2 < N) p[2] = (uint16_t)f32_to_bf16(v2);
-                    if (n + 3 < N) p[3] = (uint16_t)f32_to_bf16(v3);
-                }
+                if (row_ok) store4(dst, to_f32, (size_t)m * (size_t)N + n, n, N, vec_store, v0, v1, v2, v3);
             }
         }
     }
 }
+
 
 typedef Cfg<1, 4, 2> CfgV0;  // 128 x 256 tile, 4 waves of 128 x 64, two workgroups per CU
 typedef Cfg<2, 4, 2> CfgV1;  // 256 x 256 tile, 8 waves of 128 x 64
@@ -377,11 +399,11 @@ typedef Cfg<2, 8, 1> CfgV2;  // 256 x 256 tile, 8 waves of 256 x 32
 
 template <class CF>
 void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
-                const uint16_t *bi, uint16_t *c, uint16_t *pt, int M, int N, int K, int full_tiles, int tail_tiles,
-                int split, int vec)
+                const uint16_t *bi, uint16_t *c, void *pt, int M, int N, int K, int full_tiles, int tail_tiles,
+                int split, int vec, int f32p)
 {
     hipLaunchKernelGGL((w4a16_wide_kernel<CF>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt, M, N, K,
-                       full_tiles, tail_tiles, split, vec);
+                       full_tiles, tail_tiles, split, vec, f32p);
 }
 
 }  // namespace
@@ -390,8 +412,8 @@ namespace qmm_impl {
 
 // The per-lane copy offsets are 32-bit byte offsets within 256 rows of A: K < 2^22.
 hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
-                             void *C, void *part, int M, int N, int K, int full_tiles, int split, bool vec_store,
-                             hipStream_t stream)
+                             void *C, void *part, bool f32_part, int M, int N, int K, int full_tiles, int split,
+                             bool vec_store, hipStream_t stream)
 {
     if (K >= (1 << 22) || variant < 0 || variant > 2) return hipErrorInvalidValue;
     const int rows = wide_rows(variant);
@@ -405,13 +427,14 @@ hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const v
     const uint16_t *sc = static_cast<const uint16_t *>(scale);
     const uint16_t *bi = static_cast<const uint16_t *>(bias);
     uint16_t *c = static_cast<uint16_t *>(C);
-    uint16_t *pt = static_cast<uint16_t *>(part);
+    void *pt = part;
     const int vec = vec_store ? 1 : 0;
+    const int f32p = f32_part ? 1 : 0;
     (void)hipGetLastError();
     switch (variant) {
-    case 0: launch_cfg<CfgV0>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
-    case 1: launch_cfg<CfgV1>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
-    default: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec); break;
+    case 0: launch_cfg<CfgV0>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
+    case 1: launch_cfg<CfgV1>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
+    default: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
     }
     return hipGetLastError();
 }

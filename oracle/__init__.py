@@ -8,7 +8,8 @@ never imports this package.
 Contents
   * ``qmm_w4a16``, ``qmm_w4a16_points``, ``qmm_dense``, ``reduce_bf16``,
     ``reduce_f32``, ``dequant_w4a16``, ``bf16_round``, ``bf16_value``,
-    ``nibble``: ctypes wrappers over the plain C definitions in qmm_oracle.c
+    ``nibble``, and for the other weight formats (4- or 8-bit codes, groups of
+    32, 64 or 128) ``qmm_wq``, ``qmm_wq_points``, ``dequant_wq``, ``code``: ctypes wrappers over the plain C definitions in qmm_oracle.c
     (fp64 products in ascending k, fp32 reduce, bf16 round-to-nearest-even).
   * ``policy``: the occupancy split rule of tiny-llm "Week 2 Day 7: Split-K
     Prefill", Task 3, in its plain form.
@@ -55,6 +56,14 @@ def _lib():
         lib.oracle_qmm_w4a16_points.restype = I
         lib.oracle_qmm_dense.argtypes = [P, P, I, I, I, I, P, I]
         lib.oracle_qmm_dense.restype = I
+        lib.oracle_code.argtypes = [P, I, I, I, I]
+        lib.oracle_code.restype = I
+        lib.oracle_dequant_wq.argtypes = [P, I, I, P, P, I, I, P]
+        lib.oracle_dequant_wq.restype = I
+        lib.oracle_qmm_wq.argtypes = [I, I, P, P, P, P, I, I, I, I, P, I]
+        lib.oracle_qmm_wq.restype = I
+        lib.oracle_qmm_wq_points.argtypes = [I, I, P, P, P, P, I, I, I, I, P, P, P]
+        lib.oracle_qmm_wq_points.restype = I
         lib.oracle_reduce_bf16.argtypes = [P, I, ctypes.c_size_t, P]
         lib.oracle_reduce_bf16.restype = None
         lib.oracle_reduce_f32.argtypes = [P, I, ctypes.c_size_t, P]
@@ -150,6 +159,54 @@ def qmm_w4a16_points(A, Wq, scale, bias, M, N, K, ms, ns):
                                         out.ctypes.data_as(ctypes.c_void_p))
     if rc != 0:
         raise ValueError("oracle_qmm_w4a16_points failed (%d)" % rc)
+    return out
+
+
+def code(Wq, bits, K, n, k):
+    """q[n, k] of a bits-wide code (4 or 8), lowest field of a word first."""
+    Wq, p = _c(Wq, np.uint32)
+    return _lib().oracle_code(p, bits, K, n, k)
+
+
+def dequant_wq(Wq, bits, group, scale, bias, N, K):
+    Wq, pw = _c(Wq, np.uint32)
+    scale, ps = _c(scale, np.uint16)
+    bias, pb = _c(bias, np.uint16)
+    w = np.empty((N, K), dtype=np.float64)
+    if _lib().oracle_dequant_wq(pw, bits, group, ps, pb, N, K, w.ctypes.data_as(ctypes.c_void_p)) != 0:
+        raise ValueError("unsupported weight format bits=%d group=%d K=%d" % (bits, group, K))
+    return w
+
+
+def qmm_wq(bits, group, A, Wq, scale, bias, M, N, K, s=1, nthreads=None):
+    """fp64 C[M,N] for a (bits, group) weight format, summed per partition (s equal
+    parts of the K/128 blocks)."""
+    A, pa = _c(A, np.uint16)
+    Wq, pw = _c(Wq, np.uint32)
+    scale, ps = _c(scale, np.uint16)
+    bias, pb = _c(bias, np.uint16)
+    C = np.empty((M, N), dtype=np.float64)
+    rc = _lib().oracle_qmm_wq(bits, group, pa, pw, ps, pb, M, N, K, s, C.ctypes.data_as(ctypes.c_void_p),
+                              nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_qmm_wq failed (%d) for bits=%d group=%d M=%d N=%d K=%d s=%d"
+                         % (rc, bits, group, M, N, K, s))
+    return C
+
+
+def qmm_wq_points(bits, group, A, Wq, scale, bias, M, N, K, ms, ns):
+    """fp64 C[ms[i], ns[i]] of the unsplit product of a (bits, group) format."""
+    A, pa = _c(A, np.uint16)
+    Wq, pw = _c(Wq, np.uint32)
+    scale, ps = _c(scale, np.uint16)
+    bias, pb = _c(bias, np.uint16)
+    ms, pm = _c(ms, np.int32)
+    ns, pn = _c(ns, np.int32)
+    out = np.empty(len(ms), dtype=np.float64)
+    rc = _lib().oracle_qmm_wq_points(bits, group, pa, pw, ps, pb, M, N, K, len(ms), pm, pn,
+                                     out.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("oracle_qmm_wq_points failed (%d)" % rc)
     return out
 
 

@@ -23,6 +23,12 @@
  *            (Task 2: same reduction length, group-aligned start and end).
  *   reduce: C_bf16[m,n] = bf16_rne( fp32 sum over p = 0..s-1 of partial[p,m,n] )
  *            (Task 4: one thread per output, sum all partitions in FP32, cast once).
+ *   other weight formats (skillsdirectory "Optimize Prefill vs Decode Kernels",
+ *   step 6: weight-only W4A16 and W8A16, dequantisation fused into the matmul):
+ *            q[n,k] = field (k mod (32/b)) of word Wq[n][k/(32/b)], b = 4 or 8 bits,
+ *            lowest bits first; w[n,k] = scale[n, k/gs] * q[n,k] + bias[n, k/gs]
+ *            for a group size gs of 32, 64 or 128; the split partitions stay on
+ *            128-value boundaries (which are group boundaries for every gs).
  *   dense:  C[m,n] = sum_k A[m,k] * B[n,k], split into s near-equal partitions of
  *            32-value granules (gpu-kernels-explained "Split-K, streams and overlap",
  *            Concept / Maths: k cut into s slices, a second pass adds the partials).
@@ -254,6 +260,88 @@ int oracle_qmm_dense(const uint16_t *A, const uint16_t *B, int M, int N, int K, 
     int rc = run_threads(a, b, M, N, K, kb, s, C, nthreads);
     free(a); free(b); free(kb);
     return rc;
+}
+
+/* ---- other weight formats ------------------------------------------------- */
+
+/* q[n,k] of a b-bit code (b = 4 or 8): field (k mod (32/b)) of word
+ * Wq[n][k/(32/b)], lowest bits first. */
+int oracle_code(const uint32_t *Wq, int bits, int K, int n, int k)
+{
+    int per_word = 32 / bits;
+    uint32_t word = Wq[(size_t)n * (size_t)(K / per_word) + (size_t)(k / per_word)];
+    return (int)((word >> (bits * (k % per_word))) & ((1u << bits) - 1u));
+}
+
+static int format_ok(int bits, int group, int K)
+{
+    if (bits != 4 && bits != 8) return 0;
+    if (group != 32 && group != 64 && group != 128) return 0;
+    return K > 0 && K % ORACLE_GROUP == 0;
+}
+
+/* w[n,k] = scale[n, k/group] * q[n,k] + bias[n, k/group], in fp64. */
+static double wq_weight(const uint32_t *Wq, int bits, int group, const uint16_t *scale,
+                        const uint16_t *bias, int K, int n, int k)
+{
+    int G = K / group;
+    int g = k / group;
+    double sc = oracle_bf16_value(scale[(size_t)n * G + g]);
+    double bi = oracle_bf16_value(bias[(size_t)n * G + g]);
+    return sc * (double)oracle_code(Wq, bits, K, n, k) + bi;
+}
+
+/* The whole dequantised matrix w[N][K] of a (bits, group) format. Returns 0, or -1
+ * for an unsupported format. */
+int oracle_dequant_wq(const uint32_t *Wq, int bits, int group, const uint16_t *scale,
+                      const uint16_t *bias, int N, int K, double *w)
+{
+    if (!format_ok(bits, group, K)) return -1;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k) w[(size_t)n * K + k] = wq_weight(Wq, bits, group, scale, bias, K, n, k);
+    return 0;
+}
+
+/* C[M][N] (fp64) of a (bits, group) weight format, summed per partition: s equal
+ * partitions of the K/128 blocks of 128 values. Returns 0, -1 on a bad format,
+ * shape or split, -2 on allocation failure. */
+int oracle_qmm_wq(int bits, int group, const uint16_t *A, const uint32_t *Wq, const uint16_t *scale,
+                  const uint16_t *bias, int M, int N, int K, int s, double *C, int nthreads)
+{
+    if (M <= 0 || N <= 0 || !format_ok(bits, group, K)) return -1;
+    int B = K / ORACLE_GROUP;
+    int *kb = (int *)malloc(((size_t)s + 1) * sizeof *kb);
+    if (!kb) return -2;
+    for (int p = 0; p < s; ++p) {
+        int bb, be;
+        if (oracle_partition_groups(B, s, p, &bb, &be) != 0) { free(kb); return -1; }
+        kb[p] = bb * ORACLE_GROUP;
+        kb[p + 1] = be * ORACLE_GROUP;
+    }
+    double *a = bf16_matrix_to_f64(A, (size_t)M * K);
+    double *w = (double *)malloc((size_t)N * K * sizeof *w);
+    if (!a || !w) { free(a); free(w); free(kb); return -2; }
+    oracle_dequant_wq(Wq, bits, group, scale, bias, N, K, w);
+    int rc = run_threads(a, w, M, N, K, kb, s, C, nthreads);
+    free(a); free(w); free(kb);
+    return rc;
+}
+
+/* Selected outputs C[ms[i], ns[i]] of the unsplit product of a (bits, group) format. */
+int oracle_qmm_wq_points(int bits, int group, const uint16_t *A, const uint32_t *Wq,
+                         const uint16_t *scale, const uint16_t *bias, int M, int N, int K, int count,
+                         const int *ms, const int *ns, double *out)
+{
+    if (M <= 0 || N <= 0 || !format_ok(bits, group, K)) return -1;
+    for (int i = 0; i < count; ++i) {
+        int m = ms[i], n = ns[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return -1;
+        double total = 0.0;
+        for (int k = 0; k < K; ++k)
+            total += oracle_bf16_value(A[(size_t)m * K + k]) * wq_weight(Wq, bits, group, scale, bias, K, n, k);
+        out[i] = total;
+    }
+    return 0;
 }
 
 /* ---- the split-K reduction ------------------------------------------------ */

@@ -13,6 +13,10 @@ Recipe (the workloads' stated distributions):
   scale  ~ U[0.005, 0.02] drawn in fp32, rounded to bf16, one per (row, 128-group)
   bias   = -8 * scale (exact in bf16)
   dense  A, B ~ N(0, 1) rounded to bf16
+Other weight formats (wq_inputs): b-bit codes q ~ uniform 0..2^b-1 packed 32/b per
+uint32 along K (lowest field first), one scale/bias per (row, group of gs values),
+scale ~ U[lo, hi] with [0.005, 0.02] for b = 4 and [0.005, 0.02]/16 for b = 8 (so
+the weights span the same range), bias = -2^(b-1) * scale (exact in bf16).
 Generator: numpy PCG64 with the given seed; draws in the order A, q, scale.
 Seeds used by the tests and the benchmark: 1000 * config + index of the shape
 within its config.
@@ -45,6 +49,34 @@ def pack_nibbles(q):
     for i in range(8):
         word |= q[:, :, i] << np.uint32(4 * i)
     return word
+
+
+def pack_codes(q, bits):
+    """uint q[N, K] of `bits`-wide codes (4 or 8) -> uint32 Wq[N, K*bits/32], field i of
+    word j holding k = (32/bits)*j + i in bits bits*i .. bits*i + bits - 1."""
+    per = 32 // bits
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    if K % per:
+        raise ValueError("K must be a multiple of %d" % per)
+    q = q.reshape(N, K // per, per)
+    word = np.zeros((N, K // per), dtype=np.uint32)
+    for i in range(per):
+        word |= q[:, :, i] << np.uint32(bits * i)
+    return word
+
+
+def wq_inputs(bits, group, M, N, K, seed):
+    """A bf16[M,K], Wq uint32[N, K*bits/32], scale/bias bf16[N, K/group], plus q."""
+    if K % GROUP or K % group:
+        raise ValueError("K must be a multiple of 128 and of the group size")
+    rng = rng_for(seed)
+    A = f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint16)
+    lo, hi = (0.005, 0.02) if bits == 4 else (0.005 / 16, 0.02 / 16)
+    scale = f32_to_bf16_bits(rng.uniform(lo, hi, size=(N, K // group)).astype(np.float32))
+    bias = f32_to_bf16_bits(np.float32(-(1 << (bits - 1))) * bf16_bits_to_f32(scale))
+    return dict(A=A, Wq=pack_codes(q, bits), scale=scale, bias=bias, q=q)
 
 
 def rng_for(seed):

@@ -36,6 +36,12 @@ MUTANTS = {
                          "        for (int p = 1; p < s; ++p) acc = acc + oracle_bf16_value(partials[(size_t)p * MN + i]);"),
     "round_ties_away": ("(frac == 0.5 && fmod(fl, 2.0) != 0.0)", "(frac == 0.5)"),
     "round_truncates": ("if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;", ""),
+    "code_order_reversed": ("(word >> (bits * (k % per_word)))", "(word >> (bits * (per_word - 1 - k % per_word)))"),
+    "code_mask_four_bits": ("& ((1u << bits) - 1u));", "& 0xFu);"),
+    "format_group_index_128": ("    int g = k / group;\n", "    int g = k / 128;\n"),
+    "format_group_count_128": ("    int G = K / group;\n    int g", "    int G = K / 128;\n    int g"),
+    "format_bias_dropped": ("return sc * (double)oracle_code(Wq, bits, K, n, k) + bi;",
+                            "return sc * (double)oracle_code(Wq, bits, K, n, k);"),
 }
 
 # The pin checks run against each mutant (a representative of every pin family).
@@ -56,6 +62,11 @@ CHECKS = [
     (pins.test_reduce_f32_matches_torch, dict(s=6, M=32, N=40)),
     (pins.test_granule_partitions_near_equal, {}),
     (pins.test_group_partitions_equal_and_covering, {}),
+    (pins.test_code_order_golden, {}),
+    (pins.test_format_dequant_matches_generator_fields, dict(bits=8, group=32)),
+    (pins.test_format_bruteforce_exact_rationals, dict(bits=8, group=64)),
+    (pins.test_format_one_hot_rows, dict(bits=4, group=32)),
+    (pins.test_format_integer_weights_equal_numpy_matmul, dict(bits=8)),
 ]
 
 
@@ -79,7 +90,8 @@ def test_mutant_is_caught(tmp_path, name):
     # copy the ctypes signatures of the real library onto the mutant
     for fn in ("oracle_bf16_value", "oracle_bf16_round", "oracle_nibble", "oracle_dequant_w4a16",
                "oracle_partition_groups", "oracle_partition_granules", "oracle_qmm_w4a16",
-               "oracle_qmm_w4a16_points", "oracle_qmm_dense", "oracle_reduce_bf16", "oracle_reduce_f32"):
+               "oracle_qmm_w4a16_points", "oracle_qmm_dense", "oracle_reduce_bf16", "oracle_reduce_f32",
+               "oracle_code", "oracle_dequant_wq", "oracle_qmm_wq", "oracle_qmm_wq_points"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     caught = []

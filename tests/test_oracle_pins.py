@@ -258,6 +258,105 @@ def test_points_match_full_product():
     assert np.array_equal(pts, C[ms, ns])
 
 
+# ------------------------------------------------- other weight formats
+
+FORMATS = [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
+
+
+def test_code_order_golden():
+    g = load_golden("code_order.json")
+    for bits, key in ((8, "w8"), (4, "w4")):
+        Wq = np.array([[int(h, 16) for h in g[key]["words_hex"]]], dtype=np.uint32)
+        per = 32 // bits
+        K = per * Wq.shape[1]
+        for j, expect in enumerate(g[key]["q"]):
+            assert [oracle.code(Wq, bits, K, 0, per * j + i) for i in range(per)] == expect, (bits, j)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_format_dequant_matches_generator_fields(bits, group):
+    N, K = 5, 256
+    d = syn.wq_inputs(bits, group, 2, N, K, seed=40 + bits + group)
+    w = oracle.dequant_wq(d["Wq"], bits, group, d["scale"], d["bias"], N, K)
+    sc = syn.bf16_bits_to_f32(d["scale"]).astype(np.float64)
+    g = np.arange(K) // group
+    # bias = -2^(bits-1) * scale, so the weight is scale * (q - 2^(bits-1)) exactly
+    assert np.array_equal(w, sc[:, g] * (d["q"].astype(np.float64) - (1 << (bits - 1))))
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 64), (8, 32), (8, 64), (8, 128)])
+def test_format_bruteforce_exact_rationals(bits, group):
+    M, N, K = 2, 3, 256
+    seed = 300 + bits * 10 + group
+    d = syn.wq_inputs(bits, group, M, N, K, seed=seed)
+    scale = syn.random_bf16_any((N, K // group), seed + 1, -10, 0)
+    bias = syn.random_bf16_any((N, K // group), seed + 2, -4, 4)
+    q, A = d["q"], d["A"]
+    Af = [[bf16_fraction(A[m, k]) for k in range(K)] for m in range(M)]
+    for n in range(N):
+        w = [bf16_fraction(scale[n, k // group]) * int(q[n, k]) + bf16_fraction(bias[n, k // group])
+             for k in range(K)]
+        for m in range(M):
+            terms = [Af[m][k] * w[k] for k in range(K)]
+            exact = sum(terms, Fraction(0))
+            absum = sum((abs(t) for t in terms), Fraction(0))
+            for s in (1, 2):
+                C = oracle.qmm_wq(bits, group, A, d["Wq"], scale, bias, M, N, K, s=s, nthreads=1)
+                assert abs(Fraction(C[m, n]) - exact) <= Fraction(gamma(K)) * absum, (m, n, s)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_format_one_hot_rows(bits, group):
+    M, N, K = 8, 7, 512
+    d = syn.wq_inputs(bits, group, M, N, K, seed=50 + bits + group)
+    ks = [0, 31, 32, 63, 64, 127, 200, 511]
+    A = np.zeros((M, K), dtype=np.uint16)
+    for m, k in enumerate(ks):
+        A[m, k] = 0x3F80
+    sc = syn.bf16_bits_to_f32(d["scale"]).astype(np.float64)
+    bi = syn.bf16_bits_to_f32(d["bias"]).astype(np.float64)
+    for s in (1, 4):
+        C = oracle.qmm_wq(bits, group, A, d["Wq"], d["scale"], d["bias"], M, N, K, s=s)
+        for m, k in enumerate(ks):
+            assert np.array_equal(C[m], sc[:, k // group] * d["q"][:, k] + bi[:, k // group]), (m, s)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_format_integer_weights_equal_numpy_matmul(bits):
+    M, N, K = 12, 20, 512
+    d = syn.wq_inputs(bits, 64, M, N, K, seed=60 + bits)
+    ones = np.full((N, K // 64), 0x3F80, dtype=np.uint16)
+    zeros = np.zeros((N, K // 64), dtype=np.uint16)
+    C = oracle.qmm_wq(bits, 64, d["A"], d["Wq"], ones, zeros, M, N, K, s=1)
+    a = syn.bf16_bits_to_f32(d["A"]).astype(np.float64)
+    qf = d["q"].astype(np.float64)
+    assert np.all(np.abs(C - a @ qf.T) <= 2 * gamma(K) * (np.abs(a) @ qf.T))
+
+
+def test_format_w4_g128_is_the_w4a16_product():
+    M, N, K = 6, 9, 640
+    d = syn.w4a16_inputs(M, N, K, seed=70)
+    for s in (1, 5):
+        a = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, s=s)
+        b = oracle.qmm_wq(4, 128, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, s=s)
+        assert np.array_equal(a, b)
+
+
+def test_format_points_match_full_product_and_rejects():
+    M, N, K = 5, 6, 384
+    d = syn.wq_inputs(8, 32, M, N, K, seed=71)
+    C = oracle.qmm_wq(8, 32, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    ms = np.array([0, 4, 2], dtype=np.int32)
+    ns = np.array([5, 0, 3], dtype=np.int32)
+    assert np.array_equal(oracle.qmm_wq_points(8, 32, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns),
+                          C[ms, ns])
+    for bits, group, KK in ((5, 128, 384), (8, 16, 384), (8, 256, 512)):
+        with pytest.raises(ValueError):
+            oracle.qmm_wq(bits, group, d["A"], d["Wq"], d["scale"], d["bias"], M, N, KK)
+    with pytest.raises(ValueError):  # 3 blocks of 128 do not split in two
+        oracle.qmm_wq(8, 32, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, s=2)
+
+
 # ---------------------------------------------------------------- reduction
 
 @pytest.mark.parametrize("s,M,N", [(1, 3, 5), (2, 16, 64), (5, 48, 1000), (20, 7, 33), (32, 4, 9)])

@@ -21,8 +21,9 @@
  * Layouts (all row-major, contiguous, no strides):
  *   A      bf16   [M][K]
  *   Wq     uint32 [N][K/8]   nibble i (bits 4i..4i+3) of word j holds q[n, 8j+i]
- *   scale  bf16   [N][K/128]
- *   bias   bf16   [N][K/128]
+ *                            (qmm_wna16: [N][K*bits/32], 4- or 8-bit fields)
+ *   scale  bf16   [N][K/128]   (qmm_wna16: [N][K/group_size])
+ *   bias   bf16   [N][K/128]   (qmm_wna16: [N][K/group_size])
  *   C      bf16   [M][N]
  *   partials      [s][M][N]  bf16 (W4A16), fp32 (dense, and W4A16 through qmm_w4a16_g128_f32p)
  *   dense  A bf16 [M][K], B bf16 [N][K], C = A . B^T
@@ -151,6 +152,35 @@ int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void 
  */
 int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
                         int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Other weight-only formats (skillsdirectory "Optimize Prefill vs Decode Kernels",
+ * step 6: weight-only W4A16 and W8A16 with the dequantisation fused into the matmul
+ * loop), on the same kernels, plan and reduce as qmm_w4a16_g128.
+ *
+ *   bits        4 or 8: unsigned codes q in [0, 2^bits), packed 32/bits per 32-bit word
+ *               along K, lowest field first: field i (bits bits*i .. bits*i+bits-1) of word
+ *               j of row n holds q[n, (32/bits)*j + i]. Wq is uint32 [N][K*bits/32].
+ *   group_size  32, 64 or 128: scale and bias are bf16 [N][K/group_size], and
+ *               w[n,k] = scale[n, k/group_size] * q[n,k] + bias[n, k/group_size].
+ *   K must be a multiple of 128. The split partitions K into blocks of 128 values (each a
+ *   whole number of groups): s = 0 asks qmm_wna16_plan, s >= 1 must divide K/128.
+ *   partial_dtype QMM_PARTIAL_BF16 (workspace >= 2*s*M*N bytes) or QMM_PARTIAL_F32
+ *   (>= 4*s*M*N bytes) when the effective s > 1.
+ *   qmm_wna16(4, 128, QMM_PARTIAL_BF16, ...) is qmm_w4a16_g128, launch for launch, and
+ *   qmm_wna16(4, 128, QMM_PARTIAL_F32, ...) is qmm_w4a16_g128_f32p.
+ *   Errors as qmm_w4a16_g128; an unsupported bits, group_size or partial_dtype is
+ *   QMM_ERR_ARG.
+ */
+int qmm_wna16(int bits, int group_size, int partial_dtype, const void *A, const void *Wq,
+              const void *scale, const void *bias, void *C, int M, int N, int K, int s,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/* qmm_splitk_plan for a (bits, group_size) format: the same rule, with the large-M
+ * kernel's workgroups per CU for that format's LDS footprint. workspace_bytes is the
+ * bf16-partial size. Host only, pure. QMM_ERR_ARG for an unsupported format. */
+int qmm_wna16_plan(int bits, int group_size, int M, int N, int K, const qmm_policy *policy,
+                   qmm_plan *out);
 
 /*
  * qmm_w4a16_gemv -- the same product for decode-sized M (1 to 8 rows) on a matrix-vector

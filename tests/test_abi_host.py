@@ -115,6 +115,40 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         assert plan.full_tiles == (tiles if plan.s == 1 else 0)
 
 
+FORMATS = [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
+
+
+def _wide_lds_bytes(rows, bits, group):
+    # three stage slots of A (rows x 64 bf16) and of W (256 rows x 64 codes), two of the
+    # 128-value block's scale and bias dwords (256 rows x 128/group groups each)
+    return 3 * rows * 128 + 3 * 256 * 64 * bits // 8 + 2 * 2 * 256 * 4 * (128 // group)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_wna16_plan_follows_the_rule_for_each_format(bits, group):
+    pol = q.policy_preset("QMM_POLICY_MI355X")
+    for M, N, K in ALL_SHAPES:
+        name = "%dx%dx%d" % (M, N, K)
+        plan = q.qmm_wna16_plan(bits, group, M, N, K)
+        ref = q.qmm_splitk_plan(M, N, K)
+        assert (plan.block_m, plan.block_n, plan.base_tiles) == (ref.block_m, ref.block_n, ref.base_tiles)
+        if M <= 64 or (bits, group) == (4, 128):
+            assert (plan.s, plan.full_tiles, plan.grid_x) == (ref.s, ref.full_tiles, ref.grid_x), (name, M)
+            continue
+        wgs = 2 if plan.block_m == 128 and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024 else 1
+        tiles = plan.base_tiles
+        num_m = -(-M // plan.block_m)
+        assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
+            tiles, num_m, K, pol.target_blocks * wgs, pol.cap, pol.min_k_per_split), (name, M)
+
+
+def test_wna16_plan_lds_budget():
+    # 128-row tiles keep two workgroups per CU only for 4-bit codes in groups of 64 or 128
+    two = [f for f in FORMATS if 2 * _wide_lds_bytes(128, *f) <= 160 * 1024]
+    assert two == [(4, 64), (4, 128)]
+    assert max(_wide_lds_bytes(256, *f) for f in FORMATS) <= 160 * 1024
+
+
 def test_fill_decomposition_cases():
     # 608 tiles (gate at M=2048 in 128 x 256 tiles), 512 slots: 512 unsplit, the last
     # 96 in five partitions; 160 tiles: three partitions each; 512 tiles: no split.
@@ -187,6 +221,34 @@ def _w4f(**kw):
 ])
 def test_w4a16_f32p_rejects_before_launch(kw, code):
     assert _w4f(**kw) == code
+
+
+def _wn(bits=8, group=64, dt=0, **kw):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=32, N=1024, K=2560, s=1,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    return q.qmm_wna16(bits, group, dt, a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"],
+                       a["s"], a["workspace"], a["workspace_bytes"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("fmt,kw,code", [
+    (dict(bits=5), {}, q.QMM_ERR_ARG), (dict(bits=2), {}, q.QMM_ERR_ARG), (dict(group=16), {}, q.QMM_ERR_ARG),
+    (dict(group=256), {}, q.QMM_ERR_ARG), (dict(group=96), {}, q.QMM_ERR_ARG), (dict(dt=2), {}, q.QMM_ERR_ARG),
+    ({}, dict(A=None), q.QMM_ERR_ARG), ({}, dict(K=2560 + 64), q.QMM_ERR_SHAPE), ({}, dict(s=3), q.QMM_ERR_SHAPE),
+    ({}, dict(A=ADDR + 8), q.QMM_ERR_ALIGN), ({}, dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(dt=1), dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024), q.QMM_ERR_WORKSPACE),
+    ({}, dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024 - 2), q.QMM_ERR_WORKSPACE),
+    ({}, dict(M=1 << 30, N=1 << 30), q.QMM_ERR_SIZE),
+])
+def test_wna16_rejects_before_launch(fmt, kw, code):
+    assert _wn(**fmt, **kw) == code
+
+
+def test_wna16_plan_rejects_unsupported_formats():
+    for bits, group in [(5, 128), (8, 16), (4, 256), (16, 128)]:
+        with pytest.raises(q.QmmError) as e:
+            q.qmm_wna16_plan(bits, group, 16, 1024, 2560)
+        assert e.value.status == q.QMM_ERR_ARG
 
 
 def test_w4a16_workspace_sizes():

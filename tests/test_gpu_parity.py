@@ -437,6 +437,119 @@ def test_determinism_two_runs():
         assert np.array_equal(a, b)
 
 
+# ------------------------------------------- other weight formats (qmm_wna16)
+
+FORMATS = [(4, 32), (4, 64), (8, 32), (8, 64), (8, 128)]
+
+
+def run_wna16(dv, bits, group, M, N, K, s, guard=0, f32p=False):
+    """qmm_wna16 through the C ABI; returns C (bf16 device tensor), checking guard bands
+    around C and the workspace when guard > 0."""
+    s_eff = q.qmm_wna16_plan(bits, group, M, N, K).s if s == 0 else s
+    Cbuf = torch.full((M * N + 2 * guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    C = Cbuf[guard:guard + M * N].view(M, N)
+    ws = wbuf = None
+    wdt = torch.float32 if f32p else torch.bfloat16
+    gw = ((guard + 7) // 8) * 8
+    if s_eff > 1:
+        wbuf = torch.full((s_eff * M * N + 2 * gw,), -777.0, dtype=wdt, device="cuda")
+        ws = wbuf[gw:gw + s_eff * M * N]
+    q.qmm_wna16(bits, group, q.QMM_PARTIAL_F32 if f32p else q.QMM_PARTIAL_BF16, dv["A"], dv["Wq"], dv["scale"],
+                dv["bias"], C, M, N, K, s, ws)
+    torch.cuda.synchronize()
+    if guard:
+        g = host_bits(Cbuf)
+        canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+        assert np.all(g[:guard] == canary) and np.all(g[guard + M * N:] == canary), "C guard band written"
+        if wbuf is not None:
+            w = wbuf.cpu().numpy() if f32p else host_bits(wbuf)
+            wc = np.float32(-777.0) if f32p else host_bits(torch.tensor([-777.0], dtype=torch.bfloat16))[0]
+            assert np.all(w[:gw] == wc) and np.all(w[gw + s_eff * M * N:] == wc), "workspace guard written"
+    return C
+
+
+# small-M kernel (M <= 64, ragged N), 128-row and 256-row large-M kernels
+FORMAT_SHAPES = [(1, 1000, 2560, 4), (16, 1024, 2560, 5), (48, 1000, 1024, 2), (100, 1000, 2560, 4),
+                 (300, 520, 1024, 8)]
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("M,N,K,s", FORMAT_SHAPES)
+def test_wna16_formats_match_oracle(bits, group, M, N, K, s):
+    d = syn.wq_inputs(bits, group, M, N, K, seed=11000 + 7 * M + bits * 3 + group)
+    ref = oracle.qmm_wq(bits, group, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for ss in (1, s, 0):
+        say("wna16 bits=%d group=%d M=%d N=%d K=%d s=%d" % (bits, group, M, N, K, ss))
+        C = run_wna16(dv, bits, group, M, N, K, ss, guard=64)
+        check_tolerance(host_f64(C), ref, what="w%da16 g%d %dx%dx%d s=%d" % (bits, group, M, N, K, ss))
+    say("wna16 bits=%d group=%d M=%d fp32 partials s=%d" % (bits, group, M, s))
+    C = run_wna16(dv, bits, group, M, N, K, s, guard=64, f32p=True)
+    check_tolerance(host_f64(C), ref, what="w%da16 g%d %dx%dx%d s=%d fp32 partials" % (bits, group, M, N, K, s))
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("M", [16, 100, 300])
+def test_wna16_one_hot_rows_exact(bits, group, M):
+    """A row with a single 1 at k picks w[:, k] = scale*q + bias (exact in fp32, one
+    rounding to bf16): every split gives the correctly rounded weights, bit for bit.
+    This pins the code order, the group index and the partition bounds on the GPU."""
+    N, K = 300, 1024
+    d = syn.wq_inputs(bits, group, M, N, K, seed=12000 + M + bits + group)
+    rng = np.random.default_rng(12000 + M)
+    ks = rng.integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), ks] = 0x3F80
+    d["A"] = A
+    ref_bits = oracle.bf16_round_array(oracle.qmm_wq(bits, group, A, d["Wq"], d["scale"], d["bias"], M, N, K))
+    dv = w4a16_device(d)
+    for s in (1, 2, 8):
+        say("wna16 one-hot bits=%d group=%d M=%d s=%d" % (bits, group, M, s))
+        got = host_bits(run_wna16(dv, bits, group, M, N, K, s))
+        assert np.array_equal(got, ref_bits), "s=%d: %d of %d differ" % (s, int((got != ref_bits).sum()), got.size)
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_w8a16_rounds_once(M):
+    """8-bit codes with power-of-two scales: exact dequantisation and products, so the
+    unsplit kernel and fp32 planes round once (see check_single_cast)."""
+    N, K = 520, 2560
+    d = syn.wq_inputs(8, 128, M, N, K, seed=13000 + M)
+    e = np.random.default_rng(13001 + M).integers(-11, -8, size=d["scale"].shape)
+    sc = np.ldexp(np.float32(1.0), e).astype(np.float32)
+    d["scale"] = syn.f32_to_bf16_bits(sc)
+    d["bias"] = syn.f32_to_bf16_bits(np.float32(-128.0) * sc)
+    ref = oracle.qmm_wq(8, 128, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    say("w8a16 single cast M=%d s=1" % M)
+    check_single_cast(host_bits(run_wna16(dv, 8, 128, M, N, K, 1)), ref, 0.98, "w8a16 %d s=1" % M)
+    say("w8a16 single cast M=%d s=4 fp32 partials" % M)
+    check_single_cast(host_bits(run_wna16(dv, 8, 128, M, N, K, 4, f32p=True)), ref, 0.98, "w8a16 %d s=4 f32p" % M)
+
+
+def test_wna16_w4_g128_is_the_w4a16_launch():
+    for M, N, K in [(16, 1024, 2560), (300, 520, 1024)]:
+        d = syn.w4a16_inputs(M, N, K, seed=14000 + M)
+        dv = w4a16_device(d)
+        for s in (1, 0, 4):
+            say("wna16(4,128) vs w4a16 M=%d s=%d" % (M, s))
+            a = host_bits(run_wna16(dv, 4, 128, M, N, K, s))
+            b = host_bits(run_w4a16(dv, M, N, K, s))
+            assert np.array_equal(a, b)
+
+
+def test_w8a16_full_size_sampled():
+    """W8A16 g128 at the gate projection's full size (M = 2048) under the plan."""
+    M, N, K = 2048, 9728, 2560
+    d = syn.wq_inputs(8, 128, M, N, K, seed=15000)
+    dv = w4a16_device(d)
+    say("w8a16 full size M=%d N=%d K=%d plan" % (M, N, K))
+    C = host_f64(run_wna16(dv, 8, 128, M, N, K, 0))
+    ms, ns = sample_points(M, N, 15000)
+    ref = oracle.qmm_wq_points(8, 128, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+    check_tolerance(C[ms, ns], ref, what="w8a16 gate M=2048 (sampled)")
+
+
 # ------------------------------------------------------------- edge shapes
 
 EDGE = [(1, 1, 128, 1), (1, 17, 256, 2), (3, 33, 384, 3), (15, 100, 512, 4), (17, 64, 1024, 8),

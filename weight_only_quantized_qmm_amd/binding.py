@@ -24,7 +24,8 @@ QMM_PARTIAL_F32 = 1
 
 # Every symbol include/qmm.h declares.
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
-                      "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p")
+                      "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p",
+                      "qmm_wna16", "qmm_wna16_plan")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -70,6 +71,10 @@ def lib():
         L.qmm_w4a16_g128.restype = I
         L.qmm_w4a16_g128_f32p.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_g128_f32p.restype = I
+        L.qmm_wna16.argtypes = [I, I, I, P, P, P, P, P, I, I, I, I, P, S, P]
+        L.qmm_wna16.restype = I
+        L.qmm_wna16_plan.argtypes = [I, I, I, I, I, ctypes.POINTER(qmm_policy), ctypes.POINTER(qmm_plan)]
+        L.qmm_wna16_plan.restype = I
         L.qmm_splitk_reduce.argtypes = [P, I, I, I, I, P, P]
         L.qmm_splitk_reduce.restype = I
         L.qmm_bf16_splitk.argtypes = [P, P, P, I, I, I, I, P, S, P]
@@ -103,6 +108,16 @@ def qmm_splitk_plan(M, N, K, group_size=128, policy=None):
     rc = lib().qmm_splitk_plan(int(M), int(N), int(K), int(group_size), pol, ctypes.byref(out))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_splitk_plan")
+    return out
+
+
+def qmm_wna16_plan(bits, group_size, M, N, K, policy=None):
+    """Host-only plan for a (bits, group_size) weight format; returns a qmm_plan."""
+    out = qmm_plan()
+    pol = ctypes.byref(policy) if policy is not None else None
+    rc = lib().qmm_wna16_plan(int(bits), int(group_size), int(M), int(N), int(K), pol, ctypes.byref(out))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_wna16_plan")
     return out
 
 
@@ -154,6 +169,19 @@ def qmm_w4a16_g128_f32p(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, wor
     return rc
 
 
+def qmm_wna16(bits, group_size, partial_dtype, A, Wq, scale, bias, C, M, N, K, s=0, workspace=None,
+              workspace_bytes=None, stream=None, check=True):
+    """C = A . dequant(W)^T for `bits`-wide codes and scale/bias groups of group_size; returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_wna16(int(bits), int(group_size), int(partial_dtype), _ptr(A), _ptr(Wq), _ptr(scale),
+                         _ptr(bias), _ptr(C), int(M), int(N), int(K), int(s), _ptr(workspace),
+                         int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_wna16")
+    return rc
+
+
 def qmm_w4a16_gemv(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
                    stream=None, check=True):
     """C = A . dequant(W)^T for M <= 8 on the matrix-vector kernel; returns the status."""
@@ -200,6 +228,23 @@ def w4a16_workspace_bytes(M, N, s, f32_partials=False):
 
 def effective_split(M, N, K, s=0):
     return qmm_splitk_plan(M, N, K).s if s == 0 else s
+
+
+def wna16(bits, group_size, A, Wq, scale, bias, s=0, out=None, workspace=None, f32_partials=False):
+    """Allocating wrapper for qmm_wna16: A bf16[M,K], Wq int32/uint32[N, K*bits/32],
+    scale/bias bf16[N, K/group_size] -> C bf16[M,N]."""
+    import torch
+    M, K = A.shape
+    N = Wq.shape[0]
+    s_eff = qmm_wna16_plan(bits, group_size, M, N, K).s if s == 0 else s
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if s_eff > 1 and workspace is None:
+        workspace = torch.empty(w4a16_workspace_bytes(M, N, s_eff, f32_partials), dtype=torch.uint8,
+                                device=A.device)
+    qmm_wna16(bits, group_size, QMM_PARTIAL_F32 if f32_partials else QMM_PARTIAL_BF16, A, Wq, scale, bias, out,
+              M, N, K, s, workspace)
+    return out
 
 
 def w4a16(A, Wq, scale, bias, s=0, out=None, workspace=None, f32_partials=False):

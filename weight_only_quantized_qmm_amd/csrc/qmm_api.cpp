@@ -15,6 +15,7 @@
 
 using qmm_impl::DenseTile;
 using qmm_impl::W4A16Tile;
+using qmm_impl::WFormat;
 
 extern "C" {
 const qmm_policy QMM_POLICY_PAGE = {32, 32, 320, 16, 128};
@@ -54,11 +55,12 @@ W4A16Tile w4a16_tile(int M, int N) {
     return t;
 }
 
-hipError_t dispatch_skinny(const W4A16Tile &tile, const void *A, const void *Wq, const void *scale, const void *bias,
-                           void *out, bool f32_part, int M, int N, int K, int s, bool vec, hipStream_t st) {
-    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s);
-    return qmm_impl::launch_w4a16_skinny(tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part, M, N,
-                                         K, s, vec, st);
+hipError_t dispatch_skinny(WFormat fmt, const W4A16Tile &tile, const void *A, const void *Wq, const void *scale,
+                           const void *bias, void *out, bool f32_part, int M, int N, int K, int s, bool vec,
+                           hipStream_t st) {
+    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s, fmt.bits);
+    return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part,
+                                         M, N, K, s, vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {
@@ -131,10 +133,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
 
 }  // namespace
 
-extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *policy,
-                               qmm_plan *out)
+namespace {
+
+// The plan of an (M, N, K) product in weight format fmt (the split rule is the same for
+// every format; the large-M kernel's workgroups per CU depend on the format's LDS).
+int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_plan *out)
 {
-    if (!out || M <= 0 || N <= 0 || K <= 0 || group_size != kGroup) return QMM_ERR_ARG;
+    if (!out || M <= 0 || N <= 0 || K <= 0 || !qmm_impl::format_supported(fmt)) return QMM_ERR_ARG;
     if (K % kGroup != 0) return QMM_ERR_SHAPE;
     if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
     const qmm_policy pol = policy ? *policy : QMM_POLICY_MI355X;
@@ -148,7 +153,7 @@ extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_po
     Decomp d;
     if (tile.kind == qmm_impl::W4A16_WIDE && pol.tile_m == 0 && pol.tile_n == 0) {
         // slots: target_blocks times the workgroups of this kernel one CU holds
-        const long long slots = (long long)pol.target_blocks * qmm_impl::wide_wgs_per_cu(tile.ns);
+        const long long slots = (long long)pol.target_blocks * qmm_impl::wide_wgs_per_cu(tile.ns, fmt);
         d = wide_rule(kernel_tiles, ceil_div(M, tile.block_m()), G, K, slots, pol);
     } else {
         d.s = split_rule(base, G, K, pol);
@@ -175,13 +180,29 @@ extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_po
     return QMM_OK;
 }
 
+}  // namespace
+
+extern "C" int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *policy,
+                               qmm_plan *out)
+{
+    if (group_size != kGroup) return QMM_ERR_ARG;
+    return plan_format(WFormat{4, kGroup}, M, N, K, policy, out);
+}
+
+extern "C" int qmm_wna16_plan(int bits, int group_size, int M, int N, int K, const qmm_policy *policy,
+                              qmm_plan *out)
+{
+    return plan_format(WFormat{bits, group_size}, M, N, K, policy, out);
+}
+
 namespace {
 
-// The W4A16 matmul with partial planes of element size 2 (bf16) or 4 (fp32, f32_part).
-int w4a16_run(const void *A, const void *Wq, const void *scale, const void *bias, void *C, int M, int N, int K, int s,
-              void *workspace, size_t workspace_bytes, bool f32_part, void *stream)
+// The weight-only matmul in format fmt with partial planes of element size 2 (bf16) or
+// 4 (fp32, f32_part).
+int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const void *bias, void *C, int M, int N,
+           int K, int s, void *workspace, size_t workspace_bytes, bool f32_part, void *stream)
 {
-    if (!A || !Wq || !scale || !bias || !C) return QMM_ERR_ARG;
+    if (!A || !Wq || !scale || !bias || !C || !qmm_impl::format_supported(fmt)) return QMM_ERR_ARG;
     if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
     if (K % kGroup != 0) return QMM_ERR_SHAPE;
     if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
@@ -192,7 +213,7 @@ int w4a16_run(const void *A, const void *Wq, const void *scale, const void *bias
     int full_tiles = 0;
     if (s == 0) {
         qmm_plan plan;
-        const int rc = qmm_splitk_plan(M, N, K, kGroup, nullptr, &plan);
+        const int rc = plan_format(fmt, M, N, K, nullptr, &plan);
         if (rc != QMM_OK) return rc;
         s = plan.s;
         full_tiles = plan.full_tiles;
@@ -212,8 +233,9 @@ int w4a16_run(const void *A, const void *Wq, const void *scale, const void *bias
         const int tiles = num_m * (int)ceil_div(N, tile.block_n());
         if (s == 1) full_tiles = tiles;
         // Partial planes and C share one store-width decision (N % 4 == 0 and 8-byte C).
-        int rc = hip_status(qmm_impl::launch_w4a16_wide(tile.ns, A, Wq, scale, bias, C, s > 1 ? workspace : nullptr,
-                                                        f32_part, M, N, K, full_tiles, s, vec_c, st));
+        int rc = hip_status(qmm_impl::launch_w4a16_wide(fmt, tile.ns, A, Wq, scale, bias, C,
+                                                        s > 1 ? workspace : nullptr, f32_part, M, N, K, full_tiles,
+                                                        s, vec_c, st));
         if (rc != QMM_OK || s == 1) return rc;
         if (full_tiles == 0) {
             const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
@@ -223,9 +245,9 @@ int w4a16_run(const void *A, const void *Wq, const void *scale, const void *bias
         const bool vec_red = (N % 8 == 0) && aligned(C, 16);
         return hip_status(qmm_impl::launch_reduce_cols(workspace, f32_part, s, M, N, n_lo, C, vec_red, st));
     }
-    if (s == 1) return hip_status(dispatch_skinny(tile, A, Wq, scale, bias, C, false, M, N, K, 1, vec_c, st));
+    if (s == 1) return hip_status(dispatch_skinny(fmt, tile, A, Wq, scale, bias, C, false, M, N, K, 1, vec_c, st));
     const bool vec_ws = (N % 4 == 0);
-    int rc = hip_status(dispatch_skinny(tile, A, Wq, scale, bias, workspace, f32_part, M, N, K, s, vec_ws, st));
+    int rc = hip_status(dispatch_skinny(fmt, tile, A, Wq, scale, bias, workspace, f32_part, M, N, K, s, vec_ws, st));
     if (rc != QMM_OK) return rc;
     const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
     return hip_status(qmm_impl::launch_reduce(workspace, f32_part, s, MN, C, vec_red, st));
@@ -237,14 +259,23 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
                               void *C, int M, int N, int K, int s, void *workspace,
                               size_t workspace_bytes, void *stream)
 {
-    return w4a16_run(A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, false, stream);
+    return wq_run(WFormat{4, kGroup}, A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, false, stream);
 }
 
 extern "C" int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias,
                                    void *C, int M, int N, int K, int s, void *workspace,
                                    size_t workspace_bytes, void *stream)
 {
-    return w4a16_run(A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, true, stream);
+    return wq_run(WFormat{4, kGroup}, A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, true, stream);
+}
+
+extern "C" int qmm_wna16(int bits, int group_size, int partial_dtype, const void *A, const void *Wq,
+                         const void *scale, const void *bias, void *C, int M, int N, int K, int s, void *workspace,
+                         size_t workspace_bytes, void *stream)
+{
+    if (partial_dtype != QMM_PARTIAL_BF16 && partial_dtype != QMM_PARTIAL_F32) return QMM_ERR_ARG;
+    return wq_run(WFormat{bits, group_size}, A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes,
+                  partial_dtype == QMM_PARTIAL_F32, stream);
 }
 
 namespace {

@@ -9,7 +9,7 @@ namespace qmm_impl {
 
 // Which W4A16 kernel runs an M-row problem, and the output tile of one workgroup.
 //   SKINNY (M <= 64): a (16*mt) x (16*ns) tile, ns 2 or 4, up to 16 waves splitting its reduction;
-//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variants 1, 2).
+//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variant 2).
 enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
 
 struct W4A16Tile {
@@ -20,16 +20,32 @@ struct W4A16Tile {
     int block_n() const { return kind == W4A16_WIDE ? 256 : 16 * ns; }
 };
 
-// Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups.
+// Weight format: `bits`-wide unsigned codes (4 or 8) packed 32/bits per 32-bit word along K,
+// lowest field first, and one bf16 scale and bias per `group` consecutive values of a row
+// (32, 64 or 128). The kernels walk K in blocks of 128 values, so 128 % group == 0.
+struct WFormat {
+    int bits;
+    int group;
+    int sub() const { return 128 / group; }  // scale/bias groups per 128-value block
+};
+
+inline bool format_supported(WFormat f)
+{
+    return (f.bits == 4 || f.bits == 8) && (f.group == 32 || f.group == 64 || f.group == 128);
+}
+
+// Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups
+// (128-value blocks).
 struct SkinnyShape {
     int waves;  // waves per workgroup, each taking every waves-th group of the partition
     int gpw;    // groups whose loads one wave issues together
 };
 
-inline SkinnyShape skinny_shape(int mt, int ns, int gpp)
+inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4)
 {
     const int max_waves = (mt == 1 && ns == 2) ? 16 : 8;
-    const int max_gpw = ns == 4 ? (mt == 1 ? 3 : mt == 2 ? 2 : 1) : (mt == 4 ? 2 : 3);
+    int max_gpw = ns == 4 ? (mt == 1 ? 3 : mt == 2 ? 2 : 1) : (mt == 4 ? 2 : 3);
+    if (bits == 8 && max_gpw > 1) max_gpw -= 1;  // twice the weight registers per group
     SkinnyShape sh;
     sh.waves = gpp < max_waves ? gpp : max_waves;
     const int per_wave = (gpp + sh.waves - 1) / sh.waves;
@@ -46,23 +62,32 @@ struct DenseTile {
 };
 
 // out: C (bf16) when s = 1, else the partial planes [s][M][N], bf16 or (f32_part) fp32.
-hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
                                const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
                                int s, bool vec_store, hipStream_t stream);
 
-// Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves (two workgroups per CU);
-// 1, 2 = 256 x 256 tiles (one per CU) of 8 waves of 128 x 64, 8 waves of 256 x 32.
-// Rows per tile, and workgroups one CU holds (LDS: 76 KB for 128 rows, 124 KB for 256).
-inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
-inline int wide_wgs_per_cu(int variant) { return variant == 0 ? 2 : 1; }
+// Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves of 128 x 64; 2 = 256 x 256
+// tiles of 8 waves of 256 x 32. Rows per tile; LDS bytes of one workgroup (three stage
+// slots of A, 64 values per row, and of W, 64 codes per row, and two scale/bias slots of
+// one 128-value block); workgroups one CU holds (160 KB of LDS).
 constexpr int kWideCols = 256;
+constexpr int kLdsPerCU = 160 * 1024;
+inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
+constexpr int wide_lds_bytes(int rows, int bits, int sub)
+{
+    return 3 * rows * 64 * 2 + 3 * kWideCols * 64 * bits / 8 + 2 * 2 * kWideCols * 4 * sub;
+}
+inline int wide_wgs_per_cu(int variant, WFormat f = WFormat{4, 128})
+{
+    return variant == 0 && 2 * wide_lds_bytes(128, f.bits, f.sub()) <= kLdsPerCU ? 2 : 1;
+}
 
 // Large-M kernel: the first full_tiles tiles (M-block fastest) unsplit into C, the
 // remaining ones in `split` near-equal group partitions into the planes of `part`
 // ([split][M][N], bf16 or (f32_part) fp32; unused when split = 1).
-hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
-                             void *C, void *part, bool f32_part, int M, int N, int K, int full_tiles, int split,
-                             bool vec_store, hipStream_t stream);
+hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void *Wq, const void *scale,
+                             const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
+                             int full_tiles, int split, bool vec_store, hipStream_t stream);
 
 // Decode matrix-vector kernel (M <= 8): a partition of kp reduction values fits its A
 // staging when kp <= 10240 (at most 5 chunks of 32 per lane) and m8 * kp <= 30720

@@ -1,4 +1,6 @@
-// qmm_w4a16_skinny.hip -- W4A16 group-128 matmul kernel for few rows (M <= 64) on gfx950.
+// qmm_w4a16_skinny.hip -- weight-only quantized matmul kernel for few rows (M <= 64) on gfx950:
+// W4A16 group 128, and the other formats of the library (4- or 8-bit codes, groups of
+// 32, 64 or 128 values).
 //
 // Same contract as the other W4A16 kernels (tiny-llm "Week 2 Day 7: Split-K
 // Prefill", Task 2): blockIdx.z is the partition p, the workgroup covers groups
@@ -20,6 +22,9 @@
 //     (deterministic), rounded once to bf16 and stored with 8-byte stores.
 // Weights are dequantised in registers: w = scale*q + bias in fp32, rounded to
 // bf16 (each weight is used by all 16*MT rows of the tile from the same registers).
+// A lane's share of a 128-value block is 32 consecutive values of one row: 16 bytes of
+// 4-bit codes or 32 bytes of 8-bit codes, and the scale/bias of the group holding them
+// (block g, lane slot c: group (4g + c) * 32 / group_size).
 // The 16x16x32 MFMA takes the weights as its first operand, so a lane's result is
 // four consecutive output columns of one row.
 #include "qmm_device.h"
@@ -31,12 +36,14 @@ namespace {
 
 constexpr int MAX_WAVES = 16;
 
-template <int MT, int NS, int GPW, int MAXW>
+template <int BITS, int MT, int NS, int GPW, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                    void *__restrict__ out, int M, int N, int K, int gpp, int vec_store, int f32_part)
+                    void *__restrict__ out, int M, int N, int K, int gpp, int sub_shift, int vec_store,
+                    int f32_part)
 {
+    constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
     extern __shared__ __attribute__((aligned(16))) char red[];  // [WAVES][MT][NS][64] float4
     // Fetch every pointer argument up front, in the kernel's first scalar loads: left to
     // itself the compiler loads them after the first branch, one more dependent memory
@@ -49,7 +56,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const int slot = lane >> 4;
     const int n_blk = blockIdx.x * (16 * NS);
     const int m_blk = blockIdx.y * (16 * MT);
-    const int G = K >> 7;
+    const int GG = (K >> 7) << sub_shift;  // scale/bias entries per row (128 / group_size per block)
     const int g0 = blockIdx.z * gpp;
     // this wave's groups: g0 + wave + waves*i, i < n_w
     const int n_w = (gpp - wave + waves - 1) / waves;
@@ -60,9 +67,9 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int n = min(n_blk + 16 * j + r, N - 1);  // rows past N read row N-1, never stored
-        wptr[j] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K >> 3)) + slot;
-        sptr[j] = scale + (size_t)n * G;
-        bptr[j] = bias + (size_t)n * G;
+        wptr[j] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K * BITS / 32)) + WV * slot;
+        sptr[j] = scale + (size_t)n * GG + (slot >> (2 - sub_shift));
+        bptr[j] = bias + (size_t)n * GG + (slot >> (2 - sub_shift));
     }
     const uint4 *aptr[MT];
 #pragma unroll
@@ -78,7 +85,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int base = 0; base < n_w; base += GPW) {
-        uint4 wv[GPW][NS];
+        uint4 wv[GPW][NS][WV];
         uint4 av[GPW][MT][4];
         uint32_t sc[GPW][NS], bi[GPW][NS];
         // issue every load of the round before the first use
@@ -88,9 +95,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             const int g = g0 + wave + waves * (base + q);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                wv[q][j] = wptr[j][4 * g];
-                sc[q][j] = sptr[j][g];
-                bi[q][j] = bptr[j][g];
+#pragma unroll
+                for (int u = 0; u < WV; ++u) wv[q][j][u] = wptr[j][4 * WV * g + u];
+                sc[q][j] = sptr[j][g << sub_shift];
+                bi[q][j] = bptr[j][g << sub_shift];
             }
 #pragma unroll
             for (int i = 0; i < MT; ++i)
@@ -110,7 +118,12 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                 const float s16 = s_ * 0.0625f;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const bf16x8 b = as_bf16x8(dequant8(word_of(wv[q][j], t), s_, s16, b_));
+                    // step t: values 8t .. 8t+7 of the lane's 32 (one word of 4-bit codes,
+                    // two words of 8-bit codes)
+                    const bf16x8 b = as_bf16x8(
+                        BITS == 4 ? dequant8(word_of(wv[q][j][0], t), s_, s16, b_)
+                                  : dequant8_u8(word_of(wv[q][j][(t >> 1) % WV], 2 * (t & 1)),
+                                                word_of(wv[q][j][(t >> 1) % WV], 2 * (t & 1) + 1), s_, b_));
 #pragma unroll
                     for (int i = 0; i < MT; ++i) acc[i][j] = mfma16x16x32(b, as_bf16x8(av[q][i][t]), acc[i][j]);
                 }
@@ -164,19 +177,19 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     }
 }
 
-template <int MT, int NS, int GPW, int MAXW>
+template <int BITS, int MT, int NS, int GPW, int MAXW>
 hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, bool f32_part,
-                      int M, int N, int K, int s, int waves, bool vec_store, hipStream_t stream)
+                      int M, int N, int K, int s, int sub_shift, int waves, bool vec_store, hipStream_t stream)
 {
     const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
     const int gpp = (K / 128) / s;
     const size_t lds = (size_t)waves * MT * NS * 64 * 16;
     if (waves > MAXW) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((w4a16_skinny_kernel<MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
+    hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       out, M, N, K, gpp, vec_store ? 1 : 0, f32_part ? 1 : 0);
+                       out, M, N, K, gpp, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -188,22 +201,30 @@ namespace qmm_impl {
 // (ns 2): mt 1 with up to 16 waves and gpw <= 3; mt 2 with up to 8 waves and gpw <= 3;
 // mt 4 with up to 8 waves and gpw <= 2. 64-column tiles (ns 4), used when the 32-column
 // grid would not fit on the GPU in one round: up to 8 waves, gpw <= 3, 2, 1 for mt 1, 2,
-// 4 (register budgets of 128 VGPRs per lane at 16 waves, 256 at 8).
-hipError_t launch_w4a16_skinny(int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
+// 4 (register budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one
+// group less per round where the 4-bit limit is above one.
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
                                const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
                                int s, bool vec_store, hipStream_t stream)
 {
-    if (waves < 1 || waves > MAX_WAVES) return hipErrorInvalidValue;
-#define QMM_CFG(MT_, NS_, GPW_, MAXW_)                                                                         \
-    if (mt == MT_ && ns == NS_ && gpw == GPW_)                                                                 \
-        return launch_cfg<MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, s, waves, vec_store,   \
-                                                 stream);
-    QMM_CFG(1, 2, 1, 16) QMM_CFG(1, 2, 2, 16) QMM_CFG(1, 2, 3, 16)
-    QMM_CFG(2, 2, 1, 8) QMM_CFG(2, 2, 2, 8) QMM_CFG(2, 2, 3, 8)
-    QMM_CFG(4, 2, 1, 8) QMM_CFG(4, 2, 2, 8)
-    QMM_CFG(1, 4, 1, 8) QMM_CFG(1, 4, 2, 8) QMM_CFG(1, 4, 3, 8)
-    QMM_CFG(2, 4, 1, 8) QMM_CFG(2, 4, 2, 8)
-    QMM_CFG(4, 4, 1, 8)
+    if (waves < 1 || waves > MAX_WAVES || !format_supported(fmt)) return hipErrorInvalidValue;
+    const int sub_shift = fmt.group == 128 ? 0 : fmt.group == 64 ? 1 : 2;
+#define QMM_CFG(B_, MT_, NS_, GPW_, MAXW_)                                                                     \
+    if (fmt.bits == B_ && mt == MT_ && ns == NS_ && gpw == GPW_)                                               \
+        return launch_cfg<B_, MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, s, sub_shift,  \
+                                                     waves, vec_store, stream);
+    QMM_CFG(4, 1, 2, 1, 16) QMM_CFG(4, 1, 2, 2, 16) QMM_CFG(4, 1, 2, 3, 16)
+    QMM_CFG(4, 2, 2, 1, 8) QMM_CFG(4, 2, 2, 2, 8) QMM_CFG(4, 2, 2, 3, 8)
+    QMM_CFG(4, 4, 2, 1, 8) QMM_CFG(4, 4, 2, 2, 8)
+    QMM_CFG(4, 1, 4, 1, 8) QMM_CFG(4, 1, 4, 2, 8) QMM_CFG(4, 1, 4, 3, 8)
+    QMM_CFG(4, 2, 4, 1, 8) QMM_CFG(4, 2, 4, 2, 8)
+    QMM_CFG(4, 4, 4, 1, 8)
+    QMM_CFG(8, 1, 2, 1, 16) QMM_CFG(8, 1, 2, 2, 16)
+    QMM_CFG(8, 2, 2, 1, 8) QMM_CFG(8, 2, 2, 2, 8)
+    QMM_CFG(8, 4, 2, 1, 8)
+    QMM_CFG(8, 1, 4, 1, 8) QMM_CFG(8, 1, 4, 2, 8)
+    QMM_CFG(8, 2, 4, 1, 8)
+    QMM_CFG(8, 4, 4, 1, 8)
 #undef QMM_CFG
     return hipErrorInvalidValue;
 }

@@ -1,4 +1,7 @@
-// qmm_w4a16_wide.hip -- W4A16 group-128 matmul kernel for many rows (M > 128) on gfx950.
+// qmm_w4a16_wide.hip -- weight-only quantized matmul kernel for many rows (M > 64) on gfx950:
+// W4A16 group 128, and the library's other formats (4- or 8-bit codes, groups of 32, 64
+// or 128 values; skillsdirectory "Optimize Prefill vs Decode Kernels", step 6, names
+// W4A16 and W8A16 with the dequantisation fused into the main loop).
 //
 // Split contract of tiny-llm "Week 2 Day 7: Split-K Prefill", Task 2: a workgroup
 // computes one output tile over one group-aligned partition of the reduction and
@@ -17,9 +20,11 @@
 // Data movement: every global read of the kernel is a direct global -> LDS copy
 // (global_load_lds_*), two stages ahead of its use, into rings of three slots:
 //   A:  256 rows x 64 bf16 (32 KB per stage), four 1 KB copies per wave;
-//   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage), one copy per wave;
-//   scale/bias: the group's 256 + 256 bf16 values, one 2-byte copy per lane
-//       (zero-extended into a dword), once per group, in a ring of two.
+//   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage; 64 bytes and 16 KB for
+//       8-bit codes), 1 KB per copy;
+//   scale/bias: the 128-value block's 256 + 256 bf16 values per group it holds (one, two
+//       or four), one 2-byte copy per lane (zero-extended into a dword), once per block,
+//       in a ring of two.
 // The compiler neither sees nor waits for these copies; the kernel retires them
 // itself: at the end of stage i each wave waits (s_waitcnt vmcnt) until the copies
 // it issued for stage i+1 have landed, and the barrier that follows publishes them
@@ -32,13 +37,15 @@
 // 32x32x16 MFMA. For reduction step t of a stage, lane l (half h = l / 32) takes word
 // 4h + t of its row, so one 16-byte LDS read gives a lane its words for all four
 // steps; its A operand is the matching 8 values (16-byte chunk 4h + t of the row).
+// With 8-bit codes the same eight values are two words and a lane reads 32 bytes. A
+// lane's 32 values of a stage lie in one scale/bias group for every group size.
 // The MFMA takes the weights as its first operand, so a lane's results are four
 // consecutive output columns of one row (8-byte stores).
 //
 // LDS layouts: A rows are 128 bytes (eight 16-byte chunks), chunk c of row r stored
-// at chunk c ^ ((r >> 1) & 7); W rows are 32 bytes, chunk h of row r at
-// h ^ ((r >> 3) & 1). Both keep the 16-lane phases of the 16-byte reads on distinct
-// banks.
+// at chunk c ^ ((r >> 1) & 7); W rows of 32 bytes store chunk h of row r at
+// h ^ ((r >> 3) & 1), rows of 64 bytes chunk h at h ^ ((r >> 2) & 3). Each keeps the
+// 16-lane phases of the 16-byte reads on distinct banks.
 //
 // Block order: tiles are numbered with the M-block fastest, so with 8 M-blocks the
 // workgroups that the round-robin dispatch sends to one XCD share the same 256 rows
@@ -52,35 +59,44 @@ namespace {
 
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int W_SLOT = BN * BK / 2;  // 8 KB
-constexpr int SB_SLOT = BN * 4 * 2;  // 2 KB: 256 scale dwords, then 256 bias dwords
 constexpr int ROT_GROUPS = 8;        // k-start spread of the workgroups sharing A rows
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Tile geometry of a variant: 128*WM rows x 256 columns per workgroup, each wave a
-// (32*MI) x (32*NJ) block of 32x32 MFMA tiles, waves side by side along N first.
-template <int WM_, int MI_, int NJ_>
+// Tile geometry of a variant and weight format: 128*WM rows x 256 columns per workgroup,
+// each wave a (32*MI) x (32*NJ) block of 32x32 MFMA tiles, waves side by side along N
+// first; BITS-wide codes, SUB scale/bias groups per 128-value block.
+template <int WM_, int MI_, int NJ_, int BITS_, int SUB_>
 struct Cfg {
-    static constexpr int WM = WM_, MI = MI_, NJ = NJ_;
+    static constexpr int WM = WM_, MI = MI_, NJ = NJ_, BITS = BITS_, SUB = SUB_;
     static constexpr int BM = 128 * WM;             // rows per tile
     static constexpr int NWN = 8 / NJ;              // waves along N (256 columns)
     static constexpr int NWM = BM / (32 * MI);      // waves along M
     static constexpr int NW = NWM * NWN;            // waves per workgroup
     static constexpr int A_SLOT = BM * BK * 2;      // 16 or 32 KB
+    static constexpr int WROW = BK * BITS / 8;      // bytes of one W row per stage: 32 or 64
+    static constexpr int WCH = WROW / 16;           // 16-byte chunks per W row: 2 or 4
+    static constexpr int WSW = WCH == 2 ? 3 : 2;    // W row swizzle: chunk ^ ((r >> WSW) & (WCH-1))
+    static constexpr int WV = BITS / 4;             // 16-byte W reads per lane per stage
+    static constexpr int W_SLOT = BN * WROW;        // 8 or 16 KB
+    static constexpr int SB_SLOT = 2 * SUB * BN * 4;  // scale then bias dwords of one block
     static constexpr int AC = (BM / 8) / NW;        // A copies (1 KB each) per wave per stage
-    static constexpr int WC = 8 / NW;               // W copies (and scale/bias copies) per wave
-    static constexpr int N_EVEN = AC + 2 * WC;      // copies a wave issues in an even stage
+    static constexpr int WC = W_SLOT / 1024 / NW;   // W copies (1 KB each) per wave per stage
+    static constexpr int SC = SB_SLOT / 256 / NW;   // scale/bias copies (64 values) per wave per block
+    static constexpr int N_EVEN = AC + WC + SC;     // copies a wave issues in an even stage
     static constexpr int N_ODD = AC + WC;           // ... in an odd stage
-    static constexpr int OCC = WM == 1 ? 2 : 1;     // workgroups one CU holds (LDS)
+    static constexpr int LDS = 3 * A_SLOT + 3 * W_SLOT + 2 * SB_SLOT;
+    static constexpr int OCC = 2 * LDS <= qmm_impl::kLdsPerCU ? 2 : 1;  // workgroups one CU holds
+    static_assert(LDS == qmm_impl::wide_lds_bytes(BM, BITS, SUB), "LDS size differs from the host's");
+    static_assert(AC * NW * 8 == BM && WC * NW * 1024 == W_SLOT && SC * NW * 256 == SB_SLOT, "copy split");
 };
 
 // LDS of one workgroup: three A slots, three W slots, two scale/bias slots.
-template <int WM>
+template <class CF>
 struct Lds {
-    char a[3 * 128 * WM * BK * 2];
-    char w[3 * W_SLOT];
-    char sb[2 * SB_SLOT];
+    char a[3 * CF::A_SLOT];
+    char w[3 * CF::W_SLOT];
+    char sb[2 * CF::SB_SLOT];
 };
 
 // s_waitcnt with only the vector-memory counter limited to n (n < 64; the count's
@@ -111,14 +127,15 @@ template <class CF>
 struct Ctx {
     const char *A;      // A + m0*K (bytes), wave-uniform
     const char *Wq;     // Wq + n0*K/8 words (bytes)
-    const char *sb[CF::WC];  // scale/bias source of this wave's copies (scale or bias, + n0*G)
+    const char *sb[CF::SC];  // scale/bias source of this wave's copies (scale or bias, + n0*GG + sub)
     int gpp, rot, g_begin;
     uint32_t a_off[CF::AC];    // per-lane byte offsets of the A copies (stage k excluded)
     uint32_t w_off[CF::WC];    // per-lane byte offsets of the W copies
-    uint32_t sb_off[CF::WC];   // per-lane byte offsets of the scale/bias copies
+    uint32_t sb_off[CF::SC];   // per-lane byte offsets of the scale/bias copies
     uint32_t a_lds, w_lds, sb_lds;  // this wave's destinations inside slot 0
     uint32_t a_rd[4];   // per-lane LDS byte offsets of the A operand reads, step t
-    uint32_t w_rd, sb_rd;
+    uint32_t w_rd[CF::WV];
+    uint32_t sb_rd[2];  // scale read offset for an even / odd stage (its group in the block)
 };
 
 // Group of stage x (two stages per group), rotated per workgroup.
@@ -142,33 +159,47 @@ __device__ __forceinline__ void issue(const Ctx<CF> &c, int x, int slot3, int sb
     const uint32_t a_dst = c.a_lds + (uint32_t)slot3 * GE::A_SLOT;
 #pragma unroll
     for (int j = 0; j < GE::AC; ++j) copy16(a_dst + 1024u * j, c.a_off[j], Ab);
-    const uint32_t w_dst = c.w_lds + (uint32_t)slot3 * W_SLOT;
+    const uint32_t w_dst = c.w_lds + (uint32_t)slot3 * GE::W_SLOT;
 #pragma unroll
-    for (int j = 0; j < GE::WC; ++j) copy16(w_dst + 1024u * j, c.w_off[j], c.Wq + (size_t)(k0 >> 1));
+    for (int j = 0; j < GE::WC; ++j)
+        copy16(w_dst + 1024u * j, c.w_off[j], c.Wq + (size_t)k0 * GE::BITS / 8);
     if (WITH_SB) {
-        const uint32_t sb_dst = c.sb_lds + (uint32_t)sbslot * SB_SLOT;
+        const uint32_t sb_dst = c.sb_lds + (uint32_t)sbslot * GE::SB_SLOT;
 #pragma unroll
-        for (int j = 0; j < GE::WC; ++j) copy2(sb_dst + 256u * j, c.sb_off[j], c.sb[j] + 2 * (size_t)g);
+        for (int j = 0; j < GE::SC; ++j)
+            copy2(sb_dst + 256u * j, c.sb_off[j], c.sb[j] + 2 * (size_t)g * GE::SUB);
     }
 }
 
-// The 32 MFMAs of one stage for this wave, operands from A/W slot `slot3` and
-// scale/bias slot `sbslot`.
+// Eight dequantised weights of reduction step t (0..3) from a lane's W words of a stage.
 template <class CF>
-__device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF::WM> &L, int slot3, int sbslot,
+__device__ __forceinline__ bf16x8 weights_of_step(const uint4 (&wpk)[CF::WV], int t, float sc, float sc16,
+                                                  float bi)
+{
+    if (CF::BITS == 4) return as_bf16x8(dequant8(word_of(wpk[0], t), sc, sc16, bi));
+    const uint4 &v = wpk[(t >> 1) % CF::WV];
+    return as_bf16x8(dequant8_u8(word_of(v, 2 * (t & 1)), word_of(v, 2 * (t & 1) + 1), sc, bi));
+}
+
+// The 32 MFMAs of one stage for this wave, operands from A/W slot `slot3` and
+// scale/bias slot `sbslot`; ODD: the stage is the second half of its 128-value block.
+template <class CF, int ODD>
+__device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF> &L, int slot3, int sbslot,
                                         f32x16 (&acc)[CF::MI][CF::NJ])
 {
-    constexpr int MI = CF::MI, NJ = CF::NJ;
+    constexpr int MI = CF::MI, NJ = CF::NJ, WV = CF::WV;
     const char *As = L.a + slot3 * CF::A_SLOT;
-    const char *Ws = L.w + slot3 * W_SLOT;
-    const char *Ss = L.sb + sbslot * SB_SLOT;
-    uint4 wpk[NJ];
+    const char *Ws = L.w + slot3 * CF::W_SLOT;
+    const char *Ss = L.sb + sbslot * CF::SB_SLOT;
+    uint4 wpk[NJ][WV];
     float sc[NJ], sc16[NJ], bi[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        wpk[j] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd + 1024 * j);
-        sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd + 128 * j));
-        bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 + c.sb_rd + 128 * j));
+#pragma unroll
+        for (int u = 0; u < WV; ++u)
+            wpk[j][u] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd[u] + 32 * CF::WROW * j);
+        sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd[ODD] + 128 * j));
+        bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 * CF::SUB + c.sb_rd[ODD] + 128 * j));
         sc16[j] = sc[j] * 0.0625f;
     }
     // Software pipeline over the four reduction steps: the A operands and dequantised
@@ -179,7 +210,7 @@ __device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF::WM> &L, 
 #pragma unroll
     for (int i = 0; i < MI; ++i) af[0][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[0] + 4096 * i));
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[0][j] = as_bf16x8(dequant8(wpk[j].x, sc[j], sc16[j], bi[j]));
+    for (int j = 0; j < NJ; ++j) bfr[0][j] = weights_of_step<CF>(wpk[j], 0, sc[j], sc16[j], bi[j]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int cur = t & 1, nxt = cur ^ 1;
@@ -189,8 +220,7 @@ __device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF::WM> &L, 
             for (int i = 0; i < MI; ++i)
                 af[nxt][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t + 1] + 4096 * i));
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-                bfr[nxt][j] = as_bf16x8(dequant8(word_of(wpk[j], t + 1), sc[j], sc16[j], bi[j]));
+            for (int j = 0; j < NJ; ++j) bfr[nxt][j] = weights_of_step<CF>(wpk[j], t + 1, sc[j], sc16[j], bi[j]);
         }
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -246,13 +276,14 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 {
     typedef CF GE;
     constexpr int MI = CF::MI, NJ = CF::NJ;
-    __shared__ __attribute__((aligned(1024))) Lds<CF::WM> L;
+    __shared__ __attribute__((aligned(1024))) Lds<CF> L;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave / CF::NWN;  // row block of the wave (32*MI rows)
     const int wn = wave % CF::NWN;  // column block of the wave (32*NJ columns)
-    const int G = K >> 7;
+    const int G = K >> 7;                  // 128-value blocks
+    const int GG = G * CF::SUB;            // scale/bias entries per row
     const int b = blockIdx.x;
     int tile, p, nparts;
     if (b < full_tiles) {
@@ -287,7 +318,7 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
     // and the partition.
     c.rot = (n_idx % ROT_GROUPS) % gpp;
     c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
-    c.Wq = reinterpret_cast<const char *>(Wq) + (size_t)n0 * (size_t)(K >> 1);
+    c.Wq = reinterpret_cast<const char *>(Wq) + (size_t)n0 * (size_t)K * CF::BITS / 8;
 
     // Copy lanes. A: copy j of wave w fills LDS rows 8q .. 8q+7, q = AC*w + j; lane i
     // lands at row r = 8q + i/8, stored chunk i%8, so it fetches logical chunk
@@ -301,22 +332,29 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
     }
 #pragma unroll
     for (int j = 0; j < GE::WC; ++j) {
-        // W: copy q = w*WC + j fills rows 32q .. 32q+31 (32 bytes each); lane i -> row
-        // 32q + i/2, stored chunk i%2, logical chunk (i%2) ^ ((r>>3)&1). Rows past N
-        // re-read N-1.
+        // W: copy q = w*WC + j fills 1 KB of rows (32 rows of 32 bytes, or 16 of 64); lane
+        // i -> row (1024/WROW)*q + i/WCH, stored chunk i%WCH, logical chunk
+        // (i%WCH) ^ ((r>>WSW)&(WCH-1)). Rows past N re-read N-1.
         const int q = wave * GE::WC + j;
-        const int r = 32 * q + (lane >> 1);
-        const int h = (lane & 1) ^ ((r >> 3) & 1);
+        const int r = (1024 / GE::WROW) * q + lane / GE::WCH;
+        const int h = (lane % GE::WCH) ^ ((r >> GE::WSW) & (GE::WCH - 1));
         const int rr = min(n0 + r, N - 1) - n0;
-        c.w_off[j] = (uint32_t)(rr * (K >> 1) + 16 * h);
-        // scale (copies 0..3) / bias (copies 4..7): lane i -> row 64*(q%4) + i.
+        c.w_off[j] = (uint32_t)(rr * (K * GE::BITS / 8) + 16 * h);
+    }
+#pragma unroll
+    for (int j = 0; j < GE::SC; ++j) {
+        // scale/bias: copy q = w*SC + j carries 64 rows (lane i -> row 64*(q%4) + i) of
+        // group (q/4) % SUB of the block, from scale (q < 4*SUB) or bias.
+        const int q = wave * GE::SC + j;
         const int rs = min(n0 + 64 * (q & 3) + lane, N - 1) - n0;
-        c.sb_off[j] = (uint32_t)(2 * rs * G);
-        c.sb[j] = reinterpret_cast<const char *>(q < 4 ? scale : bias) + 2 * (size_t)n0 * (size_t)G;
+        const int sub = (q >> 2) % GE::SUB;
+        c.sb_off[j] = (uint32_t)(2 * rs * GG);
+        c.sb[j] = reinterpret_cast<const char *>(q < 4 * GE::SUB ? scale : bias) + 2 * (size_t)n0 * (size_t)GG +
+                  2 * sub;
     }
     c.a_lds = lds_addr(L.a) + 1024u * (uint32_t)(GE::AC * wave);
     c.w_lds = lds_addr(L.w) + 1024u * (uint32_t)(wave * GE::WC);
-    c.sb_lds = lds_addr(L.sb) + 256u * (uint32_t)(wave * GE::WC);
+    c.sb_lds = lds_addr(L.sb) + 256u * (uint32_t)(wave * GE::SC);
     // Operand reads: lane (r32 = lane % 32, half h = lane / 32).
     {
         const int r32 = lane & 31;
@@ -325,8 +363,15 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 #pragma unroll
         for (int t = 0; t < 4; ++t) c.a_rd[t] = (uint32_t)(arow * 128 + 16 * ((4 * h + t) ^ ((arow >> 1) & 7)));
         const int nrow = wn * 32 * NJ + r32;  // + 32 j (likewise)
-        c.w_rd = (uint32_t)(nrow * 32 + 16 * (h ^ ((nrow >> 3) & 1)));
-        c.sb_rd = (uint32_t)(4 * nrow);
+#pragma unroll
+        for (int u = 0; u < GE::WV; ++u)
+            c.w_rd[u] = (uint32_t)(nrow * GE::WROW +
+                                   16 * ((GE::WV * h + u) ^ ((nrow >> GE::WSW) & (GE::WCH - 1))));
+        // the lane's 32 values of an even (odd) stage are values 32h (64 + 32h) of the
+        // block: group (32h) * SUB / 128 (and (64 + 32h) * SUB / 128) of the block
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd)
+            c.sb_rd[odd] = (uint32_t)(4 * nrow + 1024 * (((2 * odd + h) * GE::SUB) >> 2));
     }
 
     f32x16 acc[MI][NJ];
@@ -355,13 +400,13 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
         const int s3p = s3 == 0 ? 2 : s3 - 1;    // (st+2) % 3
         const int sbs = (st >> 1) & 1;
         issue<CF, true>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
-        compute<CF>(c, L, s3, sbs, acc);
+        compute<CF, 0>(c, L, s3, sbs, acc);
         // stage st+1's copies (issued one stage earlier) are followed by this stage's
         QMM_WAIT_VMCNT(GE::N_EVEN);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         issue<CF, false>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
-        compute<CF>(c, L, s3n, sbs, acc);
+        compute<CF, 1>(c, L, s3n, sbs, acc);
         // stage st+2's copies (issued above) are followed by this stage's
         QMM_WAIT_VMCNT(GE::N_ODD);
         __syncthreads();
@@ -393,9 +438,10 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 }
 
 
-typedef Cfg<1, 4, 2> CfgV0;  // 128 x 256 tile, 4 waves of 128 x 64, two workgroups per CU
-typedef Cfg<2, 4, 2> CfgV1;  // 256 x 256 tile, 8 waves of 128 x 64
-typedef Cfg<2, 8, 1> CfgV2;  // 256 x 256 tile, 8 waves of 256 x 32
+template <int BITS, int SUB>
+using CfgV0 = Cfg<1, 4, 2, BITS, SUB>;  // 128 x 256 tile, 4 waves of 128 x 64
+template <int BITS, int SUB>
+using CfgV2 = Cfg<2, 8, 1, BITS, SUB>;  // 256 x 256 tile, 8 waves of 256 x 32
 
 template <class CF>
 void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
@@ -406,16 +452,29 @@ void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t
                        full_tiles, tail_tiles, split, vec, f32p);
 }
 
+template <int BITS, int SUB>
+void launch_variant(int variant, dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w,
+                    const uint16_t *sc, const uint16_t *bi, uint16_t *c, void *pt, int M, int N, int K,
+                    int full_tiles, int tail_tiles, int split, int vec, int f32p)
+{
+    if (variant == 0)
+        launch_cfg<CfgV0<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
+                                     f32p);
+    else
+        launch_cfg<CfgV2<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
+                                     f32p);
+}
+
 }  // namespace
 
 namespace qmm_impl {
 
 // The per-lane copy offsets are 32-bit byte offsets within 256 rows of A: K < 2^22.
-hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const void *scale, const void *bias,
-                             void *C, void *part, bool f32_part, int M, int N, int K, int full_tiles, int split,
-                             bool vec_store, hipStream_t stream)
+hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void *Wq, const void *scale,
+                             const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
+                             int full_tiles, int split, bool vec_store, hipStream_t stream)
 {
-    if (K >= (1 << 22) || variant < 0 || variant > 2) return hipErrorInvalidValue;
+    if (K >= (1 << 22) || (variant != 0 && variant != 2) || !format_supported(fmt)) return hipErrorInvalidValue;
     const int rows = wide_rows(variant);
     const int tiles = ((M + rows - 1) / rows) * ((N + BN - 1) / BN);
     if (full_tiles < 0 || full_tiles > tiles || split < 1 || split > K / 128) return hipErrorInvalidValue;
@@ -427,15 +486,15 @@ hipError_t launch_w4a16_wide(int variant, const void *A, const void *Wq, const v
     const uint16_t *sc = static_cast<const uint16_t *>(scale);
     const uint16_t *bi = static_cast<const uint16_t *>(bias);
     uint16_t *c = static_cast<uint16_t *>(C);
-    void *pt = part;
     const int vec = vec_store ? 1 : 0;
     const int f32p = f32_part ? 1 : 0;
     (void)hipGetLastError();
-    switch (variant) {
-    case 0: launch_cfg<CfgV0>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
-    case 1: launch_cfg<CfgV1>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
-    default: launch_cfg<CfgV2>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec, f32p); break;
-    }
+#define QMM_FMT(B_, S_)                                                                                          \
+    if (fmt.bits == B_ && fmt.sub() == S_)                                                                       \
+        launch_variant<B_, S_>(variant, grid, stream, a, w, sc, bi, c, part, M, N, K, full_tiles, tail_tiles,    \
+                               split, vec, f32p);
+    QMM_FMT(4, 1) QMM_FMT(4, 2) QMM_FMT(4, 4) QMM_FMT(8, 1) QMM_FMT(8, 2) QMM_FMT(8, 4)
+#undef QMM_FMT
     return hipGetLastError();
 }
 

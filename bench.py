@@ -50,17 +50,18 @@ MFMA_BF16_PEAK = 2.5e15    # flop/s, MI355X published dense bf16
 ROTATE_BYTES = 1 << 30     # distinct bytes per per-shape rotation
 
 
-def algorithmic_bytes(M, N, K):
-    """Bytes any W4A16 g128 implementation must move: packed weights, scale+bias, A, C."""
-    return N * K // 2 + N * (K // 128) * 4 + 2 * M * K + 2 * M * N
+def algorithmic_bytes(M, N, K, bits=4, group=128):
+    """Bytes any implementation of the weight-only format must move: packed codes,
+    scale+bias, A, C (W4A16 g128 by default)."""
+    return N * K * bits // 8 + N * (K // group) * 4 + 2 * M * K + 2 * M * N
 
 
 def algorithmic_flops(M, N, K):
     return 2 * M * N * K
 
 
-def roofline(M, N, K, seconds):
-    b, f = algorithmic_bytes(M, N, K), algorithmic_flops(M, N, K)
+def roofline(M, N, K, seconds, bits=4, group=128):
+    b, f = algorithmic_bytes(M, N, K, bits, group), algorithmic_flops(M, N, K)
     t_hbm, t_mfma = b / HBM_PEAK, f / MFMA_BF16_PEAK
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
     return dict(bytes=b, flops=f, bound=bound, t_roof_us=max(t_hbm, t_mfma) * 1e6,
@@ -238,6 +239,29 @@ def decode_table(torch, syn, q):
     return rows
 
 
+FORMAT_VARIANTS = [((4, 128), True), ((4, 64), False), ((4, 32), False), ((8, 128), False), ((8, 64), False),
+                   ((8, 32), False)]
+
+
+def formats_table(torch, syn, q):
+    """The other weight formats (qmm_wna16) and the fp32-partial option on the gate and
+    down projections at M = 16, 128, 2048: µs per call under the library plan over >= 1 GiB
+    of rotation, with the roofline fraction of the format's own algorithmic bytes."""
+    rows = []
+    for (bits, group), f32p in FORMAT_VARIANTS:
+        for name, M, N, K, idx in syn.projection_sweep():
+            if name not in ("gate", "down") or M not in (16, 128, 2048):
+                continue
+            sh, R, t = per_shape(torch, syn, q, name, M, N, K, idx + 500, fmt=(bits, group), f32p=f32p,
+                                 unsplit=False)
+            r = roofline(M, N, K, t[0], bits, group)
+            rows.append(dict(bits=bits, group=group, partials="fp32" if f32p else "bf16", name=name, M=M, N=N, K=K,
+                             s=sh.s, full_tiles=sh.plan.full_tiles, us=round(t[0] * 1e6, 3), bound=r["bound"],
+                             gbs=round(r["gbs"], 1), tflops=round(r["tflops"], 2), frac=round(r["frac"], 4)))
+            print("# %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    return rows
+
+
 def pmc_run():
     """Workload of the counter passes: each M = 2048 shape once unsplit, then one plain copy."""
     import torch
@@ -320,12 +344,15 @@ def parse():
 class Shape:
     """Device buffers of one projection shape: R input sets, one output, one workspace."""
 
-    def __init__(self, name, M, N, K, idx, sets, torch, syn, q):
+    def __init__(self, name, M, N, K, idx, sets, torch, syn, q, fmt=None, f32p=False):
+        """fmt = (bits, group) runs qmm_wna16 (f32p: with fp32 partials); None runs qmm_w4a16_g128."""
         self.name, self.M, self.N, self.K, self.idx = name, M, N, K, idx
         self.q = q
-        self.plan = q.qmm_splitk_plan(M, N, K)
+        self.fmt, self.f32p = fmt, f32p
+        self.plan = q.qmm_splitk_plan(M, N, K) if fmt is None else q.qmm_wna16_plan(fmt[0], fmt[1], M, N, K)
         self.s = self.plan.s
-        d = syn.w4a16_weights(N, K, seed=2000 + idx)
+        d = syn.w4a16_weights(N, K, seed=2000 + idx) if fmt is None else syn.wq_inputs(fmt[0], fmt[1], 1, N, K,
+                                                                                       seed=2000 + idx)
         A = syn.normal_bf16((M, K), seed=2500 + idx)
 
         def dev16(x):
@@ -334,17 +361,22 @@ class Shape:
         base = (dev16(A), torch.from_numpy(d["Wq"].view("int32")).cuda(), dev16(d["scale"]), dev16(d["bias"]))
         self.sets = [base] + [tuple(t.clone() for t in base) for _ in range(sets - 1)]
         self.C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        self.ws = torch.empty(max(q.w4a16_workspace_bytes(M, N, self.s), 256), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(max(q.w4a16_workspace_bytes(M, N, self.s, f32p), 256), dtype=torch.uint8,
+                              device="cuda")
 
     def call(self, r, s):
         """s = 0: the library's own plan (what a user gets); s >= 1: that explicit split."""
         A, W, S, B = self.sets[r % len(self.sets)]
         split = self.s if s == 0 else s
-        self.q.qmm_w4a16_g128(A, W, S, B, self.C, self.M, self.N, self.K, s,
-                              self.ws if split > 1 else None, self.ws.numel() if split > 1 else 0)
+        ws, wsb = (self.ws, self.ws.numel()) if split > 1 else (None, 0)
+        if self.fmt is None:
+            self.q.qmm_w4a16_g128(A, W, S, B, self.C, self.M, self.N, self.K, s, ws, wsb)
+        else:
+            self.q.qmm_wna16(self.fmt[0], self.fmt[1], 1 if self.f32p else 0, A, W, S, B, self.C, self.M, self.N,
+                             self.K, s, ws, wsb)
 
     def set_bytes(self):
-        return algorithmic_bytes(self.M, self.N, self.K)
+        return algorithmic_bytes(self.M, self.N, self.K, *(self.fmt or (4, 128)))
 
     def free(self):
         self.sets = []
@@ -380,19 +412,20 @@ def time_graph(torch, g, reps=5):
     return ts[len(ts) // 2]
 
 
-def per_shape(torch, syn, q, name, M, N, K, idx):
+def per_shape(torch, syn, q, name, M, N, K, idx, fmt=None, f32p=False, unsplit=True):
     """Per-call seconds of the policy split and of the unsplit control over >= 1 GiB of rotation."""
-    probe = Shape(name, M, N, K, idx, 1, torch, syn, q)
+    probe = Shape(name, M, N, K, idx, 1, torch, syn, q, fmt, f32p)
     R = max(8, min(1024, math.ceil(ROTATE_BYTES / probe.set_bytes())))
     probe.free()
-    sh = Shape(name, M, N, K, idx, R, torch, syn, q)
+    sh = Shape(name, M, N, K, idx, R, torch, syn, q, fmt, f32p)
     out = {}
-    for s in ([0, 1] if sh.s > 1 else [1]):
+    for s in ([0, 1] if sh.s > 1 and unsplit else [0] if sh.s > 1 else [1]):
         g = graph_of(torch, lambda: [sh.call(r, s) for r in range(R)])
         out[s] = time_graph(torch, g) / R
         del g
     if sh.s == 1:
         out[0] = out[1]
+    out.setdefault(1, None)
     sh.free()
     torch.cuda.empty_cache()
     return sh, R, out
@@ -511,10 +544,11 @@ def main():
                               roof_us=round(r["t_roof_us"], 3), frac=round(r["frac"], 4), rotation_sets=R))
             print("# %s" % json.dumps(table[-1]), file=sys.stderr, flush=True)
 
-    dense = decode = None
+    dense = decode = formats = None
     if not args.no_per_shape:
         dense = dense_sweep(torch, syn, q)
         decode = decode_table(torch, syn, q)
+        formats = formats_table(torch, syn, q)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -545,6 +579,7 @@ def main():
         "shapes": table,
         "dense_bf16_splitk": dense,
         "decode": decode,
+        "formats": formats,
     }
     if table:
         small = [t for t in table if t["M"] <= 128]

@@ -9,7 +9,8 @@ Contents
   * ``qmm_w4a16``, ``qmm_w4a16_points``, ``qmm_dense``, ``reduce_bf16``,
     ``reduce_f32``, ``dequant_w4a16``, ``bf16_round``, ``bf16_value``,
     ``nibble``, and for the other weight formats (4- or 8-bit codes, groups of
-    32, 64 or 128) ``qmm_wq``, ``qmm_wq_points``, ``dequant_wq``, ``code``: ctypes wrappers over the plain C definitions in qmm_oracle.c
+    32, 64 or 128) ``qmm_wq``, ``qmm_wq_points``, ``dequant_wq``, ``code``, and the
+    decode attention ``attn_decode``: ctypes wrappers over the plain C definitions in qmm_oracle.c
     (fp64 products in ascending k, fp32 reduce, bf16 round-to-nearest-even).
   * ``policy``: the occupancy split rule of tiny-llm "Week 2 Day 7: Split-K
     Prefill", Task 3, in its plain form.
@@ -64,6 +65,8 @@ def _lib():
         lib.oracle_qmm_wq.restype = I
         lib.oracle_qmm_wq_points.argtypes = [I, I, P, P, P, P, I, I, I, I, P, P, P]
         lib.oracle_qmm_wq_points.restype = I
+        lib.oracle_attn_decode.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_double, P]
+        lib.oracle_attn_decode.restype = I
         lib.oracle_reduce_bf16.argtypes = [P, I, ctypes.c_size_t, P]
         lib.oracle_reduce_bf16.restype = None
         lib.oracle_reduce_f32.argtypes = [P, I, ctypes.c_size_t, P]
@@ -208,6 +211,23 @@ def qmm_wq_points(bits, group, A, Wq, scale, bias, M, N, K, ms, ns):
     if rc != 0:
         raise ValueError("oracle_qmm_wq_points failed (%d)" % rc)
     return out
+
+
+def attn_decode(Q, K, V, lengths, scale):
+    """fp64 O[B, Mq, Hq, D] of decode attention: Q bf16 bits [B, Mq, Hq, D], K and V bf16
+    bits [B, Hkv, Lmax, D], lengths int [B] (keys of each request, the Mq queries last)."""
+    Q, pq = _c(Q, np.uint16)
+    K, pk = _c(K, np.uint16)
+    V, pv = _c(V, np.uint16)
+    lengths, pl = _c(lengths, np.int32)
+    B, Mq, Hq, D = Q.shape
+    _, Hkv, Lmax, _ = K.shape
+    O = np.empty((B, Mq, Hq, D), dtype=np.float64)
+    rc = _lib().oracle_attn_decode(pq, pk, pv, pl, B, Mq, Hq, Hkv, Lmax, D, float(scale),
+                                   O.ctypes.data_as(ctypes.c_void_p))
+    if rc != 0:
+        raise ValueError("oracle_attn_decode failed (%d)" % rc)
+    return O
 
 
 def qmm_dense(A, B, M, N, K, s=1, nthreads=None):

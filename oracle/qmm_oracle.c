@@ -29,6 +29,14 @@
  *            lowest bits first; w[n,k] = scale[n, k/gs] * q[n,k] + bias[n, k/gs]
  *            for a group size gs of 32, 64 or 128; the split partitions stay on
  *            128-value boundaries (which are group boundaries for every gs).
+ *   decode attention (skillsdirectory "Optimize Prefill vs Decode Kernels", step 4
+ *   and the correctness notes on split-KV with an LSE combine): for request b, query
+ *   token i of Mq and query head h,
+ *            allowed keys j < L_b - Mq + 1 + i (the query's own position and before),
+ *            s_j = scale * sum_d Q[b,i,h,d] * K[b,h/G,j,d]   (G = Hq/Hkv query heads per
+ *            key/value head), O[b,i,h,:] = sum_j softmax(s)_j * V[b,h/G,j,:].
+ *            The oracle is this plain definition in fp64; the split into key ranges
+ *            and their merge are the GPU method's business.
  *   dense:  C[m,n] = sum_k A[m,k] * B[n,k], split into s near-equal partitions of
  *            32-value granules (gpu-kernels-explained "Split-K, streams and overlap",
  *            Concept / Maths: k cut into s slices, a second pass adds the partials).
@@ -341,6 +349,52 @@ int oracle_qmm_wq_points(int bits, int group, const uint16_t *A, const uint32_t 
             total += oracle_bf16_value(A[(size_t)m * K + k]) * wq_weight(Wq, bits, group, scale, bias, K, n, k);
         out[i] = total;
     }
+    return 0;
+}
+
+/* ---- decode attention ------------------------------------------------------ */
+
+/* O[b][i][h][:] (fp64) for bf16 Q[B][Mq][Hq][D], K and V [B][Hkv][Lmax][D], key counts
+ * len[b] (Mq <= len[b] <= Lmax): softmax over the allowed keys of the scaled dot
+ * products, then the weighted sum of the value rows, every step in fp64. Returns 0,
+ * or -1 on a bad argument. */
+int oracle_attn_decode(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int *len,
+                       int B, int Mq, int Hq, int Hkv, int Lmax, int D, double scale, double *O)
+{
+    if (B <= 0 || Mq <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || D <= 0 || Hq % Hkv != 0) return -1;
+    int G = Hq / Hkv;
+    double *sc = (double *)malloc((size_t)Lmax * sizeof *sc);
+    if (!sc) return -1;
+    for (int b = 0; b < B; ++b) {
+        if (len[b] < Mq || len[b] > Lmax) { free(sc); return -1; }
+        for (int i = 0; i < Mq; ++i) {
+            int nkeys = len[b] - Mq + 1 + i;
+            for (int h = 0; h < Hq; ++h) {
+                const uint16_t *q = Q + (((size_t)b * Mq + i) * Hq + h) * D;
+                size_t kv = ((size_t)b * Hkv + (size_t)(h / G)) * (size_t)Lmax * (size_t)D;
+                double mx = -INFINITY;
+                for (int j = 0; j < nkeys; ++j) {
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        dot += oracle_bf16_value(q[d]) * oracle_bf16_value(K[kv + (size_t)j * D + d]);
+                    sc[j] = scale * dot;
+                    if (sc[j] > mx) mx = sc[j];
+                }
+                double denom = 0.0;
+                for (int j = 0; j < nkeys; ++j) {
+                    sc[j] = exp(sc[j] - mx);
+                    denom += sc[j];
+                }
+                double *o = O + (((size_t)b * Mq + i) * Hq + h) * D;
+                for (int d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int j = 0; j < nkeys; ++j) acc += sc[j] * oracle_bf16_value(V[kv + (size_t)j * D + d]);
+                    o[d] = acc / denom;
+                }
+            }
+        }
+    }
+    free(sc);
     return 0;
 }
 

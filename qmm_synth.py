@@ -79,6 +79,17 @@ def wq_inputs(bits, group, M, N, K, seed):
     return dict(A=A, Wq=pack_codes(q, bits), scale=scale, bias=bias, q=q)
 
 
+def attn_inputs(B, Mq, Hq, Hkv, Lmax, D, lengths, seed):
+    """Decode attention inputs: Q [B, Mq, Hq, D], K and V caches [B, Hkv, Lmax, D], all
+    N(0, 1) rounded to bf16 (positions past a request's length hold data too, never
+    read); lengths int32 [B]."""
+    rng = rng_for(seed)
+    Q = f32_to_bf16_bits(rng.standard_normal((B, Mq, Hq, D), dtype=np.float32))
+    K = f32_to_bf16_bits(rng.standard_normal((B, Hkv, Lmax, D), dtype=np.float32))
+    V = f32_to_bf16_bits(rng.standard_normal((B, Hkv, Lmax, D), dtype=np.float32))
+    return dict(Q=Q, K=K, V=V, lengths=np.asarray(lengths, dtype=np.int32))
+
+
 def rng_for(seed):
     return np.random.Generator(np.random.PCG64(seed))
 

@@ -40,6 +40,11 @@ MUTANTS = {
     "code_mask_four_bits": ("& ((1u << bits) - 1u));", "& 0xFu);"),
     "format_group_index_128": ("    int g = k / group;\n", "    int g = k / 128;\n"),
     "format_group_count_128": ("    int G = K / group;\n    int g", "    int G = K / 128;\n    int g"),
+    "attn_head_map_modulo": ("(size_t)(h / G)) * (size_t)Lmax", "(size_t)(h % Hkv)) * (size_t)Lmax"),
+    "attn_mask_off_by_one": ("int nkeys = len[b] - Mq + 1 + i;", "int nkeys = len[b] - Mq + i + (i > 0);"),
+    "attn_scale_dropped": ("sc[j] = scale * dot;", "sc[j] = dot;"),
+    "attn_not_normalised": ("o[d] = acc / denom;", "o[d] = acc;"),
+    "attn_values_from_keys": ("acc += sc[j] * oracle_bf16_value(V[kv", "acc += sc[j] * oracle_bf16_value(K[kv"),
     "format_bias_dropped": ("return sc * (double)oracle_code(Wq, bits, K, n, k) + bi;",
                             "return sc * (double)oracle_code(Wq, bits, K, n, k);"),
 }
@@ -67,6 +72,11 @@ CHECKS = [
     (pins.test_format_bruteforce_exact_rationals, dict(bits=8, group=64)),
     (pins.test_format_one_hot_rows, dict(bits=4, group=32)),
     (pins.test_format_integer_weights_equal_numpy_matmul, dict(bits=8)),
+    (pins.test_attn_single_key_returns_its_value_row, {}),
+    (pins.test_attn_zero_query_averages_the_allowed_values, {}),
+    (pins.test_attn_two_keys_closed_form, {}),
+    (pins.test_attn_query_heads_share_their_group_key_value_head, {}),
+    (pins.test_attn_causal_queries_match_shorter_histories, {}),
 ]
 
 
@@ -91,7 +101,7 @@ def test_mutant_is_caught(tmp_path, name):
     for fn in ("oracle_bf16_value", "oracle_bf16_round", "oracle_nibble", "oracle_dequant_w4a16",
                "oracle_partition_groups", "oracle_partition_granules", "oracle_qmm_w4a16",
                "oracle_qmm_w4a16_points", "oracle_qmm_dense", "oracle_reduce_bf16", "oracle_reduce_f32",
-               "oracle_code", "oracle_dequant_wq", "oracle_qmm_wq", "oracle_qmm_wq_points"):
+               "oracle_code", "oracle_dequant_wq", "oracle_qmm_wq", "oracle_qmm_wq_points", "oracle_attn_decode"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     caught = []

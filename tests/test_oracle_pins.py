@@ -357,6 +357,101 @@ def test_format_points_match_full_product_and_rejects():
         oracle.qmm_wq(8, 32, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, s=2)
 
 
+# ------------------------------------------------------- decode attention
+
+def _attn(B=2, Mq=1, Hq=8, Hkv=2, Lmax=40, D=16, lengths=(40, 17), seed=80):
+    return syn.attn_inputs(B, Mq, Hq, Hkv, Lmax, D, list(lengths), seed)
+
+
+def test_attn_single_key_returns_its_value_row():
+    d = _attn(lengths=(1, 1))
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 0.25)
+    V = syn.bf16_bits_to_f32(d["V"]).astype(np.float64)
+    for h in range(8):
+        assert np.array_equal(O[:, 0, h], V[:, h // 4, 0])
+
+
+def test_attn_zero_query_averages_the_allowed_values():
+    d = _attn(lengths=(40, 17))
+    d["Q"][:] = 0
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 0.125)
+    V = syn.bf16_bits_to_f32(d["V"]).astype(np.float64)
+    for b, L in enumerate((40, 17)):
+        for h in range(8):
+            ref = V[b, h // 4, :L].mean(axis=0)
+            assert np.all(np.abs(O[b, 0, h] - ref) <= 64 * U53 * np.abs(V[b, h // 4, :L]).mean(axis=0)), (b, h)
+
+
+def test_attn_two_keys_closed_form():
+    d = _attn(B=1, Hq=2, Hkv=1, Lmax=2, D=16, lengths=(2,), seed=81)
+    scale = 0.3
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], scale)
+    for h in range(2):
+        q = [bf16_fraction(x) for x in d["Q"][0, 0, h]]
+        s = [float(scale * sum(a * bf16_fraction(k) for a, k in zip(q, d["K"][0, 0, j]))) for j in range(2)]
+        w1 = math.exp(s[1] - s[0])
+        v = syn.bf16_bits_to_f32(d["V"][0, 0]).astype(np.float64)
+        ref = (v[0] + w1 * v[1]) / (1.0 + w1)
+        assert np.all(np.abs(O[0, 0, h] - ref) <= 1e-14 * (np.abs(v[0]) + np.abs(v[1]))), h
+
+
+def test_attn_query_heads_share_their_group_key_value_head():
+    # uniform weights (Q = 0) and value rows equal to the index of their key/value head
+    d = _attn(B=1, Hq=12, Hkv=3, lengths=(40,))
+    d["Q"][:] = 0
+    for g in range(3):
+        d["V"][0, g] = syn.f32_to_bf16_bits(np.full((40, 16), float(g), dtype=np.float32))
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 1.0)
+    for h in range(12):
+        assert np.all(O[0, 0, h] == float(h // 4)), h
+
+
+def test_attn_dominant_key_selects_its_value():
+    d = _attn(B=1, Hq=4, Hkv=1, lengths=(40,), seed=82)
+    q = syn.bf16_bits_to_f32(d["Q"][0, 0, 0]).astype(np.float64)
+    d["Q"][0, 0, 1:] = d["Q"][0, 0, 0]
+    # key 23 = 8 * q (bf16-exact): its score exceeds every other by > 30 at scale 1
+    d["K"][0, 0, 23] = syn.f32_to_bf16_bits((8.0 * q).astype(np.float32))
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 1.0)
+    V = syn.bf16_bits_to_f32(d["V"][0, 0]).astype(np.float64)
+    s = syn.bf16_bits_to_f32(d["K"][0, 0]).astype(np.float64) @ q
+    gap = s[23] - np.max(np.delete(s, 23))
+    assert gap > 30
+    assert np.all(np.abs(O[0, 0, 0] - V[23]) <= 40 * math.exp(-gap) * np.abs(V).max())
+
+
+def test_attn_causal_queries_match_shorter_histories():
+    d = _attn(B=2, Mq=3, lengths=(40, 17), seed=83)
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 0.25)
+    for i in range(3):
+        one = dict(d)
+        one["Q"] = np.ascontiguousarray(d["Q"][:, i:i + 1])
+        L = np.array([40 - 2 + i, 17 - 2 + i], dtype=np.int32)
+        Oi = oracle.attn_decode(one["Q"], d["K"], d["V"], L, 0.25)
+        assert np.array_equal(O[:, i], Oi[:, 0]), i
+
+
+def test_attn_permuting_keys_with_values_changes_nothing():
+    d = _attn(B=1, lengths=(40,), seed=84)
+    O = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], 0.25)
+    perm = np.random.default_rng(84).permutation(40)
+    d2 = dict(d)
+    d2["K"] = np.ascontiguousarray(d["K"][:, :, perm])
+    d2["V"] = np.ascontiguousarray(d["V"][:, :, perm])
+    O2 = oracle.attn_decode(d2["Q"], d2["K"], d2["V"], d["lengths"], 0.25)
+    V = syn.bf16_bits_to_f32(d["V"]).astype(np.float64)
+    assert np.all(np.abs(O - O2) <= 1e-13 * np.abs(V).max())
+
+
+def test_attn_rejects_bad_arguments():
+    d = _attn(lengths=(40, 17))
+    with pytest.raises(ValueError):
+        oracle.attn_decode(d["Q"], d["K"], d["V"], np.array([41, 17], dtype=np.int32), 1.0)
+    d3 = _attn(Mq=3, lengths=(40, 2))
+    with pytest.raises(ValueError):  # fewer keys than queries
+        oracle.attn_decode(d3["Q"], d3["K"], d3["V"], d3["lengths"], 1.0)
+
+
 # ---------------------------------------------------------------- reduction
 
 @pytest.mark.parametrize("s,M,N", [(1, 3, 5), (2, 16, 64), (5, 48, 1000), (20, 7, 33), (32, 4, 9)])

@@ -239,6 +239,47 @@ def decode_table(torch, syn, q):
     return rows
 
 
+ATTN_SHAPES = [(1, 4096, 1), (1, 16384, 1), (8, 4096, 1), (32, 4096, 1), (32, 16384, 1), (8, 4096, 4)]
+
+
+def attention_table(torch, q):
+    """Split-KV decode attention on Qwen3-4B's heads (32 query heads, 8 key/value heads,
+    head dimension 128) for (batch, cached keys, queries per request): µs per call under
+    the library's split and unsplit, over >= 1 GiB of rotated caches, with the HBM
+    roofline fraction of the algorithmic bytes (key and value rows read once, Q, O)."""
+    Hq, Hkv, D = 32, 8, 128
+    rows = []
+    for B, L, Mq in ATTN_SHAPES:
+        kv = 2 * B * Hkv * L * D * 2
+        R = max(1, min(256, math.ceil(ROTATE_BYTES / kv)))
+        gen = torch.Generator(device="cuda").manual_seed(4000 + B + L + Mq)
+        sets = [tuple(torch.randn(*shape, device="cuda", generator=gen).to(torch.bfloat16)
+                      for shape in ((B, Mq, Hq, D), (B, Hkv, L, D), (B, Hkv, L, D))) for _ in range(R)]
+        lengths = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        O = torch.empty(B, Mq, Hq, D, dtype=torch.bfloat16, device="cuda")
+        s_plan = q.qmm_attn_decode_split(B, Hkv, L)
+        ws = torch.empty(max(q.qmm_attn_decode_workspace_bytes(B, Mq, Hq, s_plan), 16), dtype=torch.uint8,
+                         device="cuda")
+        t = {}
+        for s in (0, 1):
+            def run(s=s):
+                for r in range(R):
+                    Q, K, V = sets[r]
+                    q.qmm_attn_decode(Q, K, V, lengths, O, B, Mq, Hq, Hkv, L, D, D ** -0.5, s,
+                                      ws if (s or s_plan) > 1 else None)
+            g = graph_of(torch, run)
+            t[s] = time_graph(torch, g) / R
+            del g
+        del sets, ws
+        torch.cuda.empty_cache()
+        byts = kv + 2 * 2 * B * Mq * Hq * D
+        rows.append(dict(B=B, L=L, Mq=Mq, Hq=Hq, Hkv=Hkv, D=D, s=s_plan, us=round(t[0] * 1e6, 3),
+                         us_unsplit=round(t[1] * 1e6, 3), tbs=round(byts / t[0] / 1e12, 3),
+                         frac_hbm=round(byts / HBM_PEAK / t[0], 4)))
+        print("# attn %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    return rows
+
+
 FORMAT_VARIANTS = [((4, 128), True), ((4, 64), False), ((4, 32), False), ((8, 128), False), ((8, 64), False),
                    ((8, 32), False)]
 
@@ -544,11 +585,12 @@ def main():
                               roof_us=round(r["t_roof_us"], 3), frac=round(r["frac"], 4), rotation_sets=R))
             print("# %s" % json.dumps(table[-1]), file=sys.stderr, flush=True)
 
-    dense = decode = formats = None
+    dense = decode = formats = attention = None
     if not args.no_per_shape:
         dense = dense_sweep(torch, syn, q)
         decode = decode_table(torch, syn, q)
         formats = formats_table(torch, syn, q)
+        attention = attention_table(torch, q)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -580,6 +622,7 @@ def main():
         "dense_bf16_splitk": dense,
         "decode": decode,
         "formats": formats,
+        "decode_attention": attention,
     }
     if table:
         small = [t for t in table if t["M"] <= 128]

@@ -228,6 +228,40 @@ int qmm_splitk_reduce(const void *partials, int partial_dtype, int s, int M, int
 int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int N, int K, int s,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * qmm_attn_decode -- split-KV decode attention with a log-sum-exp merge (skillsdirectory
+ * "Optimize Prefill vs Decode Kernels", step 4 and its correctness notes: the key/value
+ * sequence is split across workgroups, each keeps an fp32 running max and sum of
+ * exponentials, and a final pass merges the partial results with the online-softmax rule).
+ *
+ *   For request b (lengths[b] cached keys), query token i < Mq (the last Mq positions of
+ *   the cache) and query head h < Hq, with key/value head h / (Hq/Hkv):
+ *     s_j = scale * Q[b,i,h,:] . K[b,h/G,j,:]   for j < lengths[b] - Mq + 1 + i
+ *     O[b,i,h,:] = sum_j softmax(s)_j * V[b,h/G,j,:]
+ *   Layouts (bf16, row-major, contiguous): Q and O [B][Mq][Hq][head_dim], K and V
+ *   [B][Hkv][Lmax][head_dim]; lengths: device int32 [B], each in [Mq, Lmax] (values
+ *   outside are clamped into that range on the device).
+ *   head_dim must be 128, Hq a multiple of Hkv and (Hq/Hkv)*Mq <= 16 (QMM_ERR_SHAPE).
+ *   s = 0: qmm_attn_decode_split(B, Hkv, Lmax); s >= 1 (at most 64): split p of request b
+ *   covers keys [floor(p*len/s), floor((p+1)*len/s)). s > 1 needs a workspace of
+ *   qmm_attn_decode_workspace_bytes(B, Mq, Hq, s) bytes, 16-byte aligned (fp32 partial
+ *   accumulators, maxima and sums), and launches the merge after the split kernel.
+ *   Q, K, V and O 16-byte aligned, lengths 4-byte aligned. Errors as qmm_w4a16_g128;
+ *   a non-finite scale is QMM_ERR_ARG.
+ */
+int qmm_attn_decode(const void *Q, const void *K, const void *V, const int *lengths, void *O,
+                    int B, int Mq, int Hq, int Hkv, int Lmax, int head_dim, float scale, int s,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* The split qmm_attn_decode uses for s = 0: enough workgroups for one per CU
+ * (ceil(256 / (B*Hkv))), at most Lmax/256 (256 keys per split) and 16, at least 1
+ * (fitted to split sweeps of the Qwen3-4B decode shapes on MI355X).
+ * Host only; QMM_ERR_ARG for a non-positive size. */
+int qmm_attn_decode_split(int B, int Hkv, int Lmax);
+
+/* Workspace bytes of qmm_attn_decode for split s: s*B*Mq*Hq*(128 + 2)*4, 0 for s <= 1. */
+size_t qmm_attn_decode_workspace_bytes(int B, int Mq, int Hq, int s);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *qmm_status_string(int status);
 

@@ -26,7 +26,7 @@ ADDR3 = 0x7f0020000000
 
 def header_symbols():
     text = open(HEADER).read()
-    funcs = set(re.findall(r"^\s*(?:int|const char \*)\s*(qmm_\w+)\s*\(", text, re.M))
+    funcs = set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(qmm_\w+)\s*\(", text, re.M))
     data = set(re.findall(r"^extern const qmm_policy (\w+);", text, re.M))
     return funcs, data
 
@@ -249,6 +249,38 @@ def test_wna16_plan_rejects_unsupported_formats():
         with pytest.raises(q.QmmError) as e:
             q.qmm_wna16_plan(bits, group, 16, 1024, 2560)
         assert e.value.status == q.QMM_ERR_ARG
+
+
+def test_attn_split_rule():
+    for B, Hkv, L in [(1, 8, 4096), (1, 8, 1024), (8, 8, 4096), (32, 8, 16384), (1, 1, 100), (64, 8, 65536)]:
+        want = max(1, min(16, -(-256 // (B * Hkv)), L // 256))
+        assert q.qmm_attn_decode_split(B, Hkv, L) == want, (B, Hkv, L)
+    assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 4) == 4 * 2 * 32 * 130 * 4
+    assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 1) == 0
+
+
+def _at(**kw):
+    a = dict(Q=ADDR, K=ADDR2, V=ADDR3, lengths=ADDR + 0x400000, O=ADDR + 0x100000, B=2, Mq=1, Hq=32, Hkv=8,
+             Lmax=1024, D=128, scale=0.088, s=1, workspace=None, workspace_bytes=0)
+    a.update(kw)
+    return q.qmm_attn_decode(a["Q"], a["K"], a["V"], a["lengths"], a["O"], a["B"], a["Mq"], a["Hq"], a["Hkv"],
+                             a["Lmax"], a["D"], a["scale"], a["s"], a["workspace"], a["workspace_bytes"], stream=0,
+                             check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), q.QMM_ERR_ARG), (dict(lengths=None), q.QMM_ERR_ARG), (dict(B=0), q.QMM_ERR_ARG),
+    (dict(s=-1), q.QMM_ERR_ARG), (dict(scale=float("nan")), q.QMM_ERR_ARG), (dict(scale=float("inf")), q.QMM_ERR_ARG),
+    (dict(D=64), q.QMM_ERR_SHAPE), (dict(Hq=30), q.QMM_ERR_SHAPE), (dict(Mq=5), q.QMM_ERR_SHAPE),
+    (dict(Mq=4, Lmax=3), q.QMM_ERR_SHAPE), (dict(s=65), q.QMM_ERR_SHAPE),
+    (dict(Q=ADDR + 8), q.QMM_ERR_ALIGN), (dict(O=ADDR + 0x100002), q.QMM_ERR_ALIGN),
+    (dict(lengths=ADDR + 0x400002), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x800000, workspace_bytes=4 * 2 * 32 * 130 * 4 - 4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR + 0x800008, workspace_bytes=4 * 2 * 32 * 130 * 4), q.QMM_ERR_ALIGN),
+    (dict(B=1 << 20, Lmax=1 << 12), q.QMM_ERR_SIZE),
+])
+def test_attn_rejects_before_launch(kw, code):
+    assert _at(**kw) == code
 
 
 def test_w4a16_workspace_sizes():

@@ -550,6 +550,86 @@ def test_w8a16_full_size_sampled():
     check_tolerance(C[ms, ns], ref, what="w8a16 gate M=2048 (sampled)")
 
 
+# ------------------------------------------------- split-KV decode attention
+
+def run_attn(d, scale, s, guard=0):
+    """qmm_attn_decode through the C ABI; returns O [B, Mq, Hq, D] bits, checking a guard
+    band after O when guard > 0."""
+    B, Mq, Hq, D = d["Q"].shape
+    _, Hkv, Lmax, _ = d["K"].shape
+    Q, K, V = dev_bf16(d["Q"]), dev_bf16(d["K"]), dev_bf16(d["V"])
+    lengths = torch.from_numpy(d["lengths"].astype(np.int32)).cuda()
+    n = B * Mq * Hq * D
+    Obuf = torch.full((n + guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    s_eff = s or q.qmm_attn_decode_split(B, Hkv, Lmax)
+    wb = q.qmm_attn_decode_workspace_bytes(B, Mq, Hq, s_eff)
+    ws = torch.empty(max(wb, 16), dtype=torch.uint8, device="cuda") if wb else None
+    q.qmm_attn_decode(Q, K, V, lengths, Obuf, B, Mq, Hq, Hkv, Lmax, D, scale, s, ws)
+    torch.cuda.synchronize()
+    bits = host_bits(Obuf)
+    if guard:
+        canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+        assert np.all(bits[n:] == canary), "O guard band written"
+    return bits[:n].reshape(B, Mq, Hq, D)
+
+
+def check_attn(bits, ref, what):
+    got = syn.bf16_bits_to_f32(bits).astype(np.float64)
+    check_tolerance(got, ref, what=what)
+    # fp32 probabilities and accumulators, one bf16 rounding: far inside the bf16 bar
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * rms
+    assert np.all(err <= bound), "%s: %d outside the tight bound, worst %.3g" % (
+        what, int((err > bound).sum()), float(np.max(err - bound)))
+
+
+ATTN_CASES = [  # (B, Mq, Hq, Hkv, Lmax, lengths, splits)
+    (2, 1, 32, 8, 1024, (1000, 37), (1, 2, 3, 4, 8)),      # grouped heads, ragged lengths
+    (2, 4, 32, 8, 320, (300, 4), (1, 5)),                  # four draft queries (16 rows), causal
+    (3, 2, 4, 4, 200, (200, 2, 129), (1, 3, 7)),           # one head per group
+    (1, 2, 16, 2, 512, (512,), (1, 2, 16)),                # eight heads per group, two queries
+    (1, 1, 32, 8, 16384, (16384,), (1, 32)),               # a long history
+    (4, 1, 8, 8, 64, (5, 64, 1, 63), (1, 8, 64)),          # empty splits (s > length)
+]
+
+
+@pytest.mark.parametrize("B,Mq,Hq,Hkv,Lmax,lengths,splits", ATTN_CASES)
+def test_attn_decode_matches_oracle(B, Mq, Hq, Hkv, Lmax, lengths, splits):
+    d = syn.attn_inputs(B, Mq, Hq, Hkv, Lmax, 128, list(lengths), seed=16000 + B * 100 + Mq * 10 + Hkv)
+    scale = 1.0 / np.sqrt(128.0)
+    ref = oracle.attn_decode(d["Q"], d["K"], d["V"], d["lengths"], scale)
+    for s in splits + (0,):
+        say("attn B=%d Mq=%d Hq=%d Hkv=%d L=%s s=%d" % (B, Mq, Hq, Hkv, lengths, s))
+        check_attn(run_attn(d, scale, s, guard=64), ref, "attn %s s=%d" % (lengths, s))
+
+
+def test_attn_single_key_is_exact():
+    # each query sees exactly one key (lengths = Mq = 1): O is that key's value row, bit for bit
+    B, Hq, Hkv, L = 3, 32, 8, 64
+    d = syn.attn_inputs(B, 1, Hq, Hkv, L, 128, [1, 1, 1], seed=16500)
+    for s in (1, 4):
+        say("attn single key s=%d" % s)
+        got = run_attn(d, 0.1, s)
+        for h in range(Hq):
+            assert np.array_equal(got[:, 0, h], d["V"][:, h // 4, 0]), (s, h)
+
+
+def test_attn_uniform_weights_average_values():
+    # zero queries: every allowed key has weight 1/len (exact for power-of-two lengths)
+    B, Hq, Hkv, L = 2, 8, 2, 256
+    d = syn.attn_inputs(B, 1, Hq, Hkv, L, 128, [256, 128], seed=16600)
+    d["Q"][:] = 0
+    V = syn.bf16_bits_to_f32(d["V"]).astype(np.float64)
+    for s in (1, 2, 8):
+        say("attn uniform s=%d" % s)
+        got = syn.bf16_bits_to_f32(run_attn(d, 0.5, s)).astype(np.float64)
+        for b, n in enumerate((256, 128)):
+            for h in range(Hq):
+                ref = V[b, h // 4, :n].mean(axis=0)
+                assert np.all(np.abs(got[b, 0, h] - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6), (s, b, h)
+
+
 # ------------------------------------------------------------- edge shapes
 
 EDGE = [(1, 1, 128, 1), (1, 17, 256, 2), (3, 33, 384, 3), (15, 100, 512, 4), (17, 64, 1024, 8),

@@ -25,7 +25,8 @@ QMM_PARTIAL_F32 = 1
 # Every symbol include/qmm.h declares.
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
                       "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p",
-                      "qmm_wna16", "qmm_wna16_plan")
+                      "qmm_wna16", "qmm_wna16_plan", "qmm_attn_decode", "qmm_attn_decode_split",
+                      "qmm_attn_decode_workspace_bytes")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -81,6 +82,12 @@ def lib():
         L.qmm_bf16_splitk.restype = I
         L.qmm_w4a16_gemv.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_gemv.restype = I
+        L.qmm_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, I, P, S, P]
+        L.qmm_attn_decode.restype = I
+        L.qmm_attn_decode_split.argtypes = [I, I, I]
+        L.qmm_attn_decode_split.restype = I
+        L.qmm_attn_decode_workspace_bytes.argtypes = [I, I, I, I]
+        L.qmm_attn_decode_workspace_bytes.restype = S
         L.qmm_gemv_min_split.argtypes = [I, I]
         L.qmm_gemv_min_split.restype = I
         L.qmm_status_string.argtypes = [I]
@@ -192,6 +199,30 @@ def qmm_w4a16_gemv(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspac
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_w4a16_gemv")
     return rc
+
+
+def qmm_attn_decode(Q, K, V, lengths, O, B, Mq, Hq, Hkv, Lmax, head_dim, scale, s=0, workspace=None,
+                    workspace_bytes=None, stream=None, check=True):
+    """Split-KV decode attention through the C ABI; returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_attn_decode(_ptr(Q), _ptr(K), _ptr(V), _ptr(lengths), _ptr(O), int(B), int(Mq), int(Hq), int(Hkv),
+                               int(Lmax), int(head_dim), float(scale), int(s), _ptr(workspace), int(workspace_bytes),
+                               _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_attn_decode")
+    return rc
+
+
+def qmm_attn_decode_split(B, Hkv, Lmax):
+    rc = lib().qmm_attn_decode_split(int(B), int(Hkv), int(Lmax))
+    if rc < 0:
+        raise QmmError(rc, "qmm_attn_decode_split")
+    return rc
+
+
+def qmm_attn_decode_workspace_bytes(B, Mq, Hq, s):
+    return int(lib().qmm_attn_decode_workspace_bytes(int(B), int(Mq), int(Hq), int(s)))
 
 
 def qmm_gemv_min_split(M, K):

@@ -372,6 +372,53 @@ extern "C" int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int
     return hip_status(qmm_impl::launch_reduce(workspace, true, s, MN, C, vec_red, st));
 }
 
+namespace {
+constexpr int kAttnHeadDim = 128;
+constexpr int kAttnMaxSplit = 64;
+constexpr int kAttnPlanCap = 16;
+constexpr int kAttnTargetWgs = 256;     // one workgroup per CU
+constexpr int kAttnMinKeysPerSplit = 256;  // one 64-key tile per wave
+}  // namespace
+
+extern "C" int qmm_attn_decode_split(int B, int Hkv, int Lmax)
+{
+    if (B <= 0 || Hkv <= 0 || Lmax <= 0) return QMM_ERR_ARG;
+    long long s = ceil_div(kAttnTargetWgs, (long long)B * Hkv);
+    const long long by_len = Lmax / kAttnMinKeysPerSplit;
+    if (by_len < s) s = by_len;
+    if (s > kAttnPlanCap) s = kAttnPlanCap;
+    return s < 1 ? 1 : (int)s;
+}
+
+extern "C" size_t qmm_attn_decode_workspace_bytes(int B, int Mq, int Hq, int s)
+{
+    if (B <= 0 || Mq <= 0 || Hq <= 0 || s <= 1) return 0;
+    return (size_t)s * (size_t)B * (size_t)Mq * (size_t)Hq * (size_t)(kAttnHeadDim + 2) * 4;
+}
+
+extern "C" int qmm_attn_decode(const void *Q, const void *K, const void *V, const int *lengths, void *O, int B,
+                               int Mq, int Hq, int Hkv, int Lmax, int head_dim, float scale, int s, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (!Q || !K || !V || !lengths || !O) return QMM_ERR_ARG;
+    if (B <= 0 || Mq <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || head_dim <= 0 || s < 0) return QMM_ERR_ARG;
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return QMM_ERR_ARG;
+    if (head_dim != kAttnHeadDim || Hq % Hkv != 0 || (Hq / Hkv) * Mq > 16 || Mq > Lmax) return QMM_ERR_SHAPE;
+    if (s > kAttnMaxSplit) return QMM_ERR_SHAPE;
+    if ((long long)B * Hkv * Lmax > (long long)INT_MAX || (long long)B * Mq * Hq > (long long)INT_MAX / 64 ||
+        (long long)B * Hkv * kAttnMaxSplit > (long long)INT_MAX)
+        return QMM_ERR_SIZE;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(lengths, 4))
+        return QMM_ERR_ALIGN;
+    if (s == 0) s = qmm_attn_decode_split(B, Hkv, Lmax);
+    if (s > 1) {
+        if (!workspace || workspace_bytes < qmm_attn_decode_workspace_bytes(B, Mq, Hq, s)) return QMM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+    }
+    return hip_status(qmm_impl::launch_attn_decode(Q, K, V, lengths, O, s > 1 ? workspace : nullptr, B, Mq, Hq, Hkv,
+                                                   Lmax, scale, s, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" const char *qmm_status_string(int status)
 {
     switch (status) {

@@ -104,6 +104,13 @@ hipError_t launch_reduce(const void *partials, bool f32_partials, int s, size_t 
 hipError_t launch_reduce_cols(const void *partials, bool f32_partials, int s, int M, int N, int n_lo, void *C,
                               bool vec, hipStream_t stream);
 
+// Split-KV decode attention (head dimension 128, G*Mq <= 16 query rows per key/value
+// head): S splits of every request's keys; S > 1 needs the workspace (fp32
+// accumulators [S][B*Mq*Hq][128], then max and sum [S][B*Mq*Hq][2]) and runs the merge.
+hipError_t launch_attn_decode(const void *Q, const void *K, const void *V, const int *lengths, void *O,
+                              void *workspace, int B, int Mq, int Hq, int Hkv, int Lmax, float scale, int S,
+                              hipStream_t stream);
+
 hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out, bool f32_out,
                         int M, int N, int K, int s, bool vec_store, hipStream_t stream);
 

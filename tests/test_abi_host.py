@@ -253,7 +253,7 @@ def test_wna16_plan_rejects_unsupported_formats():
 
 def test_attn_split_rule():
     for B, Hkv, L in [(1, 8, 4096), (1, 8, 1024), (8, 8, 4096), (32, 8, 16384), (1, 1, 100), (64, 8, 65536)]:
-        want = max(1, min(16, -(-256 // (B * Hkv)), L // 256))
+        want = max(1, min(32, -(-256 // (B * Hkv)), L // 256))
         assert q.qmm_attn_decode_split(B, Hkv, L) == want, (B, Hkv, L)
     assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 4) == 4 * 2 * 32 * 130 * 4
     assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 1) == 0

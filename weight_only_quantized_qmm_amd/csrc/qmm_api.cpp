@@ -375,7 +375,7 @@ extern "C" int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int
 namespace {
 constexpr int kAttnHeadDim = 128;
 constexpr int kAttnMaxSplit = 64;
-constexpr int kAttnPlanCap = 16;
+constexpr int kAttnPlanCap = 32;
 constexpr int kAttnTargetWgs = 256;     // one workgroup per CU
 constexpr int kAttnMinKeysPerSplit = 256;  // one 64-key tile per wave
 }  // namespace

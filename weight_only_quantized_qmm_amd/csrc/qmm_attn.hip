@@ -292,20 +292,39 @@ attn_merge_kernel(const float *__restrict__ part_acc, const float *__restrict__ 
     if (t >= (size_t)rows * (D / 8)) return;
     const size_t row = t / (D / 8);
     const int dd = 8 * (int)(t % (D / 8));
+    // A split with no allowed key for this row stored max -inf, sum 0 and a zero
+    // accumulator: its weight exp2(-inf - m) is 0, so no branch is needed. The splits
+    // are read in batches of eight whose loads are all issued before their use.
+    constexpr int BATCH = 8;
     float m = NEG_INF;
-    for (int p = 0; p < S; ++p) m = fmaxf(m, part_ml[((size_t)p * rows + row) * 2]);
+    for (int p0 = 0; p0 < S; p0 += BATCH) {
+        float mv[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+            mv[u] = p0 + u < S ? part_ml[((size_t)(p0 + u) * rows + row) * 2] : NEG_INF;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) m = fmaxf(m, mv[u]);
+    }
     float lsum = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < S; ++p) {
-        const float mp = part_ml[((size_t)p * rows + row) * 2];
-        if (mp == NEG_INF) continue;  // a split with no allowed key for this row
-        const float f = exp2f(mp - m);
-        lsum += f * part_ml[((size_t)p * rows + row) * 2 + 1];
-        const float *pa = part_acc + ((size_t)p * rows + row) * D + dd;
-        const float4 x = *reinterpret_cast<const float4 *>(pa);
-        const float4 y = *reinterpret_cast<const float4 *>(pa + 4);
-        o[0] += f * x.x; o[1] += f * x.y; o[2] += f * x.z; o[3] += f * x.w;
-        o[4] += f * y.x; o[5] += f * y.y; o[6] += f * y.z; o[7] += f * y.w;
+    for (int p0 = 0; p0 < S; p0 += BATCH) {
+        float2 ml[BATCH];
+        float4 x[BATCH], y[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int p = min(p0 + u, S - 1);  // past S: re-read the last split, weight 0
+            ml[u] = *reinterpret_cast<const float2 *>(part_ml + ((size_t)p * rows + row) * 2);
+            const float *pa = part_acc + ((size_t)p * rows + row) * D + dd;
+            x[u] = *reinterpret_cast<const float4 *>(pa);
+            y[u] = *reinterpret_cast<const float4 *>(pa + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const float f = p0 + u < S ? exp2f(ml[u].x - m) : 0.f;
+            lsum += f * ml[u].y;
+            o[0] += f * x[u].x; o[1] += f * x[u].y; o[2] += f * x[u].z; o[3] += f * x[u].w;
+            o[4] += f * y[u].x; o[5] += f * y[u].y; o[6] += f * y[u].z; o[7] += f * y[u].w;
+        }
     }
     const float inv = 1.f / lsum;
     uint4 ov;

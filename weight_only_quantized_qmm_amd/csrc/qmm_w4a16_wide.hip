@@ -18,7 +18,7 @@
 // tile, and 64-value stages make every row of A a whole 128-byte line.
 //
 // Data movement: every global read of the kernel is a direct global -> LDS copy
-// (global_load_lds_*), two stages ahead of its use, into rings of three slots:
+// (global_load_lds_*), issued one and a half stages ahead of its use, into rings of three slots:
 //   A:  256 rows x 64 bf16 (32 KB per stage), four 1 KB copies per wave;
 //   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage; 64 bytes and 16 KB for
 //       8-bit codes), 1 KB per copy;
@@ -26,10 +26,12 @@
 //       or four), one 2-byte copy per lane (zero-extended into a dword), once per block,
 //       in a ring of two.
 // The compiler neither sees nor waits for these copies; the kernel retires them
-// itself: at the end of stage i each wave waits (s_waitcnt vmcnt) until the copies
+// itself: in the middle of stage i each wave waits (s_waitcnt vmcnt) until the copies
 // it issued for stage i+1 have landed, and the barrier that follows publishes them
-// to the whole workgroup. No other vector-memory instruction is issued in the loop,
-// so the counter arithmetic is exact.
+// to the whole workgroup; the copies of stage i+2 are issued right after it. No other
+// vector-memory instruction is issued in the loop, so the counter arithmetic is exact.
+// The next stage's first operands are read during the last step of the current one,
+// so the matrix pipeline does not drain at stage boundaries.
 //
 // Dequantisation: each wave turns its 64 columns' packed words straight into MFMA
 // operands (w = scale*q + bias in fp32, rounded to bf16). One packed 32-bit word is
@@ -181,52 +183,86 @@ __device__ __forceinline__ bf16x8 weights_of_step(const uint4 (&wpk)[CF::WV], in
     return as_bf16x8(dequant8_u8(word_of(v, 2 * (t & 1)), word_of(v, 2 * (t & 1) + 1), sc, bi));
 }
 
-// The 32 MFMAs of one stage for this wave, operands from A/W slot `slot3` and
-// scale/bias slot `sbslot`; ODD: the stage is the second half of its 128-value block.
-template <class CF, int ODD>
-__device__ __forceinline__ void compute(const Ctx<CF> &c, const Lds<CF> &L, int slot3, int sbslot,
-                                        f32x16 (&acc)[CF::MI][CF::NJ])
+// Operands carried from one stage into the next: the stage's W words and scale/bias,
+// and the A operands and dequantised weights of the step about to run.
+template <class CF>
+struct Ops {
+    uint4 wpk[CF::NJ][CF::WV];
+    float sc[CF::NJ], sc16[CF::NJ], bi[CF::NJ];
+    bf16x8 af[CF::MI];
+    bf16x8 bw[CF::NJ];
+};
+
+// The A operands (rows of this wave) and dequantised weights of reduction step t of a
+// stage whose A slot starts at As.
+template <class CF>
+__device__ __forceinline__ void step_operands(const Ctx<CF> &c, const char *As, const Ops<CF> &o, int t,
+                                              bf16x8 (&af)[CF::MI], bf16x8 (&bw)[CF::NJ])
 {
-    constexpr int MI = CF::MI, NJ = CF::NJ, WV = CF::WV;
-    const char *As = L.a + slot3 * CF::A_SLOT;
+#pragma unroll
+    for (int i = 0; i < CF::MI; ++i) af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t] + 4096 * i));
+#pragma unroll
+    for (int j = 0; j < CF::NJ; ++j) bw[j] = weights_of_step<CF>(o.wpk[j], t, o.sc[j], o.sc16[j], o.bi[j]);
+}
+
+// The head of a stage (A/W slot `slot3`, scale/bias slot `sbslot`; ODD: the second half
+// of its 128-value block): its W words, scale/bias and the operands of its step 0.
+template <class CF, int ODD>
+__device__ __forceinline__ void load_head(const Ctx<CF> &c, const Lds<CF> &L, int slot3, int sbslot, Ops<CF> &o)
+{
     const char *Ws = L.w + slot3 * CF::W_SLOT;
     const char *Ss = L.sb + sbslot * CF::SB_SLOT;
-    uint4 wpk[NJ][WV];
-    float sc[NJ], sc16[NJ], bi[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < CF::NJ; ++j) {
 #pragma unroll
-        for (int u = 0; u < WV; ++u)
-            wpk[j][u] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd[u] + 32 * CF::WROW * j);
-        sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd[ODD] + 128 * j));
-        bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 * CF::SUB + c.sb_rd[ODD] + 128 * j));
-        sc16[j] = sc[j] * 0.0625f;
+        for (int u = 0; u < CF::WV; ++u)
+            o.wpk[j][u] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd[u] + 32 * CF::WROW * j);
+        o.sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd[ODD] + 128 * j));
+        o.bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 * CF::SUB + c.sb_rd[ODD] + 128 * j));
+        o.sc16[j] = o.sc[j] * 0.0625f;
     }
-    // Software pipeline over the four reduction steps: the A operands and dequantised
-    // weights of step t+1 are produced while the MFMAs of step t run. The scheduling
-    // fences keep the compiler from sinking the next step's LDS reads down to their
-    // use, which would expose the LDS latency before every MFMA.
-    bf16x8 af[2][MI], bfr[2][NJ];
+    step_operands<CF>(c, L.a + slot3 * CF::A_SLOT, o, 0, o.af, o.bw);
+}
+
+// The 32 MFMAs of one stage (A slot `slot3`) whose head is in `o`, software-pipelined:
+// the operands of step t+1 are read and dequantised while the MFMAs of step t run.
+// Between steps 1 and 2 it calls mid() (the workgroup's stage barrier and the copies it
+// frees a slot for); during step 3 it calls next(o) to read the next stage's head, so
+// no stage starts with an empty matrix pipeline. The scheduling fences keep the
+// compiler from sinking the reads down to their use or hoisting them above mid().
+template <class CF, class Mid, class Next>
+__device__ __forceinline__ void run_stage(const Ctx<CF> &c, const Lds<CF> &L, int slot3, Ops<CF> &o,
+                                          f32x16 (&acc)[CF::MI][CF::NJ], Mid mid, Next next)
+{
+    constexpr int MI = CF::MI, NJ = CF::NJ;
+    const char *As = L.a + slot3 * CF::A_SLOT;
+    bf16x8 af2[MI], bw2[NJ];
+    __builtin_amdgcn_sched_barrier(0);
+    step_operands<CF>(c, As, o, 1, af2, bw2);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) af[0][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[0] + 4096 * i));
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[0][j] = weights_of_step<CF>(wpk[j], 0, sc[j], sc16[j], bi[j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(o.bw[j], o.af[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    step_operands<CF>(c, As, o, 2, o.af, o.bw);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int cur = t & 1, nxt = cur ^ 1;
-        __builtin_amdgcn_sched_barrier(0);
-        if (t < 3) {
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[nxt][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t + 1] + 4096 * i));
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bw2[j], af2[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+    step_operands<CF>(c, As, o, 3, af2, bw2);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) bfr[nxt][j] = weights_of_step<CF>(wpk[j], t + 1, sc[j], sc16[j], bi[j]);
-        }
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(o.bw[j], o.af[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    next(o);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bfr[cur][j], af[cur][i], acc[i][j]);
-    }
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bw2[j], af2[i], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -383,34 +419,45 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int nst = 2 * gpp;  // stages in the partition, even
-    // Prologue: stage 0 (A, W, group 0's scale/bias) and stage 1 (A, W); wait for stage 0.
+    // Prologue: stage 0 (A, W, group 0's scale/bias) and stage 1 (A, W); wait for stage 0
+    // and read its head.
     issue<CF, true>(c, 0, 0, 0);
     issue<CF, false>(c, 1, 1, 0);
     QMM_WAIT_VMCNT(GE::N_ODD);
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
+    Ops<CF> o;
+    load_head<CF, 0>(c, L, 0, 0, o);
 
-    // Stage x uses A/W slot x % 3 and scale/bias slot (x/2) % 2. Stage st (even)
-    // issues stage st+2 with its group's scale/bias (N_EVEN copies per wave), stage
-    // st+1 issues stage st+3 (N_ODD); past the last stage the copies repeat stage
-    // nst-1 into slots that are never read again, so every stage issues the same count.
+    // Stage x uses A/W slot x % 3 and scale/bias slot (x/2) % 2. In the middle of stage x
+    // each wave waits for its copies of stage x+1 (issued in the middle of stage x-1, the
+    // only ones outstanding), the barrier publishes them and certifies that every wave
+    // has left stage x-1, and the copies of stage x+2 go into stage x-1's slot (with the
+    // next group's scale/bias when x is even). Past the last stage the copies repeat
+    // stage nst-1 into slots that are never read again.
     int s3 = 0;  // st % 3
     for (int st = 0; st < nst; st += 2) {
         const int s3n = s3 == 2 ? 0 : s3 + 1;    // (st+1) % 3
         const int s3p = s3 == 0 ? 2 : s3 - 1;    // (st+2) % 3
         const int sbs = (st >> 1) & 1;
-        issue<CF, true>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
-        compute<CF, 0>(c, L, s3, sbs, acc);
-        // stage st+1's copies (issued one stage earlier) are followed by this stage's
-        QMM_WAIT_VMCNT(GE::N_EVEN);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        issue<CF, false>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
-        compute<CF, 1>(c, L, s3n, sbs, acc);
-        // stage st+2's copies (issued above) are followed by this stage's
-        QMM_WAIT_VMCNT(GE::N_ODD);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
+        const bool more = st + 2 < nst;
+        run_stage<CF>(
+            c, L, s3, o, acc,
+            [&] {
+                QMM_WAIT_VMCNT(0);
+                __syncthreads();
+                issue<CF, true>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
+            },
+            [&](Ops<CF> &n) { load_head<CF, 1>(c, L, s3n, sbs, n); });
+        run_stage<CF>(
+            c, L, s3n, o, acc,
+            [&] {
+                QMM_WAIT_VMCNT(0);
+                __syncthreads();
+                issue<CF, false>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
+            },
+            [&](Ops<CF> &n) {
+                if (more) load_head<CF, 0>(c, L, s3p, sbs ^ 1, n);
+            });
         s3 = s3p;
     }
     // No copy may still be writing LDS when the workgroup ends.

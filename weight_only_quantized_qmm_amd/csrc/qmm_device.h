@@ -28,24 +28,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Dequantise the eight 4-bit weights of one packed word, w_i = scale * q_i + bias
 // (q_i = bits 4i..4i+3), into four bf16 pairs in k order: .x = (w0, w1), ..., .w = (w6, w7).
-// The even nibbles are isolated with one mask and converted with the byte-to-float
-// conversions; the odd nibbles are masked in place, so they convert to 16*q and meet
-// scale/16 instead (the product is the same real number and the FMA rounds once, so
-// every weight is bitwise fma(q, scale, bias) whenever scale/16 is exact, i.e. for
-// |scale| >= 2^-122). 22 VALU instructions per 8 weights.
-__device__ __forceinline__ uint4 dequant8(uint32_t x, float sc, float sc16, float bi) {
-    uint32_t lo = x & 0x0F0F0F0Fu;
-    uint32_t hi = x & 0xF0F0F0F0u;
-    // keep the masks opaque so the byte extracts stay single conversion instructions
-    asm("" : "+v"(lo));
-    asm("" : "+v"(hi));
+// The even and odd nibbles are isolated into bytes (one mask; one shift and mask) and
+// converted two at a time by the fp8-to-fp32 conversion: a byte b < 16 read as an OCP
+// e4m3 number is exactly b * 2^-9 (a subnormal for b < 8, exponent 1 for 8..15). The
+// caller passes sc512 = scale * 2^9 (exact), so fma(b * 2^-9, sc512, bias) is the same
+// real number as fma(q, scale, bias), rounded once: every weight is bitwise
+// RNE_bf16(fma(q, scale, bias)) for |scale| < 2^118. 19 VALU instructions per 8 weights.
+__device__ __forceinline__ uint4 dequant8(uint32_t x, float sc512, float bi) {
+    const uint32_t lo = x & 0x0F0F0F0Fu;         // q0, q2, q4, q6
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // q1, q3, q5, q7
+    const f32x2 e01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // q0, q2 (times 2^-9)
+    const f32x2 e23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);   // q4, q6
+    const f32x2 o01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);  // q1, q3
+    const f32x2 o23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);   // q5, q7
     uint4 r;
-    r.x = pack_bf16x2(__builtin_fmaf((float)(lo & 0xFFu), sc, bi), __builtin_fmaf((float)(hi & 0xFFu), sc16, bi));
-    r.y = pack_bf16x2(__builtin_fmaf((float)((lo >> 8) & 0xFFu), sc, bi),
-                      __builtin_fmaf((float)((hi >> 8) & 0xFFu), sc16, bi));
-    r.z = pack_bf16x2(__builtin_fmaf((float)((lo >> 16) & 0xFFu), sc, bi),
-                      __builtin_fmaf((float)((hi >> 16) & 0xFFu), sc16, bi));
-    r.w = pack_bf16x2(__builtin_fmaf((float)(lo >> 24), sc, bi), __builtin_fmaf((float)(hi >> 24), sc16, bi));
+    r.x = pack_bf16x2(__builtin_fmaf(e01.x, sc512, bi), __builtin_fmaf(o01.x, sc512, bi));
+    r.y = pack_bf16x2(__builtin_fmaf(e01.y, sc512, bi), __builtin_fmaf(o01.y, sc512, bi));
+    r.z = pack_bf16x2(__builtin_fmaf(e23.x, sc512, bi), __builtin_fmaf(o23.x, sc512, bi));
+    r.w = pack_bf16x2(__builtin_fmaf(e23.y, sc512, bi), __builtin_fmaf(o23.y, sc512, bi));
     return r;
 }
 

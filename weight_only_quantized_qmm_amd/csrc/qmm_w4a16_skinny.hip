@@ -115,13 +115,13 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             for (int j = 0; j < NS; ++j) {
                 const float s_ = bf16_to_f32(sc[q][j]);
                 const float b_ = bf16_to_f32(bi[q][j]);
-                const float s16 = s_ * 0.0625f;
+                const float s512 = s_ * 512.f;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
                     // step t: values 8t .. 8t+7 of the lane's 32 (one word of 4-bit codes,
                     // two words of 8-bit codes)
                     const bf16x8 b = as_bf16x8(
-                        BITS == 4 ? dequant8(word_of(wv[q][j][0], t), s_, s16, b_)
+                        BITS == 4 ? dequant8(word_of(wv[q][j][0], t), s512, b_)
                                   : dequant8_u8(word_of(wv[q][j][(t >> 1) % WV], 2 * (t & 1)),
                                                 word_of(wv[q][j][(t >> 1) % WV], 2 * (t & 1) + 1), s_, b_));
 #pragma unroll

@@ -175,10 +175,10 @@ __device__ __forceinline__ void issue(const Ctx<CF> &c, int x, int slot3, int sb
 
 // Eight dequantised weights of reduction step t (0..3) from a lane's W words of a stage.
 template <class CF>
-__device__ __forceinline__ bf16x8 weights_of_step(const uint4 (&wpk)[CF::WV], int t, float sc, float sc16,
+__device__ __forceinline__ bf16x8 weights_of_step(const uint4 (&wpk)[CF::WV], int t, float sc, float sc512,
                                                   float bi)
 {
-    if (CF::BITS == 4) return as_bf16x8(dequant8(word_of(wpk[0], t), sc, sc16, bi));
+    if (CF::BITS == 4) return as_bf16x8(dequant8(word_of(wpk[0], t), sc512, bi));
     const uint4 &v = wpk[(t >> 1) % CF::WV];
     return as_bf16x8(dequant8_u8(word_of(v, 2 * (t & 1)), word_of(v, 2 * (t & 1) + 1), sc, bi));
 }
@@ -188,7 +188,7 @@ __device__ __forceinline__ bf16x8 weights_of_step(const uint4 (&wpk)[CF::WV], in
 template <class CF>
 struct Ops {
     uint4 wpk[CF::NJ][CF::WV];
-    float sc[CF::NJ], sc16[CF::NJ], bi[CF::NJ];
+    float sc[CF::NJ], sc512[CF::NJ], bi[CF::NJ];
     bf16x8 af[CF::MI];
     bf16x8 bw[CF::NJ];
 };
@@ -202,7 +202,7 @@ __device__ __forceinline__ void step_operands(const Ctx<CF> &c, const char *As, 
 #pragma unroll
     for (int i = 0; i < CF::MI; ++i) af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t] + 4096 * i));
 #pragma unroll
-    for (int j = 0; j < CF::NJ; ++j) bw[j] = weights_of_step<CF>(o.wpk[j], t, o.sc[j], o.sc16[j], o.bi[j]);
+    for (int j = 0; j < CF::NJ; ++j) bw[j] = weights_of_step<CF>(o.wpk[j], t, o.sc[j], o.sc512[j], o.bi[j]);
 }
 
 // The head of a stage (A/W slot `slot3`, scale/bias slot `sbslot`; ODD: the second half
@@ -219,7 +219,7 @@ __device__ __forceinline__ void load_head(const Ctx<CF> &c, const Lds<CF> &L, in
             o.wpk[j][u] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd[u] + 32 * CF::WROW * j);
         o.sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd[ODD] + 128 * j));
         o.bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 * CF::SUB + c.sb_rd[ODD] + 128 * j));
-        o.sc16[j] = o.sc[j] * 0.0625f;
+        o.sc512[j] = o.sc[j] * 512.f;
     }
     step_operands<CF>(c, L.a + slot3 * CF::A_SLOT, o, 0, o.af, o.bw);
 }

@@ -239,6 +239,37 @@ def decode_table(torch, syn, q):
     return rows
 
 
+def streamk_table(torch, syn, q, table):
+    """The stream-K decomposition (qmm_w4a16_g128_streamk, default workgroups) on the
+    M = 128 and 2048 sweep shapes, against the plan's time from the per-shape table."""
+    plan_us = {(t["name"], t["M"]): t["us"] for t in table}
+    rows = []
+    for name, M, N, K, idx in syn.projection_sweep():
+        if M < 128:
+            continue
+        probe = Shape(name, M, N, K, idx, 1, torch, syn, q)
+        R = max(8, min(1024, math.ceil(ROTATE_BYTES / probe.set_bytes())))
+        probe.free()
+        sh = Shape(name, M, N, K, idx, R, torch, syn, q)
+        nb = q.qmm_streamk_workspace_bytes(M, N, K, 0)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+        def run():
+            for r in range(R):
+                A, W, S, B = sh.sets[r]
+                q.qmm_w4a16_g128_streamk(A, W, S, B, sh.C, M, N, K, 0, ws, nb)
+        g = graph_of(torch, run)
+        t = time_graph(torch, g) / R
+        del g, ws
+        sh.free()
+        torch.cuda.empty_cache()
+        r = roofline(M, N, K, t)
+        rows.append(dict(name=name, M=M, us=round(t * 1e6, 3), plan_us=plan_us.get((name, M)),
+                         workspace_mb=round(nb / 1e6, 1), frac=round(r["frac"], 4)))
+        print("# streamk %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    return rows
+
+
 ATTN_SHAPES = [(1, 4096, 1), (1, 16384, 1), (8, 4096, 1), (32, 4096, 1), (32, 16384, 1), (8, 4096, 4)]
 
 
@@ -585,8 +616,9 @@ def main():
                               roof_us=round(r["t_roof_us"], 3), frac=round(r["frac"], 4), rotation_sets=R))
             print("# %s" % json.dumps(table[-1]), file=sys.stderr, flush=True)
 
-    dense = decode = formats = attention = None
+    dense = decode = formats = attention = streamk = None
     if not args.no_per_shape:
+        streamk = streamk_table(torch, syn, q, table)
         dense = dense_sweep(torch, syn, q)
         decode = decode_table(torch, syn, q)
         formats = formats_table(torch, syn, q)
@@ -623,6 +655,7 @@ def main():
         "decode": decode,
         "formats": formats,
         "decode_attention": attention,
+        "streamk": streamk,
     }
     if table:
         small = [t for t in table if t["M"] <= 128]

@@ -183,6 +183,31 @@ int qmm_wna16_plan(int bits, int group_size, int M, int N, int K, const qmm_poli
                    qmm_plan *out);
 
 /*
+ * qmm_w4a16_g128_streamk -- the same product with the stream-K decomposition of the
+ * large-M kernel (the persistent-style decomposition that gives every workgroup an equal
+ * share of multiply-adds across tile boundaries; the split of the pages' Task 2 with
+ * unequal, tile-crossing partitions): the (tile, 128-value block) units, tile-major, are
+ * cut into `workgroups` near-equal contiguous ranges. A tile one workgroup covers whole
+ * is written to C directly (bitwise the unsplit kernel's result); the pieces of a shared
+ * tile go to per-workgroup slots of the workspace as bf16 and a fix-up kernel adds them in
+ * reduction order in fp32, with one cast to bf16. Deterministic, no atomics.
+ *   M > 64 (QMM_ERR_SHAPE otherwise: small M runs another kernel).
+ *   workgroups = 0: one per workgroup slot of the GPU (256 times the workgroups one CU
+ *   holds for this shape's tile), at most units / 4 (four blocks, 512 reduction values, per
+ *   workgroup, the MI355X preset's floor) and at least 1; else 1 .. units, where
+ *   units = ceil(M/BM) * ceil(N/256) * K/128 and BM = 128 for M <= 128, else 256.
+ *   workspace >= qmm_streamk_workspace_bytes(M, N, K, workgroups), 16-byte aligned.
+ *   Other arguments, layouts and errors as qmm_w4a16_g128.
+ */
+int qmm_w4a16_g128_streamk(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                           int M, int N, int K, int workgroups, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Workspace of qmm_w4a16_g128_streamk: 2 * P * BM * 256 * 2 bytes for its P workgroups;
+ * 0 for shapes it does not take. Host only. */
+size_t qmm_streamk_workspace_bytes(int M, int N, int K, int workgroups);
+
+/*
  * qmm_w4a16_gemv -- the same product for decode-sized M (1 to 8 rows) on a matrix-vector
  * kernel with no matrix-core padding (tiny-llm "Week 2 Day 7", Benchmark Analysis:
  * decode runs on a separate matvec). Every packed weight is read once per call.

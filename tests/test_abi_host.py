@@ -283,6 +283,36 @@ def test_attn_rejects_before_launch(kw, code):
     assert _at(**kw) == code
 
 
+def _sk(**kw):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=300, N=520, K=1024, P=0,
+             workspace=ADDR + 0x2000000, workspace_bytes=1 << 30)
+    a.update(kw)
+    return q.qmm_w4a16_g128_streamk(a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"], a["P"],
+                                    a["workspace"], a["workspace_bytes"], stream=0, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(P=-1), q.QMM_ERR_ARG), (dict(M=0), q.QMM_ERR_ARG),
+    (dict(M=64), q.QMM_ERR_SHAPE), (dict(K=1000), q.QMM_ERR_SHAPE),
+    (dict(P=2 * 3 * 8 + 1), q.QMM_ERR_SHAPE),  # 2 x 3 tiles of 256 x 256, 8 blocks: 48 units
+    (dict(workspace=None), q.QMM_ERR_WORKSPACE),
+    (dict(P=7, workspace_bytes=2 * 7 * 256 * 256 * 2 - 2), q.QMM_ERR_WORKSPACE),
+    (dict(workspace=ADDR + 0x2000008), q.QMM_ERR_ALIGN), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN),
+])
+def test_streamk_rejects_before_launch(kw, code):
+    assert _sk(**kw) == code
+
+
+def test_streamk_workspace_sizes():
+    assert q.qmm_streamk_workspace_bytes(300, 520, 1024, 7) == 2 * 7 * 256 * 256 * 2
+    assert q.qmm_streamk_workspace_bytes(300, 520, 1024, 0) == 2 * 12 * 256 * 256 * 2  # 48 units, 4 per group
+    assert q.qmm_streamk_workspace_bytes(100, 4096, 2560, 0) == 2 * 80 * 128 * 256 * 2  # 16 tiles x 20 blocks / 4
+    assert q.qmm_streamk_workspace_bytes(100, 9728, 2560, 0) == 2 * 190 * 128 * 256 * 2  # 760 units / 4
+    assert q.qmm_streamk_workspace_bytes(2048, 9728, 2560, 0) == 2 * 256 * 256 * 256 * 2
+    assert q.qmm_streamk_workspace_bytes(64, 1024, 2560, 0) == 0
+    assert _sk(P=7, workspace_bytes=2 * 7 * 256 * 256 * 2, C=None) == q.QMM_ERR_ARG
+
+
 def test_w4a16_workspace_sizes():
     assert q.w4a16_workspace_bytes(32, 1024, 1) == 0
     assert q.w4a16_workspace_bytes(32, 1024, 4) == 2 * 4 * 32 * 1024

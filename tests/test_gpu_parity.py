@@ -147,6 +147,74 @@ def test_split_tail_decomposition():
     check_tolerance(host_f64(C)[m2, n2], ref2, what="split tail, sampled")
 
 
+# ------------------------------------------------------- stream-K decomposition
+
+def streamk_whole_tiles(T, G, P):
+    """Tiles a single workgroup covers whole under the near-equal unit ranges."""
+    U = T * G
+    whole = []
+    for w in range(P):
+        u0, u1 = w * U // P, (w + 1) * U // P
+        t_first = -(-u0 // G)              # first tile starting at or after u0
+        t_last = u1 // G                   # tiles ending at or before u1
+        whole += list(range(t_first, t_last))
+    return sorted(set(whole))
+
+
+def run_streamk(dv, M, N, K, P, guard=0):
+    nbytes = q.qmm_streamk_workspace_bytes(M, N, K, P)
+    Cbuf = torch.full((M * N + 2 * guard,), -12345.0, dtype=torch.bfloat16, device="cuda")
+    C = Cbuf[guard:guard + M * N].view(M, N)
+    gw = 64
+    wbuf = torch.full((nbytes // 2 + 2 * gw,), -777.0, dtype=torch.bfloat16, device="cuda")
+    q.qmm_w4a16_g128_streamk(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, P, wbuf[gw:gw + nbytes // 2],
+                             nbytes)
+    torch.cuda.synchronize()
+    if guard:
+        g = host_bits(Cbuf)
+        canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+        assert np.all(g[:guard] == canary) and np.all(g[guard + M * N:] == canary), "C guard band written"
+        w = host_bits(wbuf)
+        wc = host_bits(torch.tensor([-777.0], dtype=torch.bfloat16))[0]
+        assert np.all(w[:gw] == wc) and np.all(w[gw + nbytes // 2:] == wc), "workspace guard written"
+    return C
+
+
+@pytest.mark.parametrize("M,N,K,Ps", [
+    (100, 1000, 2560, (1, 7, 64, 80, 0)),      # 128-row tiles: 4 tiles x 20 blocks
+    (300, 520, 1024, (1, 5, 13, 48, 0)),       # 256-row tiles, ragged M and N: 6 tiles x 8 blocks
+    (520, 300, 1280, (3, 11, 29, 0)),
+])
+def test_streamk_matches_oracle(M, N, K, Ps):
+    d = syn.w4a16_inputs(M, N, K, seed=17000 + M)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    c1 = host_bits(run_w4a16(dv, M, N, K, 1))
+    BM = 128 if M <= 128 else 256
+    num_m, num_n, G = -(-M // BM), -(-N // 256), K // 128
+    for P in Ps:
+        Peff = P or max(1, min(num_m * num_n * G // min(4, G), 256 * (2 if BM == 128 else 1)))
+        say("streamk M=%d N=%d K=%d P=%d" % (M, N, K, Peff))
+        C = run_streamk(dv, M, N, K, P, guard=64)
+        check_tolerance(host_f64(C), ref, what="stream-K P=%d" % Peff)
+        bits = host_bits(C)
+        for t in streamk_whole_tiles(num_m * num_n, G, Peff):
+            r0, c0 = (t % num_m) * BM, (t // num_m) * 256
+            blk = (slice(r0, min(r0 + BM, M)), slice(c0, min(c0 + 256, N)))
+            assert np.array_equal(bits[blk], c1[blk]), "tile %d covered whole differs from the unsplit kernel" % t
+
+
+def test_streamk_full_size_sampled():
+    M, N, K = 2048, 2560, 9728  # the down projection: 80 tiles x 76 blocks on 256 workgroups
+    d = syn.w4a16_inputs(M, N, K, seed=17500)
+    dv = w4a16_device(d)
+    say("streamk full size M=%d N=%d K=%d" % (M, N, K))
+    C = host_f64(run_streamk(dv, M, N, K, 0))
+    ms, ns = sample_points(M, N, 17500)
+    ref = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+    check_tolerance(C[ms, ns], ref, what="stream-K down M=2048 (sampled)")
+
+
 # --------------------------------------------------- fp32 partial planes (W4A16)
 
 def check_single_cast(bits, ref, min_equal, what):

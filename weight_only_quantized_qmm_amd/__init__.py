@@ -9,4 +9,5 @@ from .binding import (  # noqa: F401
     QMM_ERR_SIZE, QMM_ERR_WORKSPACE, QMM_OK, QMM_PARTIAL_BF16, QMM_PARTIAL_F32, QmmError,
     bf16_splitk, effective_split, lib, policy_preset, qmm_bf16_splitk, qmm_plan, qmm_policy,
     qmm_gemv_min_split, qmm_splitk_plan, qmm_splitk_reduce, qmm_status_string, qmm_w4a16_g128,
-    qmm_attn_decode, qmm_attn_decode_split, qmm_attn_decode_workspace_bytes, qmm_w4a16_g128_f32p, qmm_w4a16_gemv, qmm_wna16, qmm_wna16_plan, w4a16, w4a16_workspace_bytes, wna16)
+    qmm_attn_decode, qmm_attn_decode_split, qmm_attn_decode_workspace_bytes, qmm_streamk_workspace_bytes,
+    qmm_w4a16_g128_f32p, qmm_w4a16_g128_streamk, qmm_w4a16_gemv, qmm_wna16, qmm_wna16_plan, w4a16, w4a16_workspace_bytes, wna16)

@@ -26,7 +26,7 @@ QMM_PARTIAL_F32 = 1
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
                       "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p",
                       "qmm_wna16", "qmm_wna16_plan", "qmm_attn_decode", "qmm_attn_decode_split",
-                      "qmm_attn_decode_workspace_bytes")
+                      "qmm_attn_decode_workspace_bytes", "qmm_w4a16_g128_streamk", "qmm_streamk_workspace_bytes")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -72,6 +72,10 @@ def lib():
         L.qmm_w4a16_g128.restype = I
         L.qmm_w4a16_g128_f32p.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_g128_f32p.restype = I
+        L.qmm_w4a16_g128_streamk.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
+        L.qmm_w4a16_g128_streamk.restype = I
+        L.qmm_streamk_workspace_bytes.argtypes = [I, I, I, I]
+        L.qmm_streamk_workspace_bytes.restype = S
         L.qmm_wna16.argtypes = [I, I, I, P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_wna16.restype = I
         L.qmm_wna16_plan.argtypes = [I, I, I, I, I, ctypes.POINTER(qmm_policy), ctypes.POINTER(qmm_plan)]
@@ -174,6 +178,22 @@ def qmm_w4a16_g128_f32p(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, wor
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_w4a16_g128_f32p")
     return rc
+
+
+def qmm_w4a16_g128_streamk(A, Wq, scale, bias, C, M, N, K, workgroups=0, workspace=None, workspace_bytes=None,
+                           stream=None, check=True):
+    """C = A . dequant(W)^T with the stream-K decomposition (M > 64); returns the status."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    rc = lib().qmm_w4a16_g128_streamk(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                                      int(workgroups), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_g128_streamk")
+    return rc
+
+
+def qmm_streamk_workspace_bytes(M, N, K, workgroups=0):
+    return int(lib().qmm_streamk_workspace_bytes(int(M), int(N), int(K), int(workgroups)))
 
 
 def qmm_wna16(bits, group_size, partial_dtype, A, Wq, scale, bias, C, M, N, K, s=0, workspace=None,

@@ -279,6 +279,57 @@ extern "C" int qmm_wna16(int bits, int group_size, int partial_dtype, const void
 }
 
 namespace {
+
+// Workgroups of the stream-K decomposition for workgroups = 0: one per workgroup slot,
+// and no more than leave each at least min_k_per_split reduction values (the MI355X
+// preset's floor on a partition) of units.
+long long streamk_default_wgs(WFormat fmt, int variant, long long units, int K)
+{
+    long long P = (long long)kCUs * qmm_impl::wide_wgs_per_cu(variant, fmt);
+    const long long min_units = QMM_POLICY_MI355X.min_k_per_split / kGroup;  // 4 blocks
+    const long long G = K / kGroup;
+    const long long cap = units / (min_units < G ? min_units : G);
+    if (cap < P) P = cap;
+    return P < 1 ? 1 : P;
+}
+
+}  // namespace
+
+extern "C" size_t qmm_streamk_workspace_bytes(int M, int N, int K, int workgroups)
+{
+    if (M <= 64 || N <= 0 || K <= 0 || K % kGroup != 0 || workgroups < 0) return 0;
+    const W4A16Tile tile = w4a16_tile(M, N);
+    const long long units = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n()) * (long long)(K / kGroup);
+    long long P = workgroups ? workgroups : streamk_default_wgs(WFormat{4, kGroup}, tile.ns, units, K);
+    if (P > units) P = units;
+    return qmm_impl::wide_streamk_bytes(tile.ns, (int)P, false);
+}
+
+extern "C" int qmm_w4a16_g128_streamk(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                                      int M, int N, int K, int workgroups, void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    if (!A || !Wq || !scale || !bias || !C) return QMM_ERR_ARG;
+    if (M <= 0 || N <= 0 || K <= 0 || workgroups < 0) return QMM_ERR_ARG;
+    if (K % kGroup != 0 || M <= 64) return QMM_ERR_SHAPE;
+    if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
+    if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
+        return QMM_ERR_ALIGN;
+    const WFormat fmt{4, kGroup};
+    const W4A16Tile tile = w4a16_tile(M, N);
+    const long long units = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n()) * (long long)(K / kGroup);
+    long long P = workgroups ? workgroups : streamk_default_wgs(fmt, tile.ns, units, K);
+    if (workgroups && P > units) return QMM_ERR_SHAPE;
+    if (P > units) P = units;
+    if (P > INT_MAX / 2) return QMM_ERR_SIZE;
+    if (!workspace || workspace_bytes < qmm_impl::wide_streamk_bytes(tile.ns, (int)P, false)) return QMM_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return QMM_ERR_ALIGN;
+    const bool vec_c = (N % 4 == 0) && aligned(C, 8);
+    return hip_status(qmm_impl::launch_w4a16_wide(fmt, tile.ns, A, Wq, scale, bias, C, workspace, false, M, N, K, 0,
+                                                  1, vec_c, static_cast<hipStream_t>(stream), (int)P));
+}
+
+namespace {
 int gemv_m8(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 }  // namespace
 

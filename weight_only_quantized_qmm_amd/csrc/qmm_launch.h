@@ -85,9 +85,17 @@ inline int wide_wgs_per_cu(int variant, WFormat f = WFormat{4, 128})
 // Large-M kernel: the first full_tiles tiles (M-block fastest) unsplit into C, the
 // remaining ones in `split` near-equal group partitions into the planes of `part`
 // ([split][M][N], bf16 or (f32_part) fp32; unused when split = 1).
+// streamk = P > 0 instead runs the stream-K decomposition on P workgroups (near-equal
+// ranges of the (tile, 128-value block) units; full_tiles and split are ignored), with
+// `part` holding 2P tile slots (wide_streamk_bytes) and a fix-up launch after it.
 hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void *Wq, const void *scale,
                              const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
-                             int full_tiles, int split, bool vec_store, hipStream_t stream);
+                             int full_tiles, int split, bool vec_store, hipStream_t stream, int streamk = 0);
+
+inline size_t wide_streamk_bytes(int variant, int P, bool f32_part)
+{
+    return (size_t)2 * (size_t)P * (size_t)wide_rows(variant) * (size_t)kWideCols * (f32_part ? 4 : 2);
+}
 
 // Decode matrix-vector kernel (M <= 8): a partition of kp reduction values fits its A
 // staging when kp <= 10240 (at most 5 chunks of 32 per lane) and m8 * kp <= 30720

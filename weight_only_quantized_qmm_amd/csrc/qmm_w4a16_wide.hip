@@ -297,48 +297,34 @@ __device__ __forceinline__ void store4(char *base, bool f32, size_t e, int n, in
     }
 }
 
-// Work decomposition (one-dimensional grid of full_tiles + tail_tiles * split
-// workgroups): workgroup b < full_tiles computes tile b over the whole reduction and
-// writes C; the others compute tile full_tiles + q % tail_tiles (q = b - full_tiles)
-// over partition p = q / tail_tiles, the groups [floor(p*G/split), floor((p+1)*G/split)),
-// and write plane p of `part` (C itself when split = 1). With full_tiles = 0 this is the
-// plain split into `split` partitions (equal ones when split divides G).
+// Where a segment's results go: element (m, n) of the tile is stored at
+// base + ((m - r0) * ld + (n - c0)) elements, bf16 or (f32) fp32, rows m < M and
+// columns n < N only.
+struct Dest {
+    char *base;
+    size_t ld;
+    int r0, c0;
+    bool f32;
+    int vec;  // 8/16-byte stores where four columns are in range
+};
+
+// One segment: tile `tile` (M-block fastest) over the 128-value blocks [g_lo, g_hi) of
+// the reduction, from its first copy to its last store. Every wave of the workgroup
+// calls it with the same arguments.
 template <class CF>
-__global__ void __launch_bounds__(64 * CF::NW, CF::OCC)
-w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
-                  const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                  uint16_t *__restrict__ C, void *__restrict__ part, int M, int N, int K,
-                  int full_tiles, int tail_tiles, int split, int vec_store, int f32_part)
+__device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
+                                        const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias, int M,
+                                        int N, int K, int tile, int g_lo, int g_hi, const Dest &dst)
 {
     typedef CF GE;
     constexpr int MI = CF::MI, NJ = CF::NJ;
-    __shared__ __attribute__((aligned(1024))) Lds<CF> L;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int wm = wave / CF::NWN;  // row block of the wave (32*MI rows)
     const int wn = wave % CF::NWN;  // column block of the wave (32*NJ columns)
     const int G = K >> 7;                  // 128-value blocks
     const int GG = G * CF::SUB;            // scale/bias entries per row
-    const int b = blockIdx.x;
-    int tile, p, nparts;
-    if (b < full_tiles) {
-        tile = b;
-        p = 0;
-        nparts = 1;
-    } else {
-        const int q = b - full_tiles;
-        tile = full_tiles + q % tail_tiles;
-        p = q / tail_tiles;
-        nparts = split;
-    }
-    const int g_lo = (int)(((long long)p * G) / nparts);
-    const int g_hi = (int)(((long long)(p + 1) * G) / nparts);
-    const int gpp = g_hi - g_lo;  // >= 1: nparts <= G
-    // Destination: C for an unsplit tile; else plane p of `part`, bf16 or (f32_part) fp32.
-    const bool to_f32 = nparts > 1 && f32_part;
-    char *dst = nparts > 1 ? static_cast<char *>(part) + (size_t)p * (size_t)M * (size_t)N * (f32_part ? 4 : 2)
-                           : reinterpret_cast<char *>(C);
+    const int gpp = g_hi - g_lo;           // >= 1
     const int num_m = (M + GE::BM - 1) / GE::BM;
     const int m_idx = tile % num_m;
     const int n_idx = tile / num_m;
@@ -351,7 +337,7 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
     // Workgroups that run side by side on one XCD share rows of A; starting them at
     // different groups (within a window of ROT_GROUPS) spreads their simultaneous
     // reads of A over more L2 channels. The fp32 sums' order depends only on the tile
-    // and the partition.
+    // and the block range.
     c.rot = (n_idx % ROT_GROUPS) % gpp;
     c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
     c.Wq = reinterpret_cast<const char *>(Wq) + (size_t)n0 * (size_t)K * CF::BITS / 8;
@@ -418,7 +404,7 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nst = 2 * gpp;  // stages in the partition, even
+    const int nst = 2 * gpp;  // stages in the segment, even
     // Prologue: stage 0 (A, W, group 0's scale/bias) and stage 1 (A, W); wait for stage 0
     // and read its head.
     issue<CF, true>(c, 0, 0, 0);
@@ -460,7 +446,8 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
             });
         s3 = s3p;
     }
-    // No copy may still be writing LDS when the workgroup ends.
+    // No copy may still be writing LDS when the segment ends (the next segment, or the
+    // end of the workgroup, follows).
     QMM_WAIT_VMCNT(0);
 
     // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*32*MI + 32i + (lane % 32)
@@ -478,12 +465,156 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
                 const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
                 const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
                 const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
-                if (row_ok) store4(dst, to_f32, (size_t)m * (size_t)N + n, n, N, vec_store, v0, v1, v2, v3);
+                if (row_ok)
+                    store4(dst.base, dst.f32, (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0), n, N, dst.vec,
+                           v0, v1, v2, v3);
             }
         }
     }
 }
 
+// Work decomposition, one-dimensional grid.
+//   streamk == 0: full_tiles + tail_tiles * split workgroups. Workgroup b < full_tiles
+//     computes tile b over the whole reduction and writes C; the others compute tile
+//     full_tiles + q % tail_tiles (q = b - full_tiles) over partition p = q / tail_tiles,
+//     the blocks [floor(p*G/split), floor((p+1)*G/split)), and write plane p of `part`
+//     (C itself when split = 1). With full_tiles = 0 this is the plain split into
+//     `split` partitions (equal ones when split divides G).
+//   streamk == P > 0 (stream-K): the T*G (tile, block) units, tile-major, are cut into
+//     P near-equal ranges, workgroup w taking units [floor(w*U/P), floor((w+1)*U/P)).
+//     It walks them tile by tile: a tile it covers whole goes to C; the piece of a
+//     tile it shares with other workgroups goes to its own slot of `part` (slot 2w for
+//     its first tile, 2w+1 for its last; each a BM x 256 tile, row-major), which the
+//     fix-up kernel adds in workgroup order.
+template <class CF, bool SK>
+__global__ void __launch_bounds__(64 * CF::NW, CF::OCC)
+w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
+                  const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
+                  uint16_t *__restrict__ C, void *__restrict__ part, int M, int N, int K,
+                  int full_tiles, int tail_tiles, int split, int vec_store, int f32_part, int streamk)
+{
+    __shared__ __attribute__((aligned(1024))) Lds<CF> L;
+    const int G = K >> 7;
+    const int b = blockIdx.x;
+    if (!SK) {
+        int tile, p, nparts;
+        if (b < full_tiles) {
+            tile = b;
+            p = 0;
+            nparts = 1;
+        } else {
+            const int q = b - full_tiles;
+            tile = full_tiles + q % tail_tiles;
+            p = q / tail_tiles;
+            nparts = split;
+        }
+        const int g_lo = (int)(((long long)p * G) / nparts);
+        const int g_hi = (int)(((long long)(p + 1) * G) / nparts);
+        // C for an unsplit tile; else plane p of `part`, bf16 or (f32_part) fp32.
+        Dest d;
+        d.base = nparts > 1 ? static_cast<char *>(part) + (size_t)p * (size_t)M * (size_t)N * (f32_part ? 4 : 2)
+                            : reinterpret_cast<char *>(C);
+        d.ld = (size_t)N;
+        d.r0 = d.c0 = 0;
+        d.f32 = nparts > 1 && f32_part;
+        d.vec = vec_store;
+        segment<CF>(L, A, Wq, scale, bias, M, N, K, tile, g_lo, g_hi, d);
+        return;
+    }
+    const int P = streamk;
+    const int T = full_tiles + tail_tiles;  // every tile
+    const long long U = (long long)T * G;
+    const long long u0 = ((long long)b * U) / P;
+    const long long u1 = ((long long)(b + 1) * U) / P;
+    const int num_m = (M + CF::BM - 1) / CF::BM;
+    for (long long u = u0; u < u1;) {
+        const int tile = (int)(u / G);
+        const int g_lo = (int)(u - (long long)tile * G);
+        const int g_hi = (int)min((long long)G, u1 - (long long)tile * G);
+        Dest d;
+        if (g_lo == 0 && g_hi == G) {
+            d.base = reinterpret_cast<char *>(C);
+            d.ld = (size_t)N;
+            d.r0 = d.c0 = 0;
+            d.f32 = false;
+            d.vec = vec_store;
+        } else {
+            const size_t slot = 2 * (size_t)b + (u == u0 ? 0 : 1);
+            d.base = static_cast<char *>(part) + slot * (size_t)CF::BM * BN * (f32_part ? 4 : 2);
+            d.ld = BN;
+            d.r0 = (tile % num_m) * CF::BM;
+            d.c0 = (tile / num_m) * BN;
+            d.f32 = f32_part;
+            d.vec = 1;
+        }
+        if (u != u0) __syncthreads();  // every wave has left the previous segment's LDS
+        segment<CF>(L, A, Wq, scale, bias, M, N, K, tile, g_lo, g_hi, d);
+        u = (long long)tile * G + g_hi;
+    }
+}
+
+// Stream-K fix-up: workgroup (t, chunk) merges 2048 elements (8 rows of 256) of tile t if
+// the stream-K ranges split it. The workgroups that touch tile t are those whose unit
+// ranges meet [t*G, (t+1)*G); their pieces sit in slot 2w (when the tile is w's first) or
+// 2w+1 (its last), and are added in ascending w (ascending reduction order) in fp32,
+// with one cast to bf16 into C. A lane owns eight consecutive columns (16-byte loads of
+// bf16 slots, two of fp32 ones).
+template <int BM, typename T>
+__global__ void __launch_bounds__(256)
+streamk_fixup(const T *__restrict__ part, uint16_t *__restrict__ C, int M, int N, int G, int T_tiles, int P,
+              int vec)
+{
+    const int t = blockIdx.x;
+    const long long U = (long long)T_tiles * G;
+    const long long lo = (long long)t * G, hi = lo + G;  // the tile's units
+    // first workgroup whose range contains unit lo: the largest w with floor(w*U/P) <= lo
+    int w0 = (int)((lo * P) / U);
+    while (w0 + 1 < P && ((long long)(w0 + 1) * U) / P <= lo) ++w0;
+    while (w0 > 0 && ((long long)w0 * U) / P > lo) --w0;
+    int w1 = w0;  // last workgroup whose range starts before hi
+    while (w1 + 1 < P && ((long long)(w1 + 1) * U) / P < hi) ++w1;
+    const long long s0 = ((long long)w0 * U) / P, e0 = ((long long)(w0 + 1) * U) / P;
+    if (w0 == w1 && s0 <= lo && e0 >= hi) return;  // one workgroup covered it whole: already in C
+    const int num_m = (M + BM - 1) / BM;
+    const int idx = blockIdx.y * 256 + threadIdx.x;  // 8-column group of the tile
+    const int rr = idx >> 5, cc = 8 * (idx & 31);
+    const int m = (t % num_m) * BM + rr, n = (t / num_m) * 256 + cc;
+    if (rr >= BM || m >= M || n >= N) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int w = w0; w <= w1; ++w) {
+        const size_t slot = 2 * (size_t)w + ((((long long)w * U) / P >= lo) ? 0 : 1);
+        const T *src = part + slot * (size_t)BM * 256 + (size_t)rr * 256 + cc;
+        float v[8];
+        if constexpr (sizeof(T) == 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(src);
+            const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else {
+            const uint4 x = *reinterpret_cast<const uint4 *>(src);
+            const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf16_to_f32(wd[e] & 0xFFFFu);
+                v[2 * e + 1] = bf16_to_f32(wd[e] >> 16);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
+    }
+    uint16_t *dst = C + (size_t)m * N + n;
+    if (vec && n + 7 < N) {
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *reinterpret_cast<uint4 *>(dst) = o;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (n + e < N) dst[e] = (uint16_t)f32_to_bf16(acc[e]);
+    }
+}
 
 template <int BITS, int SUB>
 using CfgV0 = Cfg<1, 4, 2, BITS, SUB>;  // 128 x 256 tile, 4 waves of 128 x 64
@@ -493,23 +624,38 @@ using CfgV2 = Cfg<2, 8, 1, BITS, SUB>;  // 256 x 256 tile, 8 waves of 256 x 32
 template <class CF>
 void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
                 const uint16_t *bi, uint16_t *c, void *pt, int M, int N, int K, int full_tiles, int tail_tiles,
-                int split, int vec, int f32p)
+                int split, int vec, int f32p, int streamk)
 {
-    hipLaunchKernelGGL((w4a16_wide_kernel<CF>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt, M, N, K,
-                       full_tiles, tail_tiles, split, vec, f32p);
+    if (streamk == 0) {
+        hipLaunchKernelGGL((w4a16_wide_kernel<CF, false>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt,
+                           M, N, K, full_tiles, tail_tiles, split, vec, f32p, 0);
+    } else if constexpr (CF::BITS == 4 && CF::SUB == 1) {  // stream-K: the W4A16 g128 format only
+        hipLaunchKernelGGL((w4a16_wide_kernel<CF, true>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt,
+                           M, N, K, full_tiles, tail_tiles, split, vec, f32p, streamk);
+        const int T = full_tiles + tail_tiles;
+        const dim3 fgrid(T, CF::BM * 256 / (256 * 8));
+        // 16-byte stores into C need N % 8 == 0 and a 16-byte aligned C
+        const int cvec = (N % 8 == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0) ? 1 : 0;
+        if (f32p)
+            hipLaunchKernelGGL((streamk_fixup<CF::BM, float>), fgrid, dim3(256), 0, stream,
+                               static_cast<const float *>(pt), c, M, N, K >> 7, T, streamk, cvec);
+        else
+            hipLaunchKernelGGL((streamk_fixup<CF::BM, uint16_t>), fgrid, dim3(256), 0, stream,
+                               static_cast<const uint16_t *>(pt), c, M, N, K >> 7, T, streamk, cvec);
+    }
 }
 
 template <int BITS, int SUB>
 void launch_variant(int variant, dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w,
                     const uint16_t *sc, const uint16_t *bi, uint16_t *c, void *pt, int M, int N, int K,
-                    int full_tiles, int tail_tiles, int split, int vec, int f32p)
+                    int full_tiles, int tail_tiles, int split, int vec, int f32p, int streamk)
 {
     if (variant == 0)
         launch_cfg<CfgV0<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
-                                     f32p);
+                                     f32p, streamk);
     else
         launch_cfg<CfgV2<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
-                                     f32p);
+                                     f32p, streamk);
 }
 
 }  // namespace
@@ -519,15 +665,22 @@ namespace qmm_impl {
 // The per-lane copy offsets are 32-bit byte offsets within 256 rows of A: K < 2^22.
 hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void *Wq, const void *scale,
                              const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
-                             int full_tiles, int split, bool vec_store, hipStream_t stream)
+                             int full_tiles, int split, bool vec_store, hipStream_t stream, int streamk)
 {
     if (K >= (1 << 22) || (variant != 0 && variant != 2) || !format_supported(fmt)) return hipErrorInvalidValue;
     const int rows = wide_rows(variant);
     const int tiles = ((M + rows - 1) / rows) * ((N + BN - 1) / BN);
+    if (streamk < 0 || (streamk > 0 && (!part || (long long)streamk > (long long)tiles * (K / 128))))
+        return hipErrorInvalidValue;
+    if (streamk > 0 && (fmt.bits != 4 || fmt.group != 128)) return hipErrorInvalidValue;
+    if (streamk > 0) {
+        full_tiles = tiles;  // T = full_tiles + tail_tiles for the kernel
+        split = 1;
+    }
     if (full_tiles < 0 || full_tiles > tiles || split < 1 || split > K / 128) return hipErrorInvalidValue;
     if (split > 1 && !part) return hipErrorInvalidValue;
     const int tail_tiles = tiles - full_tiles;
-    const dim3 grid(full_tiles + tail_tiles * split);
+    const dim3 grid(streamk > 0 ? streamk : full_tiles + tail_tiles * split);
     const uint16_t *a = static_cast<const uint16_t *>(A);
     const uint32_t *w = static_cast<const uint32_t *>(Wq);
     const uint16_t *sc = static_cast<const uint16_t *>(scale);
@@ -539,7 +692,7 @@ hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void
 #define QMM_FMT(B_, S_)                                                                                          \
     if (fmt.bits == B_ && fmt.sub() == S_)                                                                       \
         launch_variant<B_, S_>(variant, grid, stream, a, w, sc, bi, c, part, M, N, K, full_tiles, tail_tiles,    \
-                               split, vec, f32p);
+                               split, vec, f32p, streamk);
     QMM_FMT(4, 1) QMM_FMT(4, 2) QMM_FMT(4, 4) QMM_FMT(8, 1) QMM_FMT(8, 2) QMM_FMT(8, 4)
 #undef QMM_FMT
     return hipGetLastError();

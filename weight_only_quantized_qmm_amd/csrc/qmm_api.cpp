@@ -39,14 +39,16 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // 128 rows) in one block row, so each weight is dequantised once per block.
 // Kernel by row count: the small-M kernel up to 64 rows; the large-M kernel with 128-row
 // tiles (two workgroups per CU) up to 128 rows, with 256-row tiles of eight 256 x 32 waves above.
-W4A16Tile w4a16_tile(int M, int N) {
+W4A16Tile w4a16_tile(int M, int N, int K) {
     W4A16Tile t;
     if (M <= 64) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         // 64-column tiles when 32-column ones would need more than one workgroup per CU
-        // (one workgroup of the small-M kernel fills a CU's wave slots).
-        t.ns = ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs ? 4 : 2;
+        // (one workgroup of the small-M kernel fills a CU's wave slots), and for 17..64 rows
+        // over a long reduction (K >= 4096), where each activation load then feeds twice
+        // the columns (split sweeps of o and down on MI355X: 5-15 % faster).
+        t.ns = (ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs || (M > 16 && K >= 4096)) ? 4 : 2;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.mt = M <= 128 ? 8 : 16;
@@ -144,7 +146,7 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
     if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
     const qmm_policy pol = policy ? *policy : QMM_POLICY_MI355X;
     if (!policy_ok(pol)) return QMM_ERR_ARG;
-    const W4A16Tile tile = w4a16_tile(M, N);
+    const W4A16Tile tile = w4a16_tile(M, N, K);
     const int tm = pol.tile_m > 0 ? pol.tile_m : tile.block_m();
     const int tn = pol.tile_n > 0 ? pol.tile_n : tile.block_n();
     const long long base = ceil_div(M, tm) * ceil_div(N, tn);
@@ -209,7 +211,7 @@ int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const 
     if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
         return QMM_ERR_ALIGN;
     const int G = K / kGroup;
-    const W4A16Tile tile = w4a16_tile(M, N);
+    const W4A16Tile tile = w4a16_tile(M, N, K);
     int full_tiles = 0;
     if (s == 0) {
         qmm_plan plan;
@@ -298,7 +300,7 @@ long long streamk_default_wgs(WFormat fmt, int variant, long long units, int K)
 extern "C" size_t qmm_streamk_workspace_bytes(int M, int N, int K, int workgroups)
 {
     if (M <= 64 || N <= 0 || K <= 0 || K % kGroup != 0 || workgroups < 0) return 0;
-    const W4A16Tile tile = w4a16_tile(M, N);
+    const W4A16Tile tile = w4a16_tile(M, N, K);
     const long long units = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n()) * (long long)(K / kGroup);
     long long P = workgroups ? workgroups : streamk_default_wgs(WFormat{4, kGroup}, tile.ns, units, K);
     if (P > units) P = units;
@@ -316,7 +318,7 @@ extern "C" int qmm_w4a16_g128_streamk(const void *A, const void *Wq, const void 
     if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
         return QMM_ERR_ALIGN;
     const WFormat fmt{4, kGroup};
-    const W4A16Tile tile = w4a16_tile(M, N);
+    const W4A16Tile tile = w4a16_tile(M, N, K);
     const long long units = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n()) * (long long)(K / kGroup);
     long long P = workgroups ? workgroups : streamk_default_wgs(fmt, tile.ns, units, K);
     if (workgroups && P > units) return QMM_ERR_SHAPE;

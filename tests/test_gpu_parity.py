@@ -767,3 +767,81 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for b, e in zip(bufs, eager):
             assert np.array_equal(host_bits(b[5]), e), "replay %d differs" % rep
+
+
+def test_graph_capture_other_entry_points():
+    """fp32 partials, another weight format, the matrix-vector path, stream-K, the dense
+    variant and split-KV attention also enqueue kernels only: a graph of all of them
+    replays to the eager bits, replay after replay."""
+    torch.manual_seed(0)
+    calls = []
+    # fp32 partial planes, small M split
+    d = syn.w4a16_inputs(48, 1000, 2560, seed=18000)
+    dv = w4a16_device(d)
+    C1 = torch.empty(48, 1000, dtype=torch.bfloat16, device="cuda")
+    ws1 = torch.empty(4 * 5 * 48 * 1000, dtype=torch.uint8, device="cuda")
+    calls.append((C1, lambda: q.qmm_w4a16_g128_f32p(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C1, 48, 1000, 2560,
+                                                    5, ws1)))
+    # W8A16 in groups of 32 on the large-M kernel, split
+    d8 = syn.wq_inputs(8, 32, 300, 520, 1024, seed=18001)
+    dv8 = w4a16_device(d8)
+    C2 = torch.empty(300, 520, dtype=torch.bfloat16, device="cuda")
+    ws2 = torch.empty(2 * 4 * 300 * 520, dtype=torch.uint8, device="cuda")
+    calls.append((C2, lambda: q.qmm_wna16(8, 32, q.QMM_PARTIAL_BF16, dv8["A"], dv8["Wq"], dv8["scale"], dv8["bias"],
+                                          C2, 300, 520, 1024, 4, ws2)))
+    # decode matrix-vector, split
+    dg = syn.w4a16_inputs(4, 2560, 9728, seed=18002)
+    dvg = w4a16_device(dg)
+    C3 = torch.empty(4, 2560, dtype=torch.bfloat16, device="cuda")
+    ws3 = torch.empty(2 * 4 * 4 * 2560, dtype=torch.uint8, device="cuda")
+    calls.append((C3, lambda: q.qmm_w4a16_gemv(dvg["A"], dvg["Wq"], dvg["scale"], dvg["bias"], C3, 4, 2560, 9728, 4,
+                                               ws3)))
+    # stream-K
+    ds = syn.w4a16_inputs(300, 520, 1024, seed=18003)
+    dvs = w4a16_device(ds)
+    C4 = torch.empty(300, 520, dtype=torch.bfloat16, device="cuda")
+    nb = q.qmm_streamk_workspace_bytes(300, 520, 1024, 7)
+    ws4 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    calls.append((C4, lambda: q.qmm_w4a16_g128_streamk(dvs["A"], dvs["Wq"], dvs["scale"], dvs["bias"], C4, 300, 520,
+                                                       1024, 7, ws4, nb)))
+    # dense variant, split
+    dd = syn.dense_inputs(64, 96, 2048, seed=18004)
+    Ad, Bd = dev_bf16(dd["A"]), dev_bf16(dd["B"])
+    C5 = torch.empty(64, 96, dtype=torch.bfloat16, device="cuda")
+    ws5 = torch.empty(4 * 6 * 64 * 96, dtype=torch.uint8, device="cuda")
+    calls.append((C5, lambda: q.qmm_bf16_splitk(Ad, Bd, C5, 64, 96, 2048, 6, ws5)))
+    # split-KV attention with the merge
+    da = syn.attn_inputs(2, 1, 32, 8, 1024, 128, [1000, 37], seed=18005)
+    Qa, Ka, Va = dev_bf16(da["Q"]), dev_bf16(da["K"]), dev_bf16(da["V"])
+    La = torch.from_numpy(da["lengths"]).cuda()
+    C6 = torch.empty(2, 1, 32, 128, dtype=torch.bfloat16, device="cuda")
+    ws6 = torch.empty(q.qmm_attn_decode_workspace_bytes(2, 1, 32, 4), dtype=torch.uint8, device="cuda")
+    calls.append((C6, lambda: q.qmm_attn_decode(Qa, Ka, Va, La, C6, 2, 1, 32, 8, 1024, 128, 0.088, 4, ws6)))
+
+    def step():
+        for _, fn in calls:
+            fn()
+
+    say("graph (other entry points): eager reference")
+    step()
+    torch.cuda.synchronize()
+    eager = [host_bits(c).copy() for c, _ in calls]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for c, _ in calls:
+            c.fill_(5.0)  # eager work between replays
+        torch.cuda.synchronize()
+        say("graph (other entry points): replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for (c, _), e in zip(calls, eager):
+            assert np.array_equal(host_bits(c), e), "replay %d differs" % rep

@@ -550,7 +550,7 @@ def main():
         pmc_run()
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import numpy as np  # noqa: F401
     import torch

@@ -12,7 +12,8 @@
  *
  *   q[n,k] = nibble (k mod 8) of word Wq[n][k/8], low bits first
  *            (the packed uint4 layout: eight 4-bit values per 32-bit word along K;
- *             the order inside a word is this build's stated reading).
+ *             tiny-llm's page prints no order inside a word; lowest field first is the
+ *             reading taken).
  *   w[n,k] = scale[n,g] * q[n,k] + bias[n,g],  g = k / 128
  *            (tiny-llm "Week 2 Day 7: Split-K Prefill", Task 2: the W4A16 g128
  *             loader and dequantizer; per-(row, 128-group) bf16 scale and bias.)

@@ -72,7 +72,9 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * tile_m / tile_n = 0 mean "the block tile of the kernel this library launches
  * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
  *
- * With tile_m = tile_n = 0 and M > 64 (the large-M kernel, T = base tiles, M-block
+ * The small-M kernel runs M <= 64, and M <= 128 when N*K <= 2^24 (its 16*mt x 32 or x 64
+ * tiles); the large-M kernel runs the rest (128 x 256 tiles up to M = 128, 256 x 256 above).
+ * With tile_m = tile_n = 0 and the large-M kernel (T = base tiles, M-block
  * fastest, num_m tiles per column of tiles) the rule fills the kernel's workgroup
  * slots, target_blocks times the workgroups one CU holds (2 for its 128-row tiles),
  * with partitions that may differ by one group (no divisibility step); below,

@@ -97,7 +97,9 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     assert 1 <= plan.s <= min(pol.cap, G)
     assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
     assert plan.workspace_bytes == (2 * plan.s * M * N if plan.s > 1 else 0)
-    if M > 64:  # the large-M kernel: slot-filling rule, two workgroups per CU for 128-row tiles
+    # the small-M kernel runs M <= 64, and M <= 128 with N*K <= 2^24 (64-row blocks)
+    assert (plan.block_n == 256) == (M > 64 and not (M <= 128 and N * K <= 1 << 24))
+    if plan.block_n == 256:  # the large-M kernel: slot-filling rule, two workgroups per CU for 128-row tiles
         slots = pol.target_blocks * (2 if plan.block_m == 128 else 1)
         num_m = -(-M // plan.block_m)
         assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
@@ -132,7 +134,7 @@ def test_wna16_plan_follows_the_rule_for_each_format(bits, group):
         plan = q.qmm_wna16_plan(bits, group, M, N, K)
         ref = q.qmm_splitk_plan(M, N, K)
         assert (plan.block_m, plan.block_n, plan.base_tiles) == (ref.block_m, ref.block_n, ref.base_tiles)
-        if M <= 64 or (bits, group) == (4, 128):
+        if plan.block_n != 256 or (bits, group) == (4, 128):
             assert (plan.s, plan.full_tiles, plan.grid_x) == (ref.s, ref.full_tiles, ref.grid_x), (name, M)
             continue
         wgs = 2 if plan.block_m == 128 and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024 else 1

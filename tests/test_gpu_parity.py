@@ -189,9 +189,13 @@ def test_streamk_matches_oracle(M, N, K, Ps):
     d = syn.w4a16_inputs(M, N, K, seed=17000 + M)
     ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
     dv = w4a16_device(d)
-    c1 = host_bits(run_w4a16(dv, M, N, K, 1))
     BM = 128 if M <= 128 else 256
     num_m, num_n, G = -(-M // BM), -(-N // 256), K // 128
+    # one workgroup per tile: every tile whole, the large-M kernel's unsplit decomposition
+    # (the same launch as s = 1 where the plan runs that kernel)
+    c1 = host_bits(run_streamk(dv, M, N, K, num_m * num_n))
+    if q.qmm_splitk_plan(M, N, K).block_n == 256:
+        assert np.array_equal(c1, host_bits(run_w4a16(dv, M, N, K, 1)))
     for P in Ps:
         Peff = P or max(1, min(num_m * num_n * G // min(4, G), 256 * (2 if BM == 128 else 1)))
         say("streamk M=%d N=%d K=%d P=%d" % (M, N, K, Peff))
@@ -236,8 +240,10 @@ def check_single_cast(bits, ref, min_equal, what):
     return frac
 
 
-F32P_CASES = [  # (M, N, K, explicit splits): small-M kernel, 128-row and 256-row large-M kernels
-    (48, 1000, 2560, (2, 5, 20)), (100, 1000, 2560, (4, 10)), (256, 520, 4096, (2, 8, 32))]
+F32P_CASES = [  # (M, N, K, explicit splits): small-M kernel (48 rows, and 100 rows in 64-row blocks),
+    # 128-row and 256-row large-M kernels
+    (48, 1000, 2560, (2, 5, 20)), (100, 1000, 2560, (4, 10)), (100, 7000, 2560, (4, 10)),
+    (256, 520, 4096, (2, 8, 32))]
 
 
 @pytest.mark.parametrize("M,N,K,splits", F32P_CASES)
@@ -536,9 +542,10 @@ def run_wna16(dv, bits, group, M, N, K, s, guard=0, f32p=False):
     return C
 
 
-# small-M kernel (M <= 64, ragged N), 128-row and 256-row large-M kernels
+# small-M kernel (M <= 64, ragged N; 100 rows in 64-row blocks), 128-row and 256-row
+# large-M kernels
 FORMAT_SHAPES = [(1, 1000, 2560, 4), (16, 1024, 2560, 5), (48, 1000, 1024, 2), (100, 1000, 2560, 4),
-                 (300, 520, 1024, 8)]
+                 (100, 7000, 2560, 4), (300, 520, 1024, 8)]
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)
@@ -557,21 +564,22 @@ def test_wna16_formats_match_oracle(bits, group, M, N, K, s):
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)
-@pytest.mark.parametrize("M", [16, 100, 300])
-def test_wna16_one_hot_rows_exact(bits, group, M):
+@pytest.mark.parametrize("M,N,K", [(16, 300, 1024), (100, 300, 1024), (100, 7000, 2560), (300, 300, 1024)])
+def test_wna16_one_hot_rows_exact(bits, group, M, N, K):
     """A row with a single 1 at k picks w[:, k] = scale*q + bias (exact in fp32, one
     rounding to bf16): every split gives the correctly rounded weights, bit for bit.
-    This pins the code order, the group index and the partition bounds on the GPU."""
-    N, K = 300, 1024
-    d = syn.wq_inputs(bits, group, M, N, K, seed=12000 + M + bits + group)
-    rng = np.random.default_rng(12000 + M)
+    This pins the code order, the group index and the partition bounds on the GPU
+    (small-M kernel; 128-row and 256-row large-M kernels)."""
+    d = syn.wq_inputs(bits, group, M, N, K, seed=12000 + M + N + bits + group)
+    rng = np.random.default_rng(12000 + M + N)
     ks = rng.integers(0, K, M)
     A = np.zeros((M, K), dtype=np.uint16)
     A[np.arange(M), ks] = 0x3F80
     d["A"] = A
     ref_bits = oracle.bf16_round_array(oracle.qmm_wq(bits, group, A, d["Wq"], d["scale"], d["bias"], M, N, K))
     dv = w4a16_device(d)
-    for s in (1, 2, 8):
+    G = K // 128
+    for s in (1, 2, max(x for x in range(1, 9) if G % x == 0)):
         say("wna16 one-hot bits=%d group=%d M=%d s=%d" % (bits, group, M, s))
         got = host_bits(run_wna16(dv, bits, group, M, N, K, s))
         assert np.array_equal(got, ref_bits), "s=%d: %d of %d differ" % (s, int((got != ref_bits).sum()), got.size)

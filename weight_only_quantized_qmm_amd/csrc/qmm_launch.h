@@ -7,9 +7,10 @@
 
 namespace qmm_impl {
 
-// Which W4A16 kernel runs an M-row problem, and the output tile of one workgroup.
-//   SKINNY (M <= 64): a (16*mt) x (16*ns) tile, ns 2 or 4, up to 16 waves splitting its reduction;
-//   WIDE   (M > 64) : a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variant 2).
+// Which W4A16 kernel runs a problem, and the output tile of one workgroup.
+//   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x (16*ns) tile, ns 2 or 4,
+//          up to 16 waves splitting its reduction;
+//   WIDE   (otherwise): a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variant 2).
 enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
 
 struct W4A16Tile {

@@ -73,10 +73,14 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
  *
  * The small-M kernel runs M <= 64, and M <= 128 when N*K <= 2^24 (its 16*mt x 32 or x 64
- * tiles); the large-M kernel runs the rest (128 x 256 tiles up to M = 128, 256 x 256 above).
+ * tiles); the large-M kernel runs the rest, with 128 x 256 tiles up to M = 128 and, above,
+ * 128 x 256 or 256 x 256 tiles, whichever has the shorter estimated critical path: rounds of
+ * target_blocks workgroups times the 128 x 256 x 128 blocks each computes (a 256-row tile
+ * counts two), plus half a block per partition of a split tail.
  * With tile_m = tile_n = 0 and the large-M kernel (T = base tiles, M-block
  * fastest, num_m tiles per column of tiles) the rule fills the kernel's workgroup
- * slots, target_blocks times the workgroups one CU holds (2 for its 128-row tiles),
+ * slots, target_blocks times the workgroups one CU holds (2 for its 128-row tiles up to
+ * M = 128, else 1),
  * with partitions that may differ by one group (no divisibility step); below,
  * target_blocks stands for that slot count:
  *     smax = min(cap, K/128, floor(K / min_k_per_split))

@@ -100,7 +100,8 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     # the small-M kernel runs M <= 64, and M <= 128 with N*K <= 2^24 (64-row blocks)
     assert (plan.block_n == 256) == (M > 64 and not (M <= 128 and N * K <= 1 << 24))
     if plan.block_n == 256:  # the large-M kernel: slot-filling rule, two workgroups per CU for 128-row tiles
-        slots = pol.target_blocks * (2 if plan.block_m == 128 else 1)
+        # two 128-row workgroups per CU up to M = 128; above, either tile counts one per CU
+        slots = pol.target_blocks * (2 if plan.block_m == 128 and M <= 128 else 1)
         num_m = -(-M // plan.block_m)
         assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
             tiles, num_m, K, slots, pol.cap, pol.min_k_per_split)
@@ -137,7 +138,7 @@ def test_wna16_plan_follows_the_rule_for_each_format(bits, group):
         if plan.block_n != 256 or (bits, group) == (4, 128):
             assert (plan.s, plan.full_tiles, plan.grid_x) == (ref.s, ref.full_tiles, ref.grid_x), (name, M)
             continue
-        wgs = 2 if plan.block_m == 128 and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024 else 1
+        wgs = 2 if plan.block_m == 128 and M <= 128 and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024 else 1
         tiles = plan.base_tiles
         num_m = -(-M // plan.block_m)
         assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
@@ -149,6 +150,34 @@ def test_wna16_plan_lds_budget():
     two = [f for f in FORMATS if 2 * _wide_lds_bytes(128, *f) <= 160 * 1024]
     assert two == [(4, 64), (4, 128)]
     assert max(_wide_lds_bytes(256, *f) for f in FORMATS) <= 160 * 1024
+
+
+def _wide_cost(T, rows, s, full, G):
+    # critical path in 128 x 256 x 128 blocks over rounds of 256 workgroups, plus half a
+    # block per partition of a split
+    t = -(-full // 256) * G * rows / 128
+    if T - full > 0 and s > 1:
+        t += -(-((T - full) * s) // 256) * -(-G // s) * rows / 128 + 0.5 * s
+    return t
+
+
+@pytest.mark.parametrize("M,N,K", [(M, N, K) for M, N, K in ALL_SHAPES if M > 128])
+def test_large_m_variant_choice(M, N, K):
+    pol = q.policy_preset("QMM_POLICY_MI355X")
+    plan = q.qmm_splitk_plan(M, N, K)
+    G = K // 128
+    cost = {}
+    for rows in (128, 256):
+        T = -(-M // rows) * -(-N // 256)
+        s, full = opolicy.fill_decomposition(T, -(-M // rows), K, pol.target_blocks, pol.cap, pol.min_k_per_split)
+        cost[rows] = _wide_cost(T, rows, s, full, G)
+    assert plan.block_m == (128 if cost[128] < cost[256] else 256), (cost, plan.block_m)
+
+
+def test_large_m_variant_on_the_sweep():
+    # q and k/v at M = 2048 take 128-row tiles, the other projections 256-row tiles
+    got = {n: q.qmm_splitk_plan(M, N, K).block_m for n, M, N, K, _ in syn.projection_sweep() if M == 2048}
+    assert got == {"q": 128, "k": 128, "v": 128, "o": 256, "gate": 256, "up": 256, "down": 256}
 
 
 def test_fill_decomposition_cases():

@@ -35,13 +35,76 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
+// The large-M kernel's decomposition under a kernel-tile policy: (s, full_tiles).
+struct Decomp {
+    int s;
+    int full_tiles;
+};
+
+Decomp wide_rule(long long T, long long num_m, int G, int K, long long target, const qmm_policy &pol) {
+    long long smax = pol.cap;
+    if (G < smax) smax = G;
+    const long long by_k = K / pol.min_k_per_split;
+    if (by_k < smax) smax = by_k;
+    Decomp d = {1, (int)T};
+    if (smax <= 1 || target <= 0) return d;
+    if (T >= target) {
+        long long full = (T / target) * target;
+        full -= full % num_m;
+        const long long tail = T - full;
+        if (tail == 0) return d;
+        long long s = target / tail;
+        if (smax < s) s = smax;
+        if (s <= 1) return d;
+        d.s = (int)s;
+        d.full_tiles = (int)full;
+        return d;
+    }
+    long long s = target / T;
+    if (smax < s) s = smax;
+    if (s <= 1) return d;
+    d.s = (int)s;
+    d.full_tiles = 0;
+    return d;
+}
+
+// Critical path of a large-M decomposition of T tiles of `rows` rows (one workgroup per
+// CU, the unsplit rounds first, then the split tail) in units of one 128-row x 256-column x
+// 128-value block, plus half a unit per partition of a split for its planes and reduce.
+double wide_cost(long long T, int rows, const Decomp &d, int G)
+{
+    const double blk = rows / 128.0;
+    const long long full = d.full_tiles, tail = T - full;
+    double t = (double)ceil_div(full, kCUs) * G * blk;
+    if (tail > 0 && d.s > 1) t += (double)ceil_div(tail * d.s, kCUs) * ceil_div(G, d.s) * blk + 0.5 * d.s;
+    return t;
+}
+
+// Large-M variant for M > 128: 256-row tiles (variant 2) or 128-row tiles (variant 0),
+// each with one workgroup per CU, under the MI355X preset's split rule; the smaller
+// critical path wins, ties to 256-row tiles. On the Qwen3-4B shapes at M = 2048 this
+// takes 128-row tiles for q (256 tiles, no split) and k, v (1024 workgroups in four
+// partitions instead of 320 in five, with a third of the CUs idle in the last round),
+// which tile sweeps on MI355X measured 11-12 % faster, and 256-row tiles elsewhere.
+int wide_variant(int M, int N, int K)
+{
+    if (M <= 128) return 0;
+    const qmm_policy &pol = QMM_POLICY_MI355X;
+    const int G = K / kGroup;
+    const long long T2 = ceil_div(M, 256) * ceil_div(N, 256), T0 = ceil_div(M, 128) * ceil_div(N, 256);
+    const Decomp d2 = wide_rule(T2, ceil_div(M, 256), G, K, pol.target_blocks, pol);
+    const Decomp d0 = wide_rule(T0, ceil_div(M, 128), G, K, pol.target_blocks, pol);
+    return wide_cost(T0, 128, d0, G) < wide_cost(T2, 256, d2, G) ? 0 : 2;
+}
+
 // Kernel and block tile for an (M, N, K) problem. The small-M kernel takes up to 64 rows
 // in one block row, and 65..128 rows in 64-row blocks when the packed weights are at
 // most 8 MB (N*K <= 2^24): there the large-M kernel has too few 256-column tiles and must
 // split deeply, while reading the weights twice costs less (split sweeps of the Qwen3-4B
 // q, k and v projections at M = 128 on MI355X: 25-45 % faster; gate, up and down stay on
 // the large-M kernel). Otherwise the large-M kernel: 128-row tiles (two workgroups per CU)
-// up to 128 rows, 256-row tiles of eight 256 x 32 waves above.
+// up to 128 rows; above, 128-row tiles or 256-row tiles of eight 256 x 32 waves, as
+// wide_variant picks.
 W4A16Tile w4a16_tile(int M, int N, int K) {
     W4A16Tile t;
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
@@ -54,8 +117,8 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
         t.ns = (ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs || (M > 16 && K >= 4096)) ? 4 : 2;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
-        t.mt = M <= 128 ? 8 : 16;
-        t.ns = M <= 128 ? 0 : 2;
+        t.ns = wide_variant(M, N, K);
+        t.mt = t.ns == 0 ? 8 : 16;
     }
     return t;
 }
@@ -106,39 +169,6 @@ int split_rule(long long base, int G, int K, const qmm_policy &pol) {
     return s < 1 ? 1 : (int)s;
 }
 
-// The large-M kernel's decomposition under a kernel-tile policy: (s, full_tiles).
-struct Decomp {
-    int s;
-    int full_tiles;
-};
-
-Decomp wide_rule(long long T, long long num_m, int G, int K, long long target, const qmm_policy &pol) {
-    long long smax = pol.cap;
-    if (G < smax) smax = G;
-    const long long by_k = K / pol.min_k_per_split;
-    if (by_k < smax) smax = by_k;
-    Decomp d = {1, (int)T};
-    if (smax <= 1 || target <= 0) return d;
-    if (T >= target) {
-        long long full = (T / target) * target;
-        full -= full % num_m;
-        const long long tail = T - full;
-        if (tail == 0) return d;
-        long long s = target / tail;
-        if (smax < s) s = smax;
-        if (s <= 1) return d;
-        d.s = (int)s;
-        d.full_tiles = (int)full;
-        return d;
-    }
-    long long s = target / T;
-    if (smax < s) s = smax;
-    if (s <= 1) return d;
-    d.s = (int)s;
-    d.full_tiles = 0;
-    return d;
-}
-
 bool policy_ok(const qmm_policy &p) {
     return p.tile_m >= 0 && p.tile_n >= 0 && p.target_blocks >= 0 && p.cap >= 1 && p.min_k_per_split >= 1;
 }
@@ -166,8 +196,10 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
     const long long kernel_tiles = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n());
     Decomp d;
     if (tile.kind == qmm_impl::W4A16_WIDE && pol.tile_m == 0 && pol.tile_n == 0) {
-        // slots: target_blocks times the workgroups of this kernel one CU holds
-        const long long slots = (long long)pol.target_blocks * qmm_impl::wide_wgs_per_cu(tile.ns, fmt);
+        // slots: target_blocks times the workgroups of this kernel one CU holds; 128-row
+        // tiles above M = 128 count one per CU, as the variant choice does
+        const long long slots =
+            (long long)pol.target_blocks * (M > 128 ? 1 : qmm_impl::wide_wgs_per_cu(tile.ns, fmt));
         d = wide_rule(kernel_tiles, ceil_div(M, tile.block_m()), G, K, slots, pol);
     } else {
         d.s = split_rule(base, G, K, pol);

@@ -398,8 +398,8 @@ def summarize_pmc(fetch_dir, write_dir, commands):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="CPU-baseline sample budget")
     ap.add_argument("--no-per-shape", action="store_true")
@@ -468,10 +468,16 @@ def graph_of(torch, fn):
     return g
 
 
-def time_graph(torch, g, reps=5):
-    """Median seconds of one replay."""
-    g.replay()
-    torch.cuda.synchronize()
+def time_graph(torch, g, reps=5, warm_s=0.03):
+    """Median seconds of one replay, after replays for at least warm_s seconds: after an
+    idle gap (buffer set-up on the host) the first few milliseconds of work run several
+    per cent slower while the shader clock ramps up."""
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -36,11 +36,14 @@ inline bool format_supported(WFormat f)
 }
 
 // Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups
-// (128-value blocks).
+// (128-value blocks). Each wave stages the activations of its round in LDS, 4 KB per group
+// and 16-row tile, so waves * gpw * mt <= 40 (160 KB).
 struct SkinnyShape {
     int waves;  // waves per workgroup, each taking every waves-th group of the partition
     int gpw;    // groups whose loads one wave issues together
 };
+
+constexpr int kSkinnyStageUnits = 40;  // 4 KB staging units per workgroup
 
 inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4)
 {
@@ -51,6 +54,10 @@ inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4)
     sh.waves = gpp < max_waves ? gpp : max_waves;
     const int per_wave = (gpp + sh.waves - 1) / sh.waves;
     sh.gpw = per_wave < max_gpw ? per_wave : max_gpw;
+    while (sh.waves * sh.gpw * mt > kSkinnyStageUnits) {
+        if (sh.gpw > 1) --sh.gpw;
+        else --sh.waves;
+    }
     return sh;
 }
 

@@ -135,7 +135,7 @@ W4A16Tile wide_tile(int M) {
 hipError_t dispatch_skinny(WFormat fmt, const W4A16Tile &tile, const void *A, const void *Wq, const void *scale,
                            const void *bias, void *out, bool f32_part, int M, int N, int K, int s, bool vec,
                            hipStream_t st) {
-    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s, fmt.bits);
+    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s, fmt.bits, fmt.sub());
     return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part,
                                          M, N, K, s, vec, st);
 }

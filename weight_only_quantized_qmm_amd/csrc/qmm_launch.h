@@ -35,17 +35,26 @@ inline bool format_supported(WFormat f)
     return (f.bits == 4 || f.bits == 8) && (f.group == 32 || f.group == 64 || f.group == 128);
 }
 
+constexpr int kLdsPerCU = 160 * 1024;  // LDS bytes of one CU (and the most one workgroup may take)
+
 // Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups
-// (128-value blocks). Each wave stages the activations of its round in LDS, 4 KB per group
-// and 16-row tile, so waves * gpw * mt <= 40 (160 KB).
+// (128-value blocks). A wave stages a round's activations in LDS (4 KB per group and 16-row
+// tile) and its scale/bias entries (two dword arrays of 16*ns rows x gpw*sub entries, each
+// rounded up to 64); the workgroup's LDS is at most 160 KB.
 struct SkinnyShape {
     int waves;  // waves per workgroup, each taking every waves-th group of the partition
     int gpw;    // groups whose loads one wave issues together
 };
 
-constexpr int kSkinnyStageUnits = 40;  // 4 KB staging units per workgroup
+inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub)
+{
+    const size_t ew = (size_t)16 * ns * gpw * sub;
+    const size_t stage = (size_t)waves * gpw * mt * 4096 + (size_t)waves * 2 * ((ew + 63) & ~(size_t)63) * 4;
+    const size_t sums = (size_t)waves * mt * ns * 1024;
+    return stage > sums ? stage : sums;
+}
 
-inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4)
+inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4, int sub = 1)
 {
     const int max_waves = (mt == 1 && ns == 2) ? 16 : 8;
     int max_gpw = ns == 4 ? (mt == 1 ? 3 : mt == 2 ? 2 : 1) : (mt == 4 ? 2 : 3);
@@ -54,7 +63,7 @@ inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4)
     sh.waves = gpp < max_waves ? gpp : max_waves;
     const int per_wave = (gpp + sh.waves - 1) / sh.waves;
     sh.gpw = per_wave < max_gpw ? per_wave : max_gpw;
-    while (sh.waves * sh.gpw * mt > kSkinnyStageUnits) {
+    while (skinny_lds_bytes(mt, ns, sh.waves, sh.gpw, sub) > (size_t)kLdsPerCU) {
         if (sh.gpw > 1) --sh.gpw;
         else --sh.waves;
     }
@@ -79,7 +88,6 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, 
 // slots of A, 64 values per row, and of W, 64 codes per row, and two scale/bias slots of
 // one 128-value block); workgroups one CU holds (160 KB of LDS).
 constexpr int kWideCols = 256;
-constexpr int kLdsPerCU = 160 * 1024;
 inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
 constexpr int wide_lds_bytes(int rows, int bits, int sub)
 {

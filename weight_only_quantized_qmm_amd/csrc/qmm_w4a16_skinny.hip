@@ -61,6 +61,13 @@ __device__ __forceinline__ void copy16(uint32_t lds_off, uint32_t voff, const vo
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+// The same for 2 bytes per lane (global_load_lds_ushort), zero-extended into the dword at
+// LDS byte lds_off + 4*i.
+__device__ __forceinline__ void copy2(uint32_t lds_off, uint32_t voff, const void *sbase)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds_off), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int BITS, int MT, int NS, int GPW, int MAXW>
@@ -90,14 +97,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const int n_w = (gpp - wave + waves - 1) / waves;
 
     const uint4 *wptr[NS];
-    const uint16_t *sptr[NS];
-    const uint16_t *bptr[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const int n = min(n_blk + 16 * j + r, N - 1);  // rows past N read row N-1, never stored
         wptr[j] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K * BITS / 32)) + WV * slot;
-        sptr[j] = scale + (size_t)n * GG + (slot >> (2 - sub_shift));
-        bptr[j] = bias + (size_t)n * GG + (slot >> (2 - sub_shift));
     }
     // Activation copies: copy c (0 .. 4*MT-1) of a group fills staging rows 4c .. 4c+3; lane i
     // lands at row 4c + i/16, stored chunk i%16, so it fetches chunk (i%16) ^ (row%16) of the
@@ -117,6 +120,18 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 #pragma unroll
     for (int t = 0; t < 4; ++t) a_rd[t] = (uint32_t)(r * 256 + 16 * ((4 * slot + t) ^ r));
 
+    // Scale/bias: each round also copies, next to its activations, the scale and bias
+    // entries its groups need into the wave's own dword arrays [16*NS rows][GPW*SUB] (SUB =
+    // entries per 128-value block): entry (row, q, e) at row*GPW*SUB + q*SUB + e, the bias
+    // array AW dwords (whole copies) after the scale array. One copy moves 64 entries;
+    // per-group loads of 16 rows each would touch four times the cache lines.
+    const int RW = GPW << sub_shift;            // dwords per row of a wave's arrays
+    const int EW = 16 * NS * RW;                // entries per array
+    const int ncp = (EW + 63) >> 6;             // copies per array and round
+    const int AW = ncp << 6;
+    uint32_t *sbw = reinterpret_cast<uint32_t *>(smem + (size_t)waves * GPW * ABYTES) + (size_t)wave * 2 * AW;
+    const uint32_t sbw_lds = lds_addr(sbw);
+    const int sub_e = slot >> (2 - sub_shift);  // the lane's entry within a block
     f32x4 acc[MT][NS];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -128,13 +143,27 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         uint4 wv[GPW][NS][WV];
         uint32_t sc[GPW][NS], bi[GPW][NS];
         // Issue every load of the round before the first use: the activation copies into
-        // the staging slots, then the weights and scale/bias into registers.
+        // the staging slots, the scale/bias copies, then the weights into registers.
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;  // uniform across the wave
             const char *Ag = Abase + (size_t)(g0 + wave + waves * (base + q)) * 256;
 #pragma unroll
             for (int c = 0; c < 4 * MT; ++c) copy16(stage_lds + (uint32_t)(q * ABYTES + 1024 * c), a_voff[c], Ag);
+        }
+        {
+            const int nq = min(GPW, n_w - base);  // groups of this round (>= 1)
+            for (int c = 0; c < ncp; ++c) {
+                const int e = min(64 * c + lane, EW - 1);  // past the array: re-read its last entry
+                const int row_e = (e >> sub_shift) / GPW;  // = e / RW
+                const int rem = e - row_e * RW;
+                const int row = min(row_e, N - 1 - n_blk);  // rows past N re-read row N-1 (never used)
+                const int q = min(rem >> sub_shift, nq - 1);  // slots past the round re-read its last group
+                const int g = g0 + wave + waves * (base + q);
+                const uint32_t voff = 2u * (uint32_t)(row * GG + (g << sub_shift) + (rem & ((1 << sub_shift) - 1)));
+                copy2(sbw_lds + 256u * (uint32_t)c, voff, scale + (size_t)n_blk * GG);
+                copy2(sbw_lds + 4u * (uint32_t)AW + 256u * (uint32_t)c, voff, bias + (size_t)n_blk * GG);
+            }
         }
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
@@ -144,8 +173,6 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             for (int j = 0; j < NS; ++j) {
 #pragma unroll
                 for (int u = 0; u < WV; ++u) wv[q][j][u] = wptr[j][4 * WV * g + u];
-                sc[q][j] = sptr[j][g << sub_shift];
-                bi[q][j] = bptr[j][g << sub_shift];
             }
         }
         // Without the scheduling fence the compiler sinks each load next to its first use,
@@ -153,6 +180,15 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         // the wave waits for all of its loads itself before it reads the staging slots.
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < GPW; ++q) {
+            if (base + q >= n_w) break;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                sc[q][j] = sbw[(16 * j + r) * RW + (q << sub_shift) + sub_e];
+                bi[q][j] = sbw[AW + (16 * j + r) * RW + (q << sub_shift) + sub_e];
+            }
+        }
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;  // uniform across the wave
@@ -232,9 +268,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
 {
     const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
     const int gpp = (K / 128) / s;
-    const size_t stage = (size_t)waves * GPW * MT * 16 * 256;
-    const size_t sums = (size_t)waves * MT * NS * 64 * 16;
-    const size_t lds = stage > sums ? stage : sums;
+    const size_t lds = qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
     if (waves > MAXW || lds > (size_t)qmm_impl::kLdsPerCU) return hipErrorInvalidValue;
     // the activation copies take 32-bit byte offsets into A
     if ((size_t)M * (size_t)K * 2 >= ((size_t)1 << 32)) return hipErrorInvalidValue;
@@ -272,6 +306,8 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, 
     QMM_CFG(4, 1, 4, 1, 8) QMM_CFG(4, 1, 4, 2, 8) QMM_CFG(4, 1, 4, 3, 8)
     QMM_CFG(4, 2, 4, 1, 8) QMM_CFG(4, 2, 4, 2, 8)
     QMM_CFG(4, 4, 4, 1, 8)
+    QMM_CFG(4, 1, 1, 1, 16) QMM_CFG(4, 1, 1, 2, 16) QMM_CFG(4, 1, 1, 3, 16) QMM_CFG(4, 1, 1, 4, 16)
+    QMM_CFG(4, 1, 2, 4, 16) QMM_CFG(4, 1, 4, 4, 8) QMM_CFG(4, 2, 4, 3, 8) QMM_CFG(4, 4, 4, 2, 8)
     QMM_CFG(8, 1, 2, 1, 16) QMM_CFG(8, 1, 2, 2, 16)
     QMM_CFG(8, 2, 2, 1, 8) QMM_CFG(8, 2, 2, 2, 8)
     QMM_CFG(8, 4, 2, 1, 8)

@@ -108,11 +108,14 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         assert plan.full_tiles % num_m == 0 or plan.full_tiles == tiles
         assert plan.grid_x == plan.full_tiles + (tiles - plan.full_tiles) * plan.s
         assert plan.grid_y == 1 and plan.grid_z == 1
-    else:  # the page's rule over the kernel's tile
+    else:  # the page's rule over the kernel's tile; partitions of at least 2048 values up to M = 32
         assert G % plan.s == 0
+        # 16-column tiles for up to 16 rows over at most 2^24 weights
+        assert (plan.block_n == 16) == (M <= 16 and N * K <= 1 << 24)
+        min_k = max(pol.min_k_per_split, 2048) if M <= 32 else pol.min_k_per_split
         assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.block_n,
                                              target=pol.target_blocks, cap=pol.cap,
-                                             min_k_per_split=pol.min_k_per_split)
+                                             min_k_per_split=min_k)
         assert plan.grid_z == plan.s
         assert plan.grid_x * plan.grid_y == tiles
         assert plan.full_tiles == (tiles if plan.s == 1 else 0)

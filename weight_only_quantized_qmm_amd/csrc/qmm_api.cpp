@@ -30,6 +30,7 @@ namespace {
 constexpr int kGroup = 128;
 constexpr int kGranule = 32;
 constexpr int kCUs = 256;  // MI355X compute units
+constexpr int kSkinnyMinK = 2048;  // shortest partition of the small-M kernel up to 32 rows (preset)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -110,11 +111,20 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+        // Up to 16 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
+        // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o at M = 16 on
+        // MI355X: 20-30 % faster than split 32-column tiles, whose second pass costs more
+        // than the spread saves).
+        if (M <= 16 && (long long)N * K <= (1LL << 24)) {
+            t.ns = 1;
+            return t;
+        }
         // 64-column tiles when 32-column ones would need more than one workgroup per CU
         // (one workgroup of the small-M kernel fills a CU's wave slots), and for 17..64 rows
-        // over a long reduction (K >= 4096), where each activation load then feeds twice
-        // the columns (split sweeps of o and down on MI355X: 5-15 % faster).
-        t.ns = (ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs || (M > 16 && K >= 4096)) ? 4 : 2;
+        // over a long reduction (K >= 8192), where each staged activation group then feeds
+        // twice the columns (config sweeps on MI355X: down at M = 32, 64 faster with 64
+        // columns, o (K = 4096) with 32).
+        t.ns = (ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs || (M > 16 && K >= 8192)) ? 4 : 2;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.ns = wide_variant(M, N, K);
@@ -202,7 +212,14 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
             (long long)pol.target_blocks * (M > 128 ? 1 : qmm_impl::wide_wgs_per_cu(tile.ns, fmt));
         d = wide_rule(kernel_tiles, ceil_div(M, tile.block_m()), G, K, slots, pol);
     } else {
-        d.s = split_rule(base, G, K, pol);
+        qmm_policy p = pol;
+        // The small-M kernel under the preset's own tiles, up to 32 rows: a partition shorter
+        // than kSkinnyMinK reduction values saves less than the second pass costs (a launch
+        // and a round trip through HBM, about 3 us on MI355X).
+        if (tile.kind == qmm_impl::W4A16_SKINNY && pol.tile_m == 0 && pol.tile_n == 0 && M <= 32 &&
+            p.min_k_per_split < kSkinnyMinK)
+            p.min_k_per_split = kSkinnyMinK;
+        d.s = split_rule(base, G, K, p);
         d.full_tiles = d.s == 1 ? (int)kernel_tiles : 0;
     }
     const int s = d.s;

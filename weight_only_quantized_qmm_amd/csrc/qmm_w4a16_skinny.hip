@@ -284,12 +284,12 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
 
 namespace qmm_impl {
 
-// The host picks (mt, ns, gpw, waves) with SkinnyShape (qmm_launch.h). 32-column tiles
-// (ns 2): mt 1 with up to 16 waves and gpw <= 3; mt 2 with up to 8 waves and gpw <= 3;
-// mt 4 with up to 8 waves and gpw <= 2. 64-column tiles (ns 4), used when the 32-column
-// grid would not fit on the GPU in one round: up to 8 waves, gpw <= 3, 2, 1 for mt 1, 2,
-// 4 (register budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one
-// group less per round where the 4-bit limit is above one.
+// The host picks (mt, ns, gpw, waves) with skinny_shape (qmm_launch.h); these are the
+// configurations it can return: 16-column tiles (ns 1, mt 1) with up to 12 waves and gpw <= 3;
+// 32-column tiles (ns 2) with up to 16 waves (mt 1) or 8 (mt 2, 4) and gpw <= 3, 3, 2;
+// 64-column tiles (ns 4) with up to 8 waves and gpw <= 2, 2, 1 for mt 1, 2, 4 (register
+// budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one group less per
+// round where the 4-bit limit is above one.
 hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
                                const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
                                int s, bool vec_store, hipStream_t stream)
@@ -300,18 +300,18 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, 
     if (fmt.bits == B_ && mt == MT_ && ns == NS_ && gpw == GPW_)                                               \
         return launch_cfg<B_, MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, s, sub_shift,  \
                                                      waves, vec_store, stream);
+    QMM_CFG(4, 1, 1, 1, 16) QMM_CFG(4, 1, 1, 2, 16) QMM_CFG(4, 1, 1, 3, 16)
     QMM_CFG(4, 1, 2, 1, 16) QMM_CFG(4, 1, 2, 2, 16) QMM_CFG(4, 1, 2, 3, 16)
     QMM_CFG(4, 2, 2, 1, 8) QMM_CFG(4, 2, 2, 2, 8) QMM_CFG(4, 2, 2, 3, 8)
     QMM_CFG(4, 4, 2, 1, 8) QMM_CFG(4, 4, 2, 2, 8)
-    QMM_CFG(4, 1, 4, 1, 8) QMM_CFG(4, 1, 4, 2, 8) QMM_CFG(4, 1, 4, 3, 8)
+    QMM_CFG(4, 1, 4, 1, 8) QMM_CFG(4, 1, 4, 2, 8)
     QMM_CFG(4, 2, 4, 1, 8) QMM_CFG(4, 2, 4, 2, 8)
     QMM_CFG(4, 4, 4, 1, 8)
-    QMM_CFG(4, 1, 1, 1, 16) QMM_CFG(4, 1, 1, 2, 16) QMM_CFG(4, 1, 1, 3, 16) QMM_CFG(4, 1, 1, 4, 16)
-    QMM_CFG(4, 1, 2, 4, 16) QMM_CFG(4, 1, 4, 4, 8) QMM_CFG(4, 2, 4, 3, 8) QMM_CFG(4, 4, 4, 2, 8)
+    QMM_CFG(8, 1, 1, 1, 16) QMM_CFG(8, 1, 1, 2, 16)
     QMM_CFG(8, 1, 2, 1, 16) QMM_CFG(8, 1, 2, 2, 16)
     QMM_CFG(8, 2, 2, 1, 8) QMM_CFG(8, 2, 2, 2, 8)
     QMM_CFG(8, 4, 2, 1, 8)
-    QMM_CFG(8, 1, 4, 1, 8) QMM_CFG(8, 1, 4, 2, 8)
+    QMM_CFG(8, 1, 4, 1, 8)
     QMM_CFG(8, 2, 4, 1, 8)
     QMM_CFG(8, 4, 4, 1, 8)
 #undef QMM_CFG

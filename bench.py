@@ -70,20 +70,29 @@ def roofline(M, N, K, seconds, bits=4, group=128):
 
 # The dominant kernel of the step (largest share of its time): the large-M W4A16 kernel.
 DOMINANT_KERNEL = "w4a16_wide_kernel"
-DOMINANT_SOURCE = os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", "qmm_w4a16_wide.hip")
+# What the committed traffic counters were taken on: the kernel's source, the host code
+# that plans its launches, and the workload of the counter passes.
+DOMINANT_SOURCES = [os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
+                    for f in ("qmm_w4a16_wide.hip", "qmm_api.cpp")]
+DOMINANT_WORKLOAD = "first pass (qmm_w4a16_g128_pass1) of the plan, M=2048 q,k,v,o,gate,up,down"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_wide_M2048_traffic.txt")
 COPY_BYTES = 256 << 20     # size of the plain copy that calibrates the profiler's byte counters
 
 
 def dominant_shapes(shapes):
-    """The M = 2048 shapes: the large-M kernel runs them (unsplit in the timing below)."""
+    """The M = 2048 shapes: the large-M kernel runs them."""
     return [sh for sh in shapes if sh.M > 128]
 
 
-def source_digest(path):
+def source_digest(paths=None):
+    """Digest of the dominant kernel's sources and of the counter workload."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in (paths or DOMINANT_SOURCES):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(DOMINANT_WORKLOAD.encode())
+    return h.hexdigest()[:16]
 
 
 def calib_lib():
@@ -145,20 +154,21 @@ def read_traffic(alg_bytes_per_launch):
         if ":" in line and not line.startswith(" "):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel source digest") != source_digest(DOMINANT_SOURCE):
-        return None, "kernel changed since the counters were taken"
+    if fields.get("kernel source digest") != source_digest():
+        return None, "kernel, its launch plan or the counter workload changed since the counters were taken"
     t = float(fields["hbm bytes per launch (scaled)"])
     return t, "FETCH_SIZE + WRITE_SIZE per launch x copy-kernel scale; %.2fx the algorithmic bytes" % (
         t / alg_bytes_per_launch)
 
 
 def dominant_roofline(torch, shapes, rounds=4):
-    """Roofline figure of the dominant kernel: every M = 2048 shape launched unsplit
-    (one kernel per call, no reduce), `rounds` times over two buffer sets, captured
-    as one graph; HIP events on the launch stream around each replay give the mean
+    """Roofline figure of the dominant kernel: the large-M kernel's launch of every M = 2048
+    shape exactly as the timed sweep makes it (the plan's decomposition), without the second
+    pass: qmm_w4a16_g128_pass1, one kernel per call, `rounds` times over two buffer sets,
+    captured as one graph; HIP events on the launch stream around each replay give the mean
     launch duration (median of the replays)."""
     dom = dominant_shapes(shapes)
-    g = graph_of(torch, lambda: [sh.call(r, 1) for r in range(rounds) for sh in dom])
+    g = graph_of(torch, lambda: [sh.call_pass1(r) for r in range(rounds) for sh in dom])
     avg_dur = time_graph(torch, g) / (rounds * len(dom))
     del g
     flops = sum(algorithmic_flops(sh.M, sh.N, sh.K) for sh in dom) / len(dom)
@@ -168,12 +178,13 @@ def dominant_roofline(torch, shapes, rounds=4):
     traffic, traffic_note = read_traffic(nbytes)
     roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s",
             "frac": achieved / MFMA_BF16_PEAK, "traffic": traffic,
-            "kernel": "%s, unsplit, M=2048 launches (%s)" % (DOMINANT_KERNEL, ", ".join(sh.name for sh in dom)),
+            "kernel": "%s as the plan launches it (first pass), M=2048 launches (%s)" % (
+                DOMINANT_KERNEL, ", ".join("%s s=%d" % (sh.name, sh.s) for sh in dom)),
             "launches_per_replay": rounds * len(dom), "avg_launch_us": avg_dur * 1e6,
             "algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops,
             "frac_of_measured_mfma_peak": achieved / (calib["mfma_bf16_tflops"] * 1e12),
             "traffic_note": traffic_note,
-            "block_tile": [dom[0].plan.block_m, dom[0].plan.block_n]}
+            "block_tiles": {sh.name: [sh.plan.block_m, sh.plan.block_n] for sh in dom}}
     return roof, calib
 
 
@@ -335,14 +346,15 @@ def formats_table(torch, syn, q):
 
 
 def pmc_run():
-    """Workload of the counter passes: each M = 2048 shape once unsplit, then one plain copy."""
+    """Workload of the counter passes: the first pass of each M = 2048 shape's plan once, then
+    one plain copy."""
     import torch
     import qmm_synth as syn
     import weight_only_quantized_qmm_amd as q
     torch.cuda.set_device(0)
     shapes = [Shape(n, M, N, K, i, 1, torch, syn, q) for n, M, N, K, i in syn.projection_sweep() if M > 128]
     for sh in shapes:
-        sh.call(0, 1)
+        sh.call_pass1(0)
     torch.cuda.synchronize()
     L = calib_lib()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -362,23 +374,23 @@ def summarize_pmc(fetch_dir, write_dir, commands):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         if not files:
             raise SystemExit("no counter_collection.csv under %s" % d)
-        rows = {}
+        rows = []
         for f in files:
             for r in csv.DictReader(open(f)):
                 if r["Counter_Name"] != counter:
                     continue
-                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return rows
+                rows.append((int(r.get("Dispatch_Id") or len(rows)), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(rows)
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    pick = lambda rows, key: [v for k, vs in rows.items() if key in k for v in vs]
+    pick = lambda rows, key: [v for _, k, v in rows if key in k]  # dispatch order
     cf, cw = pick(fetch, "calib_copy"), pick(write, "calib_copy")
     df, dw = pick(fetch, DOMINANT_KERNEL), pick(write, DOMINANT_KERNEL)
     f_scale = COPY_BYTES / (cf[0] * 1024.0)
     w_scale = COPY_BYTES / (cw[0] * 1024.0)
     shapes = [(n, M, N, K) for n, M, N, K, _ in syn.projection_sweep() if M > 128]
     alg = [algorithmic_bytes(M, N, K) for _, M, N, K in shapes]
-    lines = ["# HBM traffic of %s (unsplit, M = 2048 Qwen3-4B projections) from rocprofv3 counters" % DOMINANT_KERNEL,
+    lines = ["# HBM traffic of %s (%s) from rocprofv3 counters" % (DOMINANT_KERNEL, DOMINANT_WORKLOAD),
              "commands:"] + ["  " + c for c in commands] + [
         "copy kernel: %d bytes read and written; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (COPY_BYTES, cf[0], cw[0]),
         "fetch scale: %.4f" % f_scale, "write scale: %.4f" % w_scale,
@@ -389,7 +401,7 @@ def summarize_pmc(fetch_dir, write_dir, commands):
         tot.append(b)
         lines.append("  %-5s M=%d N=%d K=%d: fetch %.1f KiB, write %.1f KiB -> %.3e B scaled; algorithmic %.3e B (%.2fx)"
                      % (n, M, N, K, fv, wv, b, a, b / a))
-    lines += ["kernel source digest: %s" % source_digest(DOMINANT_SOURCE),
+    lines += ["kernel source digest: %s" % source_digest(),
               "hbm bytes per launch (scaled): %.6e" % (sum(tot) / len(tot)),
               "algorithmic bytes per launch: %.6e" % (sum(alg) / len(alg))]
     print("\n".join(lines))
@@ -446,6 +458,12 @@ class Shape:
         else:
             self.q.qmm_wna16(self.fmt[0], self.fmt[1], 1 if self.f32p else 0, A, W, S, B, self.C, self.M, self.N,
                              self.K, s, ws, wsb)
+
+    def call_pass1(self, r):
+        """The first pass alone of the plan's call (W4A16 g128): the matmul kernel's launch."""
+        A, W, S, B = self.sets[r % len(self.sets)]
+        ws, wsb = (self.ws, self.ws.numel()) if self.s > 1 else (None, 0)
+        self.q.qmm_w4a16_g128_pass1(A, W, S, B, self.C, self.M, self.N, self.K, 0, ws, wsb)
 
     def set_bytes(self):
         return algorithmic_bytes(self.M, self.N, self.K, *(self.fmt or (4, 128)))

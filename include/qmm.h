@@ -72,8 +72,12 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * tile_m / tile_n = 0 mean "the block tile of the kernel this library launches
  * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
  *
- * The small-M kernel runs M <= 64, and M <= 128 when N*K <= 2^24 (its 16*mt x 32 or x 64
- * tiles); the large-M kernel runs the rest, with 128 x 256 tiles up to M = 128 and, above,
+ * The small-M kernel runs M <= 64, and M <= 128 when N*K <= 2^24. Its tiles are 16*mt rows
+ * (mt = 1, 2, 4 for M <= 16, 32, more) by 16 columns for M <= 16 with N*K <= 2^24, else by 64
+ * columns when 32-column tiles would exceed 256 workgroups or M > 16 and K >= 8192, else
+ * by 32. With tile_m = tile_n = 0 and M <= 32, its partitions hold at least 2048 reduction
+ * values (min_k_per_split is raised to 2048 in the rule): a shorter partition saves less
+ * than the second pass costs. The large-M kernel runs the rest, with 128 x 256 tiles up to M = 128 and, above,
  * 128 x 256 or 256 x 256 tiles, whichever has the shorter estimated critical path: rounds of
  * target_blocks workgroups times the 128 x 256 x 128 blocks each computes (a 256-row tile
  * counts two), plus half a block per partition of a split tail.
@@ -158,6 +162,35 @@ int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, const void 
  */
 int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
                         int M, int N, int K, int s, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two passes of qmm_w4a16_g128 as separate calls (tiny-llm "Week 2 Day 7: Split-K
+ * Prefill", Task 2 writes the partial planes, Task 4 sums them), for callers that run the
+ * second pass themselves (on another stream, or fused into their own epilogue).
+ *
+ * qmm_w4a16_g128_pass1 -- the matmul launch of qmm_w4a16_g128 with the same arguments,
+ * checks, errors and decomposition, and no second pass: every output tile computed over
+ * the whole reduction is written to C; the partitions of split tiles go to the bf16
+ * planes [s][M][N] in the workspace. *s_out receives the effective split and *n_lo_out
+ * the first column whose outputs are still in the planes: those of columns [n_lo, N) of
+ * every row (n_lo = N when s = 1; 0 when every tile is split; for the large-M kernel's
+ * split tail, the first column of the tail tiles). Neither output pointer may be NULL;
+ * both are host pointers, written before the call returns.
+ *
+ * qmm_splitk_reduce_cols -- the second pass over columns [n_lo, N): for every row m and
+ * n_lo <= n < N, C[m][n] = bf16_rne(sum over p = 0..s-1, in this order, in fp32, of
+ * partials[p][m][n]); the other columns of C are not touched. partials as for
+ * qmm_splitk_reduce; 0 <= n_lo < N.
+ *
+ * qmm_w4a16_g128_pass1, then qmm_splitk_reduce_cols(workspace, QMM_PARTIAL_BF16, s, M, N,
+ * n_lo, C) when s > 1, leaves C bitwise equal to qmm_w4a16_g128's result.
+ */
+int qmm_w4a16_g128_pass1(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                         int M, int N, int K, int s, void *workspace, size_t workspace_bytes,
+                         int *s_out, int *n_lo_out, void *stream);
+
+int qmm_splitk_reduce_cols(const void *partials, int partial_dtype, int s, int M, int N, int n_lo,
+                           void *C, void *stream);
 
 /*
  * Other weight-only formats (skillsdirectory "Optimize Prefill vs Decode Kernels",

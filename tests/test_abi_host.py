@@ -257,6 +257,42 @@ def test_w4a16_f32p_rejects_before_launch(kw, code):
     assert _w4f(**kw) == code
 
 
+def _w4p(**kw):
+    a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=32, N=1024, K=2560, s=1,
+             workspace=None, workspace_bytes=0)
+    a.update(kw)
+    rc, _, _ = q.qmm_w4a16_g128_pass1(a["A"], a["Wq"], a["scale"], a["bias"], a["C"], a["M"], a["N"], a["K"],
+                                      a["s"], a["workspace"], a["workspace_bytes"], stream=0, check=False)
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG), (dict(K=2500), q.QMM_ERR_SHAPE),
+    (dict(s=3), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=4, workspace=ADDR2 + 8, workspace_bytes=1 << 30), q.QMM_ERR_ALIGN), (dict(K=1 << 22), q.QMM_ERR_SIZE),
+])
+def test_w4a16_pass1_rejects_before_launch(kw, code):
+    # the same checks as qmm_w4a16_g128, all on the host
+    assert _w4p(**kw) == code
+
+
+def test_w4a16_pass1_needs_its_outputs():
+    f = q.lib().qmm_w4a16_g128_pass1
+    rc = f(ADDR, ADDR2, ADDR3, ADDR3 + 4096, ADDR + 0x100000, 32, 1024, 2560, 1, None, 0, None, None, None)
+    assert rc == q.QMM_ERR_ARG
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 0, 2, 4, 64, 0, ADDR), q.QMM_ERR_ARG), ((ADDR, 2, 2, 4, 64, 0, ADDR), q.QMM_ERR_ARG),
+    ((ADDR, 0, 0, 4, 64, 0, ADDR), q.QMM_ERR_ARG), ((ADDR, 0, 2, 4, 64, -1, ADDR), q.QMM_ERR_ARG),
+    ((ADDR, 0, 2, 4, 64, 64, ADDR), q.QMM_ERR_ARG), ((ADDR, 0, 2, 0, 64, 0, ADDR), q.QMM_ERR_ARG),
+    ((ADDR + 1, 0, 2, 4, 64, 0, ADDR), q.QMM_ERR_ALIGN), ((ADDR + 2, 1, 2, 4, 64, 0, ADDR), q.QMM_ERR_ALIGN),
+    ((ADDR, 0, 2, 4, 64, 0, ADDR + 1), q.QMM_ERR_ALIGN),
+])
+def test_reduce_cols_rejects_before_launch(args, code):
+    assert q.qmm_splitk_reduce_cols(*args, stream=0, check=False) == code
+
+
 def _wn(bits=8, group=64, dt=0, **kw):
     a = dict(A=ADDR, Wq=ADDR2, scale=ADDR3, bias=ADDR3 + 4096, C=ADDR + 0x100000, M=32, N=1024, K=2560, s=1,
              workspace=None, workspace_bytes=0)

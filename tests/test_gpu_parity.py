@@ -853,3 +853,40 @@ def test_graph_capture_other_entry_points():
         torch.cuda.synchronize()
         for (c, _), e in zip(calls, eager):
             assert np.array_equal(host_bits(c), e), "replay %d differs" % rep
+
+
+# ------------------------------------------------------------------ the two passes as separate calls
+
+PASS1_SHAPES = [(16, 1024, 2560, 0), (64, 4096, 2560, 0), (48, 1000, 2560, 4), (128, 9728, 2560, 0),
+                (300, 300, 1024, 0), (256, 2560, 4096, 1), (2048, 9728, 2560, 0)]
+
+
+@pytest.mark.parametrize("M,N,K,s", PASS1_SHAPES)
+def test_pass1_then_reduce_cols_equals_the_whole_call(M, N, K, s):
+    """qmm_w4a16_g128_pass1 + qmm_splitk_reduce_cols: the planes and columns the first pass
+    reports, and C bitwise equal to qmm_w4a16_g128's (small- and large-M kernels, unsplit,
+    fully split and the large-M split tail)."""
+    say("pass1 M=%d N=%d K=%d s=%d" % (M, N, K, s))
+    dv = w4a16_device(syn.w4a16_inputs(M, N, K, seed=4100 + M))
+    whole = run_w4a16(dv, M, N, K, s)
+    plan = q.qmm_splitk_plan(M, N, K)
+    s_eff = q.effective_split(M, N, K, s)
+    ws = torch.empty(max(s_eff * M * N, 8), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((M, N), -12345.0, dtype=torch.bfloat16, device="cuda")
+    rc, s_out, n_lo = q.qmm_w4a16_g128_pass1(dv["A"], dv["Wq"], dv["scale"], dv["bias"], C, M, N, K, s, ws)
+    torch.cuda.synchronize()
+    assert rc == q.QMM_OK and s_out == s_eff
+    if s_eff == 1:
+        assert n_lo == N
+    elif s == 0 and plan.block_n == 256 and plan.full_tiles > 0:
+        assert n_lo == (plan.full_tiles // -(-M // plan.block_m)) * plan.block_n
+    else:
+        assert n_lo == 0
+    got, ref = host_bits(C), host_bits(whole)
+    canary = host_bits(torch.tensor([-12345.0], dtype=torch.bfloat16))[0]
+    assert np.array_equal(got[:, :n_lo], ref[:, :n_lo]), "columns finished by the first pass"
+    assert np.all(got[:, n_lo:] == canary), "the first pass wrote a column left to the planes"
+    if s_eff > 1:
+        q.qmm_splitk_reduce_cols(ws, q.QMM_PARTIAL_BF16, s_eff, M, N, n_lo, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(C), ref)

@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     bf16_splitk, effective_split, lib, policy_preset, qmm_bf16_splitk, qmm_plan, qmm_policy,
     qmm_gemv_min_split, qmm_splitk_plan, qmm_splitk_reduce, qmm_status_string, qmm_w4a16_g128,
     qmm_attn_decode, qmm_attn_decode_split, qmm_attn_decode_workspace_bytes, qmm_streamk_workspace_bytes,
-    qmm_w4a16_g128_f32p, qmm_w4a16_g128_streamk, qmm_w4a16_gemv, qmm_wna16, qmm_wna16_plan, w4a16, w4a16_workspace_bytes, wna16)
+    qmm_splitk_reduce_cols, qmm_w4a16_g128_f32p, qmm_w4a16_g128_pass1, qmm_w4a16_g128_streamk, qmm_w4a16_gemv,
+    qmm_wna16, qmm_wna16_plan, w4a16, w4a16_workspace_bytes, wna16)

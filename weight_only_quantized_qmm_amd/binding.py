@@ -26,7 +26,8 @@ QMM_PARTIAL_F32 = 1
 EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", "qmm_bf16_splitk",
                       "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p",
                       "qmm_wna16", "qmm_wna16_plan", "qmm_attn_decode", "qmm_attn_decode_split",
-                      "qmm_attn_decode_workspace_bytes", "qmm_w4a16_g128_streamk", "qmm_streamk_workspace_bytes")
+                      "qmm_attn_decode_workspace_bytes", "qmm_w4a16_g128_streamk", "qmm_streamk_workspace_bytes",
+                      "qmm_w4a16_g128_pass1", "qmm_splitk_reduce_cols")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -82,6 +83,10 @@ def lib():
         L.qmm_wna16_plan.restype = I
         L.qmm_splitk_reduce.argtypes = [P, I, I, I, I, P, P]
         L.qmm_splitk_reduce.restype = I
+        L.qmm_w4a16_g128_pass1.argtypes = [P, P, P, P, P, I, I, I, I, P, S, ctypes.POINTER(I), ctypes.POINTER(I), P]
+        L.qmm_w4a16_g128_pass1.restype = I
+        L.qmm_splitk_reduce_cols.argtypes = [P, I, I, I, I, I, P, P]
+        L.qmm_splitk_reduce_cols.restype = I
         L.qmm_bf16_splitk.argtypes = [P, P, P, I, I, I, I, P, S, P]
         L.qmm_bf16_splitk.restype = I
         L.qmm_w4a16_gemv.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
@@ -166,6 +171,21 @@ def qmm_w4a16_g128(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspac
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_w4a16_g128")
     return rc
+
+
+def qmm_w4a16_g128_pass1(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
+                         stream=None, check=True):
+    """The matmul launch of qmm_w4a16_g128 alone; returns (status, s, n_lo): the effective split
+    and the first column whose outputs are left in the workspace planes."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0
+    s_out, n_lo = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib().qmm_w4a16_g128_pass1(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                                    int(s), _ptr(workspace), int(workspace_bytes), ctypes.byref(s_out),
+                                    ctypes.byref(n_lo), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_g128_pass1")
+    return rc, s_out.value, n_lo.value
 
 
 def qmm_w4a16_g128_f32p(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspace_bytes=None,
@@ -258,6 +278,14 @@ def qmm_splitk_reduce(partials, partial_dtype, s, M, N, C, stream=None, check=Tr
                                  _stream(stream))
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_splitk_reduce")
+    return rc
+
+
+def qmm_splitk_reduce_cols(partials, partial_dtype, s, M, N, n_lo, C, stream=None, check=True):
+    rc = lib().qmm_splitk_reduce_cols(_ptr(partials), int(partial_dtype), int(s), int(M), int(N), int(n_lo), _ptr(C),
+                                      _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_splitk_reduce_cols")
     return rc
 
 

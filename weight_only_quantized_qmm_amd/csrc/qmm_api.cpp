@@ -261,9 +261,11 @@ extern "C" int qmm_wna16_plan(int bits, int group_size, int M, int N, int K, con
 namespace {
 
 // The weight-only matmul in format fmt with partial planes of element size 2 (bf16) or
-// 4 (fp32, f32_part).
+// 4 (fp32, f32_part). With pass1 != nullptr only the matmul launch runs; pass1[0] receives
+// the effective split and pass1[1] the first column whose outputs are left in the planes.
 int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const void *bias, void *C, int M, int N,
-           int K, int s, void *workspace, size_t workspace_bytes, bool f32_part, void *stream)
+           int K, int s, void *workspace, size_t workspace_bytes, bool f32_part, void *stream,
+           int *pass1 = nullptr)
 {
     if (!A || !Wq || !scale || !bias || !C || !qmm_impl::format_supported(fmt)) return QMM_ERR_ARG;
     if (M <= 0 || N <= 0 || K <= 0 || s < 0) return QMM_ERR_ARG;
@@ -299,19 +301,27 @@ int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const 
         int rc = hip_status(qmm_impl::launch_w4a16_wide(fmt, tile.ns, A, Wq, scale, bias, C,
                                                         s > 1 ? workspace : nullptr, f32_part, M, N, K, full_tiles,
                                                         s, vec_c, st));
-        if (rc != QMM_OK || s == 1) return rc;
+        const int n_lo = s == 1 ? N : (full_tiles / num_m) * tile.block_n();
+        if (pass1) {
+            pass1[0] = s;
+            pass1[1] = n_lo;
+        }
+        if (rc != QMM_OK || s == 1 || pass1) return rc;
         if (full_tiles == 0) {
             const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
             return hip_status(qmm_impl::launch_reduce(workspace, f32_part, s, MN, C, vec_red, st));
         }
-        const int n_lo = (full_tiles / num_m) * tile.block_n();
         const bool vec_red = (N % 8 == 0) && aligned(C, 16);
         return hip_status(qmm_impl::launch_reduce_cols(workspace, f32_part, s, M, N, n_lo, C, vec_red, st));
+    }
+    if (pass1) {
+        pass1[0] = s;
+        pass1[1] = s == 1 ? N : 0;
     }
     if (s == 1) return hip_status(dispatch_skinny(fmt, tile, A, Wq, scale, bias, C, false, M, N, K, 1, vec_c, st));
     const bool vec_ws = (N % 4 == 0);
     int rc = hip_status(dispatch_skinny(fmt, tile, A, Wq, scale, bias, workspace, f32_part, M, N, K, s, vec_ws, st));
-    if (rc != QMM_OK) return rc;
+    if (rc != QMM_OK || pass1) return rc;
     const bool vec_red = (MN % 8 == 0) && aligned(C, 16);
     return hip_status(qmm_impl::launch_reduce(workspace, f32_part, s, MN, C, vec_red, st));
 }
@@ -323,6 +333,21 @@ extern "C" int qmm_w4a16_g128(const void *A, const void *Wq, const void *scale, 
                               size_t workspace_bytes, void *stream)
 {
     return wq_run(WFormat{4, kGroup}, A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int qmm_w4a16_g128_pass1(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                                    int M, int N, int K, int s, void *workspace, size_t workspace_bytes, int *s_out,
+                                    int *n_lo_out, void *stream)
+{
+    if (!s_out || !n_lo_out) return QMM_ERR_ARG;
+    int out[2] = {0, 0};
+    const int rc = wq_run(WFormat{4, kGroup}, A, Wq, scale, bias, C, M, N, K, s, workspace, workspace_bytes, false,
+                          stream, out);
+    if (rc == QMM_OK) {
+        *s_out = out[0];
+        *n_lo_out = out[1];
+    }
+    return rc;
 }
 
 extern "C" int qmm_w4a16_g128_f32p(const void *A, const void *Wq, const void *scale, const void *bias,
@@ -448,6 +473,21 @@ extern "C" int qmm_splitk_reduce(const void *partials, int partial_dtype, int s,
     const size_t MN = (size_t)M * (size_t)N;
     const bool vec = (MN % 8 == 0) && aligned(partials, 16) && aligned(C, 16);
     return hip_status(qmm_impl::launch_reduce(partials, f32, s, MN, C, vec, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int qmm_splitk_reduce_cols(const void *partials, int partial_dtype, int s, int M, int N, int n_lo,
+                                      void *C, void *stream)
+{
+    if (!partials || !C || s < 1 || M <= 0 || N <= 0 || n_lo < 0 || n_lo >= N) return QMM_ERR_ARG;
+    if (partial_dtype != QMM_PARTIAL_BF16 && partial_dtype != QMM_PARTIAL_F32) return QMM_ERR_ARG;
+    if ((long long)M * (long long)N > (long long)INT_MAX * 64) return QMM_ERR_SIZE;
+    const bool f32 = partial_dtype == QMM_PARTIAL_F32;
+    if (!aligned(partials, f32 ? 4 : 2) || !aligned(C, 2)) return QMM_ERR_ALIGN;
+    // eight columns per thread when every row's run [n_lo, N) starts and ends on 8-element
+    // boundaries of 16-byte aligned buffers
+    const bool vec = (N % 8 == 0) && (n_lo % 8 == 0) && aligned(partials, 16) && aligned(C, 16);
+    return hip_status(qmm_impl::launch_reduce_cols(partials, f32, s, M, N, n_lo, C, vec,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int N, int K, int s,

@@ -454,20 +454,69 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     // and n = n0 + wn*32*NJ + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
     const int r = lane & 31;
     const int sl = lane >> 5;
+    if (dst.f32) {  // fp32 planes: straight from the accumulators, 16-byte stores
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int m = m0 + wm * 32 * MI + 32 * i + r;
-        const bool row_ok = m < M;
+        for (int i = 0; i < MI; ++i) {
+            const int m = m0 + wm * 32 * MI + 32 * i + r;
+            const bool row_ok = m < M;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+            for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-            for (int vq = 0; vq < 4; ++vq) {
-                const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
-                const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
-                const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
-                if (row_ok)
-                    store4(dst.base, dst.f32, (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0), n, N, dst.vec,
-                           v0, v1, v2, v3);
+                for (int vq = 0; vq < 4; ++vq) {
+                    const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
+                    const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
+                    const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
+                    if (row_ok)
+                        store4(dst.base, true, (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0), n, N, dst.vec,
+                               v0, v1, v2, v3);
+                }
+            }
+        }
+        return;
+    }
+    // bf16 results go out through LDS, whose stage slots are free now: the waves write the
+    // rounded tile (or, when it does not fit, half of its rows at a time) row-major, 512
+    // bytes per row with 16-byte chunk c of row x stored at chunk c ^ (x % 32), and then
+    // every store instruction writes two whole rows of 512 contiguous bytes. Stored
+    // straight from the accumulators, each instruction would write 16 bytes into each of
+    // 32 rows (32 partly written lines), which took 4-5 us per tile.
+    constexpr int PR = CF::BM * BN * 2 <= CF::LDS ? CF::BM : CF::BM / 2;  // rows per pass
+    char *T = reinterpret_cast<char *>(&L);
+    const bool v16 = dst.vec && (dst.ld % 8) == 0 && (reinterpret_cast<uintptr_t>(dst.base) & 15) == 0;
+#pragma unroll
+    for (int h = 0; h < CF::BM / PR; ++h) {
+        __syncthreads();  // every wave is done with the stage slots, or with the previous pass
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const int rb = wm * 32 * MI + 32 * i;  // first tile row of block i (PR is a multiple of 32)
+            if (rb / PR != h) continue;            // wave-uniform
+            const int x = rb - h * PR + r;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int vq = 0; vq < 4; ++vq) {
+                    const int cc = 4 * (wn * NJ + j) + vq;  // 16-byte chunk of the 256-column row
+                    uint2 v;
+                    v.x = pack_bf16x2(acc[i][j][4 * vq], acc[i][j][4 * vq + 1]);
+                    v.y = pack_bf16x2(acc[i][j][4 * vq + 2], acc[i][j][4 * vq + 3]);
+                    *reinterpret_cast<uint2 *>(T + x * 512 + 16 * (cc ^ (x & 31)) + 8 * sl) = v;
+                }
+            }
+        }
+        __syncthreads();
+        for (int k = threadIdx.x; k < PR * 32; k += 64 * CF::NW) {
+            const int x = k >> 5, cc = k & 31;
+            const int m = m0 + h * PR + x, n = n0 + 8 * cc;
+            if (m >= M || n >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(T + x * 512 + 16 * (cc ^ (x & 31)));
+            uint16_t *g = reinterpret_cast<uint16_t *>(dst.base) + (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0);
+            if (v16 && n + 7 < N) {
+                *reinterpret_cast<uint4 *>(g) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) g[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
         }
     }

@@ -20,7 +20,7 @@
 //     the two reduction steps of the missing half are skipped;
 //   * LDS rows are 128 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7);
 //   * B is the MFMA's first operand, so a lane's results are four consecutive output
-//     columns of one row (16-byte fp32 or 8-byte bf16 stores);
+//     columns of one row; the tile is then written through LDS as whole rows;
 //   * workgroups are ordered so that each XCD computes whole partitions (see below).
 #include "qmm_device.h"
 #include "qmm_launch.h"
@@ -56,6 +56,7 @@ struct DenseLds {
     char a[RING * SLOT];
     char b[RING * SLOT];
 };
+static_assert(TM * TN * 4 <= sizeof(DenseLds), "the fp32 output tile is staged in the stage slots");
 
 struct DCtx {
     const char *A, *B;     // A + m0*K, B + n0*K (bytes)
@@ -188,43 +189,60 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
 
     // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*64 + 32i + (lane % 32)
     // and n = n0 + wn*64 + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
+    // The tile goes out through LDS (free now): the waves write it row-major, 128 values
+    // per row (512 bytes of fp32 or 256 of bf16) with 16-byte chunk c of row x stored at
+    // chunk c ^ (x % chunks per row), and then every store instruction writes whole rows.
+    // Stored straight from the accumulators, each instruction would write 16 or 8 bytes
+    // into each of 32 rows.
+    constexpr int ES = F32_OUT ? 4 : 2;    // bytes per element
+    constexpr int CPR = TN * ES / 16;      // 16-byte chunks per row: 32 or 16
+    char *T = reinterpret_cast<char *>(&L);
     const int r = lane & 31, sl = lane >> 5;
+    __syncthreads();  // every wave is done with the stage slots
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int m = m0 + wm * 64 + 32 * i + r;
-        if (m >= M) continue;
+        const int x = wm * 64 + 32 * i + r;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int vq = 0; vq < 4; ++vq) {
-                const int n = n0 + wn * 64 + 32 * j + 8 * vq + 4 * sl;
-                const size_t off = (size_t)m * (size_t)N + n;
                 const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
                 const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
+                const int col = wn * 64 + 32 * j + 8 * vq + 4 * sl;  // first of the four columns
                 if (F32_OUT) {
-                    float *dst = static_cast<float *>(out) + (size_t)p * (size_t)M * (size_t)N + off;
-                    if (vec_store && n + 3 < N) {
-                        *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
-                    } else {
-                        if (n < N) dst[0] = v0;
-                        if (n + 1 < N) dst[1] = v1;
-                        if (n + 2 < N) dst[2] = v2;
-                        if (n + 3 < N) dst[3] = v3;
-                    }
+                    const int cc = col >> 2;
+                    *reinterpret_cast<float4 *>(T + x * (CPR * 16) + 16 * (cc ^ (x & (CPR - 1)))) =
+                        make_float4(v0, v1, v2, v3);
                 } else {
-                    uint16_t *dst = static_cast<uint16_t *>(out) + off;
-                    if (vec_store && n + 3 < N) {
-                        uint2 v;
-                        v.x = pack_bf16x2(v0, v1);
-                        v.y = pack_bf16x2(v2, v3);
-                        *reinterpret_cast<uint2 *>(dst) = v;
-                    } else {
-                        if (n < N) dst[0] = (uint16_t)f32_to_bf16(v0);
-                        if (n + 1 < N) dst[1] = (uint16_t)f32_to_bf16(v1);
-                        if (n + 2 < N) dst[2] = (uint16_t)f32_to_bf16(v2);
-                        if (n + 3 < N) dst[3] = (uint16_t)f32_to_bf16(v3);
-                    }
+                    const int cc = col >> 3;
+                    uint2 v;
+                    v.x = pack_bf16x2(v0, v1);
+                    v.y = pack_bf16x2(v2, v3);
+                    *reinterpret_cast<uint2 *>(T + x * (CPR * 16) + 16 * (cc ^ (x & (CPR - 1))) + 8 * sl) = v;
                 }
+            }
+        }
+    }
+    __syncthreads();
+    char *base = static_cast<char *>(out) + (F32_OUT ? (size_t)p * (size_t)M * (size_t)N * ES : 0);
+    const bool v16 = vec_store && (N % (16 / ES)) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0;
+    for (int k = threadIdx.x; k < TM * CPR; k += 256) {
+        const int x = k / CPR, cc = k % CPR;
+        const int m = m0 + x, n = n0 + cc * (16 / ES);
+        if (m >= M || n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(T + x * (CPR * 16) + 16 * (cc ^ (x & (CPR - 1))));
+        char *g = base + ((size_t)m * (size_t)N + n) * ES;
+        if (v16 && n + 16 / ES - 1 < N) {
+            *reinterpret_cast<uint4 *>(g) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 16 / ES; ++e) {
+                if (n + e >= N) break;
+                if (F32_OUT)
+                    reinterpret_cast<uint32_t *>(g)[e] = w[e];
+                else
+                    reinterpret_cast<uint16_t *>(g)[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
             }
         }
     }

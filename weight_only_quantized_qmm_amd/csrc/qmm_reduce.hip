@@ -9,7 +9,8 @@
 //
 // MI355X layout: the op is a pure stream (reads s*M*N partial elements, writes
 // M*N outputs), so each lane owns eight consecutive outputs and moves them with
-// 128-bit loads and stores (one 16-byte load per bf16 plane, two per fp32 plane).
+// 128-bit loads and stores (one 16-byte load per bf16 plane, two per fp32 plane),
+// up to eight planes' loads in flight at once.
 // The scalar variant handles element counts or pointers that are not 16-byte
 // multiples, one output per lane.
 #include "qmm_device.h"
@@ -19,25 +20,86 @@ using namespace qmm_dev;
 
 namespace {
 
-__device__ __forceinline__ void load8(const uint16_t *p, float v[8]) {
-    const uint4 x = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(w[e] << 16);
-        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+// Raw bits of eight consecutive partial elements: one 16-byte load of bf16, two of fp32.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    uint4 x;
+    __device__ __forceinline__ void load(const uint16_t *p) { x = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = e < 2 ? x.x : e < 4 ? x.y : e < 6 ? x.z : x.w;
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
     }
-}
-
-__device__ __forceinline__ void load8(const float *p, float v[8]) {
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ float get(int e) const {
+        const float4 &v = e < 4 ? a : b;
+        const int k = e & 3;
+        return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+    }
+};
 
 __device__ __forceinline__ float load1(const uint16_t *p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float *p) { return *p; }
+
+// Planes whose loads a lane has in flight together: every load of a chunk is issued
+// before the first addition, so a lane waits for one memory round trip per chunk
+// instead of one per plane (a loop that adds each plane as it arrives makes s
+// dependent trips, which at M = 128 left the merge at a third of HBM bandwidth).
+constexpr int kChunk = 8;
+
+// acc[0..7] = sum over p < s of plane p's eight elements at offset off, ascending p.
+template <typename T>
+__device__ __forceinline__ void sum8(const T *__restrict__ part, size_t MN, size_t off, int s, float acc[8])
+{
+    for (int p0 = 0; p0 < s; p0 += kChunk) {
+        Raw8<T> r[kChunk];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k)
+            if (p0 + k < s) r[k].load(part + (size_t)(p0 + k) * MN + off);
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+            if (p0 + k >= s) break;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = (p0 + k == 0) ? r[k].get(e) : acc[e] + r[k].get(e);
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ float sum1(const T *__restrict__ part, size_t MN, size_t off, int s)
+{
+    float acc = 0.f;
+    for (int p0 = 0; p0 < s; p0 += kChunk) {
+        float v[kChunk];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k)
+            if (p0 + k < s) v[k] = load1(part + (size_t)(p0 + k) * MN + off);
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+            if (p0 + k >= s) break;
+            acc = (p0 + k == 0) ? v[k] : acc + v[k];
+        }
+    }
+    return acc;
+}
+
+__device__ __forceinline__ uint4 pack8(const float acc[8])
+{
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    return o;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -46,19 +108,8 @@ reduce_vec8(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_t 
     const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (i >= MN) return;  // MN is a multiple of 8 on this path
     float acc[8];
-    load8(part + i, acc);
-    for (int p = 1; p < s; ++p) {
-        float v[8];
-        load8(part + (size_t)p * MN + i, v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
-    }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4 *>(C + i) = o;
+    sum8(part, MN, i, s, acc);
+    *reinterpret_cast<uint4 *>(C + i) = pack8(acc);
 }
 
 template <typename T>
@@ -67,9 +118,7 @@ reduce_scalar(const T *__restrict__ part, uint16_t *__restrict__ C, int s, size_
 {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= MN) return;
-    float acc = load1(part + i);
-    for (int p = 1; p < s; ++p) acc = acc + load1(part + (size_t)p * MN + i);
-    C[i] = (uint16_t)f32_to_bf16(acc);
+    C[i] = (uint16_t)f32_to_bf16(sum1(part, MN, i, s));
 }
 
 // Columns [n_lo, N) of planes [s][M][N]: W = N - n_lo columns per row; eight
@@ -88,23 +137,10 @@ reduce_cols(const T *__restrict__ part, uint16_t *__restrict__ C, int s, int M, 
     const size_t MN = (size_t)M * (size_t)N;
     if (VEC) {
         float acc[8];
-        load8(part + off, acc);
-        for (int p = 1; p < s; ++p) {
-            float v[8];
-            load8(part + (size_t)p * MN + off, v);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = acc[e] + v[e];
-        }
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        *reinterpret_cast<uint4 *>(C + off) = o;
+        sum8(part, MN, off, s, acc);
+        *reinterpret_cast<uint4 *>(C + off) = pack8(acc);
     } else {
-        float acc = load1(part + off);
-        for (int p = 1; p < s; ++p) acc = acc + load1(part + (size_t)p * MN + off);
-        C[off] = (uint16_t)f32_to_bf16(acc);
+        C[off] = (uint16_t)f32_to_bf16(sum1(part, MN, off, s));
     }
 }
 

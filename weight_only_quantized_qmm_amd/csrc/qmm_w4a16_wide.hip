@@ -11,15 +11,15 @@
 // by one group (see the work decomposition above the kernel): on 256 CUs this fills
 // the last wave of workgroups instead of leaving it mostly idle.
 //
-// This regime is bound by the bf16 matrix cores. A workgroup of 8 wave64s owns a
-// 256 x 256 output tile (2 x 4 waves, each a 128 x 64 tile of 4 x 2
-// v_mfma_f32_32x32x16_bf16 accumulators) and walks its partition in stages of 64
-// reduction values. The square tile halves the re-reads of A against a 256 x 128
-// tile, and 64-value stages make every row of A a whole 128-byte line.
+// This regime is bound by the bf16 matrix cores. A workgroup owns a 128 x 256 tile (variant
+// 0: 4 wave64s, each 128 x 64, 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators) or a 256 x 256
+// tile (variant 2: 8 wave64s, each 256 x 32, 8 x 1 accumulators), and walks its partition
+// in stages of 64 reduction values. Tall wave tiles spread each dequantised weight over
+// 4 or 8 MFMAs, and 64-value stages make every row of A a whole 128-byte line.
 //
 // Data movement: every global read of the kernel is a direct global -> LDS copy
 // (global_load_lds_*), issued one and a half stages ahead of its use, into rings of three slots:
-//   A:  256 rows x 64 bf16 (32 KB per stage), four 1 KB copies per wave;
+//   A:  BM rows x 64 bf16 (16 or 32 KB per stage), 1 KB per copy;
 //   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage; 64 bytes and 16 KB for
 //       8-bit codes), 1 KB per copy;
 //   scale/bias: the 128-value block's 256 + 256 bf16 values per group it holds (one, two
@@ -33,7 +33,7 @@
 // The next stage's first operands are read during the last step of the current one,
 // so the matrix pipeline does not drain at stage boundaries.
 //
-// Dequantisation: each wave turns its 64 columns' packed words straight into MFMA
+// Dequantisation: each wave turns its 64 or 32 columns' packed words straight into MFMA
 // operands (w = scale*q + bias in fp32, rounded to bf16). One packed 32-bit word is
 // eight consecutive reduction values, i.e. one lane's operand of one
 // 32x32x16 MFMA. For reduction step t of a stage, lane l (half h = l / 32) takes word
@@ -42,7 +42,8 @@
 // With 8-bit codes the same eight values are two words and a lane reads 32 bytes. A
 // lane's 32 values of a stage lie in one scale/bias group for every group size.
 // The MFMA takes the weights as its first operand, so a lane's results are four
-// consecutive output columns of one row (8-byte stores).
+// consecutive output columns of one row. bf16 results leave through LDS as whole rows
+// (see the end of segment); fp32 planes are stored from the accumulators.
 //
 // LDS layouts: A rows are 128 bytes (eight 16-byte chunks), chunk c of row r stored
 // at chunk c ^ ((r >> 1) & 7); W rows of 32 bytes store chunk h of row r at
@@ -50,7 +51,7 @@
 // 16-lane phases of the 16-byte reads on distinct banks.
 //
 // Block order: tiles are numbered with the M-block fastest, so with 8 M-blocks the
-// workgroups that the round-robin dispatch sends to one XCD share the same 256 rows
+// workgroups that the round-robin dispatch sends to one XCD share the same BM rows
 // of A in that XCD's L2.
 #include "qmm_device.h"
 #include "qmm_launch.h"

@@ -890,3 +890,38 @@ def test_pass1_then_reduce_cols_equals_the_whole_call(M, N, K, s):
         q.qmm_splitk_reduce_cols(ws, q.QMM_PARTIAL_BF16, s_eff, M, N, n_lo, C)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(C), ref)
+
+
+# ------------------------------------------------------------ seeded random shapes
+
+def _random_cases(n=24, seed=13000):
+    """(bits, group, M, N, K, s) drawn from a fixed seed: every kernel and tile choice
+    (16-, 32-, 64-column small-M tiles, 64-row blocks, 128- and 256-row large-M tiles),
+    ragged M and N, and explicit splits that divide K/128."""
+    rng = np.random.default_rng(seed)
+    fmts = [(4, 128), (4, 64), (4, 32), (8, 128), (8, 64), (8, 32)]
+    cases = []
+    for i in range(n):
+        bits, group = fmts[i % len(fmts)]
+        M = int(rng.choice([1, 5, 16, 23, 32, 47, 64, 65, 100, 128, 131, 200, 257, 300]))
+        N = int(rng.integers(1, 1200))
+        G = int(rng.integers(1, 17))
+        K = 128 * G
+        divs = [d for d in range(1, G + 1) if G % d == 0]
+        s = int(rng.choice(divs + [0, 0]))
+        cases.append((bits, group, M, N, K, s))
+    return cases
+
+
+@pytest.mark.parametrize("bits,group,M,N,K,s", _random_cases())
+def test_random_shapes_match_oracle(bits, group, M, N, K, s):
+    """Seeded random shapes through qmm_wna16 (bf16 and fp32 partials) against the oracle,
+    with guard bands around C and the workspace."""
+    d = syn.wq_inputs(bits, group, M, N, K, seed=13100 + M + N + K + bits + group)
+    ref = oracle.qmm_wq(bits, group, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for f32p in (False, True):
+        say("random bits=%d group=%d M=%d N=%d K=%d s=%d f32p=%d" % (bits, group, M, N, K, s, f32p))
+        C = run_wna16(dv, bits, group, M, N, K, s, guard=48, f32p=f32p)
+        check_tolerance(host_f64(C), ref, what="random w%da16 g%d %dx%dx%d s=%d f32p=%d" % (bits, group, M, N, K, s,
+                                                                                           f32p))

@@ -119,12 +119,18 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
             t.ns = 1;
             return t;
         }
-        // 64-column tiles when 32-column ones would need more than one workgroup per CU
-        // (one workgroup of the small-M kernel fills a CU's wave slots), and for 17..64 rows
-        // over a long reduction (K >= 8192), where each staged activation group then feeds
-        // twice the columns (config sweeps on MI355X: down at M = 32, 64 faster with 64
-        // columns, o (K = 4096) with 32).
-        t.ns = (ceil_div(M, 16 * t.mt) * ceil_div(N, 32) > kCUs || (M > 16 && K >= 8192)) ? 4 : 2;
+        // 32-column tiles while they fit one workgroup per CU (one workgroup of the
+        // small-M kernel fills a CU's wave slots) over a reduction shorter than 8192;
+        // otherwise the widest tile that still spreads over the most CUs: 48 columns when
+        // those tiles fit one per CU, else 64. Wider tiles feed each staged activation group
+        // to more columns (config sweeps of the Qwen3-4B projections on MI355X: gate and up
+        // at M = 16..64 on 203 48-column tiles 10-12 % faster than on 152 64-column ones;
+        // down (K = 9728) 11-16 % faster on 48 columns in 4 partitions than on 32 or 64).
+        const long long rows = ceil_div(M, 16 * t.mt);
+        if (rows * ceil_div(N, 32) <= kCUs && K < 8192)
+            t.ns = 2;
+        else
+            t.ns = rows * ceil_div(N, 48) <= kCUs ? 3 : 4;
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.ns = wide_variant(M, N, K);

@@ -8,7 +8,7 @@
 namespace qmm_impl {
 
 // Which W4A16 kernel runs a problem, and the output tile of one workgroup.
-//   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x (16*ns) tile, ns 1, 2 or 4,
+//   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x (16*ns) tile, ns 1 to 4,
 //          up to 16 waves splitting its reduction;
 //   WIDE   (otherwise): a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variant 2).
 enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
@@ -57,10 +57,10 @@ inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub)
 inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4, int sub = 1)
 {
     // 16-column tiles: up to 12 waves; 32-column tiles of one 16-row block: 16; else 8.
-    // Groups per round: up to 3, 2 for 64-column tiles of 16 or 32 rows, 1 for 64 x 64
-    // (config sweeps of the Qwen3-4B projections at M = 16..64 on MI355X).
+    // Groups per round: up to 3, 2 for 48- and 64-column tiles of 16 or 32 rows, 1 for them
+    // with 64 rows (config sweeps of the Qwen3-4B projections at M = 16..64 on MI355X).
     const int max_waves = ns == 1 ? 12 : (mt == 1 && ns == 2) ? 16 : 8;
-    int max_gpw = ns == 4 ? (mt == 4 ? 1 : 2) : (mt == 4 ? 2 : 3);
+    int max_gpw = ns >= 3 ? (mt == 4 ? 1 : 2) : (mt == 4 ? 2 : 3);
     if (bits == 8 && max_gpw > 1) max_gpw -= 1;  // twice the weight registers per group
     SkinnyShape sh;
     sh.waves = gpp < max_waves ? gpp : max_waves;

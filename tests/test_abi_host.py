@@ -110,10 +110,10 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         assert plan.grid_y == 1 and plan.grid_z == 1
     else:  # the page's rule over the kernel's tile; partitions of at least 2048 values up to M = 32
         assert G % plan.s == 0
-        # 16-column tiles for up to 16 rows over at most 2^24 weights; else 32 columns while
+        # 16-column tiles for up to 32 rows over at most 2^24 weights; else 32 columns while
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
         rows = -(-M // plan.block_m)
-        if M <= 16 and N * K <= 1 << 24:
+        if M <= 32 and N * K <= 1 << 24:
             assert plan.block_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:
             assert plan.block_n == 32

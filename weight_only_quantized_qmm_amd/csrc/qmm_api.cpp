@@ -111,11 +111,11 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-        // Up to 16 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
-        // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o at M = 16 on
-        // MI355X: 20-30 % faster than split 32-column tiles, whose second pass costs more
-        // than the spread saves).
-        if (M <= 16 && (long long)N * K <= (1LL << 24)) {
+        // Up to 32 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
+        // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o on MI355X:
+        // at M = 16 20-30 % faster than split 32-column tiles, whose second pass costs more
+        // than the spread saves; at M = 32 11-15 % faster than 32-column tiles).
+        if (M <= 32 && (long long)N * K <= (1LL << 24)) {
             t.ns = 1;
             return t;
         }

@@ -285,7 +285,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
 namespace qmm_impl {
 
 // The host picks (mt, ns, gpw, waves) with skinny_shape (qmm_launch.h); these are the
-// configurations it can return: 16-column tiles (ns 1, mt 1) with up to 12 waves and gpw <= 3;
+// configurations it can return: 16-column tiles (ns 1, mt 1 or 2) with up to 12 waves and gpw <= 3;
 // 32-column tiles (ns 2) with up to 16 waves (mt 1) or 8 (mt 2, 4) and gpw <= 3, 3, 2;
 // 48- and 64-column tiles (ns 3, 4) with up to 8 waves and gpw <= 2, 2, 1 for mt 1, 2, 4 (register
 // budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one group less per
@@ -310,7 +310,9 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, 
     QMM_CFG(4, 1, 3, 1, 8) QMM_CFG(4, 1, 3, 2, 8)
     QMM_CFG(4, 2, 3, 1, 8) QMM_CFG(4, 2, 3, 2, 8)
     QMM_CFG(4, 4, 3, 1, 8)
+    QMM_CFG(4, 2, 1, 1, 16) QMM_CFG(4, 2, 1, 2, 16) QMM_CFG(4, 2, 1, 3, 16)
     QMM_CFG(8, 1, 1, 1, 16) QMM_CFG(8, 1, 1, 2, 16)
+    QMM_CFG(8, 2, 1, 1, 16) QMM_CFG(8, 2, 1, 2, 16)
     QMM_CFG(8, 1, 2, 1, 16) QMM_CFG(8, 1, 2, 2, 16)
     QMM_CFG(8, 2, 2, 1, 8) QMM_CFG(8, 2, 2, 2, 8)
     QMM_CFG(8, 4, 2, 1, 8)

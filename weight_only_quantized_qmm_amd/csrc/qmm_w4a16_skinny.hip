@@ -104,7 +104,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     }
     // Activation copies: copy c (0 .. 4*MT-1) of a group fills staging rows 4c .. 4c+3; lane i
     // lands at row 4c + i/16, stored chunk i%16, so it fetches chunk (i%16) ^ (row%16) of the
-    // group's 256 bytes of that row. Rows past M re-read row M-1 (never stored).
+    // group's 256 bytes of that row. Rows past M re-read row M-1; a copy whose rows all lie
+    // past M is not issued at all, and its staging rows keep whatever they held. An MFMA
+    // output row depends only on its own activation row, so such rows reach only output rows
+    // past M, which are never stored (decode with M = 1..8 saves up to 15 of 16 copies).
     uint32_t a_voff[4 * MT];
 #pragma unroll
     for (int c = 0; c < 4 * MT; ++c) {
@@ -149,7 +152,9 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             if (base + q >= n_w) break;  // uniform across the wave
             const char *Ag = Abase + (size_t)(g0 + wave + waves * (base + q)) * 256;
 #pragma unroll
-            for (int c = 0; c < 4 * MT; ++c) copy16(stage_lds + (uint32_t)(q * ABYTES + 1024 * c), a_voff[c], Ag);
+            for (int c = 0; c < 4 * MT; ++c)
+                if (m_blk + 4 * c < M)  // a copy whose four rows all lie past M is skipped (see below)
+                    copy16(stage_lds + (uint32_t)(q * ABYTES + 1024 * c), a_voff[c], Ag);
         }
         {
             const int nq = min(GPW, n_w - base);  // groups of this round (>= 1)

@@ -16,9 +16,19 @@
 // weight rows; the group's scale and bias likewise.
 //
 // Work decomposition: a workgroup of 4 waves computes 16 output columns (4 per wave)
-// over one partition; lane l of a wave takes chunks l, l+64, ..., issuing all of its
-// weight loads (NCH chunks x 4 rows) before any arithmetic. Lane partial sums are
-// reduced across the wave in a fixed order (deterministic).
+// over one partition. A wave's work is split into items of RG rows (4 or 2) by one
+// chunk; lane l takes items l, l+64, ..., so consecutive lanes read consecutive 16 bytes
+// of a row (whole cache lines) and every lane gets the same number of items to within
+// one. Per-lane sums are reduced across the wave in a fixed order (deterministic).
+//
+// Schedule: the dispatch is over before the first weight byte arrives unless every load
+// is in flight early, so a thread issues its activation loads, then the scale and bias of
+// its items, then all of its weight loads, before any arithmetic. The activation staging
+// waits only for the activation loads (they return first) and the barrier after it waits
+// only for the LDS writes, so both overlap the weight stream; each item's arithmetic then
+// waits for its own weights. Issued after the weights, the staging loads had cost a
+// second and third memory round trip per call (decode shapes of Qwen3-4B on MI355X:
+// 15-35 % of the call at M = 1).
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -43,12 +53,19 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int k)
     return ((w >> (4 * k)) & 0x000F000Fu) | 0x43004300u;
 }
 
-template <int MM, int NCH>
+// LDS writes of this wave done, then the workgroup barrier; the memory clobber keeps the
+// compiler from moving LDS accesses across it. Unlike __syncthreads() it does not wait for
+// the weight loads still in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int MM, int RG, int NCHM>
 __global__ void __launch_bounds__(256)
 gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, const uint16_t *__restrict__ scale,
             const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int M, int N, int K, int gpp)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    asm volatile("" ::"s"(A), "s"(Wq), "s"(scale), "s"(bias), "s"(out));
+    constexpr int NRG = ROWS_PER_WAVE / RG;  // row groups of a wave
     const int G = K >> 7;
     const int p = blockIdx.y;
     const int g0 = p * gpp;
@@ -56,92 +73,104 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     const int WP = gpp * 16;  // packed words of a row in the partition
     const int CP = gpp * 4;   // 16-byte chunks of a row in the partition
     const int n_blk = blockIdx.x * ROWS_PER_WG;
-    uint4 *apair = reinterpret_cast<uint4 *>(lds);                       // [MM][WP]: pairs of word w
-    float *asum = reinterpret_cast<float *>(apair + MM * WP);            // [MM][CP]
-    uint32_t *sb = reinterpret_cast<uint32_t *>(asum + MM * CP);         // [16][gpp]: scale | bias << 16
+    uint4 *apair = reinterpret_cast<uint4 *>(lds);             // [MM][WP]: pairs of word w
+    float *asum = reinterpret_cast<float *>(apair + MM * WP);  // [MM][CP]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    // Weight loads first: rows past N re-read row N-1, chunks past the partition re-read
-    // its last chunk (neither is used).
-    uint4 wr[ROWS_PER_WAVE][NCH];
+    // 1. Activation loads: each thread owns up to ITEMS (row, chunk) items of the partition
+    // (rows m >= M stage zeros). CPMAX: the most chunks a row's partition has
+    // (gemv_split_fits).
+    constexpr int CPMAX = MM == 1 || MM == 2 ? 320 : MM == 4 ? 240 : 128;
+    constexpr int ITEMS = (MM * CPMAX + 255) / 256;
+    uint4 av[ITEMS][4];
 #pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; ++r) {
-        const int n = min(n_blk + ROWS_PER_WAVE * wave + r, N - 1);
-        const uint4 *row = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K >> 3) + (k0 >> 3));
+    for (int it = 0; it < ITEMS; ++it) {
+        const int idx = threadIdx.x + 256 * it;
+        const int m = idx / CP, c = idx - m * CP;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) wr[r][i] = row[min(lane + 64 * i, CP - 1)];
-    }
-
-    // A in pair order and its chunk sums (rows m >= M are zero), then scale and bias.
-    // Each thread owns up to ITEMS (row, chunk) items and issues all of their loads
-    // before converting any, so the staging costs one memory round trip.
-    constexpr int ITEMS = (MM * 10240 / 32 + 255) / 256 < 4 ? (MM * 10240 / 32 + 255) / 256 : 4;
-    {
-        uint4 av[ITEMS][4];
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int idx = threadIdx.x + 256 * it;
-            const int m = idx / CP, c = idx - m * CP;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                av[it][w] = make_uint4(0u, 0u, 0u, 0u);
-                if (idx < MM * CP && m < M)
-                    av[it][w] = *reinterpret_cast<const uint4 *>(A + (size_t)m * (size_t)K + k0 + 32 * c + 8 * w);
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < ITEMS; ++it) {
-            const int idx = threadIdx.x + 256 * it;
-            if (idx >= MM * CP) break;
-            const int m = idx / CP, c = idx - m * CP;
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t e[4] = {av[it][w].x, av[it][w].y, av[it][w].z, av[it][w].w};
-                // e[j]: values 2j (low half) and 2j+1 (high half); pair i = (a[i], a[i+4])
-                uint4 pr;
-                pr.x = (e[0] & 0xFFFFu) | (e[2] << 16);
-                pr.y = (e[0] >> 16) | (e[2] & 0xFFFF0000u);
-                pr.z = (e[1] & 0xFFFFu) | (e[3] << 16);
-                pr.w = (e[1] >> 16) | (e[3] & 0xFFFF0000u);
-                apair[m * WP + 4 * c + w] = pr;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s += bf16_to_f32(e[j] & 0xFFFFu) + bf16_to_f32(e[j] >> 16);
-            }
-            asum[m * CP + c] = s;
+        for (int w = 0; w < 4; ++w) {
+            av[it][w] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < MM * CP && m < M)
+                av[it][w] = *reinterpret_cast<const uint4 *>(A + (size_t)m * (size_t)K + k0 + 32 * c + 8 * w);
         }
     }
-    for (int idx = threadIdx.x; idx < ROWS_PER_WG * gpp; idx += blockDim.x) {
-        const int r = idx / gpp, g = idx - r * gpp;
-        const int n = min(n_blk + r, N - 1);
-        sb[idx] = (uint32_t)scale[(size_t)n * G + g0 + g] | ((uint32_t)bias[(size_t)n * G + g0 + g] << 16);
+    // 2. Scale/bias, then weights, of the lane's items: item idx of the wave is row group
+    // idx / CP (rows RG*rg .. RG*rg + RG-1 of the wave), chunk idx % CP. Items past the
+    // wave's last re-read its last one, rows past N re-read row N-1 (neither is used).
+    const int nit = NRG * CP;
+    uint32_t sbv[NCHM][RG];
+    uint4 wr[NCHM][RG];
+#pragma unroll
+    for (int i = 0; i < NCHM; ++i) {
+        const int idx = min(lane + 64 * i, nit - 1);
+        const int rg = idx / CP, c = idx - rg * CP;
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr) {
+            const int n = min(n_blk + ROWS_PER_WAVE * wave + RG * rg + rr, N - 1);
+            const size_t e = (size_t)n * G + g0 + (c >> 2);
+            sbv[i][rr] = (uint32_t)scale[e] | ((uint32_t)bias[e] << 16);
+        }
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NCHM; ++i) {
+        const int idx = min(lane + 64 * i, nit - 1);
+        const int rg = idx / CP, c = idx - rg * CP;
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr) {
+            const int n = min(n_blk + ROWS_PER_WAVE * wave + RG * rg + rr, N - 1);
+            wr[i][rr] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K >> 3) + (k0 >> 3))[c];
+        }
+    }
+    // Without the fence the compiler sinks each load next to its first use.
+    __builtin_amdgcn_sched_barrier(0);
 
+    // 3. Activation pairs (a[i], a[i+4]) of each packed word and the chunk sums into LDS.
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const int idx = threadIdx.x + 256 * it;
+        if (idx >= MM * CP) break;
+        const int m = idx / CP, c = idx - m * CP;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t e[4] = {av[it][w].x, av[it][w].y, av[it][w].z, av[it][w].w};
+            uint4 pr;
+            pr.x = (e[0] & 0xFFFFu) | (e[2] << 16);
+            pr.y = (e[0] >> 16) | (e[2] & 0xFFFF0000u);
+            pr.z = (e[1] & 0xFFFFu) | (e[3] << 16);
+            pr.w = (e[1] >> 16) | (e[3] & 0xFFFF0000u);
+            apair[m * WP + 4 * c + w] = pr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s += bf16_to_f32(e[j] & 0xFFFFu) + bf16_to_f32(e[j] >> 16);
+        }
+        asum[m * CP + c] = s;
+    }
+    lds_barrier();
+
+    // 4. Each item as its weights arrive.
     float acc[ROWS_PER_WAVE][MM];
 #pragma unroll
     for (int r = 0; r < ROWS_PER_WAVE; ++r)
 #pragma unroll
         for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
-
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = lane + 64 * i;
-        if (c >= CP) break;  // the lane's remaining chunks are all past the partition
-        uint32_t pr[ROWS_PER_WAVE][16];
-        float sc[ROWS_PER_WAVE], bi[ROWS_PER_WAVE];
+    for (int i = 0; i < NCHM; ++i) {
+        const int idx = lane + 64 * i;
+        if (idx >= nit) break;
+        const int rg = idx / CP, c = idx - rg * CP;
+        uint32_t pr[RG][16];
+        float sc[RG], bi[RG];
 #pragma unroll
-        for (int r = 0; r < ROWS_PER_WAVE; ++r) {
-            const uint32_t wv[4] = {wr[r][i].x, wr[r][i].y, wr[r][i].z, wr[r][i].w};
+        for (int rr = 0; rr < RG; ++rr) {
+            const uint32_t wv[4] = {wr[i][rr].x, wr[i][rr].y, wr[i][rr].z, wr[i][rr].w};
 #pragma unroll
             for (int w = 0; w < 4; ++w)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) pr[r][4 * w + k] = nib_pair(wv[w], k);
-            const uint32_t v = sb[(ROWS_PER_WAVE * wave + r) * gpp + (c >> 2)];
-            sc[r] = bf16_to_f32(v & 0xFFFFu);
-            bi[r] = bf16_to_f32(v >> 16);
+                for (int k = 0; k < 4; ++k) pr[rr][4 * w + k] = nib_pair(wv[w], k);
+            sc[rr] = bf16_to_f32(sbv[i][rr] & 0xFFFFu);
+            bi[rr] = bf16_to_f32(sbv[i][rr] >> 16);
         }
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
@@ -150,16 +179,19 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
             for (int w = 0; w < 4; ++w) ap[w] = apair[m * WP + 4 * c + w];
             const float s = asum[m * CP + c];
 #pragma unroll
-            for (int r = 0; r < ROWS_PER_WAVE; ++r) {
+            for (int rr = 0; rr < RG; ++rr) {
                 float q = 0.f;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    q = dot2(pr[r][4 * w + 0], ap[w].x, q);
-                    q = dot2(pr[r][4 * w + 1], ap[w].y, q);
-                    q = dot2(pr[r][4 * w + 2], ap[w].z, q);
-                    q = dot2(pr[r][4 * w + 3], ap[w].w, q);
+                    q = dot2(pr[rr][4 * w + 0], ap[w].x, q);
+                    q = dot2(pr[rr][4 * w + 1], ap[w].y, q);
+                    q = dot2(pr[rr][4 * w + 2], ap[w].z, q);
+                    q = dot2(pr[rr][4 * w + 3], ap[w].w, q);
                 }
-                acc[r][m] += sc[r] * (q - 128.f * s) + bi[r] * s;
+                const float v = sc[rr] * (q - 128.f * s) + bi[rr] * s;
+#pragma unroll
+                for (int g = 0; g < NRG; ++g)
+                    if (NRG == 1 || rg == g) acc[RG * g + rr][m] += v;
             }
         }
     }
@@ -187,15 +219,15 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     }
 }
 
-template <int MM, int NCH>
+template <int MM, int RG, int NCHM>
 hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, int M, int N,
                       int K, int s, hipStream_t stream)
 {
     const int gpp = (K / 128) / s;
-    const size_t lds = (size_t)MM * gpp * 16 * 16 + (size_t)MM * gpp * 4 * 4 + (size_t)ROWS_PER_WG * gpp * 4;
+    const size_t lds = (size_t)MM * gpp * 16 * 16 + (size_t)MM * gpp * 4 * 4;
     const dim3 grid((N + ROWS_PER_WG - 1) / ROWS_PER_WG, s);
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemv_kernel<MM, NCH>), grid, dim3(256), lds, stream, static_cast<const uint16_t *>(A),
+    hipLaunchKernelGGL((gemv_kernel<MM, RG, NCHM>), grid, dim3(256), lds, stream, static_cast<const uint16_t *>(A),
                        static_cast<const uint32_t *>(Wq), static_cast<const uint16_t *>(scale),
                        static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(out), M, N, K, gpp);
     return hipGetLastError();
@@ -212,13 +244,23 @@ hipError_t launch_w4a16_gemv(const void *A, const void *Wq, const void *scale, c
     const int kp = K / s;
     const int mm = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     if (!gemv_split_fits(mm, kp)) return hipErrorInvalidValue;
-    const int nch = (kp / 32 + 63) / 64;
-#define QMM_G(MM_, NCH_)                                                                                         \
-    if (mm == MM_ && nch == NCH_) return launch_cfg<MM_, NCH_>(A, Wq, scale, bias, out, M, N, K, s, stream);
-    QMM_G(1, 1) QMM_G(1, 2) QMM_G(1, 3) QMM_G(1, 4) QMM_G(1, 5)
-    QMM_G(2, 1) QMM_G(2, 2) QMM_G(2, 3) QMM_G(2, 4) QMM_G(2, 5)
-    QMM_G(4, 1) QMM_G(4, 2) QMM_G(4, 3) QMM_G(4, 4)
-    QMM_G(8, 1) QMM_G(8, 2)
+    // Rows per lane item: RG = 4 shares each chunk's activation reads over 4 rows; RG = 2
+    // makes the items half as large, which evens out the lanes' work when a row's chunks are
+    // not a multiple of 64 (K = 2560: 80 chunks, 2 items of 4 rows on some lanes, 1 on the
+    // others). Per lane the cost is about items * (RG + MM/2) row-chunks of arithmetic;
+    // ties go to 4 (decode sweeps of the Qwen3-4B projections on MI355X).
+    const int cp = kp / 32;
+    const int it4 = (cp + 63) / 64, it2 = (2 * cp + 63) / 64;
+    const int rg = it2 * (4 + mm) < it4 * (8 + mm) ? 2 : 4;
+    const int nch = rg == 4 ? it4 : it2;
+    const int nchm = nch <= 2 ? 2 : nch <= 3 ? 3 : nch <= 5 ? 5 : 10;
+#define QMM_G(MM_, RG_, NCH_)                                                                                    \
+    if (mm == MM_ && rg == RG_ && nchm == NCH_) return launch_cfg<MM_, RG_, NCH_>(A, Wq, scale, bias, out, M, N, K, s, stream);
+#define QMM_GM(MM_) QMM_G(MM_, 4, 2) QMM_G(MM_, 4, 3) QMM_G(MM_, 4, 5) \
+                    QMM_G(MM_, 2, 2) QMM_G(MM_, 2, 3) QMM_G(MM_, 2, 5) QMM_G(MM_, 2, 10)
+    QMM_GM(1) QMM_GM(2) QMM_GM(4)
+    QMM_G(8, 4, 2) QMM_G(8, 2, 2) QMM_G(8, 2, 3) QMM_G(8, 2, 5)
+#undef QMM_GM
 #undef QMM_G
     return hipErrorInvalidValue;
 }

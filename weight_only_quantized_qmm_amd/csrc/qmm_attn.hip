@@ -28,7 +28,8 @@
 //     the tile and streams the value rows with 16-byte loads;
 //   * a tile's key and value loads are all issued before its first MFMA.
 // The waves then merge in LDS (same rule), and the workgroup writes either O (one
-// split) or its partial accumulator, max and sum; a second kernel merges the splits.
+// split) or its partial accumulator, max and sum; a second kernel merges the splits, 16
+// at a time with the same rule.
 // Masked and out-of-range keys read the split's last key (never past the cache) and
 // get probability 0.
 #include "qmm_device.h"
@@ -292,19 +293,15 @@ attn_merge_kernel(const float *__restrict__ part_acc, const float *__restrict__ 
     if (t >= (size_t)rows * (D / 8)) return;
     const size_t row = t / (D / 8);
     const int dd = 8 * (int)(t % (D / 8));
-    // A split with no allowed key for this row stored max -inf, sum 0 and a zero
-    // accumulator: its weight exp2(-inf - m) is 0, so no branch is needed. The splits
-    // are read in batches of eight whose loads are all issued before their use.
-    constexpr int BATCH = 8;
+    // The splits are read in batches of 16 whose loads are all issued before their use, so
+    // up to 16 splits cost one memory round trip. Each batch is folded in with the online
+    // rule: the running max m moves to the batch's max, the running sum and accumulator
+    // are rescaled by exp2(m_old - m_new), and the batch's splits are added with weights
+    // exp2(m_split - m_new). With one batch this is the plain two-pass merge (global max,
+    // then the weighted sums). A split with no allowed key for this row stored max -inf,
+    // sum 0 and a zero accumulator, so its weight is 0 and needs no branch.
+    constexpr int BATCH = 16;
     float m = NEG_INF;
-    for (int p0 = 0; p0 < S; p0 += BATCH) {
-        float mv[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u)
-            mv[u] = p0 + u < S ? part_ml[((size_t)(p0 + u) * rows + row) * 2] : NEG_INF;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) m = fmaxf(m, mv[u]);
-    }
     float lsum = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int p0 = 0; p0 < S; p0 += BATCH) {
@@ -318,13 +315,24 @@ attn_merge_kernel(const float *__restrict__ part_acc, const float *__restrict__ 
             x[u] = *reinterpret_cast<const float4 *>(pa);
             y[u] = *reinterpret_cast<const float4 *>(pa + 4);
         }
+        float mb = NEG_INF;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+            if (p0 + u < S) mb = fmaxf(mb, ml[u].x);
+        const float m_new = fmaxf(m, mb);
+        if (m_new == NEG_INF) continue;  // no allowed key in any split so far
+        const float c = exp2f(m - m_new);  // 0 for the first batch with an allowed key
+        lsum *= c;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= c;
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const float f = p0 + u < S ? exp2f(ml[u].x - m) : 0.f;
+            const float f = p0 + u < S ? exp2f(ml[u].x - m_new) : 0.f;
             lsum += f * ml[u].y;
             o[0] += f * x[u].x; o[1] += f * x[u].y; o[2] += f * x[u].z; o[3] += f * x[u].w;
             o[4] += f * y[u].x; o[5] += f * y[u].y; o[6] += f * y[u].z; o[7] += f * y[u].w;
         }
+        m = m_new;
     }
     const float inv = 1.f / lsum;
     uint4 ov;

@@ -22,7 +22,7 @@
 //     queries as the second, straight from global memory (a lane loads 16 bytes of a
 //     key row per 32-wide reduction step), so a lane holds four keys of one row;
 //   * online softmax per tile: row max and row sum across the four lanes of a row
-//     (two butterfly steps), rescale factor exp2(m_old - m_new);
+//     (two butterfly steps by lane swaps), rescale factor exp2(m_old - m_new);
 //   * P . V on the vector ALU in fp32: the tile's probabilities go to LDS transposed
 //     (key-major), a lane owns 8 head dimensions of every row for every fourth key of
 //     the tile and streams the value rows with 16-byte loads;
@@ -154,8 +154,7 @@ attn_split_kernel(AttnArgs a)
                 sc[blk][e] = v;
                 tmax = fmaxf(tmax, v);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = xor32_max(xor16_max(tmax));
         const float m_new = fmaxf(m_run, tmax);
         const float m_use = m_new == NEG_INF ? 0.f : m_new;  // a row with no allowed key yet
         const float corr = exp2f(m_run - m_use);
@@ -168,8 +167,7 @@ attn_split_kernel(AttnArgs a)
                 sc[blk][e] = pv;
                 psum += pv;
             }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
+        psum = xor32_add(xor16_add(psum));
         l_run = l_run * corr + psum;
         m_run = m_new;
         // probabilities key-major, and each row's rescale factor, for the P.V part
@@ -221,8 +219,7 @@ attn_split_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = acc[r][e];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
+            v = xor32_add(xor16_add(v));
             acc[r][e] = v;
         }
     __syncthreads();  // every wave is done with its tile area before the merge area is written

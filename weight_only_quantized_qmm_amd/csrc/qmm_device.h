@@ -84,4 +84,44 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 x, bf16x8 y, f32x16 d) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, d, 0, 0, 0);
 }
 
+// Butterfly partners 16 and 32 lanes apart on the vector ALU: v_permlane16_swap
+// (v_permlane32_swap) of two copies of v leaves lane i holding, between the two copies,
+// its own value and that of lane i ^ 16 (i ^ 32), in an order that depends on the lane.
+// A sum or maximum of the pair is therefore the butterfly step, the same on both partner
+// lanes and bit-identical to v + __shfl_xor(v, 16 or 32), without the round trip through
+// LDS that ds_bpermute makes.
+__device__ __forceinline__ float xor16_add(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_add(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over the 16 lanes of each row of the wave, left in every lane of the row, by DPP
+// moves: partners i ^ 1 and i ^ 2 (quad permutes), then the other quad of the half-row
+// (half-row mirror) and the other half of the row (row mirror). Each pairing is its own
+// inverse and every lane adds its value and its partner's, so all lanes of a row end
+// with the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_mov<0x141>(v);  // row_half_mirror
+    v += dpp_mov<0x140>(v);  // row_mirror
+    return v;
+}
+
 }  // namespace qmm_dev

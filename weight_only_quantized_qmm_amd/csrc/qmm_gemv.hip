@@ -196,14 +196,13 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
         }
     }
 
-    // Wave sums, butterfly in a fixed order; lane 0 stores.
+    // Wave sums in a fixed order (within rows of 16 lanes, then across them); lane 0 stores.
 #pragma unroll
     for (int r = 0; r < ROWS_PER_WAVE; ++r)
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             float v = acc[r][m];
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+            v = xor32_add(xor16_add(row16_sum(v)));
             acc[r][m] = v;
         }
     if (lane == 0) {

@@ -17,10 +17,11 @@
 //   * each wave issues every load of a round of up to GPW groups before it computes:
 //     the round's activations go straight into the wave's own LDS staging slots
 //     (global_load_lds, 1 KB per instruction: four rows of 256 bytes, so each copy
-//     touches 8 whole cache lines), the packed weights (one 16-byte load per lane and
-//     16-column subtile; 16 rows of 64 bytes) and the scale/bias of its rows into
-//     registers; then it waits once and runs the MFMAs of the round, reading its
-//     activation operands from LDS;
+//     touches 8 whole cache lines), the scale/bias entries of its rows into the wave's
+//     own LDS arrays (global_load_lds, 64 entries per instruction), and the packed
+//     weights into registers (one 16-byte load per lane and 16-column subtile; 16 rows
+//     of 64 bytes); then it waits once and runs the MFMAs of the round, reading its
+//     activation operands and scale/bias from LDS;
 //   * the waves' fp32 tiles meet in LDS and are summed in ascending wave order
 //     (deterministic), rounded once to bf16 and stored with 8-byte stores.
 // Loading the activations in MFMA operand order straight into registers instead touches
@@ -36,8 +37,9 @@
 //
 // LDS: wave w's staging slots are [GPW][16*MT rows][256 bytes] at w*GPW*MT*4 KB; chunk c
 // (16 bytes) of row r is stored at chunk c ^ (r % 16), so the 16 rows that one 16-lane
-// phase of an operand read touches fall on distinct banks. After the main loop the same
-// memory holds the waves' fp32 tiles for the cross-wave sum.
+// phase of an operand read touches fall on distinct banks. The waves' scale and bias
+// arrays follow the staging slots. After the main loop the same memory holds the waves'
+// fp32 tiles for the cross-wave sum.
 #include "qmm_device.h"
 #include "qmm_launch.h"
 

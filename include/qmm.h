@@ -117,8 +117,8 @@ typedef struct qmm_plan {
 
 /* The page's rule: 32 x 32 tiles, 320 target blocks, cap 16, one group per partition. */
 extern const qmm_policy QMM_POLICY_PAGE;
-/* The rule re-tuned for MI355X (256 CUs): {0, 0, 256, 16, 512}, kernel tiles, 256 target
- * blocks (the CU count), cap 16, at least 512 K values per partition; used when s = 0 is
+/* The rule re-tuned for MI355X (256 CUs): {0, 0, 256, 20, 512}, kernel tiles, 256 target
+ * blocks (the CU count), cap 20, at least 512 K values per partition; used when s = 0 is
  * passed to qmm_w4a16_g128. */
 extern const qmm_policy QMM_POLICY_MI355X;
 

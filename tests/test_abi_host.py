@@ -98,10 +98,12 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
     assert plan.workspace_bytes == (2 * plan.s * M * N if plan.s > 1 else 0)
     # the small-M kernel runs M <= 64, and M <= 128 with N*K <= 2^24 (64-row blocks)
-    assert (plan.block_n == 256) == (M > 64 and not (M <= 128 and N * K <= 1 << 24))
-    if plan.block_n == 256:  # the large-M kernel: slot-filling rule, two workgroups per CU for 128-row tiles
-        # two 128-row workgroups per CU up to M = 128; above, either tile counts one per CU
-        slots = pol.target_blocks * (2 if plan.block_m == 128 and M <= 128 else 1)
+    wide = plan.block_m >= 128
+    assert wide == (M > 64 and not (M <= 128 and N * K <= 1 << 24))
+    if wide:  # the large-M kernel: slot-filling rule over its tiles (128 x 256, 128 x 128, 256 x 256)
+        assert (plan.block_m, plan.block_n) in ((128, 256), (128, 128), (256, 256))
+        # two 128 x 256 workgroups per CU up to M = 128; every other tile counts one per CU
+        slots = pol.target_blocks * (2 if (plan.block_m, plan.block_n) == (128, 256) and M <= 128 else 1)
         num_m = -(-M // plan.block_m)
         assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
             tiles, num_m, K, slots, pol.cap, pol.min_k_per_split)
@@ -131,10 +133,10 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
 FORMATS = [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
 
 
-def _wide_lds_bytes(rows, bits, group):
-    # three stage slots of A (rows x 64 bf16) and of W (256 rows x 64 codes), two of the
-    # 128-value block's scale and bias dwords (256 rows x 128/group groups each)
-    return 3 * rows * 128 + 3 * 256 * 64 * bits // 8 + 2 * 2 * 256 * 4 * (128 // group)
+def _wide_lds_bytes(rows, bits, group, cols=256):
+    # three stage slots of A (rows x 64 bf16) and of W (cols rows x 64 codes), two of the
+    # 128-value block's scale and bias dwords (cols rows x 128/group groups each)
+    return 3 * rows * 128 + 3 * cols * 64 * bits // 8 + 2 * 2 * cols * 4 * (128 // group)
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)
@@ -145,10 +147,11 @@ def test_wna16_plan_follows_the_rule_for_each_format(bits, group):
         plan = q.qmm_wna16_plan(bits, group, M, N, K)
         ref = q.qmm_splitk_plan(M, N, K)
         assert (plan.block_m, plan.block_n, plan.base_tiles) == (ref.block_m, ref.block_n, ref.base_tiles)
-        if plan.block_n != 256 or (bits, group) == (4, 128):
+        if plan.block_m < 128 or (bits, group) == (4, 128):
             assert (plan.s, plan.full_tiles, plan.grid_x) == (ref.s, ref.full_tiles, ref.grid_x), (name, M)
             continue
-        wgs = 2 if plan.block_m == 128 and M <= 128 and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024 else 1
+        wgs = 2 if ((plan.block_m, plan.block_n) == (128, 256) and M <= 128
+                    and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024) else 1
         tiles = plan.base_tiles
         num_m = -(-M // plan.block_m)
         assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
@@ -162,32 +165,54 @@ def test_wna16_plan_lds_budget():
     assert max(_wide_lds_bytes(256, *f) for f in FORMATS) <= 160 * 1024
 
 
-def _wide_cost(T, rows, s, full, G):
+def _wide_cost(T, rows, cols, s, full, G):
     # critical path in 128 x 256 x 128 blocks over rounds of 256 workgroups, plus half a
     # block per partition of a split
-    t = -(-full // 256) * G * rows / 128
+    blk = rows / 128 * cols / 256
+    t = -(-full // 256) * G * blk
     if T - full > 0 and s > 1:
-        t += -(-((T - full) * s) // 256) * -(-G // s) * rows / 128 + 0.5 * s
+        t += -(-((T - full) * s) // 256) * -(-G // s) * blk + 0.5 * s
     return t
 
 
-@pytest.mark.parametrize("M,N,K", [(M, N, K) for M, N, K in ALL_SHAPES if M > 128])
-def test_large_m_variant_choice(M, N, K):
+def _wide_choice(M, N, K):
+    # candidates in tie order: 256 x 256 (above M = 128), 128 x 256 (two workgroups per
+    # CU up to M = 128), 128 x 128 (only as a pure split: fewer tiles than CUs)
     pol = q.policy_preset("QMM_POLICY_MI355X")
-    plan = q.qmm_splitk_plan(M, N, K)
     G = K // 128
-    cost = {}
-    for rows in (128, 256):
-        T = -(-M // rows) * -(-N // 256)
-        s, full = opolicy.fill_decomposition(T, -(-M // rows), K, pol.target_blocks, pol.cap, pol.min_k_per_split)
-        cost[rows] = _wide_cost(T, rows, s, full, G)
-    assert plan.block_m == (128 if cost[128] < cost[256] else 256), (cost, plan.block_m)
+    best = None
+    for rows, cols in ((256, 256), (128, 256), (128, 128)):
+        if rows == 256 and M <= 128:
+            continue
+        num_m = -(-M // rows)
+        T = num_m * -(-N // cols)
+        if cols == 128 and T >= 256:
+            continue
+        slots = pol.target_blocks * (2 if (rows, cols) == (128, 256) and M <= 128 else 1)
+        s, full = opolicy.fill_decomposition(T, num_m, K, slots, pol.cap, pol.min_k_per_split)
+        c = _wide_cost(T, rows, cols, s, full, G)
+        if best is None or c < best[0]:
+            best = (c, rows, cols)
+    return best[1:]
+
+
+@pytest.mark.parametrize("M,N,K", [(M, N, K) for M, N, K in ALL_SHAPES
+                                   if M > 64 and not (M <= 128 and N * K <= 1 << 24)])
+def test_large_m_variant_choice(M, N, K):
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert (plan.block_m, plan.block_n) == _wide_choice(M, N, K)
 
 
 def test_large_m_variant_on_the_sweep():
-    # q and k/v at M = 2048 take 128-row tiles, the other projections 256-row tiles
-    got = {n: q.qmm_splitk_plan(M, N, K).block_m for n, M, N, K, _ in syn.projection_sweep() if M == 2048}
-    assert got == {"q": 128, "k": 128, "v": 128, "o": 256, "gate": 256, "up": 256, "down": 256}
+    # M = 2048: q on 128 x 256 tiles, k/v on 128 x 128, the rest on 256 x 256; M = 128:
+    # gate, up and down on 128 x 128 (q, k, v, o run the small-M kernel)
+    got = {(n, M): (p.block_m, p.block_n) for n, M, N, K, _ in syn.projection_sweep() if M in (128, 2048)
+           for p in [q.qmm_splitk_plan(M, N, K)]}
+    big = {n: got[(n, 2048)] for n in ("q", "k", "v", "o", "gate", "up", "down")}
+    assert big == {"q": (128, 256), "k": (128, 128), "v": (128, 128), "o": (256, 256), "gate": (256, 256),
+                   "up": (256, 256), "down": (256, 256)}
+    assert all(got[(n, 128)] == (128, 128) for n in ("gate", "up", "down"))
+    assert all(got[(n, 128)][0] == 64 for n in ("q", "k", "v", "o"))
 
 
 def test_fill_decomposition_cases():

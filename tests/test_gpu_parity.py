@@ -194,7 +194,8 @@ def test_streamk_matches_oracle(M, N, K, Ps):
     # one workgroup per tile: every tile whole, the large-M kernel's unsplit decomposition
     # (the same launch as s = 1 where the plan runs that kernel)
     c1 = host_bits(run_streamk(dv, M, N, K, num_m * num_n))
-    if q.qmm_splitk_plan(M, N, K).block_n == 256:
+    plan = q.qmm_splitk_plan(M, N, K)
+    if (plan.block_m, plan.block_n) == (BM, 256):  # s = 1 runs the same tiles
         assert np.array_equal(c1, host_bits(run_w4a16(dv, M, N, K, 1)))
     for P in Ps:
         Peff = P or max(1, min(num_m * num_n * G // min(4, G), 256 * (2 if BM == 128 else 1)))

@@ -71,33 +71,49 @@ Decomp wide_rule(long long T, long long num_m, int G, int K, long long target, c
     return d;
 }
 
-// Critical path of a large-M decomposition of T tiles of `rows` rows (one workgroup per
+// Critical path of a large-M decomposition of T tiles of rows x cols (one workgroup per
 // CU, the unsplit rounds first, then the split tail) in units of one 128-row x 256-column x
 // 128-value block, plus half a unit per partition of a split for its planes and reduce.
-double wide_cost(long long T, int rows, const Decomp &d, int G)
+double wide_cost(long long T, int rows, int cols, const Decomp &d, int G)
 {
-    const double blk = rows / 128.0;
+    const double blk = rows / 128.0 * cols / 256.0;
     const long long full = d.full_tiles, tail = T - full;
     double t = (double)ceil_div(full, kCUs) * G * blk;
     if (tail > 0 && d.s > 1) t += (double)ceil_div(tail * d.s, kCUs) * ceil_div(G, d.s) * blk + 0.5 * d.s;
     return t;
 }
 
-// Large-M variant for M > 128: 256-row tiles (variant 2) or 128-row tiles (variant 0),
-// each with one workgroup per CU, under the MI355X preset's split rule; the smaller
-// critical path wins, ties to 256-row tiles. On the Qwen3-4B shapes at M = 2048 this
-// takes 128-row tiles for q (256 tiles, no split) and k, v (1024 workgroups in four
-// partitions instead of 320 in five, with a third of the CUs idle in the last round),
-// which tile sweeps on MI355X measured 11-12 % faster, and 256-row tiles elsewhere.
+// Large-M variant: each candidate under the preset's split rule over its own tiles, the
+// smallest critical path winning:
+//   variant 0, 128 x 256 tiles (two workgroups per CU up to M = 128, one above);
+//   variant 2, 256 x 256 tiles, above M = 128;
+//   variant 1, 128 x 128 tiles, only while they are fewer than the CUs (a pure split, one
+//   workgroup per CU): it halves the split of shapes whose 256-column tiles must split
+//   deeply. Ties go to the larger tiles (2, then 0, then 1).
+// On the Qwen3-4B shapes this takes 128 x 256 tiles for q at M = 2048 (256 tiles, no split),
+// 128 x 128 tiles for k and v at M = 2048 (128 tiles in two partitions instead of 64 in
+// four) and for gate, up and down at M = 128 (three and twelve partitions instead of five
+// and nineteen), and 256 x 256 tiles for o, gate, up and down at M = 2048. Split sweeps on
+// MI355X: k, v 8 %, gate, up 13 %, down 9 % faster than on 128 x 256 tiles.
 int wide_variant(int M, int N, int K)
 {
-    if (M <= 128) return 0;
     const qmm_policy &pol = QMM_POLICY_MI355X;
     const int G = K / kGroup;
-    const long long T2 = ceil_div(M, 256) * ceil_div(N, 256), T0 = ceil_div(M, 128) * ceil_div(N, 256);
-    const Decomp d2 = wide_rule(T2, ceil_div(M, 256), G, K, pol.target_blocks, pol);
-    const Decomp d0 = wide_rule(T0, ceil_div(M, 128), G, K, pol.target_blocks, pol);
-    return wide_cost(T0, 128, d0, G) < wide_cost(T2, 256, d2, G) ? 0 : 2;
+    int best = -1;
+    double best_cost = 0;
+    for (int v : {2, 0, 1}) {
+        if (v == 2 && M <= 128) continue;
+        const int rows = qmm_impl::wide_rows(v), cols = qmm_impl::wide_cols(v);
+        const long long num_m = ceil_div(M, rows), T = num_m * ceil_div(N, cols);
+        if (v == 1 && T >= kCUs) continue;
+        const long long slots = (long long)pol.target_blocks * (v == 0 && M <= 128 ? qmm_impl::wide_wgs_per_cu(0) : 1);
+        const double c = wide_cost(T, rows, cols, wide_rule(T, num_m, G, K, slots, pol), G);
+        if (best < 0 || c < best_cost) {
+            best = v;
+            best_cost = c;
+        }
+    }
+    return best;
 }
 
 // Kernel and block tile for an (M, N, K) problem. The small-M kernel takes up to 64 rows
@@ -105,9 +121,7 @@ int wide_variant(int M, int N, int K)
 // most 8 MB (N*K <= 2^24): there the large-M kernel has too few 256-column tiles and must
 // split deeply, while reading the weights twice costs less (split sweeps of the Qwen3-4B
 // q, k and v projections at M = 128 on MI355X: 25-45 % faster; gate, up and down stay on
-// the large-M kernel). Otherwise the large-M kernel: 128-row tiles (two workgroups per CU)
-// up to 128 rows; above, 128-row tiles or 256-row tiles of eight 256 x 32 waves, as
-// wide_variant picks.
+// the large-M kernel). Otherwise the large-M kernel, in the tile variant wide_variant picks.
 W4A16Tile w4a16_tile(int M, int N, int K) {
     W4A16Tile t;
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
@@ -136,7 +150,7 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.ns = wide_variant(M, N, K);
-        t.mt = t.ns == 0 ? 8 : 16;
+        t.mt = qmm_impl::wide_rows(t.ns) / 16;
     }
     return t;
 }
@@ -214,10 +228,10 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
     const long long kernel_tiles = ceil_div(M, tile.block_m()) * ceil_div(N, tile.block_n());
     Decomp d;
     if (tile.kind == qmm_impl::W4A16_WIDE && pol.tile_m == 0 && pol.tile_n == 0) {
-        // slots: target_blocks times the workgroups of this kernel one CU holds; 128-row
-        // tiles above M = 128 count one per CU, as the variant choice does
+        // slots: target_blocks times the workgroups of this kernel one CU holds; 128 x 256
+        // tiles above M = 128 and 128 x 128 tiles count one per CU, as the variant choice does
         const long long slots =
-            (long long)pol.target_blocks * (M > 128 ? 1 : qmm_impl::wide_wgs_per_cu(tile.ns, fmt));
+            (long long)pol.target_blocks * (M > 128 || tile.ns == 1 ? 1 : qmm_impl::wide_wgs_per_cu(tile.ns, fmt));
         d = wide_rule(kernel_tiles, ceil_div(M, tile.block_m()), G, K, slots, pol);
     } else {
         qmm_policy p = pol;

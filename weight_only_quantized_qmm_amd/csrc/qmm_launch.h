@@ -10,15 +10,20 @@ namespace qmm_impl {
 // Which W4A16 kernel runs a problem, and the output tile of one workgroup.
 //   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x (16*ns) tile, ns 1 to 4,
 //          up to 16 waves splitting its reduction;
-//   WIDE   (otherwise): a (16*mt) x 256 tile, mt = 8 (variant 0) or 16 (variant 2).
+//   WIDE   (otherwise): a 128 x 256 (variant 0), 128 x 128 (variant 1) or 256 x 256
+//          (variant 2) tile; mt = 8 or 16.
 enum W4A16Kind { W4A16_SKINNY = 0, W4A16_WIDE = 2 };
+
+// Rows and columns of a large-M kernel tile.
+inline int wide_rows(int variant) { return variant == 2 ? 256 : 128; }
+inline int wide_cols(int variant) { return variant == 1 ? 128 : 256; }
 
 struct W4A16Tile {
     W4A16Kind kind;
     int mt;  // 16-row MFMA subtiles per block (SKINNY: 1, 2, 4; WIDE: 8, 16)
-    int ns;  // SKINNY: 16-column MFMA subtiles per block (2 or 4); WIDE: kernel variant
+    int ns;  // SKINNY: 16-column MFMA subtiles per block (1 to 4); WIDE: kernel variant
     int block_m() const { return 16 * mt; }
-    int block_n() const { return kind == W4A16_WIDE ? 256 : 16 * ns; }
+    int block_n() const { return kind == W4A16_WIDE ? wide_cols(ns) : 16 * ns; }
 };
 
 // Weight format: `bits`-wide unsigned codes (4 or 8) packed 32/bits per 32-bit word along K,
@@ -86,19 +91,19 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, 
                                const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
                                int s, bool vec_store, hipStream_t stream);
 
-// Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves of 128 x 64; 2 = 256 x 256
-// tiles of 8 waves of 256 x 32. Rows per tile; LDS bytes of one workgroup (three stage
-// slots of A, 64 values per row, and of W, 64 codes per row, and two scale/bias slots of
-// one 128-value block); workgroups one CU holds (160 KB of LDS).
-constexpr int kWideCols = 256;
-inline int wide_rows(int variant) { return variant == 0 ? 128 : 256; }
-constexpr int wide_lds_bytes(int rows, int bits, int sub)
+// Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves of 128 x 64; 1 = 128 x 128
+// tiles of 4 waves of 128 x 32; 2 = 256 x 256 tiles of 8 waves of 256 x 32. LDS bytes of
+// one workgroup (three stage slots of A, 64 values per row, and of W, 64 codes per
+// column, and two scale/bias slots of one 128-value block); workgroups one CU holds
+// (160 KB of LDS).
+constexpr int kWideCols = 256;  // columns of the stream-K variants (0 and 2)
+constexpr int wide_lds_bytes(int rows, int bits, int sub, int cols = kWideCols)
 {
-    return 3 * rows * 64 * 2 + 3 * kWideCols * 64 * bits / 8 + 2 * 2 * kWideCols * 4 * sub;
+    return 3 * rows * 64 * 2 + 3 * cols * 64 * bits / 8 + 2 * 2 * cols * 4 * sub;
 }
 inline int wide_wgs_per_cu(int variant, WFormat f = WFormat{4, 128})
 {
-    return variant == 0 && 2 * wide_lds_bytes(128, f.bits, f.sub()) <= kLdsPerCU ? 2 : 1;
+    return variant != 2 && 2 * wide_lds_bytes(128, f.bits, f.sub(), wide_cols(variant)) <= kLdsPerCU ? 2 : 1;
 }
 
 // Large-M kernel: the first full_tiles tiles (M-block fastest) unsplit into C, the
@@ -106,7 +111,8 @@ inline int wide_wgs_per_cu(int variant, WFormat f = WFormat{4, 128})
 // ([split][M][N], bf16 or (f32_part) fp32; unused when split = 1).
 // streamk = P > 0 instead runs the stream-K decomposition on P workgroups (near-equal
 // ranges of the (tile, 128-value block) units; full_tiles and split are ignored), with
-// `part` holding 2P tile slots (wide_streamk_bytes) and a fix-up launch after it.
+// `part` holding 2P tile slots (wide_streamk_bytes) and a fix-up launch after it;
+// variants 0 and 2 only.
 hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void *Wq, const void *scale,
                              const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
                              int full_tiles, int split, bool vec_store, hipStream_t stream, int streamk = 0);

@@ -12,8 +12,10 @@
 // the last wave of workgroups instead of leaving it mostly idle.
 //
 // This regime is bound by the bf16 matrix cores. A workgroup owns a 128 x 256 tile (variant
-// 0: 4 wave64s, each 128 x 64, 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators) or a 256 x 256
-// tile (variant 2: 8 wave64s, each 256 x 32, 8 x 1 accumulators), and walks its partition
+// 0: 4 wave64s, each 128 x 64, 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators), a 128 x 128
+// tile (variant 1: 4 wave64s, each 128 x 32, 4 x 1 accumulators; for shapes whose 256-column
+// tiles would need a deep split) or a 256 x 256 tile (variant 2: 8 wave64s, each 256 x 32,
+// 8 x 1 accumulators), and walks its partition
 // in stages of 64 reduction values. Tall wave tiles spread each dequantised weight over
 // 4 or 8 MFMAs, and 64-value stages make every row of A a whole 128-byte line.
 //
@@ -60,21 +62,20 @@ using namespace qmm_dev;
 
 namespace {
 
-constexpr int BN = 256;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int BK = 64;
 constexpr int ROT_GROUPS = 8;        // k-start spread of the workgroups sharing A rows
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Tile geometry of a variant and weight format: 128*WM rows x 256 columns per workgroup,
+// Tile geometry of a variant and weight format: 128*WM rows x BN columns per workgroup,
 // each wave a (32*MI) x (32*NJ) block of 32x32 MFMA tiles, waves side by side along N
 // first; BITS-wide codes, SUB scale/bias groups per 128-value block.
-template <int WM_, int MI_, int NJ_, int BITS_, int SUB_>
+template <int WM_, int MI_, int NJ_, int BITS_, int SUB_, int BN_ = 256>
 struct Cfg {
-    static constexpr int WM = WM_, MI = MI_, NJ = NJ_, BITS = BITS_, SUB = SUB_;
+    static constexpr int WM = WM_, MI = MI_, NJ = NJ_, BITS = BITS_, SUB = SUB_, BN = BN_;
     static constexpr int BM = 128 * WM;             // rows per tile
-    static constexpr int NWN = 8 / NJ;              // waves along N (256 columns)
+    static constexpr int NWN = BN / (32 * NJ);      // waves along N
     static constexpr int NWM = BM / (32 * MI);      // waves along M
     static constexpr int NW = NWM * NWN;            // waves per workgroup
     static constexpr int A_SLOT = BM * BK * 2;      // 16 or 32 KB
@@ -90,8 +91,9 @@ struct Cfg {
     static constexpr int N_EVEN = AC + WC + SC;     // copies a wave issues in an even stage
     static constexpr int N_ODD = AC + WC;           // ... in an odd stage
     static constexpr int LDS = 3 * A_SLOT + 3 * W_SLOT + 2 * SB_SLOT;
+    static constexpr int SBQ = BN / 64;             // scale/bias copies per array and group
     static constexpr int OCC = 2 * LDS <= qmm_impl::kLdsPerCU ? 2 : 1;  // workgroups one CU holds
-    static_assert(LDS == qmm_impl::wide_lds_bytes(BM, BITS, SUB), "LDS size differs from the host's");
+    static_assert(LDS == qmm_impl::wide_lds_bytes(BM, BITS, SUB, BN), "LDS size differs from the host's");
     static_assert(AC * NW * 8 == BM && WC * NW * 1024 == W_SLOT && SC * NW * 256 == SB_SLOT, "copy split");
 };
 
@@ -220,7 +222,7 @@ __device__ __forceinline__ void load_head(const Ctx<CF> &c, const Lds<CF> &L, in
         for (int u = 0; u < CF::WV; ++u)
             o.wpk[j][u] = *reinterpret_cast<const uint4 *>(Ws + c.w_rd[u] + 32 * CF::WROW * j);
         o.sc[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + c.sb_rd[ODD] + 128 * j));
-        o.bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 1024 * CF::SUB + c.sb_rd[ODD] + 128 * j));
+        o.bi[j] = bf16_to_f32(*reinterpret_cast<const uint32_t *>(Ss + 4 * CF::BN * CF::SUB + c.sb_rd[ODD] + 128 * j));
         o.sc512[j] = o.sc[j] * 512.f;
     }
     step_operands<CF>(c, L.a + slot3 * CF::A_SLOT, o, 0, o.af, o.bw);
@@ -331,7 +333,7 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     const int m_idx = tile % num_m;
     const int n_idx = tile / num_m;
     const int m0 = m_idx * GE::BM;
-    const int n0 = n_idx * BN;
+    const int n0 = n_idx * CF::BN;
 
     Ctx<CF> c;
     c.gpp = gpp;
@@ -370,11 +372,11 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
         // scale/bias: copy q = w*SC + j carries 64 rows (lane i -> row 64*(q%4) + i) of
         // group (q/4) % SUB of the block, from scale (q < 4*SUB) or bias.
         const int q = wave * GE::SC + j;
-        const int rs = min(n0 + 64 * (q & 3) + lane, N - 1) - n0;
-        const int sub = (q >> 2) % GE::SUB;
+        const int rs = min(n0 + 64 * (q % GE::SBQ) + lane, N - 1) - n0;
+        const int sub = (q / GE::SBQ) % GE::SUB;
         c.sb_off[j] = (uint32_t)(2 * rs * GG);
-        c.sb[j] = reinterpret_cast<const char *>(q < 4 * GE::SUB ? scale : bias) + 2 * (size_t)n0 * (size_t)GG +
-                  2 * sub;
+        c.sb[j] = reinterpret_cast<const char *>(q < GE::SBQ * GE::SUB ? scale : bias) +
+                  2 * (size_t)n0 * (size_t)GG + 2 * sub;
     }
     c.a_lds = lds_addr(L.a) + 1024u * (uint32_t)(GE::AC * wave);
     c.w_lds = lds_addr(L.w) + 1024u * (uint32_t)(wave * GE::WC);
@@ -395,7 +397,7 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
         // block: group (32h) * SUB / 128 (and (64 + 32h) * SUB / 128) of the block
 #pragma unroll
         for (int odd = 0; odd < 2; ++odd)
-            c.sb_rd[odd] = (uint32_t)(4 * nrow + 1024 * (((2 * odd + h) * GE::SUB) >> 2));
+            c.sb_rd[odd] = (uint32_t)(4 * nrow + 4 * GE::BN * (((2 * odd + h) * GE::SUB) >> 2));
     }
 
     f32x16 acc[MI][NJ];
@@ -477,12 +479,14 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
         return;
     }
     // bf16 results go out through LDS, whose stage slots are free now: the waves write the
-    // rounded tile (or, when it does not fit, half of its rows at a time) row-major, 512
-    // bytes per row with 16-byte chunk c of row x stored at chunk c ^ (x % 32), and then
-    // every store instruction writes two whole rows of 512 contiguous bytes. Stored
+    // rounded tile (or, when it does not fit, half of its rows at a time) row-major, 2*BN
+    // bytes per row with 16-byte chunk c of row x stored at chunk c ^ (x % (BN/8)), and then
+    // every store instruction writes whole rows of contiguous bytes. Stored
     // straight from the accumulators, each instruction would write 16 bytes into each of
     // 32 rows (32 partly written lines), which took 4-5 us per tile.
-    constexpr int PR = CF::BM * BN * 2 <= CF::LDS ? CF::BM : CF::BM / 2;  // rows per pass
+    constexpr int PR = CF::BM * CF::BN * 2 <= CF::LDS ? CF::BM : CF::BM / 2;  // rows per pass
+    constexpr int CPR = CF::BN / 8;  // 16-byte chunks per row
+    constexpr int RB = CF::BN * 2;   // bytes per row
     char *T = reinterpret_cast<char *>(&L);
     const bool v16 = dst.vec && (dst.ld % 8) == 0 && (reinterpret_cast<uintptr_t>(dst.base) & 15) == 0;
 #pragma unroll
@@ -497,20 +501,20 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
             for (int j = 0; j < NJ; ++j) {
 #pragma unroll
                 for (int vq = 0; vq < 4; ++vq) {
-                    const int cc = 4 * (wn * NJ + j) + vq;  // 16-byte chunk of the 256-column row
+                    const int cc = 4 * (wn * NJ + j) + vq;  // 16-byte chunk of the row
                     uint2 v;
                     v.x = pack_bf16x2(acc[i][j][4 * vq], acc[i][j][4 * vq + 1]);
                     v.y = pack_bf16x2(acc[i][j][4 * vq + 2], acc[i][j][4 * vq + 3]);
-                    *reinterpret_cast<uint2 *>(T + x * 512 + 16 * (cc ^ (x & 31)) + 8 * sl) = v;
+                    *reinterpret_cast<uint2 *>(T + x * RB + 16 * (cc ^ (x & (CPR - 1))) + 8 * sl) = v;
                 }
             }
         }
         __syncthreads();
-        for (int k = threadIdx.x; k < PR * 32; k += 64 * CF::NW) {
-            const int x = k >> 5, cc = k & 31;
+        for (int k = threadIdx.x; k < PR * CPR; k += 64 * CF::NW) {
+            const int x = k / CPR, cc = k % CPR;
             const int m = m0 + h * PR + x, n = n0 + 8 * cc;
             if (m >= M || n >= N) continue;
-            const uint4 v = *reinterpret_cast<const uint4 *>(T + x * 512 + 16 * (cc ^ (x & 31)));
+            const uint4 v = *reinterpret_cast<const uint4 *>(T + x * RB + 16 * (cc ^ (x & (CPR - 1))));
             uint16_t *g = reinterpret_cast<uint16_t *>(dst.base) + (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0);
             if (v16 && n + 7 < N) {
                 // Non-temporal (streaming) store: the tile is not read again by this kernel,
@@ -539,7 +543,7 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
 //     P near-equal ranges, workgroup w taking units [floor(w*U/P), floor((w+1)*U/P)).
 //     It walks them tile by tile: a tile it covers whole goes to C; the piece of a
 //     tile it shares with other workgroups goes to its own slot of `part` (slot 2w for
-//     its first tile, 2w+1 for its last; each a BM x 256 tile, row-major), which the
+//     its first tile, 2w+1 for its last; each a BM x BN tile, row-major), which the
 //     fix-up kernel adds in workgroup order.
 template <class CF, bool SK>
 __global__ void __launch_bounds__(64 * CF::NW, CF::OCC)
@@ -595,10 +599,10 @@ w4a16_wide_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ W
             d.vec = vec_store;
         } else {
             const size_t slot = 2 * (size_t)b + (u == u0 ? 0 : 1);
-            d.base = static_cast<char *>(part) + slot * (size_t)CF::BM * BN * (f32_part ? 4 : 2);
-            d.ld = BN;
+            d.base = static_cast<char *>(part) + slot * (size_t)CF::BM * CF::BN * (f32_part ? 4 : 2);
+            d.ld = CF::BN;
             d.r0 = (tile % num_m) * CF::BM;
-            d.c0 = (tile / num_m) * BN;
+            d.c0 = (tile / num_m) * CF::BN;
             d.f32 = f32_part;
             d.vec = 1;
         }
@@ -675,6 +679,8 @@ template <int BITS, int SUB>
 using CfgV0 = Cfg<1, 4, 2, BITS, SUB>;  // 128 x 256 tile, 4 waves of 128 x 64
 template <int BITS, int SUB>
 using CfgV2 = Cfg<2, 8, 1, BITS, SUB>;  // 256 x 256 tile, 8 waves of 256 x 32
+template <int BITS, int SUB>
+using CfgV1 = Cfg<1, 4, 1, BITS, SUB, 128>;  // 128 x 128 tile, 4 waves of 128 x 32
 
 template <class CF>
 void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t *w, const uint16_t *sc,
@@ -684,7 +690,7 @@ void launch_cfg(dim3 grid, hipStream_t stream, const uint16_t *a, const uint32_t
     if (streamk == 0) {
         hipLaunchKernelGGL((w4a16_wide_kernel<CF, false>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt,
                            M, N, K, full_tiles, tail_tiles, split, vec, f32p, 0);
-    } else if constexpr (CF::BITS == 4 && CF::SUB == 1) {  // stream-K: the W4A16 g128 format only
+    } else if constexpr (CF::BITS == 4 && CF::SUB == 1 && CF::BN == 256) {  // stream-K: W4A16 g128, 256 columns
         hipLaunchKernelGGL((w4a16_wide_kernel<CF, true>), grid, dim3(64 * CF::NW), 0, stream, a, w, sc, bi, c, pt,
                            M, N, K, full_tiles, tail_tiles, split, vec, f32p, streamk);
         const int T = full_tiles + tail_tiles;
@@ -708,6 +714,9 @@ void launch_variant(int variant, dim3 grid, hipStream_t stream, const uint16_t *
     if (variant == 0)
         launch_cfg<CfgV0<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
                                      f32p, streamk);
+    else if (variant == 1)
+        launch_cfg<CfgV1<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
+                                     f32p, streamk);
     else
         launch_cfg<CfgV2<BITS, SUB>>(grid, stream, a, w, sc, bi, c, pt, M, N, K, full_tiles, tail_tiles, split, vec,
                                      f32p, streamk);
@@ -722,9 +731,10 @@ hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void
                              const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
                              int full_tiles, int split, bool vec_store, hipStream_t stream, int streamk)
 {
-    if (K >= (1 << 22) || (variant != 0 && variant != 2) || !format_supported(fmt)) return hipErrorInvalidValue;
-    const int rows = wide_rows(variant);
-    const int tiles = ((M + rows - 1) / rows) * ((N + BN - 1) / BN);
+    if (K >= (1 << 22) || variant < 0 || variant > 2 || !format_supported(fmt)) return hipErrorInvalidValue;
+    const int rows = wide_rows(variant), cols = wide_cols(variant);
+    const int tiles = ((M + rows - 1) / rows) * ((N + cols - 1) / cols);
+    if (streamk > 0 && variant == 1) return hipErrorInvalidValue;
     if (streamk < 0 || (streamk > 0 && (!part || (long long)streamk > (long long)tiles * (K / 128))))
         return hipErrorInvalidValue;
     if (streamk > 0 && (fmt.bits != 4 || fmt.group != 128)) return hipErrorInvalidValue;

@@ -77,13 +77,15 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * while 32-column tiles fit in 256 workgroups and K < 8192; else by 48 when 48-column tiles
  * fit in 256 workgroups, else by 64. With tile_m = tile_n = 0 and M <= 32, its partitions hold at least 2048 reduction
  * values (min_k_per_split is raised to 2048 in the rule): a shorter partition saves less
- * than the second pass costs. The large-M kernel runs the rest, with 128 x 256 tiles up to M = 128 and, above,
- * 128 x 256 or 256 x 256 tiles, whichever has the shorter estimated critical path: rounds of
- * target_blocks workgroups times the 128 x 256 x 128 blocks each computes (a 256-row tile
- * counts two), plus half a block per partition of a split tail.
+ * than the second pass costs. The large-M kernel runs the rest, with the tile of shortest
+ * estimated critical path among 128 x 256 (two workgroups per CU up to M = 128), 256 x 256
+ * (above M = 128) and 128 x 128 (only when its tiles are fewer than target_blocks, a pure
+ * split at one workgroup per CU); ties go to the larger tiles. The estimate: rounds of
+ * target_blocks workgroups times the 128 x 256 x 128 blocks each computes (a 256 x 256 tile
+ * counts two, a 128 x 128 tile one half), plus half a block per partition of a split.
  * With tile_m = tile_n = 0 and the large-M kernel (T = base tiles, M-block
  * fastest, num_m tiles per column of tiles) the rule fills the kernel's workgroup
- * slots, target_blocks times the workgroups one CU holds (2 for its 128-row tiles up to
+ * slots, target_blocks times the workgroups one CU holds (2 for its 128 x 256 tiles up to
  * M = 128, else 1),
  * with partitions that may differ by one group (no divisibility step); below,
  * target_blocks stands for that slot count:

@@ -123,6 +123,24 @@ def test_cfg2_projection_sweep(name, M, N, K, idx):
         assert np.array_equal(host_bits(C), host_bits(C1))
 
 
+# Shapes the plan runs on 128 x 128 tiles of the large-M kernel (a pure split): ragged M
+# below and above 128 rows, N not a multiple of 128 (and of 8: element-wise stores).
+TILE128_CASES = [(100, 7000, 2560), (300, 300, 1024), (256, 520, 4096), (130, 1000, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", TILE128_CASES)
+def test_128x128_tiles_match_oracle(M, N, K):
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert (plan.block_m, plan.block_n, plan.full_tiles) == (128, 128, 0) and plan.s > 1, plan.as_dict()
+    d = syn.w4a16_inputs(M, N, K, seed=18000 + M + N)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for s, f32p in ((0, False), (1, False), (2, False), (4, False), (0, True)):
+        say("128x128 tiles M=%d N=%d K=%d s=%d f32p=%d" % (M, N, K, s, f32p))
+        C = run_w4a16(dv, M, N, K, s, guard=40, f32p=f32p)
+        check_tolerance(host_f64(C), ref, what="128x128 tiles %dx%dx%d s=%d f32p=%d" % (M, N, K, s, f32p))
+
+
 def test_split_tail_decomposition():
     """Large-M plan that runs most tiles unsplit and splits only the last column of tiles
     (ragged in N): the unsplit columns equal the s = 1 kernel bit for bit, the split tail

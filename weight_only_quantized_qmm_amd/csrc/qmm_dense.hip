@@ -29,6 +29,8 @@ using namespace qmm_dev;
 
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int TM = 128, TN = 128, SK = 64;
 constexpr int SLOT = TM * SK * 2;  // 16 KB per operand per stage
 constexpr int NCOPY = 8;           // copies per wave per stage: 4 of A, 4 of B
@@ -233,7 +235,9 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
         const uint4 v = *reinterpret_cast<const uint4 *>(T + x * (CPR * 16) + 16 * (cc ^ (x & (CPR - 1))));
         char *g = base + ((size_t)m * (size_t)N + n) * ES;
         if (v16 && n + 16 / ES - 1 < N) {
-            *reinterpret_cast<uint4 *>(g) = v;
+            // Non-temporal (streaming) store: lines left dirty in the XCD's L2 are written
+            // back before the kernel completes (cfg3 at s = 16: 5 % faster with the hint).
+            __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(g));
         } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

@@ -322,9 +322,10 @@ int qmm_attn_decode(const void *Q, const void *K, const void *V, const int *leng
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* The split qmm_attn_decode uses for s = 0: enough workgroups for one per CU
- * (ceil(256 / (B*Hkv))), at most Lmax/256 (256 keys per split) and 32, at least 1
- * (fitted to split sweeps of the Qwen3-4B decode shapes on MI355X).
- * Host only; QMM_ERR_ARG for a non-positive size. */
+ * (ceil(256 / (B*Hkv))), at most Lmax/64 (a 64-key tile per split), at most
+ * max(16, Lmax/512) (past the 16 splits the merge reads in one round trip, only with 512
+ * keys per split) and 32, at least 1 (fitted to split sweeps of the Qwen3-4B decode shapes
+ * on MI355X). Host only; QMM_ERR_ARG for a non-positive size. */
 int qmm_attn_decode_split(int B, int Hkv, int Lmax);
 
 /* Workspace bytes of qmm_attn_decode for split s: s*B*Mq*Hq*(128 + 2)*4, 0 for s <= 1. */

@@ -354,9 +354,14 @@ def test_wna16_plan_rejects_unsupported_formats():
 
 
 def test_attn_split_rule():
-    for B, Hkv, L in [(1, 8, 4096), (1, 8, 1024), (8, 8, 4096), (32, 8, 16384), (1, 1, 100), (64, 8, 65536)]:
-        want = max(1, min(32, -(-256 // (B * Hkv)), L // 256))
+    # one workgroup per CU, at most one split per 64-key tile, past 16 splits (one merge
+    # batch) only with 512 keys per split, at most 32
+    for B, Hkv, L in [(1, 8, 4096), (1, 8, 1024), (1, 8, 2048), (1, 8, 16384), (2, 8, 2048), (4, 8, 1024),
+                      (8, 8, 4096), (32, 8, 16384), (1, 1, 100), (1, 1, 63), (64, 8, 65536), (1, 2, 12800)]:
+        want = max(1, min(32, -(-256 // (B * Hkv)), L // 64, max(16, L // 512)))
         assert q.qmm_attn_decode_split(B, Hkv, L) == want, (B, Hkv, L)
+    # the Qwen3-4B single-request cases the rule was fitted on
+    assert [q.qmm_attn_decode_split(1, 8, L) for L in (1024, 2048, 4096, 16384)] == [16, 16, 16, 32]
     assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 4) == 4 * 2 * 32 * 130 * 4
     assert q.qmm_attn_decode_workspace_bytes(2, 1, 32, 1) == 0
 

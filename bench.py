@@ -29,9 +29,13 @@ summary under profiles/ that the ``traffic`` field reads back (it stays null
 when the kernel source changed after the counters were taken).
 
 CPU baseline: the fp64 CPU oracle on the host cores, on a bounded sample of
-the same sweep (listed in the output), extrapolated to one whole sweep.
+the same sweep (listed in the output), extrapolated to one whole sweep, plus the
+oracle on one thread for the 32 x 1024 x 2560 K-projection case.
 
-Prints ONE JSON line.
+Output: the last line on stdout is ONE compact JSON line (the headline: metric,
+value, dominant-kernel roofline, CPU baseline, summary of the per-shape table).
+The tables (per shape, dense sweep, decode, formats, decode attention, stream-K)
+go to the JSON file named by --tables-out; stderr carries short progress lines.
 """
 import argparse
 import json
@@ -77,6 +81,11 @@ DOMINANT_SOURCES = [os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", 
 DOMINANT_WORKLOAD = "first pass (qmm_w4a16_g128_pass1) of the plan, M=2048 q,k,v,o,gate,up,down"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_wide_M2048_traffic.txt")
 COPY_BYTES = 256 << 20     # size of the plain copy that calibrates the profiler's byte counters
+
+
+def progress(kind, row, keys):
+    """One short progress line on stderr (plain text, never JSON)."""
+    print("# %s %s" % (kind, " ".join("%s=%s" % (k, row[k]) for k in keys if k in row)), file=sys.stderr, flush=True)
 
 
 def dominant_shapes(shapes):
@@ -277,7 +286,7 @@ def streamk_table(torch, syn, q, table):
         r = roofline(M, N, K, t)
         rows.append(dict(name=name, M=M, us=round(t * 1e6, 3), plan_us=plan_us.get((name, M)),
                          workspace_mb=round(nb / 1e6, 1), frac=round(r["frac"], 4)))
-        print("# streamk %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        progress("streamk", rows[-1], ("name", "M", "us", "plan_us"))
     return rows
 
 
@@ -318,7 +327,7 @@ def attention_table(torch, q):
         rows.append(dict(B=B, L=L, Mq=Mq, Hq=Hq, Hkv=Hkv, D=D, s=s_plan, us=round(t[0] * 1e6, 3),
                          us_unsplit=round(t[1] * 1e6, 3), tbs=round(byts / t[0] / 1e12, 3),
                          frac_hbm=round(byts / HBM_PEAK / t[0], 4)))
-        print("# attn %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        progress("attn", rows[-1], ("B", "L", "Mq", "s", "us", "frac_hbm"))
     return rows
 
 
@@ -341,7 +350,7 @@ def formats_table(torch, syn, q):
             rows.append(dict(bits=bits, group=group, partials="fp32" if f32p else "bf16", name=name, M=M, N=N, K=K,
                              s=sh.s, full_tiles=sh.plan.full_tiles, us=round(t[0] * 1e6, 3), bound=r["bound"],
                              gbs=round(r["gbs"], 1), tflops=round(r["tflops"], 2), frac=round(r["frac"], 4)))
-            print("# %s" % json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            progress("format", rows[-1], ("bits", "group", "partials", "name", "M", "s", "us", "frac"))
     return rows
 
 
@@ -416,6 +425,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="CPU-baseline sample budget")
     ap.add_argument("--no-per-shape", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--tables-out", default=os.path.join("gpurun_out", "bench_tables.json"),
+                    help="file that receives the per-shape and secondary tables (JSON)")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only the dominant-kernel roofline measurement (the profiled command)")
     ap.add_argument("--pmc-run", action="store_true", help="only the workload of the profiler counter passes")
@@ -557,12 +568,19 @@ def cpu_baseline(syn, budget_s):
         if (name, "M=%d" % M) not in covered:
             est_total += rate * M * N * K
     whole = len(sample) == len(shapes)
+    # the 32 x 1024 x 2560 K-projection case on one thread (the all-core figure's reference point)
+    M0, N0, K0 = 32, 1024, 2560
+    d0 = syn.w4a16_inputs(M0, N0, K0, seed=0)
+    t0 = time.perf_counter()
+    oracle.qmm_w4a16(d0["A"], d0["Wq"], d0["scale"], d0["bias"], M0, N0, K0, s=1, nthreads=1)
+    single = time.perf_counter() - t0
     return dict(value=est_total * 1e6,
                 unit="us per sweep (35 projection matmuls%s)" % ("" if whole else ", extrapolated"),
                 cores=cores, kind="oracle",
                 sample="%s; %.1f s measured%s" % (
                     "the whole sweep, each shape once" if whole else ", ".join(sample), spent,
-                    "" if whole else ", rest extrapolated by multiply-add count"))
+                    "" if whole else ", rest extrapolated by multiply-add count"),
+                single_thread_32x1024x2560_us=round(single * 1e6, 1))
 
 
 def main():
@@ -634,11 +652,13 @@ def main():
         for n, M, N, K, i in sweep:
             sh, R, t = per_shape(torch, syn, q, n, M, N, K, i)
             r = roofline(M, N, K, t[0])
-            table.append(dict(name=n, M=M, N=N, K=K, s=sh.s, full_tiles=sh.plan.full_tiles, us=round(t[0] * 1e6, 3),
+            # dispatches of one call: the matmul, plus the merge of the planes when the plan splits
+            table.append(dict(name=n, M=M, N=N, K=K, s=sh.s, dispatches=1 if sh.s == 1 else 2,
+                              full_tiles=sh.plan.full_tiles, us=round(t[0] * 1e6, 3),
                               us_unsplit=round(t[1] * 1e6, 3), speedup_vs_unsplit=round(t[1] / t[0], 3),
                               tflops=round(r["tflops"], 2), gbs=round(r["gbs"], 1), bound=r["bound"],
                               roof_us=round(r["t_roof_us"], 3), frac=round(r["frac"], 4), rotation_sets=R))
-            print("# %s" % json.dumps(table[-1]), file=sys.stderr, flush=True)
+            progress("shape", table[-1], ("name", "M", "s", "dispatches", "us", "us_unsplit", "frac"))
 
     dense = decode = formats = attention = streamk = None
     if not args.no_per_shape:
@@ -653,6 +673,19 @@ def main():
         cpu = cpu_baseline(syn, args.cpu_seconds)
 
     pol = q.policy_preset("QMM_POLICY_MI355X").as_dict()
+    tables = {
+        "shapes": table,
+        "dense_bf16_splitk": dense,
+        "decode": decode,
+        "formats": formats,
+        "decode_attention": attention,
+        "streamk": streamk,
+        "roofline_detail": roof,
+        "machine_floors": calib,
+        "policy": pol,
+        "eager_us_per_step": round(eager_step_s * 1e6, 1),
+        "wall_s_timed": round(wall, 4),
+    }
     line = {
         "metric": METRIC,
         "value": round(step_s * 1e6, 3),
@@ -667,29 +700,33 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "Qwen3-4B projection sweep: q,k,v,o,gate,up,down x M in {16,32,64,128,2048}, "
-                               "W4A16 g128, MI355X policy split",
-                   "shapes": len(sweep), "policy": pol, "timing": "hipGraph replay of the whole sweep",
-                   "wall_s_timed": round(wall, 4)},
-        "eager_us_per_step": round(eager_step_s * 1e6, 1),
-        "roofline": roof,
+                               "W4A16 g128, MI355X policy split", "shapes": len(sweep)},
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()
+                     if k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_us",
+                              "frac_of_measured_mfma_peak")},
         "cpu_baseline": cpu,
-        "machine_floors": calib,
-        "shapes": table,
-        "dense_bf16_splitk": dense,
-        "decode": decode,
-        "formats": formats,
-        "decode_attention": attention,
-        "streamk": streamk,
     }
+    line["roofline"]["kernel"] = "%s, first pass of the plan on the 7 M=2048 shapes" % DOMINANT_KERNEL
     if table:
         small = [t for t in table if t["M"] <= 128]
         line["summary"] = {
             "small_M_mean_frac": round(sum(t["frac"] for t in small) / len(small), 4),
             "M2048_mean_frac": round(sum(t["frac"] for t in table if t["M"] == 2048) / 7, 4),
-            "split_never_slower": all(t["speedup_vs_unsplit"] >= 0.98 for t in table),
+            "split_never_slower": all(t["us"] <= t["us_unsplit"] for t in table),
             "sum_per_shape_us": round(sum(t["us"] for t in table), 2),
+            "dispatches_per_sweep": sum(t["dispatches"] for t in table),
+            "decode_best_us_max": (round(max(min(r["us"], r["gemv_us"]) for r in decode), 3) if decode else None),
+            "dense_policy_us": dense["us"]["policy"] if dense else None,
         }
-    text = json.dumps(line)
+    if args.tables_out:
+        d = os.path.dirname(args.tables_out)
+        if d:
+            os.makedirs(d, exist_ok=True)
+        with open(args.tables_out, "w") as f:
+            json.dump(dict(tables, headline=line), f, indent=1)
+        line["tables"] = args.tables_out
+    text = json.dumps(line, separators=(",", ":"))
+    sys.stderr.flush()
     print(text, flush=True)
     if args.out:
         with open(args.out, "w") as f:

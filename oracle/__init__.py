@@ -33,10 +33,13 @@ _LIB = None
 def _lib():
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB) or (
-                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
-            _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        # QMM_ORACLE_LIB names another build of the same source (the sanitizer build of the tests)
+        path = os.environ.get("QMM_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]

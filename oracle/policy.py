@@ -39,43 +39,3 @@ def split_count(M, N, K, tile_m=32, tile_n=32, target=320, cap=16, min_k_per_spl
     while s > 1 and G % s != 0:
         s -= 1
     return max(s, 1)
-
-
-def fill_decomposition(T, num_m, K, slots, cap, min_k_per_split, group=128):
-    """(s, full_tiles) of the slot-filling rule for a kernel with T output tiles
-    numbered column of tiles by column of tiles (num_m tiles per column), and
-    `slots` workgroups resident at once.
-
-    This is not a rule of the pages: it is this library's occupancy rule for its
-    large-M kernel on MI355X, which drops the page's divisibility step (a
-    partition may hold one group more than another) and, when the tiles already
-    fill the slots, splits only the tiles of the last, partly filled round:
-
-        smax = min(cap, G, K // min_k)
-        T <  slots: s = min(smax, slots // T), every tile split (full_tiles = 0)
-        T >= slots: full = (T // slots) * slots, minus full % num_m (whole columns),
-                    unsplit; the remaining T - full tiles split in
-                    s = min(smax, slots // (T - full)) partitions
-        s <= 1: no split (full_tiles = T)
-    """
-    if K % group:
-        raise ValueError("K must be a multiple of the group size")
-    G = K // group
-    smax = min(cap, G, K // min_k_per_split)
-    if smax <= 1 or slots <= 0:
-        return 1, T
-    if T >= slots:
-        full = (T // slots) * slots
-        full -= full % num_m
-        tail = T - full
-        if tail == 0:
-            return 1, T
-        s = min(smax, slots // tail)
-        return (s, full) if s > 1 else (1, T)
-    s = min(smax, slots // T)
-    return (s, 0) if s > 1 else (1, T)
-
-
-def near_equal_partitions(G, s):
-    """Group ranges [floor(p*G/s), floor((p+1)*G/s)) of the s partitions of G groups."""
-    return [(p * G // s, (p + 1) * G // s) for p in range(s)]

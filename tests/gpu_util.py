@@ -46,22 +46,6 @@ def check_tolerance(got, ref, rms=None, what=""):
     return float(np.max(err / np.maximum(bound, 1e-300)))
 
 
-def sample_points(M, N, seed, n_random=2048):
-    """Output coordinates checked at full size: whole first/last rows and columns
-    plus random points (covers every column tile, every row tile, ragged edges)."""
-    rng = np.random.default_rng(seed)
-    ms, ns = [], []
-    for m in sorted({0, M - 1, M // 2}):
-        ms += [m] * N
-        ns += list(range(N))
-    for n in sorted({0, N - 1, N // 2}):
-        ms += list(range(M))
-        ns += [n] * M
-    ms += list(rng.integers(0, M, n_random))
-    ns += list(rng.integers(0, N, n_random))
-    return np.array(ms, dtype=np.int32), np.array(ns, dtype=np.int32)
-
-
 def expected_rms_w4a16(K, scale_lo=0.005, scale_hi=0.02):
     """sqrt(K * E[scale^2] * E[(q-8)^2]) for A ~ N(0,1), q ~ U{0..15}, scale ~ U[lo,hi]."""
     e_s2 = (scale_hi ** 3 - scale_lo ** 3) / (3 * (scale_hi - scale_lo))

@@ -1,0 +1,220 @@
+// host_checks.cpp -- the C-ABI host code (qmm_api.cpp) built for the CPU alone, under
+// AddressSanitizer and UndefinedBehaviorSanitizer, with the kernel launchers replaced by
+// recording stubs. It runs every entry point's argument checks and plans over a grid of
+// shapes, and checks that a rejected call launches nothing and an accepted one launches the
+// kernels its documentation names. No GPU, no HIP runtime: the pointers handed to the
+// entry points are host addresses that the host code only inspects for alignment.
+//
+// Built and run by tests/test_sanitizers.py (g++ -fsanitize=address,undefined).
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "qmm.h"
+#include "qmm_launch.h"
+
+namespace {
+int g_launches = 0;       // launches recorded since the last reset
+int g_last_split = -1;    // split of the last matmul launch
+}  // namespace
+
+namespace qmm_impl {
+hipError_t launch_w4a16_skinny(WFormat, int, int, int, int waves, const void *, const void *, const void *,
+                               const void *, void *, bool, int, int, int, int s, bool, hipStream_t)
+{
+    if (waves < 1 || waves > 16) abort();
+    ++g_launches;
+    g_last_split = s;
+    return hipSuccess;
+}
+hipError_t launch_w4a16_wide(WFormat, int variant, const void *, const void *, const void *, const void *, void *,
+                             void *, bool, int, int, int, int, int split, bool, hipStream_t, int)
+{
+    if (variant < 0 || variant > 2) abort();
+    ++g_launches;
+    g_last_split = split;
+    return hipSuccess;
+}
+hipError_t launch_w4a16_gemv(const void *, const void *, const void *, const void *, void *, int, int, int, int s,
+                             hipStream_t)
+{
+    ++g_launches;
+    g_last_split = s;
+    return hipSuccess;
+}
+hipError_t launch_reduce(const void *, bool, int, size_t, void *, bool, hipStream_t)
+{
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_reduce_cols(const void *, bool, int, int, int, int, void *, bool, hipStream_t)
+{
+    ++g_launches;
+    return hipSuccess;
+}
+hipError_t launch_attn_decode(const void *, const void *, const void *, const int *, void *, void *, int, int, int,
+                              int, int, float, int S, hipStream_t)
+{
+    ++g_launches;
+    g_last_split = S;
+    return hipSuccess;
+}
+hipError_t launch_dense(DenseTile, const void *, const void *, void *, bool, int, int, int, int s, bool, hipStream_t)
+{
+    ++g_launches;
+    g_last_split = s;
+    return hipSuccess;
+}
+}  // namespace qmm_impl
+
+namespace {
+
+int failures = 0;
+
+void expect(bool ok, const char *what, int line)
+{
+    if (!ok) {
+        fprintf(stderr, "FAIL line %d: %s\n", line, what);
+        ++failures;
+    }
+}
+#define EXPECT(c) expect((c), #c, __LINE__)
+
+// An aligned host arena standing in for device buffers (never dereferenced by the host code).
+alignas(256) unsigned char arena[1 << 16];
+void *P(size_t off) { return arena + off; }
+
+int call_w4a16(int M, int N, int K, int s, void *ws, size_t wsb, const void *A = P(0), const void *W = P(256),
+               void *C = P(1024))
+{
+    g_launches = 0;
+    return qmm_w4a16_g128(A, W, P(512), P(768), C, M, N, K, s, ws, wsb, nullptr);
+}
+
+}  // namespace
+
+int main()
+{
+    // ---- plans over a grid of shapes, every preset and a few tunables
+    const int Ms[] = {1, 2, 7, 16, 31, 32, 33, 48, 64, 65, 100, 128, 129, 255, 256, 300, 1000, 2048, 4096};
+    const int Ns[] = {1, 17, 100, 1000, 1024, 2560, 4096, 9728, 16484};
+    const int Ks[] = {128, 256, 1024, 2560, 4096, 9728, 16384};
+    const qmm_policy pols[] = {QMM_POLICY_PAGE, QMM_POLICY_MI355X, {16, 64, 512, 4, 256}, {0, 0, 1, 1, 128},
+                               {0, 0, 100000, 64, 128}};
+    long plans = 0;
+    for (int M : Ms)
+        for (int N : Ns)
+            for (int K : Ks)
+                for (const qmm_policy &pol : pols) {
+                    qmm_plan p;
+                    memset(&p, 0xA5, sizeof p);
+                    const int rc = qmm_splitk_plan(M, N, K, 128, &pol, &p);
+                    EXPECT(rc == QMM_OK);
+                    EXPECT(p.s >= 1 && p.s <= K / 128);
+                    EXPECT(p.workspace_bytes == (p.s > 1 ? (size_t)2 * p.s * M * N : 0));
+                    EXPECT(p.full_tiles >= 0 && p.full_tiles <= p.base_tiles || p.block_m < 128);
+                    for (int bits : {4, 8})
+                        for (int g : {32, 64, 128}) {
+                            qmm_plan pf;
+                            EXPECT(qmm_wna16_plan(bits, g, M, N, K, &pol, &pf) == QMM_OK);
+                        }
+                    ++plans;
+                }
+
+    // ---- plan errors
+    qmm_plan p;
+    EXPECT(qmm_splitk_plan(0, 8, 128, 128, nullptr, &p) == QMM_ERR_ARG);
+    EXPECT(qmm_splitk_plan(8, 8, 200, 128, nullptr, &p) == QMM_ERR_SHAPE);
+    EXPECT(qmm_splitk_plan(8, 8, 128, 64, nullptr, &p) == QMM_ERR_ARG);
+    EXPECT(qmm_splitk_plan(8, 8, 128, 128, nullptr, nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_splitk_plan(8, 8, 1 << 22, 128, nullptr, &p) == QMM_ERR_SIZE);
+    EXPECT(qmm_wna16_plan(5, 128, 8, 8, 128, nullptr, &p) == QMM_ERR_ARG);
+    const qmm_policy bad = {0, 0, 256, 0, 512};
+    EXPECT(qmm_splitk_plan(8, 8, 128, 128, &bad, &p) == QMM_ERR_ARG);
+
+    // ---- the matmul: rejected calls launch nothing
+    char ws_small[64];
+    (void)ws_small;
+    EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0, nullptr) == QMM_ERR_ARG && g_launches == 0);
+    EXPECT(call_w4a16(0, 1024, 2560, 1, nullptr, 0) == QMM_ERR_ARG && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2500, 1, nullptr, 0) == QMM_ERR_SHAPE && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 3, P(4096), 1 << 20) == QMM_ERR_SHAPE && g_launches == 0);  // 3 does not divide 20
+    EXPECT(call_w4a16(32, 1024, 2560, 40, P(4096), 1 << 20) == QMM_ERR_SHAPE && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 4, nullptr, 0) == QMM_ERR_WORKSPACE && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 4, P(4096), 2 * 4 * 32 * 1024 - 1) == QMM_ERR_WORKSPACE && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 4, P(4100), 1 << 20) == QMM_ERR_ALIGN && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0, P(2)) == QMM_ERR_ALIGN && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0, P(0), P(8)) == QMM_ERR_ALIGN && g_launches == 0);
+    EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0, P(0), P(256), P(1025)) == QMM_ERR_ALIGN && g_launches == 0);
+    EXPECT(call_w4a16(1 << 20, 1 << 20, 1 << 14, 1, nullptr, 0) == QMM_ERR_SIZE && g_launches == 0);
+
+    // ---- accepted calls launch the matmul, plus the merge when split
+    EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0) == QMM_OK && g_launches == 1 && g_last_split == 1);
+    EXPECT(call_w4a16(32, 1024, 2560, 4, P(4096), 1 << 20) == QMM_OK && g_launches == 2 && g_last_split == 4);
+    for (int M : {1, 16, 32, 64, 128, 2048})
+        for (int N : {1000, 1024, 2560, 9728})
+            for (int K : {2560, 4096, 9728}) {
+                qmm_plan pl;
+                EXPECT(qmm_splitk_plan(M, N, K, 128, nullptr, &pl) == QMM_OK);
+                const int rc = call_w4a16(M, N, K, 0, pl.s > 1 ? P(4096) : nullptr, pl.workspace_bytes);
+                EXPECT(rc == QMM_OK && g_launches == (pl.s > 1 ? 2 : 1) && g_last_split == pl.s);
+                int s_out = 0, n_lo = -1;
+                g_launches = 0;
+                EXPECT(qmm_w4a16_g128_pass1(P(0), P(256), P(512), P(768), P(1024), M, N, K, 0,
+                                            pl.s > 1 ? P(4096) : nullptr, pl.workspace_bytes, &s_out, &n_lo,
+                                            nullptr) == QMM_OK);
+                EXPECT(g_launches == 1 && s_out == pl.s && n_lo >= 0 && n_lo <= N);
+                EXPECT((pl.s == 1) == (n_lo == N));
+            }
+
+    // ---- the other entry points: argument errors launch nothing
+    g_launches = 0;
+    EXPECT(qmm_w4a16_gemv(P(0), P(256), P(512), P(768), P(1024), 9, 100, 256, 1, nullptr, 0, nullptr) ==
+           QMM_ERR_SHAPE);
+    EXPECT(qmm_w4a16_gemv(P(0), P(256), P(512), P(768), P(1024), 1, 100, 256, 3, nullptr, 0, nullptr) ==
+           QMM_ERR_SHAPE);
+    EXPECT(qmm_gemv_min_split(0, 256) == QMM_ERR_ARG && qmm_gemv_min_split(9, 256) == QMM_ERR_SHAPE);
+    EXPECT(qmm_splitk_reduce(nullptr, QMM_PARTIAL_BF16, 2, 4, 4, P(0), nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_splitk_reduce(P(0), 7, 2, 4, 4, P(64), nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_splitk_reduce(P(1), QMM_PARTIAL_F32, 2, 4, 4, P(64), nullptr) == QMM_ERR_ALIGN);
+    EXPECT(qmm_splitk_reduce_cols(P(0), QMM_PARTIAL_BF16, 2, 4, 4, 4, P(64), nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_bf16_splitk(P(0), P(256), P(1024), 512, 512, 100, 2, P(4096), 1 << 20, nullptr) == QMM_ERR_SHAPE);
+    EXPECT(qmm_bf16_splitk(P(0), P(256), P(1024), 512, 512, 16384, 600, P(4096), 1 << 24, nullptr) ==
+           QMM_ERR_SHAPE);
+    EXPECT(qmm_bf16_splitk(P(0), P(256), P(1024), 512, 512, 16384, 4, P(4096), 100, nullptr) ==
+           QMM_ERR_WORKSPACE);
+    EXPECT(qmm_w4a16_g128_streamk(P(0), P(256), P(512), P(768), P(1024), 64, 1024, 2560, 0, P(4096), 1 << 20,
+                                  nullptr) == QMM_ERR_SHAPE);
+    EXPECT(qmm_wna16(5, 128, QMM_PARTIAL_BF16, P(0), P(256), P(512), P(768), P(1024), 32, 1024, 2560, 1, nullptr, 0,
+                     nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_wna16(4, 128, 3, P(0), P(256), P(512), P(768), P(1024), 32, 1024, 2560, 1, nullptr, 0, nullptr) ==
+           QMM_ERR_ARG);
+    const int lengths[4] = {8, 8, 8, 8};
+    EXPECT(qmm_attn_decode(P(0), P(256), P(512), lengths, P(1024), 1, 1, 32, 8, 64, 64, 0.1f, 1, nullptr, 0,
+                           nullptr) == QMM_ERR_SHAPE);
+    EXPECT(qmm_attn_decode(P(0), P(256), P(512), lengths, P(1024), 1, 1, 32, 8, 64, 128, __builtin_nanf(""), 1,
+                           nullptr, 0, nullptr) == QMM_ERR_ARG);
+    EXPECT(qmm_attn_decode(P(0), P(256), P(512), lengths, P(1024), 1, 1, 32, 8, 64, 128, 0.1f, 65, nullptr, 0,
+                           nullptr) == QMM_ERR_SHAPE);
+    EXPECT(g_launches == 0);
+
+    // ---- accepted calls of the other entry points
+    g_launches = 0;
+    EXPECT(qmm_bf16_splitk(P(0), P(256), P(1024), 512, 512, 16384, 6, P(4096), 4 * 6 * 512 * 512, nullptr) ==
+           QMM_OK && g_launches == 2 && g_last_split == 6);
+    g_launches = 0;
+    EXPECT(qmm_w4a16_gemv(P(0), P(256), P(512), P(768), P(1024), 1, 2560, 9728, 0, P(4096), 1 << 20, nullptr) ==
+           QMM_OK && g_launches >= 1);
+    g_launches = 0;
+    EXPECT(qmm_attn_decode(P(0), P(256), P(512), lengths, P(1024), 1, 1, 32, 8, 1024, 128, 0.1f, 4, P(4096),
+                           qmm_attn_decode_workspace_bytes(1, 1, 32, 4), nullptr) == QMM_OK && g_launches == 1);
+    for (int st = -7; st <= 1; ++st) EXPECT(qmm_status_string(st) != nullptr);
+
+    if (failures) {
+        fprintf(stderr, "%d host checks failed\n", failures);
+        return 1;
+    }
+    printf("host checks ok: %ld plans\n", plans);
+    return 0;
+}

@@ -104,12 +104,7 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         assert (plan.block_m, plan.block_n) in ((128, 256), (128, 128), (256, 256))
         # two 128 x 256 workgroups per CU up to M = 128; every other tile counts one per CU
         slots = pol.target_blocks * (2 if (plan.block_m, plan.block_n) == (128, 256) and M <= 128 else 1)
-        num_m = -(-M // plan.block_m)
-        assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
-            tiles, num_m, K, slots, pol.cap, pol.min_k_per_split)
-        assert plan.full_tiles % num_m == 0 or plan.full_tiles == tiles
-        assert plan.grid_x == plan.full_tiles + (tiles - plan.full_tiles) * plan.s
-        assert plan.grid_y == 1 and plan.grid_z == 1
+        check_slot_filling(plan, M, K, slots, pol)
     else:  # the page's rule over the kernel's tile; partitions of at least 2048 values up to M = 32
         assert G % plan.s == 0
         # 16-column tiles for up to 32 rows over at most 2^24 weights; else 32 columns while
@@ -152,10 +147,7 @@ def test_wna16_plan_follows_the_rule_for_each_format(bits, group):
             continue
         wgs = 2 if ((plan.block_m, plan.block_n) == (128, 256) and M <= 128
                     and 2 * _wide_lds_bytes(128, bits, group) <= 160 * 1024) else 1
-        tiles = plan.base_tiles
-        num_m = -(-M // plan.block_m)
-        assert (plan.s, plan.full_tiles) == opolicy.fill_decomposition(
-            tiles, num_m, K, pol.target_blocks * wgs, pol.cap, pol.min_k_per_split), (name, M)
+        check_slot_filling(plan, M, K, pol.target_blocks * wgs, pol, what=name)
 
 
 def test_wna16_plan_lds_budget():
@@ -165,42 +157,17 @@ def test_wna16_plan_lds_budget():
     assert max(_wide_lds_bytes(256, *f) for f in FORMATS) <= 160 * 1024
 
 
-def _wide_cost(T, rows, cols, s, full, G):
-    # critical path in 128 x 256 x 128 blocks over rounds of 256 workgroups, plus half a
-    # block per partition of a split
-    blk = rows / 128 * cols / 256
-    t = -(-full // 256) * G * blk
-    if T - full > 0 and s > 1:
-        t += -(-((T - full) * s) // 256) * -(-G // s) * blk + 0.5 * s
-    return t
-
-
-def _wide_choice(M, N, K):
-    # candidates in tie order: 256 x 256 (above M = 128), 128 x 256 (two workgroups per
-    # CU up to M = 128), 128 x 128 (only as a pure split: fewer tiles than CUs)
-    pol = q.policy_preset("QMM_POLICY_MI355X")
-    G = K // 128
-    best = None
-    for rows, cols in ((256, 256), (128, 256), (128, 128)):
-        if rows == 256 and M <= 128:
-            continue
-        num_m = -(-M // rows)
-        T = num_m * -(-N // cols)
-        if cols == 128 and T >= 256:
-            continue
-        slots = pol.target_blocks * (2 if (rows, cols) == (128, 256) and M <= 128 else 1)
-        s, full = opolicy.fill_decomposition(T, num_m, K, slots, pol.cap, pol.min_k_per_split)
-        c = _wide_cost(T, rows, cols, s, full, G)
-        if best is None or c < best[0]:
-            best = (c, rows, cols)
-    return best[1:]
-
-
 @pytest.mark.parametrize("M,N,K", [(M, N, K) for M, N, K in ALL_SHAPES
                                    if M > 64 and not (M <= 128 and N * K <= 1 << 24)])
-def test_large_m_variant_choice(M, N, K):
+def test_large_m_tile_choice_is_admissible(M, N, K):
+    # the large-M kernel's three tiles: 256 x 256 only above 128 rows, 128 x 128 only while
+    # its tiles are fewer than the CUs (a pure split at one workgroup per CU)
     plan = q.qmm_splitk_plan(M, N, K)
-    assert (plan.block_m, plan.block_n) == _wide_choice(M, N, K)
+    assert (plan.block_m, plan.block_n) in ((128, 256), (128, 128), (256, 256))
+    if plan.block_m == 256:
+        assert M > 128
+    if plan.block_n == 128:
+        assert -(-M // 128) * -(-N // 128) < 256 and plan.full_tiles == 0
 
 
 def test_large_m_variant_on_the_sweep():
@@ -215,19 +182,74 @@ def test_large_m_variant_on_the_sweep():
     assert all(got[(n, 128)][0] == 64 for n in ("q", "k", "v", "o"))
 
 
-def test_fill_decomposition_cases():
-    # 608 tiles (gate at M=2048 in 128 x 256 tiles), 512 slots: 512 unsplit, the last
-    # 96 in five partitions; 160 tiles: three partitions each; 512 tiles: no split.
-    assert opolicy.fill_decomposition(608, 16, 2560, 512, 16, 512) == (5, 512)
-    assert opolicy.fill_decomposition(160, 16, 9728, 512, 16, 512) == (3, 0)
-    assert opolicy.fill_decomposition(512, 16, 2560, 512, 16, 512) == (1, 512)
-    assert opolicy.fill_decomposition(520, 8, 2560, 512, 16, 512) == (5, 512)
-    # full rounded down to whole columns of tiles: 1100 tiles, 3 per column
-    assert opolicy.fill_decomposition(1100, 3, 2560, 512, 16, 512) == (5, 1023)
-    assert opolicy.fill_decomposition(7, 1, 128, 512, 16, 512) == (1, 7)  # K < 2 * min_k
-    assert opolicy.near_equal_partitions(20, 8) == [(0, 2), (2, 5), (5, 7), (7, 10), (10, 12), (12, 15),
-                                                   (15, 17), (17, 20)]
-    assert opolicy.near_equal_partitions(20, 5) == [(4 * p, 4 * p + 4) for p in range(5)]
+def check_slot_filling(plan, M, K, slots, pol, what=""):
+    """Properties of the large-M kernel's slot-filling decomposition (the library's own
+    rule for that kernel, stated in qmm.h), checked without restating the rule:
+      * the split respects the cap, the group count and the shortest partition;
+      * the unsplit tiles are whole columns of tiles and come first;
+      * a split's last round fits the workgroup slots, and one more partition would not
+        (the split is as deep as the slots allow, unless capped);
+      * with the tiles already filling whole rounds of slots, nothing is split."""
+    G = K // 128
+    T = plan.base_tiles
+    num_m = -(-M // plan.block_m)
+    smax = min(pol.cap, G, K // pol.min_k_per_split)
+    assert 1 <= plan.s <= max(1, smax), what
+    assert plan.grid_x == plan.full_tiles + (T - plan.full_tiles) * plan.s, what
+    assert plan.grid_y == 1 and plan.grid_z == 1, what
+    if plan.s == 1:
+        assert plan.full_tiles == T, what
+        if T < slots:  # an unsplit pure grid: two partitions would not fit, or splitting is barred
+            assert 2 * T > slots or smax <= 1, what
+        else:  # full rounds: the columns left after whole rounds do not fit two partitions
+            full = (T // slots) * slots
+            full -= full % num_m
+            assert T - full == 0 or 2 * (T - full) > slots or smax <= 1, what
+        return
+    assert plan.full_tiles % num_m == 0 and 0 <= plan.full_tiles < T, what
+    tail = T - plan.full_tiles
+    assert tail * plan.s <= slots, what  # the split tiles' workgroups fit one round of slots
+    assert plan.s == smax or tail * (plan.s + 1) > slots, what
+    if plan.full_tiles:
+        assert plan.full_tiles >= slots - num_m and T >= slots, what  # only past whole rounds
+
+
+# Hand-derived decompositions of the Qwen3-4B sweep under the MI355X preset {0, 0, 256, 20, 512}
+# (G = K/128 groups; smax = min(20, G, K/512)):
+#   gate/up M=2048: 256 x 256 tiles, 8 x 38 = 304 >= 256 slots; 256 whole (a multiple of 8 rows
+#                   of tiles) unsplit, the 48 left in min(5, 256 // 48 = 5) = 5 partitions
+#   down M=2048:    8 x 10 = 80 tiles, s = min(19, 256 // 80 = 3) = 3
+#   o M=2048:       8 x 10 = 80 tiles, s = min(8, 3) = 3
+#   q M=2048:       128 x 256 tiles, 16 x 16 = 256 = the slots: one full round, no split
+#   k/v M=2048:     128 x 128 tiles, 16 x 8 = 128, s = min(5, 256 // 128 = 2) = 2
+#   gate/up M=128:  128 x 128 tiles, 76, s = min(5, 256 // 76 = 3) = 3
+#   down M=128:     128 x 128 tiles, 20, s = min(19, 256 // 20 = 12) = 12
+HAND_PLANS = {("gate", 2048): (5, 256), ("up", 2048): (5, 256), ("down", 2048): (3, 0), ("o", 2048): (3, 0),
+              ("q", 2048): (1, 256), ("k", 2048): (2, 0), ("v", 2048): (2, 0),
+              ("gate", 128): (3, 0), ("up", 128): (3, 0), ("down", 128): (12, 0)}
+
+
+def test_large_m_plan_hand_derived_cases():
+    got = {(n, M): (p.s, p.full_tiles) for n, M, N, K, _ in syn.projection_sweep() if (n, M) in HAND_PLANS
+           for p in [q.qmm_splitk_plan(M, N, K)]}
+    assert got == HAND_PLANS
+
+
+def test_large_m_plan_split_tail_hand_derived():
+    # 1000 x (64*256 + 100) x 2560 on 128 x 256 tiles: 8 x 65 = 520 >= 256 slots; 512 whole
+    # tiles (two rounds, a multiple of 8) unsplit, the last column of 8 tiles in
+    # min(5, 256 // 8) = 5 partitions
+    p = q.qmm_splitk_plan(1000, 64 * 256 + 100, 2560)
+    assert (p.block_m, p.block_n, p.s, p.full_tiles, p.grid_x) == (128, 256, 5, 512, 512 + 8 * 5)
+    # whole columns: 300 x (342*256) x 2560 on 128 x 256 tiles: 3 x 342 = 1026 tiles; four
+    # rounds are 1024, rounded down to 1023 (a multiple of 3); 3 left in min(5, 256 // 3) = 5
+    p = q.qmm_splitk_plan(300, 342 * 256, 2560)
+    assert (p.block_m, p.block_n, p.s, p.full_tiles) == (128, 256, 5, 1023)
+    # 300 x 100000: 3 x 391 = 1173 tiles, 1023 whole, the 150 left fit only one partition each
+    p = q.qmm_splitk_plan(300, 100000, 2560)
+    assert (p.s, p.full_tiles) == (1, p.base_tiles)
+    # K below two shortest partitions (512 values): never split
+    assert q.qmm_splitk_plan(2048, 256, 768).s == 1
 
 
 def test_plan_rejects_bad_arguments():

@@ -33,7 +33,8 @@
  * never allocates, frees or synchronises; it enqueues its kernels on `stream`
  * (a hipStream_t; NULL is the default stream) and returns. Results are defined
  * once the stream reaches that point. C must not overlap any input or the
- * workspace. Calls are thread-safe; the library holds no state.
+ * workspace. Calls are thread-safe; the library holds no state, apart from the
+ * static scratch array of qmm_w4a16_g128_noalloc.
  *
  * Errors: every entry point returns QMM_OK (0) or a negative QMM_ERR_* code.
  * All argument checks happen on the host before any launch, so a call that
@@ -57,7 +58,8 @@ enum {
     QMM_ERR_ALIGN = -3,     /* A / Wq / B / workspace not 16-byte aligned, or an element misaligned */
     QMM_ERR_WORKSPACE = -4, /* split requested and workspace NULL or smaller than needed */
     QMM_ERR_HIP = -5,       /* a kernel launch failed (hipGetLastError) */
-    QMM_ERR_SIZE = -6       /* a size would overflow the library's 32-bit indexing (M*N, N*K, M*K > 2^37, or K >= 2^22) */
+    QMM_ERR_SIZE = -6,      /* a size would overflow the library's 32-bit indexing (M*N, N*K, M*K > 2^37, or K >= 2^22) */
+    QMM_ERR_SCRATCH = -7    /* qmm_w4a16_g128_noalloc: the split's planes exceed QMM_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Partial-plane element types for qmm_splitk_reduce. */
@@ -193,6 +195,29 @@ int qmm_w4a16_g128_pass1(const void *A, const void *Wq, const void *scale, const
 
 int qmm_splitk_reduce_cols(const void *partials, int partial_dtype, int s, int M, int N, int n_lo,
                            void *C, void *stream);
+
+/*
+ * qmm_w4a16_g128_noalloc -- qmm_w4a16_g128 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * bf16 partial planes of a split live in a static device array of the library, of
+ * QMM_NOALLOC_SCRATCH_BYTES (64 MiB), instead of a caller's workspace. The caller still
+ * passes the inputs and C.
+ *   Same arguments (without the workspace), layouts, decomposition, kernels, results and
+ *   errors as qmm_w4a16_g128; the result is bitwise equal to qmm_w4a16_g128's for the same
+ *   arguments. A split whose planes (2*s*M*N bytes for the effective s > 1) would exceed the
+ *   array returns QMM_ERR_SCRATCH and launches nothing (every Qwen3-4B projection up to
+ *   M = 128, and q, k, v, o and down at M = 2048, fit under the plan; gate and up at M = 2048
+ *   need 199 MB: pass s = 1 there).
+ *   The first call on a device looks up that device's copy of the array (with the device
+ *   current; `stream` must belong to the current device); no call allocates, frees or
+ *   synchronises. Each GPU's array is held until the process ends and is shared by every
+ *   call on that GPU: calls that overlap in time on one GPU (on different streams or
+ *   threads) race on it and must be serialised by the caller. Nothing in it needs to start
+ *   at zero; it keeps the last call's planes.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qmm_w4a16_g128_noalloc(const void *A, const void *Wq, const void *scale, const void *bias, void *C,
+                           int M, int N, int K, int s, void *stream);
 
 /*
  * Other weight-only formats (skillsdirectory "Optimize Prefill vs Decode Kernels",

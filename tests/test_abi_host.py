@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     for code in (q.QMM_OK, q.QMM_ERR_ARG, q.QMM_ERR_SHAPE, q.QMM_ERR_ALIGN, q.QMM_ERR_WORKSPACE,
-                 q.QMM_ERR_HIP, q.QMM_ERR_SIZE):
+                 q.QMM_ERR_HIP, q.QMM_ERR_SIZE, q.QMM_ERR_SCRATCH):
         assert q.qmm_status_string(code).startswith("QMM")
     assert "unknown" in q.qmm_status_string(12345)
 

@@ -19,6 +19,8 @@ QMM_ERR_ALIGN = -3
 QMM_ERR_WORKSPACE = -4
 QMM_ERR_HIP = -5
 QMM_ERR_SIZE = -6
+QMM_ERR_SCRATCH = -7
+QMM_NOALLOC_SCRATCH_BYTES = 64 << 20
 QMM_PARTIAL_BF16 = 0
 QMM_PARTIAL_F32 = 1
 
@@ -27,7 +29,7 @@ EXPORTED_FUNCTIONS = ("qmm_splitk_plan", "qmm_w4a16_g128", "qmm_splitk_reduce", 
                       "qmm_status_string", "qmm_w4a16_gemv", "qmm_gemv_min_split", "qmm_w4a16_g128_f32p",
                       "qmm_wna16", "qmm_wna16_plan", "qmm_attn_decode", "qmm_attn_decode_split",
                       "qmm_attn_decode_workspace_bytes", "qmm_w4a16_g128_streamk", "qmm_streamk_workspace_bytes",
-                      "qmm_w4a16_g128_pass1", "qmm_splitk_reduce_cols")
+                      "qmm_w4a16_g128_pass1", "qmm_splitk_reduce_cols", "qmm_w4a16_g128_noalloc")
 EXPORTED_DATA = ("QMM_POLICY_PAGE", "QMM_POLICY_MI355X")
 
 
@@ -71,6 +73,8 @@ def lib():
         L.qmm_splitk_plan.restype = I
         L.qmm_w4a16_g128.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_g128.restype = I
+        L.qmm_w4a16_g128_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, P]
+        L.qmm_w4a16_g128_noalloc.restype = I
         L.qmm_w4a16_g128_f32p.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
         L.qmm_w4a16_g128_f32p.restype = I
         L.qmm_w4a16_g128_streamk.argtypes = [P, P, P, P, P, I, I, I, I, P, S, P]
@@ -170,6 +174,16 @@ def qmm_w4a16_g128(A, Wq, scale, bias, C, M, N, K, s=0, workspace=None, workspac
                               int(s), _ptr(workspace), int(workspace_bytes), _stream(stream))
     if check and rc != QMM_OK:
         raise QmmError(rc, "qmm_w4a16_g128")
+    return rc
+
+
+def qmm_w4a16_g128_noalloc(A, Wq, scale, bias, C, M, N, K, s=0, stream=None, check=True):
+    """qmm_w4a16_g128 with the split's planes in the library's static device scratch (no
+    workspace argument, nothing allocated); returns the status."""
+    rc = lib().qmm_w4a16_g128_noalloc(_ptr(A), _ptr(Wq), _ptr(scale), _ptr(bias), _ptr(C), int(M), int(N), int(K),
+                                      int(s), _stream(stream))
+    if check and rc != QMM_OK:
+        raise QmmError(rc, "qmm_w4a16_g128_noalloc")
     return rc
 
 

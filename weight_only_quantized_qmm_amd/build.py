@@ -27,7 +27,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-I" + INCLUDE, "-I" + CSRC, "-Wall"]
 
 SOURCES = ["qmm_w4a16_skinny.hip", "qmm_w4a16_wide.hip", "qmm_gemv.hip", "qmm_reduce.hip", "qmm_dense.hip",
-           "qmm_attn.hip", "qmm_api.cpp"]
+           "qmm_attn.hip", "qmm_noalloc.hip", "qmm_api.cpp"]
 CALIB_SOURCES = ["qmm_calib.hip"]
 
 

@@ -615,6 +615,7 @@ extern "C" const char *qmm_status_string(int status)
     case QMM_ERR_WORKSPACE: return "QMM_ERR_WORKSPACE: workspace missing or too small for the split";
     case QMM_ERR_HIP: return "QMM_ERR_HIP: kernel launch failed";
     case QMM_ERR_SIZE: return "QMM_ERR_SIZE: problem too large for the library's indexing";
+    case QMM_ERR_SCRATCH: return "QMM_ERR_SCRATCH: the split's partial planes exceed the library's static scratch";
     default: return "QMM: unknown status";
     }
 }

@@ -23,10 +23,14 @@ Timing:
   * machine floors measured in the same run: empty-kernel dispatch, HBM
     stream read and copy, bf16 MFMA rate (libqmm_calib.so).
 
-Traffic: ``--pmc-run`` is the workload of two rocprofv3 --pmc passes
-(FETCH_SIZE, WRITE_SIZE) and ``--summarize-pmc`` turns them into the text
-summary under profiles/ that the ``traffic`` field reads back (it stays null
-when the kernel source changed after the counters were taken).
+Counters: ``--pmc-run [large|small]`` is the workload of rocprofv3 --pmc passes.
+For the dominant kernel, two passes (FETCH_SIZE, WRITE_SIZE) turn into the text
+summary under profiles/ that the ``traffic`` field reads back (``--summarize-pmc``;
+it stays null when the kernel source changed after the counters were taken), and
+two more (MIX_COUNTERS) into its instruction mix and unit utilisation
+(``--summarize-mix``). For the small-M kernel, FETCH_SIZE and WRITE_SIZE passes
+and a kernel trace give its per-launch HBM traffic and rate
+(``--summarize-small-pmc``).
 
 CPU baseline: the fp64 CPU oracle on the host cores, on a bounded sample of
 the same sweep (listed in the output), extrapolated to one whole sweep, plus the
@@ -354,23 +358,201 @@ def formats_table(torch, syn, q):
     return rows
 
 
-def pmc_run():
-    """Workload of the counter passes: the first pass of each M = 2048 shape's plan once, then
-    one plain copy."""
+SMALL_KERNEL = "w4a16_skinny_kernel"
+SMALL_WORKLOAD = ("the plan's call (matmul kernel, and the merge when split) of every sweep shape the small-M "
+                  "kernel runs, second of two rounds")
+
+
+def small_shapes():
+    """The sweep shapes the small-M kernel runs (M <= 64, and q, k, v, o at M = 128)."""
+    import weight_only_quantized_qmm_amd as q
+    import qmm_synth as syn
+    return [(n, M, N, K, i) for n, M, N, K, i in syn.projection_sweep() if q.qmm_splitk_plan(M, N, K).block_m < 128]
+
+
+def pmc_run(kind="large"):
+    """Workload of the counter passes. large: the first pass of each M = 2048 shape's plan
+    once; small: the plan's whole call of each shape the small-M kernel runs, once. Then one
+    plain copy (calibrates the byte counters)."""
     import torch
     import qmm_synth as syn
     import weight_only_quantized_qmm_amd as q
     torch.cuda.set_device(0)
-    shapes = [Shape(n, M, N, K, i, 1, torch, syn, q) for n, M, N, K, i in syn.projection_sweep() if M > 128]
-    for sh in shapes:
-        sh.call_pass1(0)
+    if kind == "large":
+        shapes = [Shape(n, M, N, K, i, 1, torch, syn, q) for n, M, N, K, i in syn.projection_sweep() if M > 128]
+        for sh in shapes:
+            sh.call_pass1(0)
+        what = "%d launches of %s" % (len(shapes), DOMINANT_KERNEL)
+    else:
+        # two rounds over two buffer sets: the second reads cold buffers with the clock up;
+        # the summary takes its launches
+        shapes = [Shape(n, M, N, K, i, 2, torch, syn, q) for n, M, N, K, i in small_shapes()]
+        for r in range(2):
+            for sh in shapes:
+                sh.call(r, 0)
+                torch.cuda.synchronize()
+        what = "two rounds of %d calls on %s" % (len(shapes), SMALL_KERNEL)
     torch.cuda.synchronize()
     L = calib_lib()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
     L.qmm_calib_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    print("pmc run: %d launches of %s + one %d-byte copy" % (len(shapes), DOMINANT_KERNEL, COPY_BYTES), flush=True)
+    print("pmc run: %s + one %d-byte copy" % (what, COPY_BYTES), flush=True)
+
+
+def _counter_rows(d, counters):
+    """{counter: [(dispatch id, kernel name, value)]} from a rocprofv3 --pmc output folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    out = {c: [] for c in counters}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] in out:
+                out[r["Counter_Name"]].append((int(r.get("Dispatch_Id") or 0), r["Kernel_Name"],
+                                               float(r["Counter_Value"])))
+    return {c: sorted(v) for c, v in out.items()}
+
+
+def _trace_durations(d):
+    """[(dispatch id, kernel name, ns)] from a rocprofv3 --kernel-trace output folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_trace.csv under %s" % d)
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return sorted(rows)
+
+
+def summarize_small_pmc(fetch_dir, write_dir, trace_dir, commands):
+    """Text summary of the small-M kernel's HBM traffic: FETCH_SIZE and WRITE_SIZE per launch
+    (scaled by the copy kernel), beside the algorithmic bytes and, with the launch's duration
+    from a kernel trace of the same workload, the achieved HBM rate."""
+    fetch = _counter_rows(fetch_dir, ["FETCH_SIZE"])["FETCH_SIZE"]
+    write = _counter_rows(write_dir, ["WRITE_SIZE"])["WRITE_SIZE"]
+    trace = _trace_durations(trace_dir)
+    pick = lambda rows, key: [v for _, k, v in rows if key in k]
+    cf, cw = pick(fetch, "calib_copy"), pick(write, "calib_copy")
+    f_scale, w_scale = COPY_BYTES / (cf[0] * 1024.0), COPY_BYTES / (cw[0] * 1024.0)
+    import weight_only_quantized_qmm_amd as q
+    shapes = small_shapes()
+    # the second of the workload's two rounds
+    df, dw, dt = [pick(rows, SMALL_KERNEL)[len(shapes):] for rows in (fetch, write, trace)]
+    lines = ["# HBM traffic of %s (%s) from rocprofv3 counters" % (SMALL_KERNEL, SMALL_WORKLOAD),
+             "commands:"] + ["  " + c for c in commands] + [
+        "copy kernel: %d bytes read and written; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (COPY_BYTES, cf[0], cw[0]),
+        "fetch scale: %.4f" % f_scale, "write scale: %.4f" % w_scale,
+        "per launch of the matmul kernel (the merge kernel of split calls not included); bytes = scaled FETCH + WRITE;",
+        "algorithmic = packed weights + scale/bias + A + C; us = kernel-trace duration of the same launch",
+        "%-5s %5s %5s %5s %3s  %10s %10s %10s %6s %8s %8s" % ("proj", "M", "N", "K", "s", "fetch B", "write B",
+                                                          "algo B", "ratio", "us", "HBM GB/s")]
+    tot_b = tot_a = tot_t = 0.0
+    for (n, M, N, K, _), fv, wv, ns in zip(shapes, df, dw, dt):
+        s = q.qmm_splitk_plan(M, N, K).s
+        fb, wb = fv * 1024 * f_scale, wv * 1024 * w_scale
+        a = algorithmic_bytes(M, N, K)
+        lines.append("%-5s %5d %5d %5d %3d  %10.4g %10.4g %10.4g %6.2f %8.2f %8.1f" % (
+            n, M, N, K, s, fb, wb, a, (fb + wb) / a, ns / 1e3, (fb + wb) / ns))
+        tot_b += fb + wb
+        tot_a += a
+        tot_t += ns
+    lines += ["all %d launches: %.4g bytes against %.4g algorithmic (%.2fx), %.1f GB/s over %.1f us of kernel time"
+              % (len(dt), tot_b, tot_a, tot_b / tot_a, tot_b / tot_t, tot_t / 1e3),
+              "kernel source digest: %s" % source_digest([os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
+                                                          for f in ("qmm_w4a16_skinny.hip", "qmm_api.cpp")])]
+    print("\n".join(lines))
+
+
+def summarize_trace(trace_dir, commands, title, bench_avg_us=None):
+    """Text summary of a rocprofv3 --kernel-trace --stats folder: calls and average duration
+    of every kernel, the dominant kernel's variants combined."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
+    rows = [r for f in files for r in csv.DictReader(open(f))]
+
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+        return name.split("(")[0][:70]
+
+    lines = ["# " + title, "commands:"] + ["  " + c for c in commands] + [
+        "%-72s %7s %11s %9s" % ("kernel", "calls", "average_us", "pct")]
+    dom_calls, dom_ns = 0, 0.0
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("%-72s %7d %11.3f %9.2f" % (short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                                                 float(r["Percentage"])))
+        if DOMINANT_KERNEL in r["Name"]:
+            dom_calls += int(r["Calls"])
+            dom_ns += float(r["TotalDurationNs"])
+    if dom_calls:
+        lines.append("%s, all variants together: %d calls, average %.3f us" % (DOMINANT_KERNEL, dom_calls,
+                                                                             dom_ns / dom_calls / 1e3))
+    if bench_avg_us:
+        lines.append("bench.py's own figure in the same process (HIP events around graph replays): avg_launch_us = %s"
+                     % bench_avg_us)
+    print("\n".join(lines))
+
+
+MIX_COUNTERS = (["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU", "SQ_INSTS_MFMA"],
+                ["GRBM_GUI_ACTIVE", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS",
+                 "SQ_VALU_MFMA_COEXEC_CYCLES"])
+
+
+def summarize_mix(dir1, dir2, commands, n_xcc=8, n_cu=256):
+    """Text summary of the dominant kernel's instruction mix and unit utilisation from two
+    rocprofv3 --pmc passes (MIX_COUNTERS) over the large-M workload (pmc_run("large")).
+    GRBM_GUI_ACTIVE is reported summed over the 8 XCDs, so the launch's active cycles are
+    that sum / 8; per-SIMD counters are summed over the GPU's 1024 SIMDs, and the quad-cycle
+    counters of a CU's 4 SIMDs (SQ_ACTIVE_INST_VALU) give the per-SIMD busy fraction as is."""
+    a = _counter_rows(dir1, MIX_COUNTERS[0])
+    b = _counter_rows(dir2, MIX_COUNTERS[1])
+    import qmm_synth as syn
+    shapes = [(n, M, N, K) for n, M, N, K, _ in syn.projection_sweep() if M > 128]
+
+    def vals(rows, c):
+        return [v for _, k, v in rows[c] if DOMINANT_KERNEL in k]
+
+    simds = 4 * n_cu
+    lines = ["# Instruction mix and unit utilisation of %s (%s) from rocprofv3 counters" % (
+        DOMINANT_KERNEL, DOMINANT_WORKLOAD), "commands:"] + ["  " + c for c in commands] + [
+        "active cycles = GRBM_GUI_ACTIVE / %d (summed over the XCDs); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES /"
+        " (active cycles x %d SIMDs);" % (n_xcc, simds),
+        "VALU busy = SQ_ACTIVE_INST_VALU / (active cycles x %d CUs) (quad-cycles summed over a CU's 4 SIMDs: the"
+        " per-SIMD fraction); LDS busy = SQ_LDS_IDX_ACTIVE / (active cycles x %d CUs);" % (n_cu, n_cu),
+        "bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; co-issue = SQ_VALU_MFMA_COEXEC_CYCLES /"
+        " SQ_VALU_MFMA_BUSY_CYCLES",
+        "%-5s %6s %9s %9s %9s %9s %9s %8s %9s" % ("proj", "MFMA", "VALU/MFMA", "LDS/MFMA", "MFMA busy", "VALU busy",
+                                                 "LDS busy", "bank cf", "co-issue")]
+    rows = []
+    for i, (n, M, N, K) in enumerate(shapes):
+        g1, g2 = vals(a, "GRBM_GUI_ACTIVE")[i] / n_xcc, vals(b, "GRBM_GUI_ACTIVE")[i] / n_xcc
+        mb = vals(a, "SQ_VALU_MFMA_BUSY_CYCLES")[i]
+        va = vals(a, "SQ_ACTIVE_INST_VALU")[i]
+        iv, im = vals(a, "SQ_INSTS_VALU")[i], vals(a, "SQ_INSTS_MFMA")[i]
+        li, lb, il = vals(b, "SQ_LDS_IDX_ACTIVE")[i], vals(b, "SQ_LDS_BANK_CONFLICT")[i], vals(b, "SQ_INSTS_LDS")[i]
+        co = vals(b, "SQ_VALU_MFMA_COEXEC_CYCLES")[i]
+        r = dict(mfma=im, valu_per_mfma=(iv - im) / im, lds_per_mfma=il / im, mfma_busy=mb / (g1 * simds),
+                 valu_busy=va / (g1 * n_cu), lds_busy=li / (g2 * n_cu), bank=lb / max(li, 1), coexec=co / max(mb, 1))
+        rows.append(r)
+        lines.append("%-5s %6.3g %9.2f %9.2f %9.3f %9.3f %9.3f %8.4f %9.3f" % (
+            n, r["mfma"], r["valu_per_mfma"], r["lds_per_mfma"], r["mfma_busy"], r["valu_busy"], r["lds_busy"],
+            r["bank"], r["coexec"]))
+    mean = {k: sum(r[k] for r in rows) / len(rows) for k in rows[0]}
+    lines += ["mean  %6.3g %9.2f %9.2f %9.3f %9.3f %9.3f %8.4f %9.3f" % (
+        mean["mfma"], mean["valu_per_mfma"], mean["lds_per_mfma"], mean["mfma_busy"], mean["valu_busy"],
+        mean["lds_busy"], mean["bank"], mean["coexec"]),
+        "(SQ_INSTS_VALU counts the MFMA instructions too; VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA)",
+        "kernel source digest: %s" % source_digest()]
+    print("\n".join(lines))
 
 
 def summarize_pmc(fetch_dir, write_dir, commands):
@@ -429,7 +611,16 @@ def parse():
                     help="file that receives the per-shape and secondary tables (JSON)")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only the dominant-kernel roofline measurement (the profiled command)")
-    ap.add_argument("--pmc-run", action="store_true", help="only the workload of the profiler counter passes")
+    ap.add_argument("--pmc-run", nargs="?", const="large", choices=("large", "small"),
+                    help="only the workload of the profiler counter passes (large: the M = 2048 first passes; "
+                         "small: the small-M kernel's shapes)")
+    ap.add_argument("--summarize-small-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="print the small-M kernel's traffic summary of two --pmc passes and a kernel trace")
+    ap.add_argument("--summarize-mix", nargs=2, metavar=("DIR1", "DIR2"),
+                    help="print the dominant kernel's instruction-mix summary of two --pmc passes (MIX_COUNTERS)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "TITLE"),
+                    help="print the kernel summary of a rocprofv3 --kernel-trace --stats folder")
+    ap.add_argument("--bench-avg-us", default=None, help="bench.py's avg_launch_us of the traced run (recorded)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc output folders")
     ap.add_argument("--pmc-commands", nargs="*", default=[], help="commands recorded in the traffic summary")
@@ -588,8 +779,17 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_commands)
         return
+    if args.summarize_small_pmc:
+        summarize_small_pmc(*args.summarize_small_pmc, args.pmc_commands)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], args.pmc_commands, args.summarize_trace[1], args.bench_avg_us)
+        return
+    if args.summarize_mix:
+        summarize_mix(*args.summarize_mix, args.pmc_commands)
+        return
     if args.pmc_run:
-        pmc_run()
+        pmc_run(args.pmc_run)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)

@@ -11,11 +11,14 @@
  * starts from, and the split of the reduction dimension it adds).
  *
  * When the unsplit output grid under-fills the GPU, an occupancy policy cuts the
- * reduction into s equal partitions on 128-value group boundaries; each
+ * reduction into s partitions on 128-value group boundaries (equal when s divides
+ * the group count, as on the page; otherwise lengths that differ by one group); each
  * partition writes its own bf16 partial plane without atomics, and a second
  * kernel sums the planes in fp32 and casts once to bf16 (same page, Tasks 2-4).
  * When the grid is already full the policy returns s = 1 and the unsplit kernel
- * runs unchanged. A dense bf16 split-K variant with fp32 partials is exported
+ * runs unchanged -- except for the large-M kernel under the MI355X preset, which
+ * splits the columns of tiles left over after whole rounds of workgroup slots
+ * (the split tail of qmm_splitk_plan, below). A dense bf16 split-K variant with fp32 partials is exported
  * beside it (gpu-kernels-explained "Split-K, streams and overlap", Concept).
  *
  * Layouts (all row-major, contiguous, no strides):
@@ -140,7 +143,11 @@ int qmm_splitk_plan(int M, int N, int K, int group_size, const qmm_policy *polic
  *   s = 0  : the decomposition comes from qmm_splitk_plan(M, N, K, 128, NULL)
  *            (its s, and its full_tiles for the large-M kernel)
  *   s = 1  : the unsplit kernel (the control; also what the policy falls back to)
- *   s > 1  : explicit split of every tile into s equal partitions; s must divide K/128.
+ *   s > 1  : explicit split of every tile into s partitions, 2 <= s <= K/128: partition p
+ *            covers the 128-value groups [floor(p*G/s), floor((p+1)*G/s)), G = K/128
+ *            (equal partitions when s divides G; otherwise they differ by one group).
+ *            An explicit s equal to the plan's reproduces the plan's launch whenever the
+ *            plan splits every tile (full_tiles = 0).
  *            Launches the split kernel, writing bf16 partial planes [s][M][N] into
  *            `workspace`, then the reduce into C (of the split tiles' columns only,
  *            when the plan runs the first tiles unsplit).
@@ -230,7 +237,8 @@ int qmm_w4a16_g128_noalloc(const void *A, const void *Wq, const void *scale, con
  *   group_size  32, 64 or 128: scale and bias are bf16 [N][K/group_size], and
  *               w[n,k] = scale[n, k/group_size] * q[n,k] + bias[n, k/group_size].
  *   K must be a multiple of 128. The split partitions K into blocks of 128 values (each a
- *   whole number of groups): s = 0 asks qmm_wna16_plan, s >= 1 must divide K/128.
+ *   whole number of groups): s = 0 asks qmm_wna16_plan, 1 <= s <= K/128 splits as for
+ *   qmm_w4a16_g128 (partition p covers blocks [floor(p*G/s), floor((p+1)*G/s)), G = K/128).
  *   partial_dtype QMM_PARTIAL_BF16 (workspace >= 2*s*M*N bytes) or QMM_PARTIAL_F32
  *   (>= 4*s*M*N bytes) when the effective s > 1.
  *   qmm_wna16(4, 128, QMM_PARTIAL_BF16, ...) is qmm_w4a16_g128, launch for launch, and

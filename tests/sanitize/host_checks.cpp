@@ -139,7 +139,10 @@ int main()
     EXPECT(call_w4a16(32, 1024, 2560, 1, nullptr, 0, nullptr) == QMM_ERR_ARG && g_launches == 0);
     EXPECT(call_w4a16(0, 1024, 2560, 1, nullptr, 0) == QMM_ERR_ARG && g_launches == 0);
     EXPECT(call_w4a16(32, 1024, 2500, 1, nullptr, 0) == QMM_ERR_SHAPE && g_launches == 0);
-    EXPECT(call_w4a16(32, 1024, 2560, 3, P(4096), 1 << 20) == QMM_ERR_SHAPE && g_launches == 0);  // 3 does not divide 20
+    EXPECT(call_w4a16(32, 1024, 2560, 21, P(4096), 1 << 20) == QMM_ERR_SHAPE && g_launches == 0);  // 21 > 20 groups
+    // a split that does not divide the 20 groups: near-equal partitions, accepted
+    EXPECT(call_w4a16(32, 1024, 2560, 3, P(4096), 1 << 20) == QMM_OK && g_launches == 2 && g_last_split == 3);
+    EXPECT(call_w4a16(128, 9728, 2560, 3, P(4096), 1 << 24) == QMM_OK && g_launches == 2 && g_last_split == 3);
     EXPECT(call_w4a16(32, 1024, 2560, 40, P(4096), 1 << 20) == QMM_ERR_SHAPE && g_launches == 0);
     EXPECT(call_w4a16(32, 1024, 2560, 4, nullptr, 0) == QMM_ERR_WORKSPACE && g_launches == 0);
     EXPECT(call_w4a16(32, 1024, 2560, 4, P(4096), 2 * 4 * 32 * 1024 - 1) == QMM_ERR_WORKSPACE && g_launches == 0);

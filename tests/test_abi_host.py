@@ -278,7 +278,7 @@ def _w4(**kw):
     (dict(A=None), q.QMM_ERR_ARG), (dict(Wq=None), q.QMM_ERR_ARG), (dict(scale=None), q.QMM_ERR_ARG),
     (dict(bias=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG),
     (dict(M=0), q.QMM_ERR_ARG), (dict(N=-1), q.QMM_ERR_ARG), (dict(K=0), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG),
-    (dict(K=2500), q.QMM_ERR_SHAPE), (dict(s=3), q.QMM_ERR_SHAPE), (dict(s=40), q.QMM_ERR_SHAPE),
+    (dict(K=2500), q.QMM_ERR_SHAPE), (dict(s=21), q.QMM_ERR_SHAPE), (dict(s=40), q.QMM_ERR_SHAPE),
     (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(Wq=ADDR2 + 4), q.QMM_ERR_ALIGN), (dict(C=ADDR + 1), q.QMM_ERR_ALIGN),
     (dict(scale=ADDR3 + 1), q.QMM_ERR_ALIGN),
     (dict(s=4), q.QMM_ERR_WORKSPACE),
@@ -300,7 +300,7 @@ def _w4f(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(A=None), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG), (dict(K=2500), q.QMM_ERR_SHAPE),
-    (dict(s=3), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=21), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
     # fp32 planes: the bf16-sized workspace is too small by half
     (dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024), q.QMM_ERR_WORKSPACE),
     (dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=4 * 4 * 32 * 1024 - 4), q.QMM_ERR_WORKSPACE),
@@ -322,7 +322,7 @@ def _w4p(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(A=None), q.QMM_ERR_ARG), (dict(s=-1), q.QMM_ERR_ARG), (dict(K=2500), q.QMM_ERR_SHAPE),
-    (dict(s=3), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
+    (dict(s=21), q.QMM_ERR_SHAPE), (dict(A=ADDR + 8), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
     (dict(s=4, workspace=ADDR2 + 8, workspace_bytes=1 << 30), q.QMM_ERR_ALIGN), (dict(K=1 << 22), q.QMM_ERR_SIZE),
 ])
 def test_w4a16_pass1_rejects_before_launch(kw, code):
@@ -358,7 +358,7 @@ def _wn(bits=8, group=64, dt=0, **kw):
 @pytest.mark.parametrize("fmt,kw,code", [
     (dict(bits=5), {}, q.QMM_ERR_ARG), (dict(bits=2), {}, q.QMM_ERR_ARG), (dict(group=16), {}, q.QMM_ERR_ARG),
     (dict(group=256), {}, q.QMM_ERR_ARG), (dict(group=96), {}, q.QMM_ERR_ARG), (dict(dt=2), {}, q.QMM_ERR_ARG),
-    ({}, dict(A=None), q.QMM_ERR_ARG), ({}, dict(K=2560 + 64), q.QMM_ERR_SHAPE), ({}, dict(s=3), q.QMM_ERR_SHAPE),
+    ({}, dict(A=None), q.QMM_ERR_ARG), ({}, dict(K=2560 + 64), q.QMM_ERR_SHAPE), ({}, dict(s=21), q.QMM_ERR_SHAPE),
     ({}, dict(A=ADDR + 8), q.QMM_ERR_ALIGN), ({}, dict(s=4), q.QMM_ERR_WORKSPACE),
     (dict(dt=1), dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024), q.QMM_ERR_WORKSPACE),
     ({}, dict(s=4, workspace=ADDR + 0x200000, workspace_bytes=2 * 4 * 32 * 1024 - 2), q.QMM_ERR_WORKSPACE),

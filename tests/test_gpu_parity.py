@@ -117,6 +117,40 @@ def test_cfg2_projection_sweep(name, M, N, K, idx):
         assert np.array_equal(host_bits(C), host_bits(C1))
 
 
+# Explicit splits that do not divide the group count: partition p covers groups
+# [floor(p*G/s), floor((p+1)*G/s)) on both matmul kernels (small-M kernel: 48 and 100 rows;
+# large-M kernel: 128 x 128 tiles at 128 rows, 256 x 256 tiles at 300 rows).
+NONDIV_CASES = [(48, 1000, 2560, (3, 7, 9, 13)), (100, 1000, 2560, (3, 6)), (128, 9728, 2560, (3, 7)),
+                (300, 520, 1024, (3, 5))]
+
+
+@pytest.mark.parametrize("M,N,K,splits", NONDIV_CASES)
+def test_non_divisor_splits_match_oracle(M, N, K, splits):
+    d = syn.w4a16_inputs(M, N, K, seed=18500 + M)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    G = K // 128
+    for s in splits:
+        assert G % s != 0
+        for f32p in (False, True):
+            say("non-divisor split M=%d N=%d K=%d s=%d f32p=%d" % (M, N, K, s, f32p))
+            C = run_w4a16(dv, M, N, K, s, guard=40, f32p=f32p)
+            check_tolerance(host_f64(C), ref, what="%dx%dx%d s=%d f32p=%d" % (M, N, K, s, f32p))
+
+
+def test_explicit_split_reproduces_the_plan():
+    """gate at M = 128: the plan splits every 128 x 128 tile in 3 (20 groups: 6, 7, 7);
+    the same s passed explicitly is the same launch, bit for bit."""
+    M, N, K = 128, 9728, 2560
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert (plan.s, plan.full_tiles) == (3, 0)
+    dv = w4a16_device(syn.w4a16_inputs(M, N, K, seed=18600))
+    say("explicit s=3 against the plan M=%d N=%d K=%d" % (M, N, K))
+    a = host_bits(run_w4a16(dv, M, N, K, 0))
+    b = host_bits(run_w4a16(dv, M, N, K, 3))
+    assert np.array_equal(a, b)
+
+
 # Shapes the plan runs on 128 x 128 tiles of the large-M kernel (a pure split): ragged M
 # below and above 128 rows, N not a multiple of 128 (and of 8: element-wise stores).
 TILE128_CASES = [(100, 7000, 2560), (300, 300, 1024), (256, 520, 4096), (130, 1000, 3072)]
@@ -565,9 +599,9 @@ def run_wna16(dv, bits, group, M, N, K, s, guard=0, f32p=False):
 
 
 # small-M kernel (M <= 64, ragged N; 100 rows in 64-row blocks), 128-row and 256-row
-# large-M kernels
+# large-M kernels; the last two split into partitions of unequal length (3 of 20 and 8 groups)
 FORMAT_SHAPES = [(1, 1000, 2560, 4), (16, 1024, 2560, 5), (48, 1000, 1024, 2), (100, 1000, 2560, 4),
-                 (100, 7000, 2560, 4), (300, 520, 1024, 8)]
+                 (100, 7000, 2560, 4), (300, 520, 1024, 8), (48, 1000, 2560, 3), (300, 520, 1024, 3)]
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)

@@ -167,7 +167,9 @@ W4A16Tile wide_tile(int M) {
 hipError_t dispatch_skinny(WFormat fmt, const W4A16Tile &tile, const void *A, const void *Wq, const void *scale,
                            const void *bias, void *out, bool f32_part, int M, int N, int K, int s, bool vec,
                            hipStream_t st) {
-    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (K / kGroup) / s, fmt.bits, fmt.sub());
+    // the longest partition: ceil(G / s) blocks (near-equal partitions differ by at most one)
+    const int G = K / kGroup;
+    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (G + s - 1) / s, fmt.bits, fmt.sub());
     return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part,
                                          M, N, K, s, vec, st);
 }
@@ -304,7 +306,7 @@ int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const 
         if (rc != QMM_OK) return rc;
         s = plan.s;
         full_tiles = plan.full_tiles;
-    } else if (s > G || G % s != 0) {
+    } else if (s > G) {
         return QMM_ERR_SHAPE;
     }
     const size_t MN = (size_t)M * (size_t)N;

@@ -42,7 +42,7 @@ inline bool format_supported(WFormat f)
 
 constexpr int kLdsPerCU = 160 * 1024;  // LDS bytes of one CU (and the most one workgroup may take)
 
-// Wave count and groups per load round of the SKINNY kernel for a partition of gpp groups
+// Wave count and groups per load round of the SKINNY kernel for partitions of at most gpp groups
 // (128-value blocks). A wave stages a round's activations in LDS (4 KB per group and 16-row
 // tile) and its scale/bias entries (two dword arrays of 16*ns rows x gpw*sub entries, each
 // rounded up to 64); the workgroup's LDS is at most 160 KB.

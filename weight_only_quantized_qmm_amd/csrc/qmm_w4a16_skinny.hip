@@ -3,9 +3,10 @@
 // the library (4- or 8-bit codes, groups of 32, 64 or 128 values).
 //
 // Same contract as the other W4A16 kernels (tiny-llm "Week 2 Day 7: Split-K
-// Prefill", Task 2): blockIdx.z is the partition p, the workgroup covers groups
-// [p*gpp, (p+1)*gpp) of the reduction and writes its tile into plane p of `out`
-// (C itself when s = 1), with plain stores and no atomics.
+// Prefill", Task 2): blockIdx.z is the partition p of s = gridDim.z, the workgroup covers
+// the 128-value blocks [floor(p*G/s), floor((p+1)*G/s)) of the reduction (the page's equal
+// partitions when s divides G) and writes its tile into plane p of `out` (C itself when
+// s = 1), with plain stores and no atomics.
 //
 // With few rows the op streams the packed weights once and is bound by memory
 // latency and bandwidth, not by the matrix cores (a dispatch on MI355X costs about
@@ -76,7 +77,7 @@ template <int BITS, int MT, int NS, int GPW, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                    void *__restrict__ out, int M, int N, int K, int gpp, int sub_shift, int vec_store,
+                    void *__restrict__ out, int M, int N, int K, int sub_shift, int vec_store,
                     int f32_part)
 {
     constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
@@ -94,7 +95,9 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const int n_blk = blockIdx.x * (16 * NS);
     const int m_blk = blockIdx.y * (16 * MT);
     const int GG = (K >> 7) << sub_shift;  // scale/bias entries per row (128 / group_size per block)
-    const int g0 = blockIdx.z * gpp;
+    const int G = K >> 7;  // 128-value blocks of the reduction
+    const int g0 = (int)(((long long)blockIdx.z * G) / gridDim.z);
+    const int gpp = (int)(((long long)(blockIdx.z + 1) * G) / gridDim.z) - g0;  // this partition's blocks
     // this wave's groups: g0 + wave + waves*i, i < n_w
     const int n_w = (gpp - wave + waves - 1) / waves;
 
@@ -274,7 +277,6 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
                       int M, int N, int K, int s, int sub_shift, int waves, bool vec_store, hipStream_t stream)
 {
     const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
-    const int gpp = (K / 128) / s;
     const size_t lds = qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
     if (waves > MAXW || lds > (size_t)qmm_impl::kLdsPerCU) return hipErrorInvalidValue;
     // the activation copies take 32-bit byte offsets into A
@@ -283,7 +285,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
     hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       out, M, N, K, gpp, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
+                       out, M, N, K, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -78,7 +78,8 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * for that M" (the MI355X preset); the page's own rule counts 32 x 32 tiles.
  *
  * The small-M kernel runs M <= 64, and M <= 128 when N*K <= 2^24. Its tiles are 16*mt rows
- * (mt = 1, 2, 4 for M <= 16, 32, more) by 16 columns for M <= 32 with N*K <= 2^24; else by 32
+ * (mt = 1, 2, 4 for M <= 16, 32, more) by 16 columns for M <= 32 with N*K <= 2^24 and for
+ * M <= 8 with N <= 4096; else by 32
  * while 32-column tiles fit in 256 workgroups and K < 8192; else by 48 when 48-column tiles
  * fit in 256 workgroups, else by 64. With tile_m = tile_n = 0 and M <= 32, its partitions hold at least 2048 reduction
  * values (min_k_per_split is raised to 2048 in the rule): a shorter partition saves less

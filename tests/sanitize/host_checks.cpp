@@ -11,19 +11,27 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <set>
+#include <tuple>
+
 #include "qmm.h"
 #include "qmm_launch.h"
 
 namespace {
 int g_launches = 0;       // launches recorded since the last reset
 int g_last_split = -1;    // split of the last matmul launch
+// (bits, mt, ns, gpw, waves) of every small-M launch: printed at the end, checked by the test
+// against the configurations the kernel source instantiates
+std::set<std::tuple<int, int, int, int, int>> g_skinny_cfgs;
 }  // namespace
 
 namespace qmm_impl {
-hipError_t launch_w4a16_skinny(WFormat, int, int, int, int waves, const void *, const void *, const void *,
-                               const void *, void *, bool, int, int, int, int s, bool, hipStream_t)
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *, const void *,
+                               const void *, const void *, void *, bool, int M, int, int, int s, bool, hipStream_t)
 {
     if (waves < 1 || waves > 16) abort();
+    if (M < 1 || skinny_lds_bytes(mt, ns, waves, gpw, fmt.sub()) > (size_t)kLdsPerCU) abort();
+    g_skinny_cfgs.insert(std::make_tuple(fmt.bits, mt, ns, gpw, waves));
     ++g_launches;
     g_last_split = s;
     return hipSuccess;
@@ -213,6 +221,30 @@ int main()
     EXPECT(qmm_attn_decode(P(0), P(256), P(512), lengths, P(1024), 1, 1, 32, 8, 1024, 128, 0.1f, 4, P(4096),
                            qmm_attn_decode_workspace_bytes(1, 1, 32, 4), nullptr) == QMM_OK && g_launches == 1);
     for (int st = -7; st <= 1; ++st) EXPECT(qmm_status_string(st) != nullptr);
+
+    // ---- every small-M configuration the host can pick: decode and small rows, every
+    // format, plan and explicit splits
+    for (int M : {1, 2, 3, 4, 5, 7, 8, 9, 12, 16, 20, 24, 32, 40, 48, 64, 80, 100, 128})
+        for (int N : {16, 100, 1000, 1024, 2560, 4096, 5000, 9728})
+            for (int K : {128, 384, 1024, 2560, 4096, 9728, 16384})
+                for (int bits : {4, 8})
+                    for (int g : {32, 64, 128})
+                        for (int s : {0, 1, 2, 3, 5}) {
+                            if (s > K / 128) continue;
+                            qmm_plan pl;
+                            if (qmm_wna16_plan(bits, g, M, N, K, nullptr, &pl) != QMM_OK) continue;
+                            const int s_eff = s ? s : pl.s;
+                            const size_t ws = (size_t)4 * s_eff * M * N;
+                            static unsigned char *big = nullptr;
+                            (void)big;
+                            g_launches = 0;
+                            const int rc = qmm_wna16(bits, g, QMM_PARTIAL_BF16, P(0), P(256), P(512), P(768), P(1024),
+                                                     M, N, K, s, s_eff > 1 ? P(4096) : nullptr, ws, nullptr);
+                            EXPECT(rc == QMM_OK);
+                        }
+    for (const auto &c : g_skinny_cfgs)
+        printf("skinny config %d %d %d %d %d\n", std::get<0>(c), std::get<1>(c), std::get<2>(c), std::get<3>(c),
+               std::get<4>(c));
 
     if (failures) {
         fprintf(stderr, "%d host checks failed\n", failures);

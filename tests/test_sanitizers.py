@@ -41,6 +41,18 @@ def test_host_code_under_sanitizers(tmp_path):
                        env=dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1"))
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "host checks ok" in r.stdout
+    # every small-M configuration the host picked is one the kernel source instantiates
+    # (bits, mt, ns, gpw, at most MAXW waves)
+    import re
+    src = open(os.path.join(CSRC, "qmm_w4a16_skinny.hip")).read()
+    built = {tuple(int(x) for x in m) for m in re.findall(r"QMM_CFG\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+    assert built
+    maxw = {c[:4]: c[4] for c in built}
+    picked = [tuple(int(x) for x in l.split()[2:]) for l in r.stdout.splitlines() if l.startswith("skinny config")]
+    assert picked
+    for bits, mt, ns, gpw, waves in picked:
+        assert (bits, mt, ns, gpw) in maxw, ("no kernel instantiation for", bits, mt, ns, gpw)
+        assert waves <= maxw[(bits, mt, ns, gpw)], ("too many waves for", bits, mt, ns, gpw, waves)
 
 
 @needs_runtimes

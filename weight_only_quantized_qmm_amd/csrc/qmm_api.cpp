@@ -130,8 +130,12 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
         // Up to 32 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
         // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o on MI355X:
         // at M = 16 20-30 % faster than split 32-column tiles, whose second pass costs more
-        // than the spread saves; at M = 32 11-15 % faster than 32-column tiles).
-        if (M <= 32 && (long long)N * K <= (1LL << 24)) {
+        // than the spread saves; at M = 32 11-15 % faster than 32-column tiles). Decode (up
+        // to 8 rows) also over more weights while those tiles fit one round of workgroups
+        // (N <= 4096): the long reduction then runs unsplit instead of in split 48-column
+        // tiles plus a second pass (down at M = 1, 4, 8 on MI355X: 8.6, 9.2, 10.2 us against
+        // 10.3, 10.6, 10.9).
+        if (M <= 32 && ((long long)N * K <= (1LL << 24) || (M <= 8 && N <= 16 * kCUs))) {
             t.ns = 1;
             return t;
         }

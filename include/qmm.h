@@ -320,8 +320,10 @@ int qmm_splitk_reduce(const void *partials, int partial_dtype, int s, int M, int
  * (gpu-kernels-explained "Split-K, streams and overlap", Concept: a small output
  * with a long k cut into s slices, partial sums added by a second pass).
  *   K must be a multiple of 32. The reduction is cut into s near-equal partitions of
- *   32-value granules: partition p covers granules [floor(p*U/s), floor((p+1)*U/s)),
- *   U = K/32, so any 1 <= s <= U is allowed.
+ *   units of 64 values when K is a multiple of 64, else of 32-value granules: partition p
+ *   covers units [floor(p*U/s), floor((p+1)*U/s)), U = K/64 (K/32), so any 1 <= s <= U
+ *   is allowed (QMM_ERR_SHAPE beyond). Bounds on the 64-value grid keep every row's reads
+ *   on whole 128-byte lines.
  *   s = 0 picks s with the MI355X occupancy rule over this kernel's tile.
  *   s = 1 writes C directly; s > 1 writes fp32 partial planes [s][M][N] to the
  *   workspace (>= 4*s*M*N bytes, 16-byte aligned), then reduces them into C.

@@ -234,7 +234,8 @@ def attn_decode(Q, K, V, lengths, scale):
 
 
 def qmm_dense(A, B, M, N, K, s=1, nthreads=None):
-    """fp64 C[M,N] = A @ B.T over bf16 inputs, summed per partition (32-value granules)."""
+    """fp64 C[M,N] = A @ B.T over bf16 inputs, summed per partition (64-value units when K is a
+    multiple of 64, else 32-value granules)."""
     A, pa = _c(A, np.uint16)
     B, pb = _c(B, np.uint16)
     C = np.empty((M, N), dtype=np.float64)

@@ -39,8 +39,9 @@
  *            The oracle is this plain definition in fp64; the split into key ranges
  *            and their merge are the GPU method's business.
  *   dense:  C[m,n] = sum_k A[m,k] * B[n,k], split into s near-equal partitions of
- *            32-value granules (gpu-kernels-explained "Split-K, streams and overlap",
- *            Concept / Maths: k cut into s slices, a second pass adds the partials).
+ *            64-value units when K is a multiple of 64, else of 32-value granules
+ *            (gpu-kernels-explained "Split-K, streams and overlap", Concept / Maths: k
+ *            cut into s slices, a second pass adds the partials).
  *
  * All matmul arithmetic is fp64 in ascending k (inner) and ascending p (outer).
  * The reduce is fp32 because the page fixes FP32 for that sum.
@@ -249,19 +250,20 @@ int oracle_qmm_w4a16_points(const uint16_t *A, const uint32_t *Wq, const uint16_
 }
 
 /* C[M][N] (fp64) = A @ B.T for bf16 A[M][K], B[N][K], summed per partition over
- * s near-equal partitions of 32-value granules. */
+ * s near-equal partitions of 64-value units (K a multiple of 64) or of 32-value granules. */
 int oracle_qmm_dense(const uint16_t *A, const uint16_t *B, int M, int N, int K, int s,
                      double *C, int nthreads)
 {
     if (M <= 0 || N <= 0 || K <= 0 || K % ORACLE_GRANULE != 0) return -1;
-    int U = K / ORACLE_GRANULE;
+    const int unit = K % (2 * ORACLE_GRANULE) == 0 ? 2 * ORACLE_GRANULE : ORACLE_GRANULE;
+    int U = K / unit;
     int *kb = (int *)malloc(((size_t)s + 1) * sizeof *kb);
     if (!kb) return -2;
     for (int p = 0; p < s; ++p) {
         int ub, ue;
         if (oracle_partition_granules(U, s, p, &ub, &ue) != 0) { free(kb); return -1; }
-        kb[p] = ub * ORACLE_GRANULE;
-        kb[p + 1] = ue * ORACLE_GRANULE;
+        kb[p] = ub * unit;
+        kb[p + 1] = ue * unit;
     }
     double *a = bf16_matrix_to_f64(A, (size_t)M * K);
     double *b = bf16_matrix_to_f64(B, (size_t)N * K);

@@ -514,7 +514,8 @@ def test_gemv_rejects_before_launch(kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(A=None), q.QMM_ERR_ARG), (dict(B=None), q.QMM_ERR_ARG), (dict(C=None), q.QMM_ERR_ARG),
-    (dict(K=100), q.QMM_ERR_SHAPE), (dict(s=513), q.QMM_ERR_SHAPE), (dict(M=-2), q.QMM_ERR_ARG),
+    (dict(K=100), q.QMM_ERR_SHAPE), (dict(s=257), q.QMM_ERR_SHAPE), (dict(K=32 * 71, s=72), q.QMM_ERR_SHAPE),
+    (dict(M=-2), q.QMM_ERR_ARG),
     (dict(A=ADDR + 4), q.QMM_ERR_ALIGN), (dict(s=4), q.QMM_ERR_WORKSPACE),
     (dict(s=4, workspace=ADDR3, workspace_bytes=4 * 4 * 512 * 512 - 4), q.QMM_ERR_WORKSPACE),
 ])

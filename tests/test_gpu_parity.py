@@ -384,16 +384,19 @@ def test_cfg3_dense_split_sweep(cfg3, s):
     check_tolerance(host_f64(C), ref, what="dense s=%d" % s)
 
 
-def test_dense_ragged_and_reduce_fp32():
-    M, N, K = 37, 45, 32 * 70
-    d = syn.dense_inputs(M, N, K, seed=3001)
+@pytest.mark.parametrize("K,splits", [(32 * 71, (1, 3, 7, 71)), (64 * 35, (2, 3, 6, 35))])
+def test_dense_ragged_and_reduce_fp32(K, splits):
+    # K = 32 * 71: partitions of 32-value granules (half stages at the odd ones, one granule
+    # each at s = 71); K = 64 * 35: 64-value units (one each at s = 35)
+    M, N = 37, 45
+    d = syn.dense_inputs(M, N, K, seed=3001 + K)
     ref = oracle.qmm_dense(d["A"], d["B"], M, N, K)
     A, B = dev_bf16(d["A"]), dev_bf16(d["B"])
-    for s in (1, 3, 7, 70):
+    for s in splits:
         say("dense ragged M=%d N=%d K=%d s=%d" % (M, N, K, s))
         C = q.bf16_splitk(A, B, s=s)
         torch.cuda.synchronize()
-        check_tolerance(host_f64(C), ref, what="dense ragged s=%d" % s)
+        check_tolerance(host_f64(C), ref, what="dense ragged K=%d s=%d" % (K, s))
 
 
 # ----------------------------------------------------------- config 4 (decode)

@@ -526,7 +526,9 @@ extern "C" int qmm_bf16_splitk(const void *A, const void *B, void *C, int M, int
     if (K % kGranule != 0) return QMM_ERR_SHAPE;
     if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 2)) return QMM_ERR_ALIGN;
-    const int U = K / kGranule;
+    // partition units: 64 values when K is a multiple of 64 (whole 128-byte lines per stage),
+    // else 32-value granules
+    const int U = K / ((K % 64) == 0 ? 64 : kGranule);
     const DenseTile tile = dense_tile(M, N);
     if (s == 0) {
         // The occupancy rule over this kernel's tile: fill one wave of workgroups.

@@ -4,8 +4,8 @@
 // output with a long reduction gives too few output tiles to fill the GPU; cutting k
 // into s slices multiplies the workgroups by s, each computes one tile over one slice,
 // and a second pass adds the s partial sums. Here the slices are near-equal runs of
-// 32-value granules: partition p covers granules [floor(p*U/s), floor((p+1)*U/s)),
-// U = K/32. Each partition writes an fp32 partial plane (plain stores, no atomics);
+// 64-value units when K is a multiple of 64 (32-value granules otherwise): partition p
+// covers units [floor(p*U/s), floor((p+1)*U/s)), U = K/64 (K/32). Each partition writes an fp32 partial plane (plain stores, no atomics);
 // with s = 1 the workgroup writes the bf16 result directly.
 //
 // Structure (the same pipeline as the large-M W4A16 kernel, without the dequant):
@@ -15,7 +15,7 @@
 //     (128 bytes each) are copied global -> LDS by global_load_lds_dwordx4, two stages
 //     ahead, into rings of three 16 KB slots each (96 KB); each wave waits for its own
 //     copies of the next stage (s_waitcnt vmcnt) before the barrier that ends a stage;
-//   * a partition with an odd number of granules ends with a half stage (32 values):
+//   * a partition with an odd number of 32-value granules ends with a half stage (32 values):
 //     its copies re-read the first half of the row instead of reading past it, and
 //     the two reduction steps of the missing half are skipped;
 //   * LDS rows are 128 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7);
@@ -123,15 +123,20 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     const int p = L_idx / tiles;
     const int m0 = (tile % num_m) * TM;
     const int n0 = (tile / num_m) * TN;
-    const long long U = K >> 5;
+    // Partition bounds in units of 64 values (one stage, a whole 128-byte line of every row)
+    // when K allows, else of 32-value granules: bounds off the 64-value grid make every
+    // stage's 128 bytes of a row straddle two lines (cfg3 at s = 6 and 12: 49 and 33 us on
+    // granule bounds, 34 and 24 us on 64-value bounds).
+    const int UNIT = (K & 63) == 0 ? 64 : 32;
+    const long long U = K / UNIT;
     const int u_lo = (int)(((long long)p * U) / s);
     const int u_hi = (int)(((long long)(p + 1) * U) / s);
 
     DCtx c;
     c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
     c.B = reinterpret_cast<const char *>(B) + 2 * (size_t)n0 * (size_t)K;
-    c.k_begin = 32 * u_lo;
-    c.k_end = 32 * u_hi;
+    c.k_begin = UNIT * u_lo;
+    c.k_end = UNIT * u_hi;
     // Copy j of wave w fills LDS rows 8q .. 8q+7, q = 4w + j; lane i -> row 8q + i/8,
     // stored chunk i%8, logical chunk (i%8) ^ ((r>>1)&7); a half stage reads logical
     // chunk & 3 (the stage's valid half). Rows past M (N) re-read the last row.
@@ -256,13 +261,14 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
 
 namespace qmm_impl {
 
-// K < 2^22 (32-bit copy offsets over 128 rows); s <= K/32. vec_store: N % 4 == 0 and
+// K < 2^22 (32-bit copy offsets over 128 rows); s <= K/64 when K % 64 == 0, else s <= K/32
+// (no empty partition). vec_store: N % 4 == 0 and
 // the output 16-byte (fp32 planes) or 8-byte (bf16 C) aligned.
 hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out, bool f32_out,
                         int M, int N, int K, int s, bool vec_store, hipStream_t stream)
 {
     if (tile.block_m() != TM || tile.block_n() != TN) return hipErrorInvalidValue;
-    if (K >= (1 << 22) || s < 1 || s > K / 32) return hipErrorInvalidValue;
+    if (K >= (1 << 22) || s < 1 || s > K / ((K & 63) == 0 ? 64 : 32)) return hipErrorInvalidValue;
     const int tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     const dim3 grid(tiles * s);
     (void)hipGetLastError();

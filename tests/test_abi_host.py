@@ -525,3 +525,12 @@ def test_dense_rejects_before_launch(kw, code):
     rc = q.qmm_bf16_splitk(a["A"], a["B"], a["C"], a["M"], a["N"], a["K"], a["s"], a["workspace"],
                            a["workspace_bytes"], stream=0, check=False)
     assert rc == code
+
+
+def test_decode_tile_rule_edges():
+    """The plan's tile at the decode rule's edges (the GPU edge-shape tests run these shapes against the oracle)."""
+    tiles = {(M, N, K): (p.block_m, p.block_n, p.s) for M, N, K in [(8, 4096, 8192), (9, 4096, 8192),
+                                                                  (5, 4097, 8192), (7, 2500, 9728)]
+             for p in [q.qmm_splitk_plan(M, N, K)]}
+    assert tiles[(8, 4096, 8192)][:2] == (16, 16) and tiles[(7, 2500, 9728)][:2] == (16, 16)
+    assert tiles[(9, 4096, 8192)][1] != 16 and tiles[(5, 4097, 8192)][1] != 16

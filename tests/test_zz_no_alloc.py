@@ -31,10 +31,12 @@ def without_workspace(dv, M, N, K, s):
     return C
 
 
-# calls in this order, each split's planes smaller than the previous call's (bytes 2*s*M*N):
+# calls in this order, each split's planes smaller than the previous call's (2*s*M*N bytes):
 # o at M = 2048 (plan: 3 partitions, 31.5 MB), down at M = 128 (12, 7.9 MB), 48 x 1000 in 5
-# (480 KB), the K projection at M = 32 in 4 (262 KB), then an unsplit call
-CALLS = [(2048, 2560, 4096, 0), (128, 2560, 9728, 0), (48, 1000, 2560, 5), (32, 1024, 2560, 4), (64, 4096, 2560, 1)]
+# (480 KB), the K projection at M = 32 in 4 (262 KB), 40 x 1000 in 3 unequal partitions
+# (240 KB), then an unsplit call
+CALLS = [(2048, 2560, 4096, 0), (128, 2560, 9728, 0), (48, 1000, 2560, 5), (32, 1024, 2560, 4), (40, 1000, 2560, 3),
+         (64, 4096, 2560, 1)]
 
 
 def test_noalloc_matches_the_workspace_entry_point():

@@ -119,7 +119,8 @@ def calib_lib():
     L.qmm_calib_read.argtypes = [P, S, P, P]
     L.qmm_calib_copy.argtypes = [P, P, S, P]
     L.qmm_calib_mfma.argtypes = [I, I, P, P]
-    for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_copy, L.qmm_calib_mfma):
+    L.qmm_calib_step.argtypes = [I, I, I, I, P, P]
+    for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_copy, L.qmm_calib_mfma, L.qmm_calib_step):
         f.restype = I
     return L
 
@@ -146,13 +147,22 @@ def calibrate(torch):
     del buf, buf2
     grid, iters = 256 * 8, 4096
     t_mfma = timed(lambda: L.qmm_calib_mfma(grid, iters, out.data_ptr(), torch.cuda.current_stream().cuda_stream), 4)
+    step_grid, steps = 256, 2048
+    step = {}
+    for name, lds_reads, dequant in (("mfma", 0, 0), ("mfma_lds", 1, 0), ("mfma_lds_dequant", 1, 1)):
+        t = timed(lambda: L.qmm_calib_step(step_grid, steps, lds_reads, dequant, out.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream), 4)
+        step[name] = round(step_grid * 8 * steps * 8 * 32768 / t / 1e12, 1)
     torch.cuda.empty_cache()
     return {"empty_dispatch_us": round(t_empty * 1e6, 3),
             "hbm_read_TBps": round(nbytes / t_read / 1e12, 3),
             "hbm_copy_TBps": round(nbytes / t_copy / 1e12, 3),  # bytes read + bytes written
             "mfma_bf16_tflops": round(grid * 4 * iters * 4 * 32768 / t_mfma / 1e12, 1),
+            "step_loop_tflops": step,
             "note": "empty kernel back to back in a graph; 2 GiB read; 1 GiB copy; "
-                    "v_mfma_f32_32x32x16_bf16 loop on 2048 workgroups"}
+                    "v_mfma_f32_32x32x16_bf16 loop on 2048 workgroups; step loop: the large-M kernel's "
+                    "step (8 waves of 256 x 32 per CU, 8 MFMAs per wave and step) without global memory, "
+                    "alone, with its 8 LDS operand reads, and with those and one dequantised word"}
 
 
 def read_traffic(alg_bytes_per_launch):
@@ -196,6 +206,7 @@ def dominant_roofline(torch, shapes, rounds=4):
             "launches_per_replay": rounds * len(dom), "avg_launch_us": avg_dur * 1e6,
             "algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops,
             "frac_of_measured_mfma_peak": achieved / (calib["mfma_bf16_tflops"] * 1e12),
+            "frac_of_step_loop": achieved / (calib["step_loop_tflops"]["mfma_lds_dequant"] * 1e12),
             "traffic_note": traffic_note,
             "block_tiles": {sh.name: [sh.plan.block_m, sh.plan.block_n] for sh in dom}}
     return roof, calib
@@ -903,7 +914,7 @@ def main():
                                "W4A16 g128, MI355X policy split", "shapes": len(sweep)},
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()
                      if k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_us",
-                              "frac_of_measured_mfma_peak")},
+                              "frac_of_measured_mfma_peak", "frac_of_step_loop")},
         "cpu_baseline": cpu,
     }
     line["roofline"]["kernel"] = "%s, first pass of the plan on the 7 M=2048 shapes" % DOMINANT_KERNEL

@@ -8,9 +8,14 @@
 //   * a streaming read and a streaming copy of a large buffer (achievable HBM
 //     bandwidth; the copy of a known size also calibrates the profiler's
 //     FETCH_SIZE / WRITE_SIZE counters);
-//   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate).
+//   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate);
+//   * the large-M kernel's reduction step without global memory (the rate its inner
+//     loop allows on this GPU, with and without the LDS operand reads and the
+//     dequantisation).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "qmm_device.h"
 
 namespace {
 
@@ -72,6 +77,53 @@ __global__ void __launch_bounds__(256) calib_mfma_kernel(int iters, float *out)
     if (s == 1.2345f) out[0] = s;
 }
 
+// The large-M kernel's inner step (256 x 256 tiles: eight waves of 256 x 32, one workgroup
+// per CU, so two waves per SIMD), with no global memory: per step each wave runs eight
+// v_mfma_f32_32x32x16_bf16 (a 256 x 32 tile over 16 reduction values) on the operands of
+// the previous step and prepares the next step's operands as the kernel does: with
+// LDSR, eight 16-byte A-operand reads from LDS (consecutive lanes on consecutive 16-byte
+// chunks: conflict-free); with DEQ, one packed word dequantised by the library's
+// dequant8. Without them the operands are carried over unchanged.
+constexpr int kStepLds16 = 2048;  // 32 KB of bf16 operands
+template <bool LDSR, bool DEQ>
+__global__ void __launch_bounds__(512) calib_step_kernel(int steps, float *out)
+{
+    using namespace qmm_dev;
+    __shared__ uint4 lds[kStepLds16];
+    for (int i = threadIdx.x; i < kStepLds16; i += blockDim.x)  // bf16 values in [0.25, 1)
+        lds[i] = make_uint4(0x3E803F00u ^ (uint32_t)(i & 0x3F), 0x3F403E90u, 0x3EA03F10u ^ (uint32_t)(i & 0x1F),
+                            0x3F203EC0u);
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    f32x16 acc[8];
+    bf16x8 af[8];
+    for (int i = 0; i < 8; ++i) {
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+        af[i] = as_bf16x8(lds[(lane + 64 * i) & (kStepLds16 - 1)]);
+    }
+    uint32_t w = 0x9E3779B9u ^ (uint32_t)threadIdx.x;
+    const float sc512 = (0.01f + 1e-4f * (float)lane) * 512.f, bi = -0.08f;
+    bf16x8 bw = as_bf16x8(dequant8(w, sc512, bi));
+    uint32_t off = (uint32_t)lane;
+    for (int s = 0; s < steps; ++s) {
+        bf16x8 af2[8], bw2 = bw;
+        off = (off + 512u) & (kStepLds16 - 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af2[i] = LDSR ? as_bf16x8(lds[(off + 64u * i) & (kStepLds16 - 1)]) : af[i];
+        w = w * 1664525u + 1013904223u;
+        if (DEQ) bw2 = as_bf16x8(dequant8(w, sc512, bi));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = mfma32x32x16(bw, af[i], acc[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = af2[i];
+        bw = bw2;
+    }
+    float t = 0.f;
+    for (int i = 0; i < 8; ++i)
+        for (int e = 0; e < 16; ++e) t += acc[i][e];
+    if (t == 1.2345f) out[0] = t;
+}
+
 }  // namespace
 
 // All entry points enqueue on `stream` and return the hipError_t of the launch.
@@ -103,6 +155,24 @@ int qmm_calib_mfma(int grid, int iters, void *out, void *stream)
 {
     hipLaunchKernelGGL(calib_mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters,
                        static_cast<float *>(out));
+    return (int)hipGetLastError();
+}
+
+// The large-M kernel's step loop: grid workgroups of eight waves, `steps` steps each;
+// lds_reads / dequant switch the LDS operand reads and the dequantisation on.
+// flops = grid * 8 waves * steps * 8 * 32768; out: one float of device memory.
+int qmm_calib_step(int grid, int steps, int lds_reads, int dequant, void *out, void *stream)
+{
+    float *o = static_cast<float *>(out);
+    const hipStream_t st = (hipStream_t)stream;
+    if (lds_reads && dequant)
+        hipLaunchKernelGGL((calib_step_kernel<true, true>), dim3(grid), dim3(512), 0, st, steps, o);
+    else if (lds_reads)
+        hipLaunchKernelGGL((calib_step_kernel<true, false>), dim3(grid), dim3(512), 0, st, steps, o);
+    else if (dequant)
+        hipLaunchKernelGGL((calib_step_kernel<false, true>), dim3(grid), dim3(512), 0, st, steps, o);
+    else
+        hipLaunchKernelGGL((calib_step_kernel<false, false>), dim3(grid), dim3(512), 0, st, steps, o);
     return (int)hipGetLastError();
 }
 

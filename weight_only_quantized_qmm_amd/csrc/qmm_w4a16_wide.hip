@@ -20,7 +20,7 @@
 // 4 or 8 MFMAs, and 64-value stages make every row of A a whole 128-byte line.
 //
 // Data movement: every global read of the kernel is a direct global -> LDS copy
-// (global_load_lds_*), issued one and a half stages ahead of its use, into rings of three slots:
+// (global_load_lds_*), issued one to one and a half stages ahead of its use, into rings of three slots:
 //   A:  BM rows x 64 bf16 (16 or 32 KB per stage), 1 KB per copy;
 //   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage; 64 bytes and 16 KB for
 //       8-bit codes), 1 KB per copy;
@@ -30,8 +30,12 @@
 // The compiler neither sees nor waits for these copies; the kernel retires them
 // itself: in the middle of stage i each wave waits (s_waitcnt vmcnt) until the copies
 // it issued for stage i+1 have landed, and the barrier that follows publishes them
-// to the whole workgroup; the copies of stage i+2 are issued right after it. No other
-// vector-memory instruction is issued in the loop, so the counter arithmetic is exact.
+// to the whole workgroup; the A copies of stage i+2 are issued right after it, its W
+// and scale/bias copies during the stage's last step. No other vector-memory
+// instruction is issued in the loop, so the counter arithmetic is exact. In the 8-wave
+// variant only waves 0-3, one per SIMD, issue copies (twice the share each): while a
+// copying wave issues them, the other wave of its SIMD keeps the matrix core busy
+// (2-4 % faster than copies from every wave).
 // The next stage's first operands are read during the last step of the current one,
 // so the matrix pipeline does not drain at stage boundaries.
 //
@@ -78,6 +82,7 @@ struct Cfg {
     static constexpr int NWN = BN / (32 * NJ);      // waves along N
     static constexpr int NWM = BM / (32 * MI);      // waves along M
     static constexpr int NW = NWM * NWN;            // waves per workgroup
+    static constexpr int CW = NW == 8 ? 4 : NW;      // waves that issue the copies (one per SIMD for 8)
     static constexpr int A_SLOT = BM * BK * 2;      // 16 or 32 KB
     static constexpr int WROW = BK * BITS / 8;      // bytes of one W row per stage: 32 or 64
     static constexpr int WCH = WROW / 16;           // 16-byte chunks per W row: 2 or 4
@@ -85,16 +90,16 @@ struct Cfg {
     static constexpr int WV = BITS / 4;             // 16-byte W reads per lane per stage
     static constexpr int W_SLOT = BN * WROW;        // 8 or 16 KB
     static constexpr int SB_SLOT = 2 * SUB * BN * 4;  // scale then bias dwords of one block
-    static constexpr int AC = (BM / 8) / NW;        // A copies (1 KB each) per wave per stage
-    static constexpr int WC = W_SLOT / 1024 / NW;   // W copies (1 KB each) per wave per stage
-    static constexpr int SC = SB_SLOT / 256 / NW;   // scale/bias copies (64 values) per wave per block
-    static constexpr int N_EVEN = AC + WC + SC;     // copies a wave issues in an even stage
+    static constexpr int AC = (BM / 8) / CW;        // A copies (1 KB each) per copying wave per stage
+    static constexpr int WC = W_SLOT / 1024 / CW;   // W copies (1 KB each) per copying wave per stage
+    static constexpr int SC = SB_SLOT / 256 / CW;   // scale/bias copies (64 values) per copying wave per block
+    static constexpr int N_EVEN = AC + WC + SC;     // copies a copying wave issues in an even stage
     static constexpr int N_ODD = AC + WC;           // ... in an odd stage
     static constexpr int LDS = 3 * A_SLOT + 3 * W_SLOT + 2 * SB_SLOT;
     static constexpr int SBQ = BN / 64;             // scale/bias copies per array and group
     static constexpr int OCC = 2 * LDS <= qmm_impl::kLdsPerCU ? 2 : 1;  // workgroups one CU holds
     static_assert(LDS == qmm_impl::wide_lds_bytes(BM, BITS, SUB, BN), "LDS size differs from the host's");
-    static_assert(AC * NW * 8 == BM && WC * NW * 1024 == W_SLOT && SC * NW * 256 == SB_SLOT, "copy split");
+    static_assert(AC * CW * 8 == BM && WC * CW * 1024 == W_SLOT && SC * CW * 256 == SB_SLOT, "copy split");
 };
 
 // LDS of one workgroup: three A slots, three W slots, two scale/bias slots.
@@ -135,6 +140,7 @@ struct Ctx {
     const char *Wq;     // Wq + n0*K/8 words (bytes)
     const char *sb[CF::SC];  // scale/bias source of this wave's copies (scale or bias, + n0*GG + sub)
     int gpp, rot, g_begin;
+    int copier;  // this wave issues copies (wave < CW; wave-uniform)
     uint32_t a_off[CF::AC];    // per-lane byte offsets of the A copies (stage k excluded)
     uint32_t w_off[CF::WC];    // per-lane byte offsets of the W copies
     uint32_t sb_off[CF::SC];   // per-lane byte offsets of the scale/bias copies
@@ -154,17 +160,23 @@ __device__ __forceinline__ int stage_group(const Ctx<CF> &c, int x)
 }
 
 // The copies of stage x into A/W slot `slot3` (and its group's scale/bias into
-// slot `sbslot` when WITH_SB): AC + WC (+ WC) vector-memory instructions per wave.
-template <class CF, bool WITH_SB>
+// slot `sbslot` when WITH_SB): AC + WC (+ SC) vector-memory instructions per copying
+// wave, none for the others. PART 0 issues them all, PART 1 the A copies, PART 2 the
+// W and scale/bias copies.
+template <class CF, bool WITH_SB, int PART = 0>
 __device__ __forceinline__ void issue(const Ctx<CF> &c, int x, int slot3, int sbslot)
 {
     typedef CF GE;
+    if (GE::CW < GE::NW && !c.copier) return;
     const int g = __builtin_amdgcn_readfirstlane(stage_group(c, x));
     const int k0 = g * 128 + (x & 1) * BK;
     const char *Ab = c.A + 2 * (size_t)k0;
     const uint32_t a_dst = c.a_lds + (uint32_t)slot3 * GE::A_SLOT;
+    if (PART != 2) {
 #pragma unroll
-    for (int j = 0; j < GE::AC; ++j) copy16(a_dst + 1024u * j, c.a_off[j], Ab);
+        for (int j = 0; j < GE::AC; ++j) copy16(a_dst + 1024u * j, c.a_off[j], Ab);
+    }
+    if (PART == 1) return;
     const uint32_t w_dst = c.w_lds + (uint32_t)slot3 * GE::W_SLOT;
 #pragma unroll
     for (int j = 0; j < GE::WC; ++j)
@@ -338,6 +350,7 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     Ctx<CF> c;
     c.gpp = gpp;
     c.g_begin = g_lo;
+    c.copier = wave < CF::CW;
     // Workgroups that run side by side on one XCD share rows of A; starting them at
     // different groups (within a window of ROT_GROUPS) spreads their simultaneous
     // reads of A over more L2 channels. The fp32 sums' order depends only on the tile
@@ -346,7 +359,7 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
     c.Wq = reinterpret_cast<const char *>(Wq) + (size_t)n0 * (size_t)K * CF::BITS / 8;
 
-    // Copy lanes. A: copy j of wave w fills LDS rows 8q .. 8q+7, q = AC*w + j; lane i
+    // Copy lanes (copying waves, w < CW). A: copy j of wave w fills rows 8q .. 8q+7, q = AC*w + j; lane i
     // lands at row r = 8q + i/8, stored chunk i%8, so it fetches logical chunk
     // (i%8) ^ ((r>>1)&7). Rows past M re-read row M-1 (never stored).
 #pragma unroll
@@ -419,11 +432,13 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     load_head<CF, 0>(c, L, 0, 0, o);
 
     // Stage x uses A/W slot x % 3 and scale/bias slot (x/2) % 2. In the middle of stage x
-    // each wave waits for its copies of stage x+1 (issued in the middle of stage x-1, the
-    // only ones outstanding), the barrier publishes them and certifies that every wave
-    // has left stage x-1, and the copies of stage x+2 go into stage x-1's slot (with the
-    // next group's scale/bias when x is even). Past the last stage the copies repeat
-    // stage nst-1 into slots that are never read again.
+    // each wave waits for its copies of stage x+1 (issued during stage x-1, the only ones
+    // outstanding), the barrier publishes them and certifies that every wave has left
+    // stage x-1, and the copies of stage x+2 go into stage x-1's slot (with the next
+    // group's scale/bias when x is even, whose slot the group of stages x-2 and x-1 has
+    // left): the A copies at once, the W and scale/bias copies during the last step of
+    // stage x, before the head of stage x+1 is read. Past the last stage the copies
+    // repeat stage nst-1 into slots that are never read again.
     int s3 = 0;  // st % 3
     for (int st = 0; st < nst; st += 2) {
         const int s3n = s3 == 2 ? 0 : s3 + 1;    // (st+1) % 3
@@ -435,17 +450,21 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
             [&] {
                 QMM_WAIT_VMCNT(0);
                 __syncthreads();
-                issue<CF, true>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
+                issue<CF, true, 1>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
             },
-            [&](Ops<CF> &n) { load_head<CF, 1>(c, L, s3n, sbs, n); });
+            [&](Ops<CF> &n) {
+                issue<CF, true, 2>(c, min(st + 2, nst - 1), s3p, sbs ^ 1);
+                load_head<CF, 1>(c, L, s3n, sbs, n);
+            });
         run_stage<CF>(
             c, L, s3n, o, acc,
             [&] {
                 QMM_WAIT_VMCNT(0);
                 __syncthreads();
-                issue<CF, false>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
+                issue<CF, false, 1>(c, min(st + 3, nst - 1), s3, 0);  // (st+3) % 3 == st % 3
             },
             [&](Ops<CF> &n) {
+                issue<CF, false, 2>(c, min(st + 3, nst - 1), s3, 0);
                 if (more) load_head<CF, 0>(c, L, s3p, sbs ^ 1, n);
             });
         s3 = s3p;

@@ -42,6 +42,15 @@ def test_library_exports_every_declared_symbol():
         ctypes.c_int.in_dll(L, d)  # resolves the data symbol
 
 
+def test_calibration_library_exports_what_the_bench_binds():
+    # libqmm_calib.so holds only the benchmark's measurement kernels; bench.py binds
+    # these entry points by name (loading it initialises no GPU)
+    import bench
+    L = bench.calib_lib()
+    for f in ("qmm_calib_empty", "qmm_calib_read", "qmm_calib_copy", "qmm_calib_mfma", "qmm_calib_step"):
+        assert hasattr(L, f), f
+
+
 def test_status_strings():
     for code in (q.QMM_OK, q.QMM_ERR_ARG, q.QMM_ERR_SHAPE, q.QMM_ERR_ALIGN, q.QMM_ERR_WORKSPACE,
                  q.QMM_ERR_HIP, q.QMM_ERR_SIZE, q.QMM_ERR_SCRATCH):

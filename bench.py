@@ -119,7 +119,7 @@ def calib_lib():
     L.qmm_calib_read.argtypes = [P, S, P, P]
     L.qmm_calib_copy.argtypes = [P, P, S, P]
     L.qmm_calib_mfma.argtypes = [I, I, P, P]
-    L.qmm_calib_step.argtypes = [I, I, I, I, P, P]
+    L.qmm_calib_step.argtypes = [I, I, I, I, I, P, P]
     for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_copy, L.qmm_calib_mfma, L.qmm_calib_step):
         f.restype = I
     return L
@@ -149,10 +149,13 @@ def calibrate(torch):
     t_mfma = timed(lambda: L.qmm_calib_mfma(grid, iters, out.data_ptr(), torch.cuda.current_stream().cuda_stream), 4)
     step_grid, steps = 256, 2048
     step = {}
-    for name, lds_reads, dequant in (("mfma", 0, 0), ("mfma_lds", 1, 0), ("mfma_lds_dequant", 1, 1)):
-        t = timed(lambda: L.qmm_calib_step(step_grid, steps, lds_reads, dequant, out.data_ptr(),
-                                           torch.cuda.current_stream().cuda_stream), 4)
-        step[name] = round(step_grid * 8 * steps * 8 * 32768 / t / 1e12, 1)
+    for layout, lname in ((0, "w256x32"), (1, "w128x64")):
+        step[lname] = {}
+        for name, lds_reads, dequant in (("mfma", 0, 0), ("mfma_lds", 1, 0), ("mfma_dequant", 0, 1),
+                                         ("mfma_lds_dequant", 1, 1)):
+            t = timed(lambda: L.qmm_calib_step(step_grid, steps, layout, lds_reads, dequant, out.data_ptr(),
+                                               torch.cuda.current_stream().cuda_stream), 4)
+            step[lname][name] = round(step_grid * 8 * steps * 8 * 32768 / t / 1e12, 1)
     torch.cuda.empty_cache()
     return {"empty_dispatch_us": round(t_empty * 1e6, 3),
             "hbm_read_TBps": round(nbytes / t_read / 1e12, 3),
@@ -161,8 +164,9 @@ def calibrate(torch):
             "step_loop_tflops": step,
             "note": "empty kernel back to back in a graph; 2 GiB read; 1 GiB copy; "
                     "v_mfma_f32_32x32x16_bf16 loop on 2048 workgroups; step loop: the large-M kernel's "
-                    "step (8 waves of 256 x 32 per CU, 8 MFMAs per wave and step) without global memory, "
-                    "alone, with its 8 LDS operand reads, and with those and one dequantised word"}
+                    "step (8 waves per CU, 8 MFMAs per wave and step) without global memory, in its "
+                    "256 x 32 waves (8 LDS operand reads, 1 dequantised word) and in 128 x 64 waves "
+                    "(4 reads, 2 words), with neither, either or both"}
 
 
 def read_traffic(alg_bytes_per_launch):
@@ -206,7 +210,7 @@ def dominant_roofline(torch, shapes, rounds=4):
             "launches_per_replay": rounds * len(dom), "avg_launch_us": avg_dur * 1e6,
             "algorithmic_bytes_per_launch": nbytes, "flops_per_launch": flops,
             "frac_of_measured_mfma_peak": achieved / (calib["mfma_bf16_tflops"] * 1e12),
-            "frac_of_step_loop": achieved / (calib["step_loop_tflops"]["mfma_lds_dequant"] * 1e12),
+            "frac_of_step_loop": achieved / (calib["step_loop_tflops"]["w256x32"]["mfma_lds_dequant"] * 1e12),
             "traffic_note": traffic_note,
             "block_tiles": {sh.name: [sh.plan.block_m, sh.plan.block_n] for sh in dom}}
     return roof, calib

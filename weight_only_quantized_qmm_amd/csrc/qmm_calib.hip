@@ -11,7 +11,8 @@
 //   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate);
 //   * the large-M kernel's reduction step without global memory (the rate its inner
 //     loop allows on this GPU, with and without the LDS operand reads and the
-//     dequantisation).
+//     dequantisation), in its wave layout and in the other one that fits two waves
+//     per SIMD.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -77,15 +78,16 @@ __global__ void __launch_bounds__(256) calib_mfma_kernel(int iters, float *out)
     if (s == 1.2345f) out[0] = s;
 }
 
-// The large-M kernel's inner step (256 x 256 tiles: eight waves of 256 x 32, one workgroup
-// per CU, so two waves per SIMD), with no global memory: per step each wave runs eight
-// v_mfma_f32_32x32x16_bf16 (a 256 x 32 tile over 16 reduction values) on the operands of
-// the previous step and prepares the next step's operands as the kernel does: with
-// LDSR, eight 16-byte A-operand reads from LDS (consecutive lanes on consecutive 16-byte
-// chunks: conflict-free); with DEQ, one packed word dequantised by the library's
-// dequant8. Without them the operands are carried over unchanged.
+// The large-M kernel's inner step (256 x 256 tiles of eight waves, one workgroup per CU,
+// so two waves per SIMD), with no global memory. A wave's tile is (32*MI) x (32*NJ): per
+// step (16 reduction values) it runs MI*NJ v_mfma_f32_32x32x16_bf16 on the operands of the
+// previous step and prepares the next step's operands as the kernel does: with LDSR, MI
+// 16-byte A-operand reads from LDS (consecutive lanes on consecutive 16-byte chunks:
+// conflict-free); with DEQ, NJ packed words dequantised by the library's dequant8.
+// Without them the operands are carried over unchanged. MI = 8, NJ = 1 is the kernel's
+// layout (256 x 32 waves); MI = 4, NJ = 2 the other one that fits two waves per SIMD.
 constexpr int kStepLds16 = 2048;  // 32 KB of bf16 operands
-template <bool LDSR, bool DEQ>
+template <int MI, int NJ, bool LDSR, bool DEQ>
 __global__ void __launch_bounds__(512) calib_step_kernel(int steps, float *out)
 {
     using namespace qmm_dev;
@@ -95,33 +97,52 @@ __global__ void __launch_bounds__(512) calib_step_kernel(int steps, float *out)
                             0x3F203EC0u);
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    f32x16 acc[8];
-    bf16x8 af[8];
-    for (int i = 0; i < 8; ++i) {
-        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    f32x16 acc[MI][NJ];
+    bf16x8 af[MI], bw[NJ];
+    for (int i = 0; i < MI; ++i) {
+        for (int j = 0; j < NJ; ++j)
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
         af[i] = as_bf16x8(lds[(lane + 64 * i) & (kStepLds16 - 1)]);
     }
     uint32_t w = 0x9E3779B9u ^ (uint32_t)threadIdx.x;
     const float sc512 = (0.01f + 1e-4f * (float)lane) * 512.f, bi = -0.08f;
-    bf16x8 bw = as_bf16x8(dequant8(w, sc512, bi));
+    for (int j = 0; j < NJ; ++j) bw[j] = as_bf16x8(dequant8(w + (uint32_t)j, sc512, bi));
     uint32_t off = (uint32_t)lane;
     for (int s = 0; s < steps; ++s) {
-        bf16x8 af2[8], bw2 = bw;
-        off = (off + 512u) & (kStepLds16 - 1);
+        bf16x8 af2[MI], bw2[NJ];
+        off = (off + 64u * MI) & (kStepLds16 - 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af2[i] = LDSR ? as_bf16x8(lds[(off + 64u * i) & (kStepLds16 - 1)]) : af[i];
+        for (int i = 0; i < MI; ++i) af2[i] = LDSR ? as_bf16x8(lds[(off + 64u * i) & (kStepLds16 - 1)]) : af[i];
         w = w * 1664525u + 1013904223u;
-        if (DEQ) bw2 = as_bf16x8(dequant8(w, sc512, bi));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = mfma32x32x16(bw, af[i], acc[i]);
+        for (int j = 0; j < NJ; ++j) bw2[j] = DEQ ? as_bf16x8(dequant8(w + (uint32_t)j, sc512, bi)) : bw[j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = af2[i];
-        bw = bw2;
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bw[j], af[i], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[i] = af2[i];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bw[j] = bw2[j];
     }
     float t = 0.f;
-    for (int i = 0; i < 8; ++i)
-        for (int e = 0; e < 16; ++e) t += acc[i][e];
+    for (int i = 0; i < MI; ++i)
+        for (int j = 0; j < NJ; ++j)
+            for (int e = 0; e < 16; ++e) t += acc[i][j][e];
     if (t == 1.2345f) out[0] = t;
+}
+
+template <int MI, int NJ>
+void launch_step(dim3 grid, hipStream_t st, int steps, float *o, int lds_reads, int dequant)
+{
+    if (lds_reads && dequant)
+        hipLaunchKernelGGL((calib_step_kernel<MI, NJ, true, true>), grid, dim3(512), 0, st, steps, o);
+    else if (lds_reads)
+        hipLaunchKernelGGL((calib_step_kernel<MI, NJ, true, false>), grid, dim3(512), 0, st, steps, o);
+    else if (dequant)
+        hipLaunchKernelGGL((calib_step_kernel<MI, NJ, false, true>), grid, dim3(512), 0, st, steps, o);
+    else
+        hipLaunchKernelGGL((calib_step_kernel<MI, NJ, false, false>), grid, dim3(512), 0, st, steps, o);
 }
 
 }  // namespace
@@ -158,21 +179,21 @@ int qmm_calib_mfma(int grid, int iters, void *out, void *stream)
     return (int)hipGetLastError();
 }
 
-// The large-M kernel's step loop: grid workgroups of eight waves, `steps` steps each;
-// lds_reads / dequant switch the LDS operand reads and the dequantisation on.
+// The large-M kernel's step loop: grid workgroups of eight waves, `steps` steps each, in
+// the wave layout `layout` (0: 256 x 32 waves, eight MFMAs, eight A reads and one word per
+// step; 1: 128 x 64 waves, eight MFMAs, four A reads and two words); lds_reads / dequant
+// switch the LDS operand reads and the dequantisation on.
 // flops = grid * 8 waves * steps * 8 * 32768; out: one float of device memory.
-int qmm_calib_step(int grid, int steps, int lds_reads, int dequant, void *out, void *stream)
+int qmm_calib_step(int grid, int steps, int layout, int lds_reads, int dequant, void *out, void *stream)
 {
     float *o = static_cast<float *>(out);
     const hipStream_t st = (hipStream_t)stream;
-    if (lds_reads && dequant)
-        hipLaunchKernelGGL((calib_step_kernel<true, true>), dim3(grid), dim3(512), 0, st, steps, o);
-    else if (lds_reads)
-        hipLaunchKernelGGL((calib_step_kernel<true, false>), dim3(grid), dim3(512), 0, st, steps, o);
-    else if (dequant)
-        hipLaunchKernelGGL((calib_step_kernel<false, true>), dim3(grid), dim3(512), 0, st, steps, o);
+    if (layout == 0)
+        launch_step<8, 1>(dim3(grid), st, steps, o, lds_reads, dequant);
+    else if (layout == 1)
+        launch_step<4, 2>(dim3(grid), st, steps, o, lds_reads, dequant);
     else
-        hipLaunchKernelGGL((calib_step_kernel<false, false>), dim3(grid), dim3(512), 0, st, steps, o);
+        return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
 

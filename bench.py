@@ -84,6 +84,7 @@ DOMINANT_SOURCES = [os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", 
                     for f in ("qmm_w4a16_wide.hip", "qmm_api.cpp")]
 DOMINANT_WORKLOAD = "first pass (qmm_w4a16_g128_pass1) of the plan, M=2048 q,k,v,o,gate,up,down"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_wide_M2048_traffic.txt")
+STEP_LOOP_STEPS = 2048     # steps per workgroup of the step-loop calibration
 COPY_BYTES = 256 << 20     # size of the plain copy that calibrates the profiler's byte counters
 
 
@@ -147,7 +148,7 @@ def calibrate(torch):
     del buf, buf2
     grid, iters = 256 * 8, 4096
     t_mfma = timed(lambda: L.qmm_calib_mfma(grid, iters, out.data_ptr(), torch.cuda.current_stream().cuda_stream), 4)
-    step_grid, steps = 256, 2048
+    step_grid, steps = 256, STEP_LOOP_STEPS
     step = {}
     for layout, lname in ((0, "w256x32"), (1, "w128x64")):
         step[lname] = {}
@@ -570,6 +571,50 @@ def summarize_mix(dir1, dir2, commands, n_xcc=8, n_cu=256):
     print("\n".join(lines))
 
 
+LDS_COUNTERS = ["GRBM_GUI_ACTIVE", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL",
+                "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_INST_LDS", "SQ_BUSY_CYCLES"]
+
+
+def summarize_lds(d, commands, n_xcc=8, n_cu=256):
+    """Text summary of one rocprofv3 --pmc pass (LDS_COUNTERS) over bench.py --dominant-only:
+    LDS activity of the step-loop calibration kernels (whose LDS read bytes are known) beside
+    that of the large-M kernel's variants, per kernel, summed over its dispatches."""
+    import re
+    rows = _counter_rows(d, LDS_COUNTERS)
+    per = {}
+    for c in LDS_COUNTERS:
+        for disp, k, v in rows[c]:
+            if "calib_step_kernel" not in k and DOMINANT_KERNEL not in k:
+                continue
+            name = re.sub(r"\(.*", "", k.split("::")[-1])
+            per.setdefault(name, {}).setdefault(c, {})
+            per[name][c][disp] = per[name][c].get(disp, 0.0) + v
+    lines = ["# LDS activity of the large-M kernel's step loop without global memory (calib_step_kernel<MI, NJ, "
+             "LDS reads, dequantisation>: 8 waves of (32*MI) x (32*NJ) per CU, %d steps) and of %s, from rocprofv3 "
+             "counters" % (STEP_LOOP_STEPS, DOMINANT_KERNEL), "commands:"] + ["  " + c for c in commands] + [
+        "active cycles = GRBM_GUI_ACTIVE / %d; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x %d SIMDs); LDS active ="
+        " SQ_LDS_IDX_ACTIVE / (cycles x %d CUs);" % (n_xcc, 4 * n_cu, n_cu),
+        "LDS insts, FIFO full (data, command) and LDS waits (SQ_WAIT_INST_LDS) per CU and cycle; B/LDS-active cycle ="
+        " the step loop's LDS read bytes (8 waves x MI x 1 KB per step) / SQ_LDS_IDX_ACTIVE",
+        "%-46s %5s %9s %9s %9s %9s %9s %9s %11s" % ("kernel", "calls", "MFMA busy", "LDS act", "LDS inst", "data full",
+                                                    "cmd full", "LDS wait", "B/LDS-cyc")]
+    for name in sorted(per):
+        c = {k: sum(v.values()) for k, v in per[name].items()}
+        calls = len(per[name]["GRBM_GUI_ACTIVE"])
+        cyc = c["GRBM_GUI_ACTIVE"] / n_xcc
+        bpc = ""
+        m = re.match(r"calib_step_kernel<(\d+), (\d+), (true|false), (true|false)>", name)
+        if m and m.group(3) == "true" and c["SQ_LDS_IDX_ACTIVE"] > 0:
+            nbytes = calls * n_cu * 8 * STEP_LOOP_STEPS * int(m.group(1)) * 1024
+            bpc = "%.0f" % (nbytes / c["SQ_LDS_IDX_ACTIVE"])
+        lines.append("%-46s %5d %9.3f %9.3f %9.4f %9.4f %9.4f %9.4f %11s" % (
+            name, calls, c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 4 * n_cu), c["SQ_LDS_IDX_ACTIVE"] / (cyc * n_cu),
+            c["SQ_INSTS_LDS"] / (cyc * n_cu), c["SQ_LDS_DATA_FIFO_FULL"] / (cyc * n_cu),
+            c["SQ_LDS_CMD_FIFO_FULL"] / (cyc * n_cu), c["SQ_WAIT_INST_LDS"] / (cyc * n_cu), bpc))
+    lines.append("kernel source digest: %s" % source_digest())
+    print("\n".join(lines))
+
+
 def summarize_pmc(fetch_dir, write_dir, commands):
     """Text summary of two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over pmc_run()."""
     import csv
@@ -631,6 +676,8 @@ def parse():
                          "small: the small-M kernel's shapes)")
     ap.add_argument("--summarize-small-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="print the small-M kernel's traffic summary of two --pmc passes and a kernel trace")
+    ap.add_argument("--summarize-lds", metavar="DIR",
+                    help="print the LDS-activity summary of one --pmc pass (LDS_COUNTERS) over --dominant-only")
     ap.add_argument("--summarize-mix", nargs=2, metavar=("DIR1", "DIR2"),
                     help="print the dominant kernel's instruction-mix summary of two --pmc passes (MIX_COUNTERS)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "TITLE"),
@@ -802,6 +849,9 @@ def main():
         return
     if args.summarize_mix:
         summarize_mix(*args.summarize_mix, args.pmc_commands)
+        return
+    if args.summarize_lds:
+        summarize_lds(args.summarize_lds, args.pmc_commands)
         return
     if args.pmc_run:
         pmc_run(args.pmc_run)

@@ -99,12 +99,17 @@ def dominant_shapes(shapes):
 
 
 def source_digest(paths=None):
-    """Digest of the dominant kernel's sources and of the counter workload."""
+    """Digest of the dominant kernel's sources (code only: comments and whitespace are
+    dropped, so an edited comment leaves it unchanged) and of the counter workload."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for path in (paths or DOMINANT_SOURCES):
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     h.update(DOMINANT_WORKLOAD.encode())
     return h.hexdigest()[:16]
 

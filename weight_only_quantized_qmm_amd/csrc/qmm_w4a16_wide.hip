@@ -22,9 +22,9 @@
 // Data movement: every global read of the kernel is a direct global -> LDS copy
 // (global_load_lds_*), issued one to one and a half stages ahead of its use, into rings of three slots:
 //   A:  BM rows x 64 bf16 (16 or 32 KB per stage), 1 KB per copy;
-//   W:  256 rows x 32 bytes of packed nibbles (8 KB per stage; 64 bytes and 16 KB for
-//       8-bit codes), 1 KB per copy;
-//   scale/bias: the 128-value block's 256 + 256 bf16 values per group it holds (one, two
+//   W:  BN (256 or 128) rows x 32 bytes of packed nibbles (8 or 4 KB per stage; rows of
+//       64 bytes for 8-bit codes), 1 KB per copy;
+//   scale/bias: the 128-value block's BN + BN bf16 values per group it holds (one, two
 //       or four), one 2-byte copy per lane (zero-extended into a dword), once per block,
 //       in a ring of two.
 // The compiler neither sees nor waits for these copies; the kernel retires them

@@ -591,7 +591,7 @@ def summarize_lds(d, commands, n_xcc=8, n_cu=256):
         for disp, k, v in rows[c]:
             if "calib_step_kernel" not in k and DOMINANT_KERNEL not in k:
                 continue
-            name = re.sub(r"\(.*", "", k.split("::")[-1])
+            name = re.sub(r"\(.*", "", k.replace("(anonymous namespace)::", "").replace("void ", "", 1))
             per.setdefault(name, {}).setdefault(c, {})
             per[name][c][disp] = per[name][c].get(disp, 0.0) + v
     lines = ["# LDS activity of the large-M kernel's step loop without global memory (calib_step_kernel<MI, NJ, "
@@ -601,7 +601,7 @@ def summarize_lds(d, commands, n_xcc=8, n_cu=256):
         " SQ_LDS_IDX_ACTIVE / (cycles x %d CUs);" % (n_xcc, 4 * n_cu, n_cu),
         "LDS insts, FIFO full (data, command) and LDS waits (SQ_WAIT_INST_LDS) per CU and cycle; B/LDS-active cycle ="
         " the step loop's LDS read bytes (8 waves x MI x 1 KB per step) / SQ_LDS_IDX_ACTIVE",
-        "%-46s %5s %9s %9s %9s %9s %9s %9s %11s" % ("kernel", "calls", "MFMA busy", "LDS act", "LDS inst", "data full",
+        "%-52s %5s %9s %9s %9s %9s %9s %9s %11s" % ("kernel", "calls", "MFMA busy", "LDS act", "LDS inst", "data full",
                                                     "cmd full", "LDS wait", "B/LDS-cyc")]
     for name in sorted(per):
         c = {k: sum(v.values()) for k, v in per[name].items()}
@@ -612,7 +612,7 @@ def summarize_lds(d, commands, n_xcc=8, n_cu=256):
         if m and m.group(3) == "true" and c["SQ_LDS_IDX_ACTIVE"] > 0:
             nbytes = calls * n_cu * 8 * STEP_LOOP_STEPS * int(m.group(1)) * 1024
             bpc = "%.0f" % (nbytes / c["SQ_LDS_IDX_ACTIVE"])
-        lines.append("%-46s %5d %9.3f %9.3f %9.4f %9.4f %9.4f %9.4f %11s" % (
+        lines.append("%-52s %5d %9.3f %9.3f %9.4f %9.4f %9.4f %9.4f %11s" % (
             name, calls, c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * 4 * n_cu), c["SQ_LDS_IDX_ACTIVE"] / (cyc * n_cu),
             c["SQ_INSTS_LDS"] / (cyc * n_cu), c["SQ_LDS_DATA_FIFO_FULL"] / (cyc * n_cu),
             c["SQ_LDS_CMD_FIFO_FULL"] / (cyc * n_cu), c["SQ_WAIT_INST_LDS"] / (cyc * n_cu), bpc))

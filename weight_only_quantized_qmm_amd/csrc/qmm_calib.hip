@@ -7,7 +7,8 @@
 //   * an empty kernel (the dispatch floor of one launch);
 //   * a streaming read and a streaming copy of a large buffer (achievable HBM
 //     bandwidth; the copy of a known size also calibrates the profiler's
-//     FETCH_SIZE / WRITE_SIZE counters);
+//     FETCH_SIZE / WRITE_SIZE counters), and the read of a small call's bytes on a
+//     grid sized to them (the practical floor of an HBM-bound call);
 //   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate);
 //   * the large-M kernel's reduction step without global memory (the rate its inner
 //     loop allows on this GPU, with and without the LDS operand reads and the
@@ -160,6 +161,15 @@ int qmm_calib_empty(int grid, void *stream)
 int qmm_calib_read(const void *src, size_t bytes, void *out, void *stream)
 {
     hipLaunchKernelGGL(calib_read_kernel, dim3(256 * 32), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
+    return (int)hipGetLastError();
+}
+
+// The same read on `grid` workgroups (the practical floor of a small HBM-bound call:
+// a plain read of its bytes on a grid sized to them).
+int qmm_calib_read_grid(const void *src, size_t bytes, int grid, void *out, void *stream)
+{
+    hipLaunchKernelGGL(calib_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
     return (int)hipGetLastError();
 }

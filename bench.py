@@ -124,11 +124,12 @@ def calib_lib():
     L.qmm_calib_empty.argtypes = [I, P]
     L.qmm_calib_read.argtypes = [P, S, P, P]
     L.qmm_calib_read_grid.argtypes = [P, S, I, P, P]
+    L.qmm_calib_chain.argtypes = [P, S, I, P, P]
     L.qmm_calib_copy.argtypes = [P, P, S, P]
     L.qmm_calib_mfma.argtypes = [I, I, P, P]
     L.qmm_calib_step.argtypes = [I, I, I, I, I, P, P]
-    for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_read_grid, L.qmm_calib_copy, L.qmm_calib_mfma,
-              L.qmm_calib_step):
+    for f in (L.qmm_calib_empty, L.qmm_calib_read, L.qmm_calib_read_grid, L.qmm_calib_chain, L.qmm_calib_copy,
+              L.qmm_calib_mfma, L.qmm_calib_step):
         f.restype = I
     return L
 
@@ -178,12 +179,14 @@ def calibrate(torch):
 
 
 def stream_floors(torch, sizes):
-    """Practical floor of the HBM-bound calls: seconds per call of a plain streaming read of
-    `nbytes` (libqmm_calib's read kernel on max(1024, nbytes/4096) workgroups, 16 bytes per
-    load), each call on its own slice of a 1 GiB pool, as the per-shape timings rotate their
-    inputs so that no call finds its bytes in a cache; {nbytes: seconds}."""
+    """Practical floors of the HBM-bound calls, seconds per call for `nbytes`: a plain
+    streaming read (libqmm_calib's read kernel on max(1024, nbytes/4096) workgroups, 16 bytes
+    per load) and the same read followed by a dependent one-dword store per thread (the
+    load -> store chain every matmul call has), each call on its own slice of a 1 GiB pool,
+    as the per-shape timings rotate their inputs so that no call finds its bytes in a
+    cache; {nbytes: (read seconds, chain seconds)}."""
     L = calib_lib()
-    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = torch.zeros(8192 * 256, dtype=torch.int32, device="cuda")
     pool = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device="cuda")
     base = pool.data_ptr()
     res = {}
@@ -191,11 +194,13 @@ def stream_floors(torch, sizes):
         n = -(-nbytes // 256) * 256  # slices on 256-byte boundaries
         R = max(2, min(1024, ROTATE_BYTES // n))
         grid = min(8192, max(1024, -(-n // 4096)))
-        g = graph_of(torch, lambda: [L.qmm_calib_read_grid(base + r * n, n, grid, out.data_ptr(),
-                                                           torch.cuda.current_stream().cuda_stream)
-                                     for r in range(R)])
-        res[nbytes] = time_graph(torch, g) / R
-        del g
+        t = []
+        for fn in (L.qmm_calib_read_grid, L.qmm_calib_chain):
+            g = graph_of(torch, lambda fn=fn: [fn(base + r * n, n, grid, out.data_ptr(),
+                                                  torch.cuda.current_stream().cuda_stream) for r in range(R)])
+            t.append(time_graph(torch, g) / R)
+            del g
+        res[nbytes] = tuple(t)
     del pool
     torch.cuda.empty_cache()
     return res
@@ -961,9 +966,11 @@ def main():
         floors = stream_floors(torch, [algorithmic_bytes(t["M"], t["N"], t["K"]) for t in table if t["M"] <= 128])
         for t in table:
             if t["M"] <= 128:
-                f = floors[algorithmic_bytes(t["M"], t["N"], t["K"])]
+                f, c = floors[algorithmic_bytes(t["M"], t["N"], t["K"])]
                 t["stream_floor_us"] = round(f * 1e6, 3)
                 t["frac_of_stream_floor"] = round(f * 1e6 / t["us"], 4)
+                t["chain_floor_us"] = round(c * 1e6, 3)
+                t["frac_of_chain_floor"] = round(c * 1e6 / t["us"], 4)
 
     dense = decode = formats = attention = streamk = None
     if not args.no_per_shape:
@@ -1017,6 +1024,7 @@ def main():
         line["summary"] = {
             "small_M_mean_frac": round(sum(t["frac"] for t in small) / len(small), 4),
             "small_M_mean_frac_of_stream_floor": round(sum(t["frac_of_stream_floor"] for t in small) / len(small), 4),
+            "small_M_mean_frac_of_chain_floor": round(sum(t["frac_of_chain_floor"] for t in small) / len(small), 4),
             "M2048_mean_frac": round(sum(t["frac"] for t in table if t["M"] == 2048) / 7, 4),
             "split_never_slower": all(t["us"] <= t["us_unsplit"] for t in table),
             "sum_per_shape_us": round(sum(t["us"] for t in table), 2),

@@ -47,8 +47,8 @@ def test_calibration_library_exports_what_the_bench_binds():
     # these entry points by name (loading it initialises no GPU)
     import bench
     L = bench.calib_lib()
-    for f in ("qmm_calib_empty", "qmm_calib_read", "qmm_calib_read_grid", "qmm_calib_copy", "qmm_calib_mfma",
-              "qmm_calib_step"):
+    for f in ("qmm_calib_empty", "qmm_calib_read", "qmm_calib_read_grid", "qmm_calib_chain", "qmm_calib_copy",
+              "qmm_calib_mfma", "qmm_calib_step"):
         assert hasattr(L, f), f
 
 

@@ -8,7 +8,8 @@
 //   * a streaming read and a streaming copy of a large buffer (achievable HBM
 //     bandwidth; the copy of a known size also calibrates the profiler's
 //     FETCH_SIZE / WRITE_SIZE counters), and the read of a small call's bytes on a
-//     grid sized to them (the practical floor of an HBM-bound call);
+//     grid sized to them, alone and followed by a dependent store per thread (the
+//     practical floors of an HBM-bound call);
 //   * a dense bf16 MFMA loop with no memory traffic (achievable matrix-core rate);
 //   * the large-M kernel's reduction step without global memory (the rate its inner
 //     loop allows on this GPU, with and without the LDS operand reads and the
@@ -48,6 +49,25 @@ __global__ void __launch_bounds__(256) calib_read_kernel(const uint4 *__restrict
         acc.w ^= a.w;
     }
     if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9E3779B9u) out[0] = 1u;
+}
+
+// The same read with a dependent store: every thread writes the xor of what it read to
+// out[thread], so the kernel ends only after each thread's loads have returned and its
+// store has gone out (the shape of any load -> compute -> store call).
+__global__ void __launch_bounds__(256) calib_chain_kernel(const uint4 *__restrict__ src, size_t n16,
+                                                          uint32_t *__restrict__ out)
+{
+    uint4 acc = {0u, 0u, 0u, 0u};
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (size_t i = t; i < n16; i += stride) {
+        const uint4 a = src[i];
+        acc.x ^= a.x;
+        acc.y ^= a.y;
+        acc.z ^= a.z;
+        acc.w ^= a.w;
+    }
+    out[t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
 __global__ void __launch_bounds__(256) calib_copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
@@ -170,6 +190,15 @@ int qmm_calib_read(const void *src, size_t bytes, void *out, void *stream)
 int qmm_calib_read_grid(const void *src, size_t bytes, int grid, void *out, void *stream)
 {
     hipLaunchKernelGGL(calib_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
+    return (int)hipGetLastError();
+}
+
+// The load -> store chain floor: the read on `grid` workgroups, each thread then storing
+// one dword; out: grid * 256 dwords of device memory.
+int qmm_calib_chain(const void *src, size_t bytes, int grid, void *out, void *stream)
+{
+    hipLaunchKernelGGL(calib_chain_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        static_cast<const uint4 *>(src), bytes / 16, static_cast<uint32_t *>(out));
     return (int)hipGetLastError();
 }

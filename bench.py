@@ -17,20 +17,24 @@ Timing:
   * per shape: a graph of R back-to-back calls over R distinct buffer sets
     totalling >= 1 GiB, for the policy's split and for the unsplit control;
   * the dominant kernel (largest share of the step: the large-M kernel) is
-    timed on its own for the roofline figure: the seven M = 2048 shapes launched
-    unsplit, back to back in one graph, HIP events on the launch stream around
-    each replay (``--dominant-only`` runs just this part, for the profiler);
-  * machine floors measured in the same run: empty-kernel dispatch, HBM
-    stream read and copy, bf16 MFMA rate (libqmm_calib.so).
+    timed on its own for the roofline figure: its first-pass launches of the
+    seven M = 2048 shapes with the plan's decomposition, back to back in one
+    graph, HIP events on the launch stream around each replay
+    (``--dominant-only`` runs just this part, for the profiler);
+  * machine floors measured in the same run (libqmm_calib.so): empty-kernel
+    dispatch, HBM stream read and copy, bf16 MFMA rate, and the large-M kernel's
+    step loop without global memory; for every M <= 128 shape, a plain read of
+    its bytes and that read followed by a dependent store (its practical floors).
 
 Counters: ``--pmc-run [large|small]`` is the workload of rocprofv3 --pmc passes.
 For the dominant kernel, two passes (FETCH_SIZE, WRITE_SIZE) turn into the text
 summary under profiles/ that the ``traffic`` field reads back (``--summarize-pmc``;
 it stays null when the kernel source changed after the counters were taken), and
 two more (MIX_COUNTERS) into its instruction mix and unit utilisation
-(``--summarize-mix``). For the small-M kernel, FETCH_SIZE and WRITE_SIZE passes
-and a kernel trace give its per-launch HBM traffic and rate
-(``--summarize-small-pmc``).
+(``--summarize-mix``); one pass of LDS counters over ``--dominant-only`` sets its
+LDS activity beside that of the step-loop calibration (``--summarize-lds``). For
+the small-M kernel, FETCH_SIZE and WRITE_SIZE passes and a kernel trace give its
+per-launch HBM traffic and rate (``--summarize-small-pmc``).
 
 CPU baseline: the fp64 CPU oracle on the host cores, on a bounded sample of
 the same sweep (listed in the output), extrapolated to one whole sweep, plus the

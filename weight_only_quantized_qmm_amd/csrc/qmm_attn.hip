@@ -85,8 +85,18 @@ attn_split_kernel(AttnArgs a)
     const int G = a.Hq / a.Hkv;
     const int R = G * a.Mq;
     const int len = min(max(a.lengths[b], a.Mq), a.Lmax);
-    const int k_lo = (int)(((long long)p * len) / S);
-    const int k_hi = (int)(((long long)(p + 1) * len) / S);
+    // floor(p*len/S): in 32-bit unsigned arithmetic when (p+1)*len fits (len < 2^25, p < 64),
+    // which keeps the software 64-bit division off the path from the length to the first
+    // key address
+    int k_lo, k_hi;
+    if ((unsigned)len < (1u << 25)) {
+        const unsigned lu = (unsigned)len, Su = (unsigned)S, pu = (unsigned)p;
+        k_lo = (int)((pu * lu) / Su);
+        k_hi = (int)(((pu + 1) * lu) / Su);
+    } else {
+        k_lo = (int)(((long long)p * len) / S);
+        k_hi = (int)(((long long)(p + 1) * len) / S);
+    }
     const size_t kv_base = ((size_t)b * a.Hkv + kvh) * (size_t)a.Lmax * D;
 
     // this lane's query row (scores) and its key limit

@@ -96,10 +96,15 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const int m_blk = blockIdx.y * (16 * MT);
     const int GG = (K >> 7) << sub_shift;  // scale/bias entries per row (128 / group_size per block)
     const int G = K >> 7;  // 128-value blocks of the reduction
-    const int g0 = (int)(((long long)blockIdx.z * G) / gridDim.z);
-    const int gpp = (int)(((long long)(blockIdx.z + 1) * G) / gridDim.z) - g0;  // this partition's blocks
-    // this wave's groups: g0 + wave + waves*i, i < n_w
-    const int n_w = (gpp - wave + waves - 1) / waves;
+    // Partition bounds floor(p*G/s) in 32-bit unsigned arithmetic ((p+1)*G < 2^31: the host
+    // keeps K below 2^22), and none at all when unsplit: every wave evaluates them on the
+    // CU's shared scalar unit before its first load, and a 64-bit division is a software
+    // routine of over a hundred scalar instructions.
+    const unsigned Gu = (unsigned)G, S = gridDim.z, Z = blockIdx.z;
+    const int g0 = S == 1 ? 0 : (int)((Z * Gu) / S);
+    const int gpp = S == 1 ? G : (int)(((Z + 1) * Gu) / S) - g0;  // this partition's blocks
+    // this wave's groups: g0 + wave + waves*i, i < n_w (the dividend is at least gpp > 0)
+    const int n_w = (int)((unsigned)(gpp - wave + waves - 1) / (unsigned)waves);
 
     const uint4 *wptr[NS];
 #pragma unroll

@@ -784,6 +784,20 @@ def test_edge_shapes(M, N, K, s):
         check_tolerance(host_f64(C), ref, what="edge %dx%dx%d s=%d" % (M, N, K, ss))
 
 
+def test_largest_k_partition_bounds():
+    # K just under 2^22 (the host's limit: G = 32767 groups) on the small-M kernel, unsplit,
+    # split 7 ways, 20000 ways (partitions of one or two groups: p*G up to 6.6e8) and one
+    # group per partition: the partition bounds floor(p*G/s) at their largest values
+    M, N, K = 3, 40, ((1 << 22) // 128 - 1) * 128
+    d = syn.w4a16_inputs(M, N, K, seed=7050)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for s in (1, 7, 20000, K // 128):
+        say("largest K M=%d N=%d K=%d s=%d" % (M, N, K, s))
+        C = run_w4a16(dv, M, N, K, s, guard=24)
+        check_tolerance(host_f64(C), ref, what="largest K s=%d" % s)
+
+
 def test_error_leaves_output_untouched():
     M, N, K = 16, 64, 256
     d = syn.w4a16_inputs(M, N, K, seed=7100)

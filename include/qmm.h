@@ -83,7 +83,9 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * while 32-column tiles fit in 256 workgroups and K < 8192; else by 48 when 48-column tiles
  * fit in 256 workgroups, else by 64. With tile_m = tile_n = 0 and M <= 32, its partitions hold at least 2048 reduction
  * values (min_k_per_split is raised to 2048 in the rule): a shorter partition saves less
- * than the second pass costs. The large-M kernel runs the rest, with the tile of shortest
+ * than the second pass costs. An unsplit grid of 16-column tiles with fewer tiles than 256
+ * runs tiles of ceil(N / (256 / row blocks)) columns instead (block_n below), so that it
+ * covers every CU once; the split rule still counts the 16-column tiles (tile_n). The large-M kernel runs the rest, with the tile of shortest
  * estimated critical path among 128 x 256 (two workgroups per CU up to M = 128), 256 x 256
  * (above M = 128) and 128 x 128 (only when its tiles are fewer than target_blocks, a pure
  * split at one workgroup per CU); ties go to the larger tiles. The estimate: rounds of
@@ -117,7 +119,8 @@ typedef struct qmm_plan {
     int base_tiles;         /* ceil(M/tile_m) * ceil(N/tile_n) under the policy's tile */
     int tile_m, tile_n;     /* tile the occupancy count used */
     int grid_x, grid_y, grid_z; /* grid of the matmul kernel this library launches for (M,N,K,s) */
-    int block_m, block_n;   /* output tile of one workgroup of that kernel */
+    int block_m, block_n;   /* output tile of one workgroup of that kernel (block_n < tile_n for
+                               a narrowed unsplit small-M grid) */
     size_t workspace_bytes; /* 2*s*M*N for s > 1, else 0 */
     int full_tiles;         /* kernel tiles computed unsplit ahead of the split ones: all of them
                                when s = 1, 0 for a uniform split, in between for a split tail */

@@ -26,10 +26,13 @@ std::set<std::tuple<int, int, int, int, int>> g_skinny_cfgs;
 }  // namespace
 
 namespace qmm_impl {
-hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *, const void *,
-                               const void *, const void *, void *, bool, int M, int, int, int s, bool, hipStream_t)
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int waves, const void *,
+                               const void *, const void *, const void *, void *, bool, int M, int N, int, int s, bool,
+                               hipStream_t)
 {
     if (waves < 1 || waves > 16) abort();
+    if (tw < 1 || tw > 16 * ns || (tw < 16 * ns && (ns != 1 || s != 1))) abort();  // narrowed: unsplit 16-column only
+    if ((long long)(N + tw - 1) / tw > 65535) abort();  // grid x
     if (M < 1 || skinny_lds_bytes(mt, ns, waves, gpw, fmt.sub()) > (size_t)kLdsPerCU) abort();
     g_skinny_cfgs.insert(std::make_tuple(fmt.bits, mt, ns, gpw, waves));
     ++g_launches;

@@ -101,8 +101,9 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     pol = q.policy_preset("QMM_POLICY_MI355X")
     plan = q.qmm_splitk_plan(M, N, K)
     G = K // 128
-    assert plan.tile_m == plan.block_m and plan.tile_n == plan.block_n
-    tiles = -(-M // plan.block_m) * -(-N // plan.block_n)
+    # the occupancy count uses the kernel's tile; only an unsplit small-M grid narrows it
+    assert plan.tile_m == plan.block_m and (plan.tile_n == plan.block_n or plan.s == 1)
+    tiles = -(-M // plan.tile_m) * -(-N // plan.tile_n)
     assert plan.base_tiles == tiles
     assert 1 <= plan.s <= min(pol.cap, G)
     assert plan.s == 1 or K // plan.s >= pol.min_k_per_split
@@ -122,18 +123,26 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
         rows = -(-M // plan.block_m)
         if M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096)):
-            assert plan.block_n == 16
+            assert plan.tile_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:
-            assert plan.block_n == 32
+            assert plan.tile_n == 32
         else:
-            assert plan.block_n == (48 if rows * -(-N // 48) <= 256 else 64)
+            assert plan.tile_n == (48 if rows * -(-N // 48) <= 256 else 64)
         min_k = max(pol.min_k_per_split, 2048) if M <= 32 else pol.min_k_per_split
-        assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.block_n,
+        assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.tile_n,
                                              target=pol.target_blocks, cap=pol.cap,
                                              min_k_per_split=min_k)
+        # an unsplit grid of 16-column tiles with fewer tiles than CUs runs narrower tiles,
+        # ceil(N / (256 // rows)) columns, so that it covers every CU once
+        if plan.s == 1 and plan.tile_n == 16 and tiles < 256:
+            assert plan.block_n == -(-N // (256 // rows))
+        else:
+            assert plan.block_n == plan.tile_n
+        run_tiles = rows * -(-N // plan.block_n)
+        assert run_tiles <= max(tiles, 256)
         assert plan.grid_z == plan.s
-        assert plan.grid_x * plan.grid_y == tiles
-        assert plan.full_tiles == (tiles if plan.s == 1 else 0)
+        assert (plan.grid_x, plan.grid_y) == (-(-N // plan.block_n), rows)
+        assert plan.full_tiles == (run_tiles if plan.s == 1 else 0)
 
 
 FORMATS = [(4, 32), (4, 64), (4, 128), (8, 32), (8, 64), (8, 128)]
@@ -539,8 +548,10 @@ def test_dense_rejects_before_launch(kw, code):
 
 def test_decode_tile_rule_edges():
     """The plan's tile at the decode rule's edges (the GPU edge-shape tests run these shapes against the oracle)."""
-    tiles = {(M, N, K): (p.block_m, p.block_n, p.s) for M, N, K in [(8, 4096, 8192), (9, 4096, 8192),
-                                                                  (5, 4097, 8192), (7, 2500, 9728)]
+    tiles = {(M, N, K): (p.block_m, p.tile_n, p.s, p.block_n) for M, N, K in [(8, 4096, 8192), (9, 4096, 8192),
+                                                                            (5, 4097, 8192), (7, 2500, 9728)]
              for p in [q.qmm_splitk_plan(M, N, K)]}
     assert tiles[(8, 4096, 8192)][:2] == (16, 16) and tiles[(7, 2500, 9728)][:2] == (16, 16)
     assert tiles[(9, 4096, 8192)][1] != 16 and tiles[(5, 4097, 8192)][1] != 16
+    # 256 16-column tiles fill the CUs as they are; 157 of them run as 250 tiles of 10 columns
+    assert tiles[(8, 4096, 8192)][3] == 16 and tiles[(7, 2500, 9728)][2:] == (1, 10)

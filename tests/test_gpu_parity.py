@@ -784,6 +784,52 @@ def test_edge_shapes(M, N, K, s):
         check_tolerance(host_f64(C), ref, what="edge %dx%dx%d s=%d" % (M, N, K, ss))
 
 
+# Unsplit grids of 16-column small-M tiles with fewer tiles than CUs run narrower tiles of
+# ceil(N / (256 // row blocks)) columns: widths of 1 (one column per workgroup), 2, 4 (whole
+# 4-column stores), 10 and 12 (pairs), 11 (odd: pairs and single columns), ragged last tiles,
+# and a 256-tile grid that is left as it is.
+NARROW = [(1, 1, 256, 1), (5, 40, 384, 1), (16, 300, 512, 2), (29, 1000, 640, 4), (7, 2500, 9728, 10),
+          (32, 2561, 1024, 11), (3, 3000, 1280, 12), (20, 4095, 256, 16)]
+
+
+@pytest.mark.parametrize("M,N,K,tw", NARROW)
+def test_narrowed_tiles(M, N, K, tw):
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert (plan.s, plan.block_n) == (1, tw)
+    d = syn.w4a16_inputs(M, N, K, seed=7100 + M + N)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for f32p in (False, True):
+        say("narrowed tiles M=%d N=%d K=%d width=%d f32p=%d" % (M, N, K, tw, f32p))
+        C = run_w4a16(dv, M, N, K, 1, guard=40, f32p=f32p)
+        check_tolerance(host_f64(C), ref, what="narrowed %dx%dx%d" % (M, N, K))
+    # one-hot rows: every column of every narrowed tile is the correctly rounded weight
+    rng = np.random.default_rng(7100 + N)
+    ks = rng.integers(0, K, M)
+    A = np.zeros((M, K), dtype=np.uint16)
+    A[np.arange(M), ks] = 0x3F80
+    dv["A"] = dev_bf16(A)
+    say("narrowed tiles one-hot M=%d N=%d K=%d" % (M, N, K))
+    got = host_bits(run_w4a16(dv, M, N, K, 1, guard=40)).copy()
+    expect = oracle.bf16_round_array(oracle.dequant_w4a16(d["Wq"], d["scale"], d["bias"], N, K)[:, ks].T)
+    got[got == 0x8000] = 0
+    expect[expect == 0x8000] = 0
+    assert np.array_equal(got, expect), "%d of %d differ" % (int((got != expect).sum()), got.size)
+
+
+def test_narrowed_tiles_other_formats():
+    # the 8-bit codes and groups of 32 take the same narrowed tiles (1000 columns: width 4)
+    M, N, K = 16, 1000, 1024
+    for bits, group in ((8, 128), (4, 32)):
+        plan = q.qmm_wna16_plan(bits, group, M, N, K)
+        assert (plan.s, plan.block_n) == (1, 4)
+        d = syn.wq_inputs(bits, group, M, N, K, seed=7200 + bits + group)
+        ref = oracle.qmm_wq(bits, group, d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+        say("narrowed tiles w%da16 g%d" % (bits, group))
+        C = run_wna16(w4a16_device(d), bits, group, M, N, K, 1, guard=40)
+        check_tolerance(host_f64(C), ref, what="narrowed w%da16 g%d" % (bits, group))
+
+
 def test_largest_k_partition_bounds():
     # K just under 2^22 (the host's limit: G = 32767 groups) on the small-M kernel, unsplit,
     # split 7 ways, 20000 ways (partitions of one or two groups: p*G up to 6.6e8) and one

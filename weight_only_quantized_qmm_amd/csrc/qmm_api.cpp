@@ -116,14 +116,33 @@ int wide_variant(int M, int N, int K)
     return best;
 }
 
+// An unsplit grid of 16-column small-M tiles with fewer tiles than CUs leaves CUs idle, and
+// a workgroup's time grows with the weight bytes it streams: narrow the tiles to
+// ceil(N / tiles-per-row-block) columns so that the grid covers every CU once (the MFMA
+// subtile keeps 16 columns, the ones past the tile idle). Each workgroup still reads all of
+// A, so this pays where the weights are a large share of its bytes (A/B on MI355X: down at
+// M = 4 and 8 6-8 % faster, k and v at M = 32 3 %, o at M = 32 2 %; 48-column tiles of gate
+// and up narrowed to 38 or 40 columns were unchanged, so wider tiles are left as they are).
+W4A16Tile narrow_skinny(W4A16Tile t, int M, int N, int s)
+{
+    t.tw = 16 * t.ns;
+    if (s != 1 || t.ns != 1) return t;
+    const long long per_row = kCUs / ceil_div(M, t.block_m());  // column tiles one round holds
+    if (per_row < 1 || ceil_div(N, t.tw) >= per_row) return t;
+    const long long tw = ceil_div(N, per_row);
+    if (tw < t.tw) t.tw = (int)tw;
+    return t;
+}
+
 // Kernel and block tile for an (M, N, K) problem. The small-M kernel takes up to 64 rows
 // in one block row, and 65..128 rows in 64-row blocks when the packed weights are at
 // most 8 MB (N*K <= 2^24): there the large-M kernel has too few 256-column tiles and must
 // split deeply, while reading the weights twice costs less (split sweeps of the Qwen3-4B
 // q, k and v projections at M = 128 on MI355X: 25-45 % faster; gate, up and down stay on
 // the large-M kernel). Otherwise the large-M kernel, in the tile variant wide_variant picks.
-W4A16Tile w4a16_tile(int M, int N, int K) {
+W4A16Tile w4a16_tile(int M, int N, int K, int s) {
     W4A16Tile t;
+    t.tw = 0;
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
         t.kind = qmm_impl::W4A16_SKINNY;
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
@@ -137,7 +156,7 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
         // 10.3, 10.6, 10.9).
         if (M <= 32 && ((long long)N * K <= (1LL << 24) || (M <= 8 && N <= 16 * kCUs))) {
             t.ns = 1;
-            return t;
+            return narrow_skinny(t, M, N, s);
         }
         // 32-column tiles while they fit one workgroup per CU (one workgroup of the
         // small-M kernel fills a CU's wave slots) over a reduction shorter than 8192;
@@ -151,6 +170,7 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
             t.ns = 2;
         else
             t.ns = rows * ceil_div(N, 48) <= kCUs ? 3 : 4;
+        return narrow_skinny(t, M, N, s);
     } else {
         t.kind = qmm_impl::W4A16_WIDE;
         t.ns = wide_variant(M, N, K);
@@ -162,6 +182,7 @@ W4A16Tile w4a16_tile(int M, int N, int K) {
 // The large-M kernel's tile for M > 64, whichever kernel the plan picks (stream-K runs it).
 W4A16Tile wide_tile(int M) {
     W4A16Tile t;
+    t.tw = 0;
     t.kind = qmm_impl::W4A16_WIDE;
     t.mt = M <= 128 ? 8 : 16;
     t.ns = M <= 128 ? 0 : 2;
@@ -174,8 +195,8 @@ hipError_t dispatch_skinny(WFormat fmt, const W4A16Tile &tile, const void *A, co
     // the longest partition: ceil(G / s) blocks (near-equal partitions differ by at most one)
     const int G = K / kGroup;
     const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (G + s - 1) / s, fmt.bits, fmt.sub());
-    return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, sh.gpw, sh.waves, A, Wq, scale, bias, out, f32_part,
-                                         M, N, K, s, vec, st);
+    return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, tile.tw, sh.gpw, sh.waves, A, Wq, scale, bias, out,
+                                         f32_part, M, N, K, s, vec, st);
 }
 
 DenseTile dense_tile(int /*M*/, int /*N*/) {
@@ -226,7 +247,8 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
     if (!sizes_ok(M, N, K)) return QMM_ERR_SIZE;
     const qmm_policy pol = policy ? *policy : QMM_POLICY_MI355X;
     if (!policy_ok(pol)) return QMM_ERR_ARG;
-    const W4A16Tile tile = w4a16_tile(M, N, K);
+    // the split rule counts the kernel's full-width tiles; an unsplit plan then narrows them
+    const W4A16Tile tile = w4a16_tile(M, N, K, 0);
     const int tm = pol.tile_m > 0 ? pol.tile_m : tile.block_m();
     const int tn = pol.tile_n > 0 ? pol.tile_n : tile.block_n();
     const long long base = ceil_div(M, tm) * ceil_div(N, tn);
@@ -248,9 +270,11 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
             p.min_k_per_split < kSkinnyMinK)
             p.min_k_per_split = kSkinnyMinK;
         d.s = split_rule(base, G, K, p);
-        d.full_tiles = d.s == 1 ? (int)kernel_tiles : 0;
+        d.full_tiles = 0;
     }
     const int s = d.s;
+    const W4A16Tile run = w4a16_tile(M, N, K, s);
+    if (s == 1) d.full_tiles = (int)(ceil_div(M, run.block_m()) * ceil_div(N, run.block_n()));
     out->s = s;
     out->base_tiles = base > INT_MAX ? INT_MAX : (int)base;
     out->tile_m = tm;
@@ -261,12 +285,12 @@ int plan_format(WFormat fmt, int M, int N, int K, const qmm_policy *policy, qmm_
         out->grid_y = 1;
         out->grid_z = 1;
     } else {
-        out->grid_x = (int)ceil_div(N, tile.block_n());
-        out->grid_y = (int)ceil_div(M, tile.block_m());
+        out->grid_x = (int)ceil_div(N, run.block_n());
+        out->grid_y = (int)ceil_div(M, run.block_m());
         out->grid_z = s;
     }
-    out->block_m = tile.block_m();
-    out->block_n = tile.block_n();
+    out->block_m = run.block_m();
+    out->block_n = run.block_n();
     out->workspace_bytes = s > 1 ? (size_t)2 * (size_t)s * (size_t)M * (size_t)N : 0;
     return QMM_OK;
 }
@@ -302,7 +326,6 @@ int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const 
     if (!aligned(A, 16) || !aligned(Wq, 16) || !aligned(scale, 2) || !aligned(bias, 2) || !aligned(C, 2))
         return QMM_ERR_ALIGN;
     const int G = K / kGroup;
-    const W4A16Tile tile = w4a16_tile(M, N, K);
     int full_tiles = 0;
     if (s == 0) {
         qmm_plan plan;
@@ -313,6 +336,7 @@ int wq_run(WFormat fmt, const void *A, const void *Wq, const void *scale, const 
     } else if (s > G) {
         return QMM_ERR_SHAPE;
     }
+    const W4A16Tile tile = w4a16_tile(M, N, K, s);
     const size_t MN = (size_t)M * (size_t)N;
     const size_t esz = f32_part ? 4 : 2;
     if (s > 1) {

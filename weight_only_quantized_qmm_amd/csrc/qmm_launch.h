@@ -22,8 +22,9 @@ struct W4A16Tile {
     W4A16Kind kind;
     int mt;  // 16-row MFMA subtiles per block (SKINNY: 1, 2, 4; WIDE: 8, 16)
     int ns;  // SKINNY: 16-column MFMA subtiles per block (1 to 4); WIDE: kernel variant
+    int tw;  // SKINNY: columns per workgroup, 1 to 16*ns (the last subtile may be partly idle)
     int block_m() const { return 16 * mt; }
-    int block_n() const { return kind == W4A16_WIDE ? wide_cols(ns) : 16 * ns; }
+    int block_n() const { return kind == W4A16_WIDE ? wide_cols(ns) : tw; }
 };
 
 // Weight format: `bits`-wide unsigned codes (4 or 8) packed 32/bits per 32-bit word along K,
@@ -87,9 +88,10 @@ struct DenseTile {
 };
 
 // out: C (bf16) when s = 1, else the partial planes [s][M][N], bf16 or (f32_part) fp32.
-hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
-                               const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
-                               int s, bool vec_store, hipStream_t stream);
+// Workgroup (x, y, z) computes columns [x*tw, x*tw + tw) of rows [16*mt*y, 16*mt*(y+1)).
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int waves, const void *A,
+                               const void *Wq, const void *scale, const void *bias, void *out, bool f32_part, int M,
+                               int N, int K, int s, bool vec_store, hipStream_t stream);
 
 // Large-M kernel variants: 0 = 128 x 256 tiles of 4 waves of 128 x 64; 1 = 128 x 128
 // tiles of 4 waves of 128 x 32; 2 = 256 x 256 tiles of 8 waves of 256 x 32. LDS bytes of

@@ -12,8 +12,10 @@
 // latency and bandwidth, not by the matrix cores (a dispatch on MI355X costs about
 // 1.6 us before the first byte arrives). The design therefore maximises the bytes
 // in flight per wave and keeps the work in one dispatch where possible:
-//   * a workgroup owns a (16*MT) x (16*NS) output tile and up to 16 waves; the
-//     waves split the tile's reduction range, wave w taking groups g0 + w,
+//   * a workgroup owns a (16*MT) x tw output tile (tw <= 16*NS columns: the host narrows
+//     an unsplit grid of 16-column tiles that has fewer tiles than CUs, and the subtile's
+//     columns past tw re-read the tile's last weight row and are not stored) and up to 16
+//     waves; the waves split the tile's reduction range, wave w taking groups g0 + w,
 //     g0 + w + WAVES, ... of its partition;
 //   * each wave issues every load of a round of up to GPW groups before it computes:
 //     the round's activations go straight into the wave's own LDS staging slots
@@ -24,7 +26,8 @@
 //     of 64 bytes); then it waits once and runs the MFMAs of the round, reading its
 //     activation operands and scale/bias from LDS;
 //   * the waves' fp32 tiles meet in LDS and are summed in ascending wave order
-//     (deterministic), rounded once to bf16 and stored with 8-byte stores.
+//     (deterministic), rounded once to bf16 and stored with 8-byte stores (4-byte pairs
+//     where a tile's width is not a multiple of 4).
 // Loading the activations in MFMA operand order straight into registers instead touches
 // four times as many cache lines per byte (16 rows x 4 pieces per instruction); on the
 // Qwen3-4B projections at M = 16..64 the staged copies are 5-15 % faster.
@@ -77,7 +80,7 @@ template <int BITS, int MT, int NS, int GPW, int MAXW>
 __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
-                    void *__restrict__ out, int M, int N, int K, int sub_shift, int vec_store,
+                    void *__restrict__ out, int M, int N, int K, int tw, int sub_shift, int vec_store,
                     int f32_part)
 {
     constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
@@ -92,7 +95,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15;
     const int slot = lane >> 4;
-    const int n_blk = blockIdx.x * (16 * NS);
+    // The workgroup's columns: [n_blk, n_end), tw of them (tw <= 16*NS; fewer than the
+    // subtiles hold when the host narrows the tiles to spread the grid over every CU).
+    const int n_blk = blockIdx.x * tw;
+    const int n_end = min(N, n_blk + tw);
     const int m_blk = blockIdx.y * (16 * MT);
     const int GG = (K >> 7) << sub_shift;  // scale/bias entries per row (128 / group_size per block)
     const int G = K >> 7;  // 128-value blocks of the reduction
@@ -109,7 +115,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     const uint4 *wptr[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-        const int n = min(n_blk + 16 * j + r, N - 1);  // rows past N read row N-1, never stored
+        const int n = min(n_blk + 16 * j + r, n_end - 1);  // rows past the tile re-read its last row, never stored
         wptr[j] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K * BITS / 32)) + WV * slot;
     }
     // Activation copies: copy c (0 .. 4*MT-1) of a group fills staging rows 4c .. 4c+3; lane i
@@ -172,7 +178,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                 const int e = min(64 * c + lane, EW - 1);  // past the array: re-read its last entry
                 const int row_e = (e >> sub_shift) / GPW;  // = e / RW
                 const int rem = e - row_e * RW;
-                const int row = min(row_e, N - 1 - n_blk);  // rows past N re-read row N-1 (never used)
+                const int row = min(row_e, n_end - 1 - n_blk);  // rows past the tile re-read its last row (never used)
                 const int q = min(rem >> sub_shift, nq - 1);  // slots past the round re-read its last group
                 const int g = g0 + wave + waves * (base + q);
                 const uint32_t voff = 2u * (uint32_t)(row * GG + (g << sub_shift) + (rem & ((1 << sub_shift) - 1)));
@@ -251,26 +257,44 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         if (m < M) {
             // C (bf16) when unsplit, else plane blockIdx.z of bf16 or (f32_part) fp32 partials
             const size_t e = (size_t)blockIdx.z * (size_t)M * (size_t)N + (size_t)m * (size_t)N + n;
+            // vec_store (N % 4 == 0, aligned buffers): a whole quad starting on a multiple of 4
+            // in one store, else pairs starting on an even column (tiles of a width that is
+            // not a multiple of 4 start on any even column), else single elements
+            const bool quad = vec_store && (n & 3) == 0 && n + 3 < n_end;
             if (f32_part && gridDim.z > 1) {
                 float *dst = static_cast<float *>(out) + e;
-                if (vec_store && n + 3 < N) {
+                if (quad) {
                     *reinterpret_cast<float4 *>(dst) = make_float4(sum[0], sum[1], sum[2], sum[3]);
                 } else {
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2)
-                        if (n + e2 < N) dst[e2] = sum[e2];
+                    for (int e2 = 0; e2 < 4; e2 += 2) {
+                        const int c = n + e2;
+                        if (vec_store && (c & 1) == 0 && c + 1 < n_end) {
+                            *reinterpret_cast<float2 *>(dst + e2) = make_float2(sum[e2], sum[e2 + 1]);
+                        } else {
+                            if (c < n_end) dst[e2] = sum[e2];
+                            if (c + 1 < n_end) dst[e2 + 1] = sum[e2 + 1];
+                        }
+                    }
                 }
             } else {
                 uint16_t *dst = static_cast<uint16_t *>(out) + e;
-                if (vec_store && n + 3 < N) {
+                if (quad) {
                     uint2 v;
                     v.x = pack_bf16x2(sum[0], sum[1]);
                     v.y = pack_bf16x2(sum[2], sum[3]);
                     *reinterpret_cast<uint2 *>(dst) = v;
                 } else {
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2)
-                        if (n + e2 < N) dst[e2] = (uint16_t)f32_to_bf16(sum[e2]);
+                    for (int e2 = 0; e2 < 4; e2 += 2) {
+                        const int c = n + e2;
+                        if (vec_store && (c & 1) == 0 && c + 1 < n_end) {
+                            *reinterpret_cast<uint32_t *>(dst + e2) = pack_bf16x2(sum[e2], sum[e2 + 1]);
+                        } else {
+                            if (c < n_end) dst[e2] = (uint16_t)f32_to_bf16(sum[e2]);
+                            if (c + 1 < n_end) dst[e2 + 1] = (uint16_t)f32_to_bf16(sum[e2 + 1]);
+                        }
+                    }
                 }
             }
         }
@@ -279,9 +303,11 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 
 template <int BITS, int MT, int NS, int GPW, int MAXW>
 hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, bool f32_part,
-                      int M, int N, int K, int s, int sub_shift, int waves, bool vec_store, hipStream_t stream)
+                      int M, int N, int K, int tw, int s, int sub_shift, int waves, bool vec_store,
+                      hipStream_t stream)
 {
-    const dim3 grid((N + 16 * NS - 1) / (16 * NS), (M + 16 * MT - 1) / (16 * MT), s);
+    if (tw < 1 || tw > 16 * NS) return hipErrorInvalidValue;
+    const dim3 grid((N + tw - 1) / tw, (M + 16 * MT - 1) / (16 * MT), s);
     const size_t lds = qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
     if (waves > MAXW || lds > (size_t)qmm_impl::kLdsPerCU) return hipErrorInvalidValue;
     // the activation copies take 32-bit byte offsets into A
@@ -290,7 +316,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
     hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       out, M, N, K, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
+                       out, M, N, K, tw, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -304,16 +330,16 @@ namespace qmm_impl {
 // 48- and 64-column tiles (ns 3, 4) with up to 8 waves and gpw <= 2, 2, 1 for mt 1, 2, 4 (register
 // budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one group less per
 // round where the 4-bit limit is above one.
-hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int gpw, int waves, const void *A, const void *Wq,
-                               const void *scale, const void *bias, void *out, bool f32_part, int M, int N, int K,
-                               int s, bool vec_store, hipStream_t stream)
+hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int waves, const void *A,
+                               const void *Wq, const void *scale, const void *bias, void *out, bool f32_part, int M,
+                               int N, int K, int s, bool vec_store, hipStream_t stream)
 {
     if (waves < 1 || waves > MAX_WAVES || !format_supported(fmt)) return hipErrorInvalidValue;
     const int sub_shift = fmt.group == 128 ? 0 : fmt.group == 64 ? 1 : 2;
 #define QMM_CFG(B_, MT_, NS_, GPW_, MAXW_)                                                                     \
     if (fmt.bits == B_ && mt == MT_ && ns == NS_ && gpw == GPW_)                                               \
-        return launch_cfg<B_, MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, s, sub_shift,  \
-                                                     waves, vec_store, stream);
+        return launch_cfg<B_, MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, tw, s,         \
+                                                     sub_shift, waves, vec_store, stream);
     QMM_CFG(4, 1, 1, 1, 16) QMM_CFG(4, 1, 1, 2, 16) QMM_CFG(4, 1, 1, 3, 16)
     QMM_CFG(4, 1, 2, 1, 16) QMM_CFG(4, 1, 2, 2, 16) QMM_CFG(4, 1, 2, 3, 16)
     QMM_CFG(4, 2, 2, 1, 8) QMM_CFG(4, 2, 2, 2, 8) QMM_CFG(4, 2, 2, 3, 8)

@@ -289,8 +289,10 @@ size_t qmm_streamk_workspace_bytes(int M, int N, int K, int workgroups);
  * qmm_w4a16_gemv -- the same product for decode-sized M (1 to 8 rows) on a matrix-vector
  * kernel with no matrix-core padding (tiny-llm "Week 2 Day 7", Benchmark Analysis:
  * decode runs on a separate matvec). Every packed weight is read once per call. On the
- * Qwen3-4B projections on MI355X it is 4-24 % faster than qmm_w4a16_g128 at M = 1; from
- * M = 4 on, the matmul's 16-row MFMA tile is faster (the dot-product work here grows with M).
+ * Qwen3-4B projections on MI355X it is faster than qmm_w4a16_g128 at M = 1 (down 6.5 against
+ * 8.1 us); from M = 4 on, the matmul's 16-row MFMA tile is faster (the dot-product work
+ * here grows with M). A workgroup computes 16 output columns, or 10 for one or two rows
+ * when that spreads the columns over more CUs.
  *   M in 1..8, else QMM_ERR_SHAPE. Same layouts, alignment, ownership and errors as
  *   qmm_w4a16_g128.
  *   s = 0  : qmm_gemv_min_split(M, K), the smallest split whose partitions fit the

@@ -456,7 +456,9 @@ def test_gemv_decode_shapes(name, M, N, K, idx):
 # lanes' work: K = 128, 256, 384, 2560 at M = 2, 6400 with up to 7 items per lane) and
 # ragged N.
 GEMV_EDGE = [(1, 1, 128), (3, 17, 256), (5, 100, 384), (8, 33, 4096), (2, 1000, 10240), (7, 4100, 1280),
-             (4, 64, 7680), (6, 15, 3968), (1, 50, 6400), (2, 70, 2560)]
+             (4, 64, 7680), (6, 15, 3968), (1, 50, 6400), (2, 70, 2560),
+             # 10-row workgroups with a ragged last one (5, 3 and 7 rows)
+             (1, 2555, 9728), (2, 33, 1280), (1, 7, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMV_EDGE)

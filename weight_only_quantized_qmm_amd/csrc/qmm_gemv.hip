@@ -15,8 +15,11 @@
 // A's pairs and chunk sums are staged in LDS once per workgroup and shared by its 16
 // weight rows; the group's scale and bias likewise.
 //
-// Work decomposition: a workgroup of 4 waves computes 16 output columns (4 per wave)
-// over one partition. A wave's work is split into items of RG rows (4 or 2) by one
+// Work decomposition: a workgroup computes 16 output columns with 4 waves of 4, or 10 with
+// 5 waves of 2, over one partition. A workgroup's time follows the weight bytes it
+// streams, so the host takes the layout whose busiest CU holds fewer rows (for one or two
+// activation rows; down at M = 1 on MI355X: 256 workgroups of 10 rows instead of 160 of
+// 16, 7.6 -> 6.5 us). A wave's work is split into items of RG rows (4 or 2) by one
 // chunk; lane l takes items l, l+64, ..., so consecutive lanes read consecutive 16 bytes
 // of a row (whole cache lines) and every lane gets the same number of items to within
 // one. Per-lane sums are reduced across the wave in a fixed order (deterministic).
@@ -36,8 +39,6 @@ using namespace qmm_dev;
 
 namespace {
 
-constexpr int ROWS_PER_WAVE = 4;
-constexpr int ROWS_PER_WG = 16;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -58,21 +59,23 @@ __device__ __forceinline__ uint32_t nib_pair(uint32_t w, int k)
 // the weight loads still in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int MM, int RG, int NCHM>
-__global__ void __launch_bounds__(256)
+// RPW rows (output columns) per wave, NW waves per workgroup: 4 x 4 or 2 x 5.
+template <int MM, int RG, int NCHM, int RPW, int NW>
+__global__ void __launch_bounds__(64 * NW)
 gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, const uint16_t *__restrict__ scale,
             const uint16_t *__restrict__ bias, uint16_t *__restrict__ out, int M, int N, int K, int gpp)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     asm volatile("" ::"s"(A), "s"(Wq), "s"(scale), "s"(bias), "s"(out));
-    constexpr int NRG = ROWS_PER_WAVE / RG;  // row groups of a wave
+    constexpr int NT = 64 * NW;            // threads of the workgroup
+    constexpr int NRG = RPW / RG;          // row groups of a wave
     const int G = K >> 7;
     const int p = blockIdx.y;
     const int g0 = p * gpp;
     const int k0 = g0 * 128;
     const int WP = gpp * 16;  // packed words of a row in the partition
     const int CP = gpp * 4;   // 16-byte chunks of a row in the partition
-    const int n_blk = blockIdx.x * ROWS_PER_WG;
+    const int n_blk = blockIdx.x * (RPW * NW);
     uint4 *apair = reinterpret_cast<uint4 *>(lds);             // [MM][WP]: pairs of word w
     float *asum = reinterpret_cast<float *>(apair + MM * WP);  // [MM][CP]
 
@@ -83,11 +86,11 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     // (rows m >= M stage zeros). CPMAX: the most chunks a row's partition has
     // (gemv_split_fits).
     constexpr int CPMAX = MM == 1 || MM == 2 ? 320 : MM == 4 ? 240 : 128;
-    constexpr int ITEMS = (MM * CPMAX + 255) / 256;
+    constexpr int ITEMS = (MM * CPMAX + NT - 1) / NT;
     uint4 av[ITEMS][4];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int idx = threadIdx.x + 256 * it;
+        const int idx = threadIdx.x + NT * it;
         const int m = idx / CP, c = idx - m * CP;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -108,7 +111,7 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
         const int rg = idx / CP, c = idx - rg * CP;
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) {
-            const int n = min(n_blk + ROWS_PER_WAVE * wave + RG * rg + rr, N - 1);
+            const int n = min(n_blk + RPW * wave + RG * rg + rr, N - 1);
             const size_t e = (size_t)n * G + g0 + (c >> 2);
             sbv[i][rr] = (uint32_t)scale[e] | ((uint32_t)bias[e] << 16);
         }
@@ -119,7 +122,7 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
         const int rg = idx / CP, c = idx - rg * CP;
 #pragma unroll
         for (int rr = 0; rr < RG; ++rr) {
-            const int n = min(n_blk + ROWS_PER_WAVE * wave + RG * rg + rr, N - 1);
+            const int n = min(n_blk + RPW * wave + RG * rg + rr, N - 1);
             wr[i][rr] = reinterpret_cast<const uint4 *>(Wq + (size_t)n * (size_t)(K >> 3) + (k0 >> 3))[c];
         }
     }
@@ -129,7 +132,7 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     // 3. Activation pairs (a[i], a[i+4]) of each packed word and the chunk sums into LDS.
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
-        const int idx = threadIdx.x + 256 * it;
+        const int idx = threadIdx.x + NT * it;
         if (idx >= MM * CP) break;
         const int m = idx / CP, c = idx - m * CP;
         float s = 0.f;
@@ -150,9 +153,9 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     lds_barrier();
 
     // 4. Each item as its weights arrive.
-    float acc[ROWS_PER_WAVE][MM];
+    float acc[RPW][MM];
 #pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int m = 0; m < MM; ++m) acc[r][m] = 0.f;
 #pragma unroll
@@ -198,7 +201,7 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
 
     // Wave sums in a fixed order (within rows of 16 lanes, then across them); lane 0 stores.
 #pragma unroll
-    for (int r = 0; r < ROWS_PER_WAVE; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int m = 0; m < MM; ++m) {
             float v = acc[r][m];
@@ -208,8 +211,8 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     if (lane == 0) {
         uint16_t *dst = out + (size_t)p * (size_t)M * (size_t)N;
 #pragma unroll
-        for (int r = 0; r < ROWS_PER_WAVE; ++r) {
-            const int n = n_blk + ROWS_PER_WAVE * wave + r;
+        for (int r = 0; r < RPW; ++r) {
+            const int n = n_blk + RPW * wave + r;
             if (n >= N) continue;
 #pragma unroll
             for (int m = 0; m < MM; ++m)
@@ -218,18 +221,26 @@ gemv_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq, con
     }
 }
 
-template <int MM, int RG, int NCHM>
+template <int MM, int RG, int NCHM, int RPW, int NW>
 hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, int M, int N,
                       int K, int s, hipStream_t stream)
 {
     const int gpp = (K / 128) / s;
     const size_t lds = (size_t)MM * gpp * 16 * 16 + (size_t)MM * gpp * 4 * 4;
-    const dim3 grid((N + ROWS_PER_WG - 1) / ROWS_PER_WG, s);
+    const dim3 grid((N + RPW * NW - 1) / (RPW * NW), s);
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemv_kernel<MM, RG, NCHM>), grid, dim3(256), lds, stream, static_cast<const uint16_t *>(A),
-                       static_cast<const uint32_t *>(Wq), static_cast<const uint16_t *>(scale),
-                       static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(out), M, N, K, gpp);
+    hipLaunchKernelGGL((gemv_kernel<MM, RG, NCHM, RPW, NW>), grid, dim3(64 * NW), lds, stream,
+                       static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
+                       static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
+                       static_cast<uint16_t *>(out), M, N, K, gpp);
     return hipGetLastError();
+}
+
+// Rows of the busiest CU when ceil(N / rows) * s workgroups of `rows` rows spread evenly.
+long long busiest_rows(int N, int s, int rows)
+{
+    const long long wgs = (long long)((N + rows - 1) / rows) * s;
+    return (wgs + 255) / 256 * rows;
 }
 
 }  // namespace
@@ -243,18 +254,31 @@ hipError_t launch_w4a16_gemv(const void *A, const void *Wq, const void *scale, c
     const int kp = K / s;
     const int mm = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     if (!gemv_split_fits(mm, kp)) return hipErrorInvalidValue;
+    const int cp = kp / 32;
+    const int it4 = (cp + 63) / 64, it2 = (2 * cp + 63) / 64;
+    const auto bucket = [](int nch) { return nch <= 2 ? 2 : nch <= 3 ? 3 : nch <= 5 ? 5 : 10; };
+    // Workgroup layout: 16 rows (4 waves of 4) or 10 rows (5 waves of 2). A workgroup's time
+    // follows the weight bytes it streams, so for one or two activation rows the layout whose
+    // busiest CU holds fewer rows wins (down at M = 1: 256 workgroups of 10 rows instead of
+    // 160 of 16). The 2-row waves take items of one row pair and one chunk.
+    if (mm <= 2 && busiest_rows(N, s, 10) < busiest_rows(N, s, 16)) {
+        const int nchm = bucket(it4);
+#define QMM_G10(MM_, NCH_)                                                                                       \
+    if (mm == MM_ && nchm == NCH_) return launch_cfg<MM_, 2, NCH_, 2, 5>(A, Wq, scale, bias, out, M, N, K, s, stream);
+        QMM_G10(1, 2) QMM_G10(1, 3) QMM_G10(1, 5) QMM_G10(2, 2) QMM_G10(2, 3) QMM_G10(2, 5)
+#undef QMM_G10
+        return hipErrorInvalidValue;
+    }
     // Rows per lane item: RG = 4 shares each chunk's activation reads over 4 rows; RG = 2
     // makes the items half as large, which evens out the lanes' work when a row's chunks are
     // not a multiple of 64 (K = 2560: 80 chunks, 2 items of 4 rows on some lanes, 1 on the
     // others). Per lane the cost is about items * (RG + MM/2) row-chunks of arithmetic;
     // ties go to 4 (decode sweeps of the Qwen3-4B projections on MI355X).
-    const int cp = kp / 32;
-    const int it4 = (cp + 63) / 64, it2 = (2 * cp + 63) / 64;
     const int rg = it2 * (4 + mm) < it4 * (8 + mm) ? 2 : 4;
-    const int nch = rg == 4 ? it4 : it2;
-    const int nchm = nch <= 2 ? 2 : nch <= 3 ? 3 : nch <= 5 ? 5 : 10;
+    const int nchm = bucket(rg == 4 ? it4 : it2);
 #define QMM_G(MM_, RG_, NCH_)                                                                                    \
-    if (mm == MM_ && rg == RG_ && nchm == NCH_) return launch_cfg<MM_, RG_, NCH_>(A, Wq, scale, bias, out, M, N, K, s, stream);
+    if (mm == MM_ && rg == RG_ && nchm == NCH_)                                                                  \
+        return launch_cfg<MM_, RG_, NCH_, 4, 4>(A, Wq, scale, bias, out, M, N, K, s, stream);
 #define QMM_GM(MM_) QMM_G(MM_, 4, 2) QMM_G(MM_, 4, 3) QMM_G(MM_, 4, 5) \
                     QMM_G(MM_, 2, 2) QMM_G(MM_, 2, 3) QMM_G(MM_, 2, 5) QMM_G(MM_, 2, 10)
     QMM_GM(1) QMM_GM(2) QMM_GM(4)

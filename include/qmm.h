@@ -83,7 +83,8 @@ enum { QMM_PARTIAL_BF16 = 0, QMM_PARTIAL_F32 = 1 };
  * while 32-column tiles fit in 256 workgroups and K < 8192; else by 48 when 48-column tiles
  * fit in 256 workgroups, else by 64. With tile_m = tile_n = 0 and M <= 32, its partitions hold at least 2048 reduction
  * values (min_k_per_split is raised to 2048 in the rule): a shorter partition saves less
- * than the second pass costs. An unsplit grid of 16-column tiles with fewer tiles than 256
+ * than the second pass costs; and the rule's last step (the divisor of K/128) is left out,
+ * partition p covering groups [floor(p*G/s), floor((p+1)*G/s)). An unsplit grid of 16-column tiles with fewer tiles than 256
  * runs tiles of ceil(N / (256 / row blocks)) columns instead (block_n below), so that it
  * covers every CU once; the split rule still counts the 16-column tiles (tile_n). The large-M kernel runs the rest, with the tile of shortest
  * estimated critical path among 128 x 256 (two workgroups per CU up to M = 128), 256 x 256

@@ -116,8 +116,8 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         # two 128 x 256 workgroups per CU up to M = 128; every other tile counts one per CU
         slots = pol.target_blocks * (2 if (plan.block_m, plan.block_n) == (128, 256) and M <= 128 else 1)
         check_slot_filling(plan, M, K, slots, pol)
-    else:  # the page's rule over the kernel's tile; partitions of at least 2048 values up to M = 32
-        assert G % plan.s == 0
+    else:  # the page's rule over the kernel's tile without its divisor step (near-equal
+        # partitions); partitions of at least 2048 values up to M = 32
         # 16-column tiles for up to 32 rows over at most 2^24 weights (and for up to 8 rows
         # with at most 4096 columns); else 32 columns while
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
@@ -129,9 +129,11 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         else:
             assert plan.tile_n == (48 if rows * -(-N // 48) <= 256 else 64)
         min_k = max(pol.min_k_per_split, 2048) if M <= 32 else pol.min_k_per_split
-        assert plan.s == opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.tile_n,
-                                             target=pol.target_blocks, cap=pol.cap,
-                                             min_k_per_split=min_k)
+        assert plan.s == max(1, min(pol.cap, pol.target_blocks // tiles, K // min_k, G))
+        # the page's rule would lower that to a divisor of G
+        page_s = opolicy.split_count(M, N, K, tile_m=plan.block_m, tile_n=plan.tile_n, target=pol.target_blocks,
+                                     cap=pol.cap, min_k_per_split=min_k)
+        assert page_s <= plan.s and G % page_s == 0
         # an unsplit grid of 16-column tiles with fewer tiles than CUs runs narrower tiles,
         # ceil(N / (256 // rows)) columns, so that it covers every CU once
         if plan.s == 1 and plan.tile_n == 16 and tiles < 256:

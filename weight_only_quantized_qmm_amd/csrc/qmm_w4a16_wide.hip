@@ -48,8 +48,8 @@
 // With 8-bit codes the same eight values are two words and a lane reads 32 bytes. A
 // lane's 32 values of a stage lie in one scale/bias group for every group size.
 // The MFMA takes the weights as its first operand, so a lane's results are four
-// consecutive output columns of one row. bf16 results leave through LDS as whole rows
-// (see the end of segment); fp32 planes are stored from the accumulators.
+// consecutive output columns of one row. Results leave through LDS as whole rows (see the
+// end of segment): bf16 tiles in one or two passes, fp32 planes in passes of 64 rows.
 //
 // LDS layouts: A rows are 128 bytes (eight 16-byte chunks), chunk c of row r stored
 // at chunk c ^ ((r >> 1) & 7); W rows of 32 bytes store chunk h of row r at
@@ -282,37 +282,6 @@ __device__ __forceinline__ void run_stage(const Ctx<CF> &c, const Lds<CF> &L, in
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Four consecutive outputs (columns n .. n+3 of one row, element offset e) as bf16 or
-// fp32: one 8- or 16-byte store when vec and n+3 < N, else element by element up to N.
-__device__ __forceinline__ void store4(char *base, bool f32, size_t e, int n, int N, int vec, float v0, float v1,
-                                       float v2, float v3)
-{
-    if (f32) {
-        float *q = reinterpret_cast<float *>(base) + e;
-        if (vec && n + 3 < N) {
-            *reinterpret_cast<float4 *>(q) = make_float4(v0, v1, v2, v3);
-        } else {
-            if (n < N) q[0] = v0;
-            if (n + 1 < N) q[1] = v1;
-            if (n + 2 < N) q[2] = v2;
-            if (n + 3 < N) q[3] = v3;
-        }
-    } else {
-        uint16_t *q = reinterpret_cast<uint16_t *>(base) + e;
-        if (vec && n + 3 < N) {
-            uint2 v;
-            v.x = pack_bf16x2(v0, v1);
-            v.y = pack_bf16x2(v2, v3);
-            *reinterpret_cast<uint2 *>(q) = v;
-        } else {
-            if (n < N) q[0] = (uint16_t)f32_to_bf16(v0);
-            if (n + 1 < N) q[1] = (uint16_t)f32_to_bf16(v1);
-            if (n + 2 < N) q[2] = (uint16_t)f32_to_bf16(v2);
-            if (n + 3 < N) q[3] = (uint16_t)f32_to_bf16(v3);
-        }
-    }
-}
-
 // Where a segment's results go: element (m, n) of the tile is stored at
 // base + ((m - r0) * ld + (n - c0)) elements, bf16 or (f32) fp32, rows m < M and
 // columns n < N only.
@@ -477,21 +446,53 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     // and n = n0 + wn*32*NJ + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
     const int r = lane & 31;
     const int sl = lane >> 5;
-    if (dst.f32) {  // fp32 planes: straight from the accumulators, 16-byte stores
+    char *T = reinterpret_cast<char *>(&L);
+    if (dst.f32) {
+        // fp32 planes go out through LDS like the bf16 results below: 4*BN bytes per row,
+        // chunk c of row x at chunk c ^ (x % (BN/4)), as many rows per pass as the LDS
+        // holds (a multiple of 32, so that each 32-row block of a wave lies in one pass),
+        // then whole rows per store instruction. Stored straight from the accumulators,
+        // every instruction wrote 16 bytes into each of 32 rows.
+        constexpr int CPR4 = CF::BN / 4;  // 16-byte chunks per row
+        constexpr int RB4 = CF::BN * 4;   // bytes per row
+        constexpr int PR4 = CF::BM * RB4 <= CF::LDS ? CF::BM : (CF::BM / 2) * RB4 <= CF::LDS ? CF::BM / 2 : CF::BM / 4;
+        static_assert(PR4 >= 32 && PR4 % 32 == 0 && PR4 * RB4 <= CF::LDS, "fp32 epilogue pass");
+        const bool v16f = dst.vec && (dst.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(dst.base) & 15) == 0;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const int m = m0 + wm * 32 * MI + 32 * i + r;
-            const bool row_ok = m < M;
+        for (int h = 0; h < CF::BM / PR4; ++h) {
+            __syncthreads();  // every wave is done with the stage slots, or with the previous pass
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            for (int i = 0; i < MI; ++i) {
+                const int rb = wm * 32 * MI + 32 * i;
+                if (rb / PR4 != h) continue;  // wave-uniform
+                const int x = rb - h * PR4 + r;
 #pragma unroll
-                for (int vq = 0; vq < 4; ++vq) {
-                    const int n = n0 + wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;
-                    const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
-                    const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
-                    if (row_ok)
-                        store4(dst.base, true, (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0), n, N, dst.vec,
-                               v0, v1, v2, v3);
+                for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                    for (int vq = 0; vq < 4; ++vq) {
+                        const int cc = 8 * (wn * NJ + j) + 2 * vq + sl;  // columns 4cc .. 4cc+3 of the tile
+                        *reinterpret_cast<float4 *>(T + x * RB4 + 16 * (cc ^ (x & (CPR4 - 1)))) =
+                            make_float4(acc[i][j][4 * vq], acc[i][j][4 * vq + 1], acc[i][j][4 * vq + 2],
+                                        acc[i][j][4 * vq + 3]);
+                    }
+                }
+            }
+            __syncthreads();
+            for (int k = threadIdx.x; k < PR4 * CPR4; k += 64 * CF::NW) {
+                const int x = k / CPR4, cc = k % CPR4;
+                const int m = m0 + h * PR4 + x, n = n0 + 4 * cc;
+                if (m >= M || n >= N) continue;
+                const float4 v = *reinterpret_cast<const float4 *>(T + x * RB4 + 16 * (cc ^ (x & (CPR4 - 1))));
+                float *g = reinterpret_cast<float *>(dst.base) + (size_t)(m - dst.r0) * dst.ld + (size_t)(n - dst.c0);
+                if (v16f && n + 3 < N) {
+                    __builtin_nontemporal_store(
+                        u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)},
+                        reinterpret_cast<u32x4 *>(g));
+                } else {
+                    const float w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) g[e] = w[e];
                 }
             }
         }
@@ -506,7 +507,6 @@ __device__ __forceinline__ void segment(Lds<CF> &L, const uint16_t *__restrict__
     constexpr int PR = CF::BM * CF::BN * 2 <= CF::LDS ? CF::BM : CF::BM / 2;  // rows per pass
     constexpr int CPR = CF::BN / 8;  // 16-byte chunks per row
     constexpr int RB = CF::BN * 2;   // bytes per row
-    char *T = reinterpret_cast<char *>(&L);
     const bool v16 = dst.vec && (dst.ld % 8) == 0 && (reinterpret_cast<uintptr_t>(dst.base) & 15) == 0;
 #pragma unroll
     for (int h = 0; h < CF::BM / PR; ++h) {

@@ -52,11 +52,19 @@ struct SkinnyShape {
     int gpw;    // groups whose loads one wave issues together
 };
 
-inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub)
+inline size_t skinny_stage_bytes(int mt, int ns, int waves, int gpw, int sub)
 {
     const size_t ew = (size_t)16 * ns * gpw * sub;
-    const size_t stage = (size_t)waves * gpw * mt * 4096 + (size_t)waves * 2 * ((ew + 63) & ~(size_t)63) * 4;
-    const size_t sums = (size_t)waves * mt * ns * 1024;
+    return (size_t)waves * gpw * mt * 4096 + (size_t)waves * 2 * ((ew + 63) & ~(size_t)63) * 4;
+}
+inline size_t skinny_sum_bytes(int mt, int ns, int waves) { return (size_t)waves * mt * ns * 1024; }
+// The least LDS a configuration needs: the waves' fp32 tiles reuse the staging memory once
+// every wave has left it. (When staging and tiles fit side by side, the kernel keeps them
+// apart instead, so that a wave can store its tile without waiting for the others.)
+inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub)
+{
+    const size_t stage = skinny_stage_bytes(mt, ns, waves, gpw, sub);
+    const size_t sums = skinny_sum_bytes(mt, ns, waves);
     return stage > sums ? stage : sums;
 }
 

@@ -42,8 +42,8 @@
 // LDS: wave w's staging slots are [GPW][16*MT rows][256 bytes] at w*GPW*MT*4 KB; chunk c
 // (16 bytes) of row r is stored at chunk c ^ (r % 16), so the 16 rows that one 16-lane
 // phase of an operand read touches fall on distinct banks. The waves' scale and bias
-// arrays follow the staging slots. After the main loop the same memory holds the waves'
-// fp32 tiles for the cross-wave sum.
+// arrays follow the staging slots. The waves' fp32 tiles for the cross-wave sum follow
+// those when everything fits in the LDS, else reuse the staging memory after the main loop.
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
                     void *__restrict__ out, int M, int N, int K, int tw, int sub_shift, int vec_store,
-                    int f32_part)
+                    int f32_part, int sum_off)
 {
     constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
     constexpr int ABYTES = MT * 16 * 256;  // one staged group of activations: 16*MT rows x 128 values
@@ -236,11 +236,13 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         }
     }
 
-    // Cross-wave sum in LDS: once every wave has left its staging slots, wave w stores its
-    // tiles, then each of the MT*NS*64 lane-quads (i, j, lane) is owned by one thread
-    // (strided over the workgroup), which adds the waves' values in order w = 0, 1, ...
-    __syncthreads();
-    f32x4 *red4 = reinterpret_cast<f32x4 *>(smem);
+    // Cross-wave sum in LDS: wave w stores its tiles, then each of the MT*NS*64 lane-quads
+    // (i, j, lane) is owned by one thread (strided over the workgroup), which adds the
+    // waves' values in order w = 0, 1, ... The tiles sit at byte sum_off: past the staging
+    // memory when both fit (a wave stores as soon as it is done), else over it (sum_off = 0:
+    // every wave must first have left its staging slots).
+    if (sum_off == 0) __syncthreads();  // uniform: a kernel argument
+    f32x4 *red4 = reinterpret_cast<f32x4 *>(smem + sum_off);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -308,7 +310,12 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
 {
     if (tw < 1 || tw > 16 * NS) return hipErrorInvalidValue;
     const dim3 grid((N + tw - 1) / tw, (M + 16 * MT - 1) / (16 * MT), s);
-    const size_t lds = qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
+    const size_t stage = qmm_impl::skinny_stage_bytes(MT, NS, waves, GPW, 1 << sub_shift);
+    const size_t sums = qmm_impl::skinny_sum_bytes(MT, NS, waves);
+    // the waves' tiles beside the staging memory when both fit (16-byte aligned: stage is a
+    // multiple of 256), else over it
+    const bool apart = stage + sums <= (size_t)qmm_impl::kLdsPerCU;
+    const size_t lds = apart ? stage + sums : qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
     if (waves > MAXW || lds > (size_t)qmm_impl::kLdsPerCU) return hipErrorInvalidValue;
     // the activation copies take 32-bit byte offsets into A
     if ((size_t)M * (size_t)K * 2 >= ((size_t)1 << 32)) return hipErrorInvalidValue;
@@ -316,7 +323,7 @@ hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const vo
     hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
-                       out, M, N, K, tw, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0);
+                       out, M, N, K, tw, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0, apart ? (int)stage : 0);
     return hipGetLastError();
 }
 

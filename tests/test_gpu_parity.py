@@ -832,6 +832,21 @@ def test_narrowed_tiles_other_formats():
         check_tolerance(host_f64(C), ref, what="narrowed w%da16 g%d" % (bits, group))
 
 
+# 256 x 256 tiles of a split with ragged M and N (N % 4 = 2 and 1): the epilogues' whole-row
+# stores through LDS, bf16 and fp32 planes, with the partial quads stored element by element.
+@pytest.mark.parametrize("M,N,K", [(900, 4098, 1536), (1300, 3001, 1536)])
+def test_256_row_tiles_ragged_planes(M, N, K):
+    plan = q.qmm_splitk_plan(M, N, K)
+    assert (plan.block_m, plan.block_n) == (256, 256) and plan.s > 1
+    d = syn.w4a16_inputs(M, N, K, seed=7300 + N)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for f32p in (False, True):
+        say("256-row tiles ragged M=%d N=%d K=%d s=%d f32p=%d" % (M, N, K, plan.s, f32p))
+        C = run_w4a16(dv, M, N, K, 0, guard=40, f32p=f32p)
+        check_tolerance(host_f64(C), ref, what="256-row ragged %dx%dx%d f32p=%d" % (M, N, K, f32p))
+
+
 def test_largest_k_partition_bounds():
     # K just under 2^22 (the host's limit: G = 32767 groups) on the small-M kernel, unsplit,
     # split 7 ways, 20000 ways (partitions of one or two groups: p*G up to 6.6e8) and one

@@ -707,7 +707,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=25.0, help="CPU-baseline sample budget")
     ap.add_argument("--no-per-shape", action="store_true")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
-    ap.add_argument("--tables-out", default=os.path.join("gpurun_out", "bench_tables.json"),
+    ap.add_argument("--tables-out", default="bench_tables.json",
                     help="file that receives the per-shape and secondary tables (JSON)")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only the dominant-kernel roofline measurement (the profiled command)")

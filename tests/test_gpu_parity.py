@@ -861,6 +861,30 @@ def test_largest_k_partition_bounds():
         check_tolerance(host_f64(C), ref, what="largest K s=%d" % s)
 
 
+def test_largest_k_large_m_kernel():
+    # the large-M kernel (129 rows) at the largest K the host accepts (32767 groups): its
+    # 32-bit per-lane copy offsets reach 2*255*K bytes; unsplit, split 7 ways, at the cap
+    # and under the plan, on sampled outputs (every edge row and column among them).
+    # Inputs: a seeded block of 151 groups repeated 217 times along K (generating 5.4e8
+    # activations takes minutes); an offset that wrapped at 2^32 bytes would land at a
+    # different position within the block.
+    M, N, K = 129, 64, ((1 << 22) // 128 - 1) * 128
+    kb = 151 * 128
+    blk = syn.w4a16_inputs(M, N, kb, seed=7060)
+    d = {key: np.tile(blk[key], (1, K // kb)) for key in ("A", "Wq", "scale", "bias")}
+    rng = np.random.default_rng(7060)
+    ms = np.concatenate([np.repeat([0, 1, 127, 128], 3), rng.integers(0, M, 60)]).astype(np.int32)
+    ns = np.concatenate([np.tile([0, 31, 63], 4), rng.integers(0, N, 60)]).astype(np.int32)
+    ref = oracle.qmm_w4a16_points(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K, ms, ns)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    dv = w4a16_device(d)
+    del d
+    for s in (1, 7, 20, 0):
+        say("largest K large-M kernel M=%d N=%d K=%d s=%d" % (M, N, K, s))
+        C = host_f64(run_w4a16(dv, M, N, K, s, guard=24))
+        check_tolerance(C[ms, ns], ref, rms=rms, what="largest K large-M s=%d" % s)
+
+
 def test_error_leaves_output_untouched():
     M, N, K = 16, 64, 256
     d = syn.w4a16_inputs(M, N, K, seed=7100)

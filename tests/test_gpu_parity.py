@@ -384,11 +384,12 @@ def test_cfg3_dense_split_sweep(cfg3, s):
     check_tolerance(host_f64(C), ref, what="dense s=%d" % s)
 
 
-@pytest.mark.parametrize("K,splits", [(32 * 71, (1, 3, 7, 71)), (64 * 35, (2, 3, 6, 35))])
-def test_dense_ragged_and_reduce_fp32(K, splits):
+@pytest.mark.parametrize("M,N,K,splits", [(37, 45, 32 * 71, (1, 3, 7, 71)), (37, 45, 64 * 35, (2, 3, 6, 35)),
+                                          (200, 300, 2048, (1, 5, 16))])
+def test_dense_ragged_and_reduce_fp32(M, N, K, splits):
     # K = 32 * 71: partitions of 32-value granules (half stages at the odd ones, one granule
-    # each at s = 71); K = 64 * 35: 64-value units (one each at s = 35)
-    M, N = 37, 45
+    # each at s = 71); K = 64 * 35: 64-value units (one each at s = 35); 200 x 300: 2 x 3
+    # tiles, the last row and column of tiles partial
     d = syn.dense_inputs(M, N, K, seed=3001 + K)
     ref = oracle.qmm_dense(d["A"], d["B"], M, N, K)
     A, B = dev_bf16(d["A"]), dev_bf16(d["B"])

@@ -9,8 +9,8 @@
 // with s = 1 the workgroup writes the bf16 result directly.
 //
 // Structure (the same pipeline as the large-M W4A16 kernel, without the dequant):
-//   * a workgroup of 4 wave64s owns a 128 x 128 output tile (2 x 2 waves, each a
-//     64 x 64 block of 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators);
+//   * a workgroup of 8 wave64s (two per SIMD) owns a 128 x 128 output tile (2 x 4 waves,
+//     each a 64 x 32 block of 2 x 1 v_mfma_f32_32x32x16_bf16 accumulators);
 //   * the partition is walked in stages of 64 reduction values; A and B rows of a stage
 //     (128 bytes each) are copied global -> LDS by global_load_lds_dwordx4, two stages
 //     ahead, into rings of three 16 KB slots each (96 KB); each wave waits for its own
@@ -33,7 +33,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 128, TN = 128, SK = 64;
 constexpr int SLOT = TM * SK * 2;  // 16 KB per operand per stage
-constexpr int NCOPY = 8;           // copies per wave per stage: 4 of A, 4 of B
+// Waves per workgroup: NW = 4 (2 x 2 waves of 64 x 64) or 8 (2 x 4 waves of 64 x 32, two per
+// SIMD); each stage's 16 A and 16 B copies are shared out evenly.
+template <int NW> struct DGeom {
+    static constexpr int WN = NW / 2;        // waves along N
+    static constexpr int NJ = 2 * 2 / WN;    // 32-column MFMA blocks per wave: 2 or 1
+    static constexpr int CP = 16 / NW;       // copies of A (and of B) per wave and stage: 4 or 2
+    static constexpr int NCOPY = 2 * CP;     // copies per wave per stage
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -60,56 +67,64 @@ struct DenseLds {
 };
 static_assert(TM * TN * 4 <= sizeof(DenseLds), "the fp32 output tile is staged in the stage slots");
 
+template <int NW>
 struct DCtx {
+    using GE = DGeom<NW>;
     const char *A, *B;     // A + m0*K, B + n0*K (bytes)
     int k_begin, k_end;    // reduction range of the partition
-    uint32_t a_off[4][2];  // per-lane byte offsets of the A copies: full / half stage
-    uint32_t b_off[4][2];
+    uint32_t a_off[GE::CP][2];  // per-lane byte offsets of the A copies: full / half stage
+    uint32_t b_off[GE::CP][2];
     uint32_t a_lds, b_lds; // this wave's copy destinations inside slot 0
     uint32_t a_rd[4], b_rd[4];  // operand read offsets, reduction step t
 };
 
-// Copies of stage x (k0 = k_begin + 64x) into slot `slot`: 8 instructions per wave.
-__device__ __forceinline__ void issue(const DCtx &c, int x, int slot)
+// Copies of stage x (k0 = k_begin + 64x) into slot `slot`: NCOPY instructions per wave.
+template <int NW>
+__device__ __forceinline__ void issue(const DCtx<NW> &c, int x, int slot)
 {
     const int k0 = c.k_begin + SK * x;
     const int half = (c.k_end - k0) < SK ? 1 : 0;
     const char *Ab = c.A + 2 * (size_t)k0;
     const char *Bb = c.B + 2 * (size_t)k0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) copy16(c.a_lds + (uint32_t)slot * SLOT + 1024u * j, c.a_off[j][half], Ab);
+    for (int j = 0; j < DGeom<NW>::CP; ++j) copy16(c.a_lds + (uint32_t)slot * SLOT + 1024u * j, c.a_off[j][half], Ab);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) copy16(c.b_lds + (uint32_t)slot * SLOT + 1024u * j, c.b_off[j][half], Bb);
+    for (int j = 0; j < DGeom<NW>::CP; ++j) copy16(c.b_lds + (uint32_t)slot * SLOT + 1024u * j, c.b_off[j][half], Bb);
 }
 
-__device__ __forceinline__ void compute(const DCtx &c, const DenseLds &L, int slot, bool half, f32x16 (&acc)[2][2])
+template <int NW>
+__device__ __forceinline__ void compute(const DCtx<NW> &c, const DenseLds &L, int slot, bool half,
+                                        f32x16 (&acc)[2][DGeom<NW>::NJ])
 {
+    constexpr int NJ = DGeom<NW>::NJ;
     const char *As = L.a + slot * SLOT;
     const char *Bs = L.b + slot * SLOT;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         if (half && t >= 2) break;  // uniform: the missing half of a half stage
-        bf16x8 af[2], bf[2];
+        bf16x8 af[2], bf[NJ];
 #pragma unroll
         for (int i = 0; i < 2; ++i) af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(As + c.a_rd[t] + 4096 * i));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(Bs + c.b_rd[t] + 4096 * j));
+        for (int j = 0; j < NJ; ++j) bf[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(Bs + c.b_rd[t] + 4096 * j));
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(bf[j], af[i], acc[i][j]);
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(bf[j], af[i], acc[i][j]);
     }
 }
 
-template <bool F32_OUT>
-__global__ void __launch_bounds__(256, 1)
+template <bool F32_OUT, int NW>
+__global__ void __launch_bounds__(64 * NW, 1)
 dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, void *__restrict__ out,
              int M, int N, int K, int s, int vec_store)
 {
+    using GE = DGeom<NW>;
+    constexpr int NJ = GE::NJ;
     __shared__ __attribute__((aligned(1024))) DenseLds L;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / GE::WN, wn = wave % GE::WN;  // 64-row block, 32*NJ-column block
     const int num_m = (M + TM - 1) / TM;
     const int tiles = num_m * ((N + TN - 1) / TN);
     // XCD-aware order: the dispatcher sends workgroup b to XCD b % 8, so when the grid
@@ -132,17 +147,17 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     const int u_lo = (int)(((long long)p * U) / s);
     const int u_hi = (int)(((long long)(p + 1) * U) / s);
 
-    DCtx c;
+    DCtx<NW> c;
     c.A = reinterpret_cast<const char *>(A) + 2 * (size_t)m0 * (size_t)K;
     c.B = reinterpret_cast<const char *>(B) + 2 * (size_t)n0 * (size_t)K;
     c.k_begin = UNIT * u_lo;
     c.k_end = UNIT * u_hi;
-    // Copy j of wave w fills LDS rows 8q .. 8q+7, q = 4w + j; lane i -> row 8q + i/8,
+    // Copy j of wave w fills LDS rows 8q .. 8q+7, q = CP*w + j; lane i -> row 8q + i/8,
     // stored chunk i%8, logical chunk (i%8) ^ ((r>>1)&7); a half stage reads logical
     // chunk & 3 (the stage's valid half). Rows past M (N) re-read the last row.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 8 * (4 * wave + j) + (lane >> 3);
+    for (int j = 0; j < GE::CP; ++j) {
+        const int r = 8 * (GE::CP * wave + j) + (lane >> 3);
         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
         const int ra = min(m0 + r, M - 1) - m0;
         const int rb = min(n0 + r, N - 1) - n0;
@@ -151,13 +166,13 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
         c.b_off[j][0] = 2u * ((uint32_t)rb * (uint32_t)K + 8u * (uint32_t)chunk);
         c.b_off[j][1] = 2u * ((uint32_t)rb * (uint32_t)K + 8u * (uint32_t)(chunk & 3));
     }
-    c.a_lds = lds_addr(L.a) + 4096u * (uint32_t)wave;
-    c.b_lds = lds_addr(L.b) + 4096u * (uint32_t)wave;
+    c.a_lds = lds_addr(L.a) + 1024u * GE::CP * (uint32_t)wave;
+    c.b_lds = lds_addr(L.b) + 1024u * GE::CP * (uint32_t)wave;
     {
         // Reduction step t, lane half h: logical chunk 2t + h (eight values) of the row.
         const int r32 = lane & 31, h = lane >> 5;
         const int arow = wm * 64 + r32;  // + 32 i: same swizzle
-        const int brow = wn * 64 + r32;  // + 32 j
+        const int brow = wn * 32 * NJ + r32;  // + 32 j
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             c.a_rd[t] = (uint32_t)(arow * 128 + 16 * ((2 * t + h) ^ ((arow >> 1) & 7)));
@@ -165,11 +180,11 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
         }
     }
 
-    f32x16 acc[2][2];
+    f32x16 acc[2][NJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -179,7 +194,7 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     const int nst = (c.k_end - c.k_begin + SK - 1) / SK;  // >= 1
     issue(c, 0, 0);
     issue(c, min(1, nst - 1), 1);
-    QMM_WAIT_VMCNT(NCOPY);
+    QMM_WAIT_VMCNT(GE::NCOPY);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     int slot = 0;  // st % 3
@@ -187,7 +202,7 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
         const int slot_issue = slot == 0 ? 2 : slot - 1;  // (st + 2) % 3: the slot stage st-1 used
         issue(c, min(st + 2, nst - 1), slot_issue);
         compute(c, L, slot, (c.k_end - (c.k_begin + SK * st)) < SK, acc);
-        QMM_WAIT_VMCNT(NCOPY);  // the copies of stage st+1 landed; this stage's 8 may remain
+        QMM_WAIT_VMCNT(GE::NCOPY);  // the copies of stage st+1 landed; this stage's may remain
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         slot = slot == 2 ? 0 : slot + 1;
@@ -195,7 +210,7 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     QMM_WAIT_VMCNT(0);  // no copy may still be writing LDS when the workgroup ends
 
     // Lane holds, for tile (i, j), C[m][n..n+3] with m = m0 + wm*64 + 32i + (lane % 32)
-    // and n = n0 + wn*64 + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
+    // and n = n0 + wn*32*NJ + 32j + 8*vq + 4*(lane / 32), values 4vq .. 4vq+3.
     // The tile goes out through LDS (free now): the waves write it row-major, 128 values
     // per row (512 bytes of fp32 or 256 of bf16) with 16-byte chunk c of row x stored at
     // chunk c ^ (x % chunks per row), and then every store instruction writes whole rows.
@@ -210,12 +225,12 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     for (int i = 0; i < 2; ++i) {
         const int x = wm * 64 + 32 * i + r;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
             for (int vq = 0; vq < 4; ++vq) {
                 const float v0 = acc[i][j][4 * vq], v1 = acc[i][j][4 * vq + 1];
                 const float v2 = acc[i][j][4 * vq + 2], v3 = acc[i][j][4 * vq + 3];
-                const int col = wn * 64 + 32 * j + 8 * vq + 4 * sl;  // first of the four columns
+                const int col = wn * 32 * NJ + 32 * j + 8 * vq + 4 * sl;  // first of the four columns
                 if (F32_OUT) {
                     const int cc = col >> 2;
                     *reinterpret_cast<float4 *>(T + x * (CPR * 16) + 16 * (cc ^ (x & (CPR - 1)))) =
@@ -233,7 +248,7 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     __syncthreads();
     char *base = static_cast<char *>(out) + (F32_OUT ? (size_t)p * (size_t)M * (size_t)N * ES : 0);
     const bool v16 = vec_store && (N % (16 / ES)) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0;
-    for (int k = threadIdx.x; k < TM * CPR; k += 256) {
+    for (int k = threadIdx.x; k < TM * CPR; k += 64 * NW) {
         const int x = k / CPR, cc = k % CPR;
         const int m = m0 + x, n = n0 + cc * (16 / ES);
         if (m >= M || n >= N) continue;
@@ -271,13 +286,18 @@ hipError_t launch_dense(DenseTile tile, const void *A, const void *B, void *out,
     if (K >= (1 << 22) || s < 1 || s > K / ((K & 63) == 0 ? 64 : 32)) return hipErrorInvalidValue;
     const int tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
     const dim3 grid(tiles * s);
+    // eight 64 x 32 waves, two per SIMD, so that one wave's LDS reads and copy waits hide under
+    // the other's MFMAs (cfg3 on MI355X: 8 % faster than four 64 x 64 waves at s = 1..8, 5 % at
+    // s = 12, 1 % at s = 16)
+    constexpr int NW = 8;
     (void)hipGetLastError();
     if (f32_out)
-        hipLaunchKernelGGL((dense_kernel<true>), grid, dim3(256), 0, stream, static_cast<const uint16_t *>(A),
+        hipLaunchKernelGGL((dense_kernel<true, NW>), grid, dim3(64 * NW), 0, stream, static_cast<const uint16_t *>(A),
                            static_cast<const uint16_t *>(B), out, M, N, K, s, vec_store ? 1 : 0);
     else
-        hipLaunchKernelGGL((dense_kernel<false>), grid, dim3(256), 0, stream, static_cast<const uint16_t *>(A),
-                           static_cast<const uint16_t *>(B), out, M, N, K, s, vec_store ? 1 : 0);
+        hipLaunchKernelGGL((dense_kernel<false, NW>), grid, dim3(64 * NW), 0, stream,
+                           static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(B), out, M, N, K, s,
+                           vec_store ? 1 : 0);
     return hipGetLastError();
 }
 

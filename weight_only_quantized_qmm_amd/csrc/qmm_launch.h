@@ -8,7 +8,8 @@
 namespace qmm_impl {
 
 // Which W4A16 kernel runs a problem, and the output tile of one workgroup.
-//   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x (16*ns) tile, ns 1 to 4,
+//   SKINNY (M <= 64, or M <= 128 with N*K <= 2^24): a (16*mt) x tw tile (tw = 16*ns, ns 1 to 4,
+//          or fewer columns for a narrowed unsplit grid of 16-column tiles),
 //          up to 16 waves splitting its reduction;
 //   WIDE   (otherwise): a 128 x 256 (variant 0), 128 x 128 (variant 1) or 256 x 256
 //          (variant 2) tile; mt = 8 or 16.
@@ -87,7 +88,7 @@ inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4, int sub =
     return sh;
 }
 
-// Dense bf16 kernel: 2 x 2 waves, each 16*mt rows by 16*ns columns.
+// Dense bf16 kernel tile: 32*mt rows by 32*ns columns (the kernel has 128 x 128 only).
 struct DenseTile {
     int mt;
     int ns;

@@ -11,6 +11,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <set>
 #include <tuple>
 
@@ -25,9 +26,76 @@ int g_last_split = -1;    // split of the last matmul launch
 std::set<std::tuple<int, int, int, int, int>> g_skinny_cfgs;
 }  // namespace
 
+// Every global load the small-M kernel issues, its offsets computed as the kernel computes
+// them (partition bounds, each wave's groups and rounds, the activation copies, the weight
+// loads and the scale/bias copies), for the first and the last workgroup of each grid
+// dimension and every partition and wave: each must fall inside A, Wq or the scale/bias
+// arrays. A wave with no groups (a partition with fewer groups than waves) issues nothing.
+void check_skinny_offsets(qmm_impl::WFormat fmt, int mt, int ns, int tw, int gpw, int waves, int M, int N, int K,
+                          int s)
+{
+    const int sub_shift = fmt.group == 128 ? 0 : fmt.group == 64 ? 1 : 2;
+    const int G = K >> 7, GG = G << sub_shift;
+    const int WV = fmt.bits / 4;
+    const long long row_u4 = (long long)K * fmt.bits / 128;  // 16-byte units per weight row
+    const int RW = gpw << sub_shift, EW = 16 * ns * RW, ncp = (EW + 63) >> 6;
+    const int gx = (N + tw - 1) / tw, gy = (M + 16 * mt - 1) / (16 * mt);
+    for (int bx : {0, gx - 1})
+        for (int by : {0, gy - 1})
+            for (int z = 0; z < s; ++z)
+                for (int wave = 0; wave < waves; ++wave) {
+                    const int n_blk = bx * tw, n_end = std::min(N, n_blk + tw), m_blk = by * 16 * mt;
+                    if (n_blk >= N || m_blk >= M) abort();
+                    const unsigned Gu = (unsigned)G, S = (unsigned)s, Z = (unsigned)z;
+                    const int g0 = S == 1 ? 0 : (int)((Z * Gu) / S);
+                    const int gpp = S == 1 ? G : (int)(((Z + 1) * Gu) / S) - g0;
+                    if (gpp < 1) abort();
+                    const int n_w = (int)((unsigned)(gpp - wave + waves - 1) / (unsigned)waves);
+                    if (n_w < 1) continue;
+                    for (int base = 0; base < n_w; base += gpw) {
+                        for (int q = 0; q < gpw && base + q < n_w; ++q) {
+                            const int g = g0 + wave + waves * (base + q);
+                            if (g < g0 || g >= g0 + gpp) abort();
+                            for (int r = 0; r < 16; ++r)
+                                for (int j = 0; j < ns; ++j) {
+                                    const int n = std::min(n_blk + 16 * j + r, n_end - 1);
+                                    for (int slot = 0; slot < 4; ++slot)
+                                        for (int u = 0; u < WV; ++u) {
+                                            const long long i4 = (long long)WV * slot + 4LL * WV * g + u;
+                                            if (n < 0 || n >= N || i4 < 0 || i4 >= row_u4) abort();
+                                        }
+                                }
+                            for (int c = 0; c < 4 * mt; ++c)
+                                for (int lane = 0; lane < 64; ++lane) {
+                                    const int row = 4 * c + (lane >> 4);
+                                    if (m_blk + 4 * c >= M) continue;  // copy not issued
+                                    const long long m = std::min(m_blk + row, M - 1);
+                                    const long long off = m * K * 2 + 16LL * ((lane & 15) ^ (row & 15)) + 256LL * g;
+                                    if (off < 0 || off + 16 > 2LL * M * K || off >= (1LL << 32)) abort();
+                                }
+                        }
+                        const int nq = std::min(gpw, n_w - base);
+                        for (int c = 0; c < ncp; ++c)
+                            for (int lane = 0; lane < 64; ++lane) {
+                                const int e = std::min(64 * c + lane, EW - 1);
+                                const int row_e = (e >> sub_shift) / gpw;
+                                const int rem = e - row_e * RW;
+                                const int row = std::min(row_e, n_end - 1 - n_blk);
+                                const int q = std::min(rem >> sub_shift, nq - 1);
+                                const long long g = g0 + wave + (long long)waves * (base + q);
+                                const long long idx =
+                                    (long long)row * GG + (g << sub_shift) + (rem & ((1 << sub_shift) - 1));
+                                if (idx < 0 || (long long)n_blk * GG + idx >= (long long)N * GG ||
+                                    2 * idx >= (1LL << 32))
+                                    abort();
+                            }
+                    }
+                }
+}
+
 namespace qmm_impl {
 hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int waves, const void *,
-                               const void *, const void *, const void *, void *, bool, int M, int N, int, int s, bool,
+                               const void *, const void *, const void *, void *, bool, int M, int N, int K, int s, bool,
                                hipStream_t)
 {
     if (waves < 1 || waves > 16) abort();
@@ -35,6 +103,7 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int
     if ((long long)(N + tw - 1) / tw > 65535) abort();  // grid x
     if (M < 1 || skinny_lds_bytes(mt, ns, waves, gpw, fmt.sub()) > (size_t)kLdsPerCU) abort();
     g_skinny_cfgs.insert(std::make_tuple(fmt.bits, mt, ns, gpw, waves));
+    check_skinny_offsets(fmt, mt, ns, tw, gpw, waves, M, N, K, s);
     ++g_launches;
     g_last_split = s;
     return hipSuccess;

@@ -24,7 +24,8 @@
 //     own LDS arrays (global_load_lds, 64 entries per instruction), and the packed
 //     weights into registers (one 16-byte load per lane and 16-column subtile; 16 rows
 //     of 64 bytes); then it waits once and runs the MFMAs of the round, reading its
-//     activation operands and scale/bias from LDS;
+//     activation operands and scale/bias from LDS; with one group per round the next
+//     round's weights and scale/bias go out before those MFMAs, the activations after;
 //   * the waves' fp32 tiles meet in LDS and are summed in ascending wave order
 //     (deterministic), rounded once to bf16 and stored with 8-byte stores (4-byte pairs
 //     where a tile's width is not a multiple of 4).
@@ -158,11 +159,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const char *Abase = reinterpret_cast<const char *>(A);
-    for (int base = 0; base < n_w; base += GPW) {
-        uint4 wv[GPW][NS][WV];
-        uint32_t sc[GPW][NS], bi[GPW][NS];
-        // Issue every load of the round before the first use: the activation copies into
-        // the staging slots, the scale/bias copies, then the weights into registers.
+    // The loads of the round starting at group index base (of this wave's n_w groups):
+    // activation copies into the staging slots, scale/bias copies into the wave's arrays,
+    // packed weights into registers.
+    auto issue_a = [&](const int base) {
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;  // uniform across the wave
@@ -172,20 +172,23 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                 if (m_blk + 4 * c < M)  // a copy whose four rows all lie past M is skipped (see below)
                     copy16(stage_lds + (uint32_t)(q * ABYTES + 1024 * c), a_voff[c], Ag);
         }
-        {
-            const int nq = min(GPW, n_w - base);  // groups of this round (>= 1)
-            for (int c = 0; c < ncp; ++c) {
-                const int e = min(64 * c + lane, EW - 1);  // past the array: re-read its last entry
-                const int row_e = (e >> sub_shift) / GPW;  // = e / RW
-                const int rem = e - row_e * RW;
-                const int row = min(row_e, n_end - 1 - n_blk);  // rows past the tile re-read its last row (never used)
-                const int q = min(rem >> sub_shift, nq - 1);  // slots past the round re-read its last group
-                const int g = g0 + wave + waves * (base + q);
-                const uint32_t voff = 2u * (uint32_t)(row * GG + (g << sub_shift) + (rem & ((1 << sub_shift) - 1)));
-                copy2(sbw_lds + 256u * (uint32_t)c, voff, scale + (size_t)n_blk * GG);
-                copy2(sbw_lds + 4u * (uint32_t)AW + 256u * (uint32_t)c, voff, bias + (size_t)n_blk * GG);
-            }
+    };
+    auto issue_sb = [&](const int base) {
+        const int nq = min(GPW, n_w - base);  // groups of this round (>= 1)
+        for (int c = 0; c < ncp; ++c) {
+            const int e = min(64 * c + lane, EW - 1);  // past the array: re-read its last entry
+            const int row_e = (e >> sub_shift) / GPW;  // = e / RW
+            const int rem = e - row_e * RW;
+            const int row = min(row_e, n_end - 1 - n_blk);  // rows past the tile re-read its last row (never used)
+            const int q = min(rem >> sub_shift, nq - 1);  // slots past the round re-read its last group
+            const int g = g0 + wave + waves * (base + q);
+            const uint32_t voff = 2u * (uint32_t)(row * GG + (g << sub_shift) + (rem & ((1 << sub_shift) - 1)));
+            copy2(sbw_lds + 256u * (uint32_t)c, voff, scale + (size_t)n_blk * GG);
+            copy2(sbw_lds + 4u * (uint32_t)AW + 256u * (uint32_t)c, voff, bias + (size_t)n_blk * GG);
         }
+    };
+    uint4 wn[GPW][NS][WV];  // the packed weights of the next round, in flight
+    auto issue_w = [&](const int base) {
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;  // uniform across the wave
@@ -193,14 +196,31 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
 #pragma unroll
-                for (int u = 0; u < WV; ++u) wv[q][j][u] = wptr[j][4 * WV * g + u];
+                for (int u = 0; u < WV; ++u) wn[q][j][u] = wptr[j][4 * WV * g + u];
             }
         }
-        // Without the scheduling fence the compiler sinks each load next to its first use,
+    };
+    // A wave may have no groups at all (n_w = 0: a partition with fewer groups than the
+    // workgroup has waves); it issues nothing and contributes zeros to the sum.
+    if (n_w > 0) {
+        issue_a(0);
+        issue_sb(0);
+        issue_w(0);
+    }
+    for (int base = 0; base < n_w; base += GPW) {
+        // Without the scheduling fences the compiler sinks each load next to its first use,
         // one memory round trip per load. The copies are invisible to the compiler, so
         // the wave waits for all of its loads itself before it reads the staging slots.
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint4 wv[GPW][NS][WV];
+        uint32_t sc[GPW][NS], bi[GPW][NS];
+#pragma unroll
+        for (int q = 0; q < GPW; ++q)
+#pragma unroll
+            for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int u = 0; u < WV; ++u) wv[q][j][u] = wn[q][j][u];
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;
@@ -210,6 +230,21 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                 bi[q][j] = sbw[AW + (16 * j + r) * RW + (q << sub_shift) + sub_e];
             }
         }
+        // With one group per round, the next round's weights and scale/bias entries go out
+        // before this round's MFMAs (the scale/bias arrays are free once read), so their
+        // memory latency overlaps this round's arithmetic and the next round's activation
+        // copies, which wait for the staging slots that this round's operand reads still
+        // use. With two or three groups per round the early loads were slower (MI355X, the
+        // Qwen3-4B projections at M = 1..64), and the whole next round goes out after the
+        // MFMAs.
+        constexpr bool kEarly = GPW == 1;
+        const bool more = base + GPW < n_w;  // uniform across the wave
+        if (kEarly && more) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_sb(base + GPW);
+            issue_w(base + GPW);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
             if (base + q >= n_w) break;  // uniform across the wave
@@ -232,6 +267,16 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 #pragma unroll
                     for (int i = 0; i < MT; ++i) acc[i][j] = mfma16x16x32(b, as_bf16x8(av[i]), acc[i][j]);
                 }
+            }
+        }
+        if (more) {
+            // every operand read of the staging slots (and of the scale/bias arrays) has
+            // returned before they are refilled
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            issue_a(base + GPW);
+            if (!kEarly) {
+                issue_sb(base + GPW);
+                issue_w(base + GPW);
             }
         }
     }

@@ -85,7 +85,7 @@ DOMINANT_KERNEL = "w4a16_wide_kernel"
 # What the committed traffic counters were taken on: the kernel's source, the host code
 # that plans its launches, and the workload of the counter passes.
 DOMINANT_SOURCES = [os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
-                    for f in ("qmm_w4a16_wide.hip", "qmm_api.cpp")]
+                    for f in ("qmm_w4a16_wide.hip", "qmm_api.cpp", "qmm_launch.h", "qmm_device.h")]
 DOMINANT_WORKLOAD = "first pass (qmm_w4a16_g128_pass1) of the plan, M=2048 q,k,v,o,gate,up,down"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "w4a16_wide_M2048_traffic.txt")
 STEP_LOOP_STEPS = 2048     # steps per workgroup of the step-loop calibration
@@ -522,7 +522,8 @@ def summarize_small_pmc(fetch_dir, write_dir, trace_dir, commands):
     lines += ["all %d launches: %.4g bytes against %.4g algorithmic (%.2fx), %.1f GB/s over %.1f us of kernel time"
               % (len(dt), tot_b, tot_a, tot_b / tot_a, tot_b / tot_t, tot_t / 1e3),
               "kernel source digest: %s" % source_digest([os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
-                                                          for f in ("qmm_w4a16_skinny.hip", "qmm_api.cpp")])]
+                                                          for f in ("qmm_w4a16_skinny.hip", "qmm_api.cpp",
+                                                                    "qmm_launch.h", "qmm_device.h")])]
     print("\n".join(lines))
 
 

@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <set>
+#include <vector>
 #include <tuple>
 
 #include "qmm.h"
@@ -174,8 +175,45 @@ int call_w4a16(int M, int N, int K, int s, void *ws, size_t wsb, const void *A =
 
 }  // namespace
 
+// The large-M kernel's XCD order: for every region shape and every panel height that divides
+// the row blocks, wide_item maps the region's workgroups one to one onto its (partition,
+// column block, row block) items; wide_panel returns 0 or such a divisor.
+void check_wide_order()
+{
+    long regions = 0;
+    std::vector<char> seen;
+    for (int P = 1; P <= 7; ++P)
+        for (int nb = 1; nb <= 40; nb += (nb < 12 ? 1 : 7))
+            for (int num_m = 1; num_m <= 17; ++num_m) {
+                const int wr = P * nb * num_m;
+                for (int pm = 1; pm <= num_m; ++pm) {
+                    if (num_m % pm) continue;
+                    seen.assign((size_t)wr, 0);
+                    for (int r = 0; r < wr; ++r) {
+                        const qmm_impl::WideItem it = qmm_impl::wide_item(r, wr, num_m, nb, pm);
+                        EXPECT(it.p >= 0 && it.p < P && it.n >= 0 && it.n < nb && it.m >= 0 && it.m < num_m);
+                        const size_t idx = ((size_t)it.p * nb + it.n) * num_m + it.m;
+                        EXPECT(!seen[idx]);
+                        seen[idx] = 1;
+                    }
+                    ++regions;
+                }
+                for (double ratio : {0.05, 0.3, 1.0, 3.0, 20.0}) {
+                    const int pm = qmm_impl::wide_panel(P, nb, num_m, 1.0, ratio);
+                    EXPECT(pm == 0 || (pm >= 1 && pm <= num_m && num_m % pm == 0));
+                }
+            }
+    // the Qwen3-4B M = 2048 regions: an XCD-blocked order where one XCD would otherwise read
+    // every column block (gate's whole tiles: 8 x 32 tiles of 256 x 256; o and down: 3
+    // partitions of 8 x 10)
+    EXPECT(qmm_impl::wide_panel(1, 32, 8, 20 * 65536.0, 20 * 256 * 68.0) > 0);
+    EXPECT(qmm_impl::wide_panel(3, 10, 8, 76 / 3.0 * 65536.0, 76 / 3.0 * 256 * 68.0) > 0);
+    printf("wide order regions %ld\n", regions);
+}
+
 int main()
 {
+    check_wide_order();
     // ---- plans over a grid of shapes, every preset and a few tunables
     const int Ms[] = {1, 2, 7, 16, 31, 32, 33, 48, 64, 65, 100, 128, 129, 255, 256, 300, 1000, 2048, 4096};
     const int Ns[] = {1, 17, 100, 1000, 1024, 2560, 4096, 9728, 16484};

@@ -128,6 +128,74 @@ hipError_t launch_w4a16_wide(WFormat fmt, int variant, const void *A, const void
                              const void *bias, void *C, void *part, bool f32_part, int M, int N, int K,
                              int full_tiles, int split, bool vec_store, hipStream_t stream, int streamk = 0);
 
+// Order of the large-M kernel's work items over the XCDs. The grid has one or two regions:
+// the whole tiles (one partition), then the split ones (split partitions); a region holds
+// wr = P * nb * num_m items, P partitions of nb column blocks of num_m row blocks. The
+// dispatcher deals workgroups round-robin over the 8 XCDs, so the workgroups r, r + 8,
+// r + 16, ... of a region share an L2; they get one contiguous run of items, read in
+// panels of pm row blocks:
+//   L = k*(wr/8) + min(k, wr%8) + j  for workgroup r = 8j + k of the region (a bijection
+//       onto 0 .. wr-1: run k holds wr/8 items, one more for k < wr%8),
+//   p = L / (nb*num_m); within the partition, panel = l / (pm*nb) covers row blocks
+//   panel*pm .. panel*pm + pm-1, and l % (pm*nb) walks them row block fastest, then the
+//   column blocks.
+// So one XCD's workgroups read a few row blocks of A against a few column blocks of W
+// (about pm x (wr/8)/pm tiles) instead of one row block of A against every column block.
+// pm divides num_m. Each workgroup still computes one whole tile over one partition.
+struct WideItem {
+    int p, n, m;  // partition, column block, row block
+};
+constexpr WideItem wide_item(int r, int wr, int num_m, int nb, int pm)
+{
+    const int k = r & 7, j = r >> 3;
+    const int q = wr >> 3, rem = wr & 7;
+    const int L = k * q + (k < rem ? k : rem) + j;
+    const int per_p = nb * num_m;
+    const int p = L / per_p;
+    const int l = L - p * per_p;
+    const int panel = l / (pm * nb);
+    const int w = l - panel * pm * nb;
+    return WideItem{p, w / pm, panel * pm + w % pm};
+}
+
+// The panel height for a region (0: the plain order, workgroup r taking item r, row block
+// fastest): the divisor of num_m whose XCD runs read the fewest bytes, A's row blocks at
+// a_mp bytes each and W's column blocks (with their scale/bias) at w_np bytes each, per
+// partition. A run of c = ceil(wr/8) items covers min(pm, c) row blocks by ceil(c/pm)
+// column blocks while it fits one panel, else whole panels; the plain order gives an XCD
+// every eighth item: num_m/8 row blocks by all nb column blocks of every partition when 8
+// divides num_m, one row block by nb*num_m/8 column blocks when num_m divides 8.
+inline int wide_panel(int P, int nb, int num_m, double a_mp, double w_np)
+{
+    if (P < 1 || nb < 1 || num_m < 1) return 0;
+    const long long wr = (long long)P * nb * num_m;
+    const long long c = (wr + 7) / 8;
+    double plain;
+    if (num_m % 8 == 0)
+        plain = P * (num_m / 8 * a_mp + nb * w_np);
+    else if (8 % num_m == 0)
+        plain = P * (a_mp + ((nb * num_m + 7) / 8) * w_np);
+    else
+        plain = P * (num_m * a_mp + nb * w_np);
+    int best = 0;
+    double best_cost = plain;
+    for (int pm = 1; pm <= num_m; ++pm) {
+        if (num_m % pm) continue;
+        double cost;
+        if (c <= (long long)pm * nb)
+            cost = (double)(c < pm ? c : pm) * a_mp + (double)((c + pm - 1) / pm) * w_np;
+        else if (c <= (long long)nb * num_m)
+            cost = (double)((c + nb - 1) / nb) * a_mp + nb * w_np;
+        else
+            cost = (double)((c + nb * num_m - 1) / (nb * num_m)) * (num_m * a_mp + nb * w_np);
+        if (cost < best_cost * 0.98) {  // a clear gain over the best so far, else keep it
+            best_cost = cost;
+            best = pm;
+        }
+    }
+    return best;
+}
+
 inline size_t wide_streamk_bytes(int variant, int P, bool f32_part)
 {
     return (size_t)2 * (size_t)P * (size_t)wide_rows(variant) * (size_t)kWideCols * (f32_part ? 4 : 2);

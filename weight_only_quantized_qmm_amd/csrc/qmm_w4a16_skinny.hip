@@ -87,11 +87,14 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
     constexpr int ABYTES = MT * 16 * 256;  // one staged group of activations: 16*MT rows x 128 values
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // staging, then [WAVES][MT][NS][64] float4
-    // Fetch every pointer argument up front, in the kernel's first scalar loads: left to
-    // itself the compiler loads them after the first branch, one more dependent memory
-    // round trip before the first weight load.
-    asm volatile("" ::"s"(A), "s"(Wq), "s"(scale), "s"(bias), "s"(out));
-    const int waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
+    // Fetch every argument (and the grid's partition count and workgroup size) up front,
+    // in one batch of scalar loads: left to itself the compiler loads the pointers after
+    // the first branch, and a use of the pointers alone splits the loads into two
+    // dependent memory round trips before the first weight load.
+    const unsigned nz = gridDim.z, nt = blockDim.x;
+    asm volatile("" ::"s"(A), "s"(Wq), "s"(scale), "s"(bias), "s"(out), "s"(M), "s"(N), "s"(K), "s"(tw),
+                 "s"(sub_shift), "s"(vec_store), "s"(f32_part), "s"(sum_off), "s"(nz), "s"(nt));
+    const int waves = __builtin_amdgcn_readfirstlane(nt >> 6);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int r = lane & 15;
@@ -107,11 +110,13 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     // keeps K below 2^22), and none at all when unsplit: every wave evaluates them on the
     // CU's shared scalar unit before its first load, and a 64-bit division is a software
     // routine of over a hundred scalar instructions.
-    const unsigned Gu = (unsigned)G, S = gridDim.z, Z = blockIdx.z;
+    const unsigned Gu = (unsigned)G, S = nz, Z = blockIdx.z;
     const int g0 = S == 1 ? 0 : (int)((Z * Gu) / S);
     const int gpp = S == 1 ? G : (int)(((Z + 1) * Gu) / S) - g0;  // this partition's blocks
-    // this wave's groups: g0 + wave + waves*i, i < n_w (the dividend is at least gpp > 0)
-    const int n_w = (int)((unsigned)(gpp - wave + waves - 1) / (unsigned)waves);
+    // this wave's groups: g0 + wave + waves*i for the i with has(i), i.e. i < ceil((gpp -
+    // wave) / waves), tested without the division (a few dozen scalar instructions per wave,
+    // on the CU's shared scalar unit, before the first load)
+    auto has = [&](const int i) { return wave + waves * i < gpp; };
 
     const uint4 *wptr[NS];
 #pragma unroll
@@ -159,13 +164,13 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         for (int j = 0; j < NS; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const char *Abase = reinterpret_cast<const char *>(A);
-    // The loads of the round starting at group index base (of this wave's n_w groups):
+    // The loads of the round starting at group index base (of this wave's groups):
     // activation copies into the staging slots, scale/bias copies into the wave's arrays,
     // packed weights into registers.
     auto issue_a = [&](const int base) {
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-            if (base + q >= n_w) break;  // uniform across the wave
+            if (!has(base + q)) break;  // uniform across the wave
             const char *Ag = Abase + (size_t)(g0 + wave + waves * (base + q)) * 256;
 #pragma unroll
             for (int c = 0; c < 4 * MT; ++c)
@@ -174,7 +179,10 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         }
     };
     auto issue_sb = [&](const int base) {
-        const int nq = min(GPW, n_w - base);  // groups of this round (>= 1)
+        int nq = 1;  // groups of this round (has(base) holds)
+#pragma unroll
+        for (int q = 1; q < GPW; ++q)
+            if (has(base + q)) nq = q + 1;
         for (int c = 0; c < ncp; ++c) {
             const int e = min(64 * c + lane, EW - 1);  // past the array: re-read its last entry
             const int row_e = (e >> sub_shift) / GPW;  // = e / RW
@@ -191,7 +199,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     auto issue_w = [&](const int base) {
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-            if (base + q >= n_w) break;  // uniform across the wave
+            if (!has(base + q)) break;  // uniform across the wave
             const int g = g0 + wave + waves * (base + q);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
@@ -200,14 +208,14 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             }
         }
     };
-    // A wave may have no groups at all (n_w = 0: a partition with fewer groups than the
-    // workgroup has waves); it issues nothing and contributes zeros to the sum.
-    if (n_w > 0) {
+    // A wave may have no groups at all (a partition with fewer groups than the workgroup
+    // has waves); it issues nothing and contributes zeros to the sum.
+    if (has(0)) {
         issue_a(0);
         issue_sb(0);
         issue_w(0);
     }
-    for (int base = 0; base < n_w; base += GPW) {
+    for (int base = 0; has(base); base += GPW) {
         // Without the scheduling fences the compiler sinks each load next to its first use,
         // one memory round trip per load. The copies are invisible to the compiler, so
         // the wave waits for all of its loads itself before it reads the staging slots.
@@ -223,7 +231,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                 for (int u = 0; u < WV; ++u) wv[q][j][u] = wn[q][j][u];
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-            if (base + q >= n_w) break;
+            if (!has(base + q)) break;
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 sc[q][j] = sbw[(16 * j + r) * RW + (q << sub_shift) + sub_e];
@@ -238,7 +246,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         // Qwen3-4B projections at M = 1..64), and the whole next round goes out after the
         // MFMAs.
         constexpr bool kEarly = GPW == 1;
-        const bool more = base + GPW < n_w;  // uniform across the wave
+        const bool more = has(base + GPW);  // uniform across the wave
         if (kEarly && more) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             issue_sb(base + GPW);
@@ -247,7 +255,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < GPW; ++q) {
-            if (base + q >= n_w) break;  // uniform across the wave
+            if (!has(base + q)) break;  // uniform across the wave
             const char *As = stage + q * ABYTES;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -293,7 +301,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
 #pragma unroll
         for (int j = 0; j < NS; ++j) red4[((wave * MT + i) * NS + j) * 64 + lane] = acc[i][j];
     __syncthreads();
-    for (int t = threadIdx.x; t < MT * NS * 64; t += blockDim.x) {
+    for (int t = threadIdx.x; t < MT * NS * 64; t += (int)nt) {
         f32x4 sum = red4[t];
         for (int w = 1; w < waves; ++w) sum += red4[w * MT * NS * 64 + t];
         const int l = t & 63;
@@ -308,7 +316,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             // in one store, else pairs starting on an even column (tiles of a width that is
             // not a multiple of 4 start on any even column), else single elements
             const bool quad = vec_store && (n & 3) == 0 && n + 3 < n_end;
-            if (f32_part && gridDim.z > 1) {
+            if (f32_part && nz > 1) {
                 float *dst = static_cast<float *>(out) + e;
                 if (quad) {
                     *reinterpret_cast<float4 *>(dst) = make_float4(sum[0], sum[1], sum[2], sum[3]);

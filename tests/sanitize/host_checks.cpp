@@ -22,9 +22,9 @@
 namespace {
 int g_launches = 0;       // launches recorded since the last reset
 int g_last_split = -1;    // split of the last matmul launch
-// (bits, mt, ns, gpw, waves) of every small-M launch: printed at the end, checked by the test
-// against the configurations the kernel source instantiates
-std::set<std::tuple<int, int, int, int, int>> g_skinny_cfgs;
+// (bits, mt, ns, gpw, waves, staged rows) of every small-M launch: printed at the end, checked
+// by the test against the configurations the kernel source instantiates
+std::set<std::tuple<int, int, int, int, int, int>> g_skinny_cfgs;
 }  // namespace
 
 // Every global load the small-M kernel issues, its offsets computed as the kernel computes
@@ -66,7 +66,7 @@ void check_skinny_offsets(qmm_impl::WFormat fmt, int mt, int ns, int tw, int gpw
                                             if (n < 0 || n >= N || i4 < 0 || i4 >= row_u4) abort();
                                         }
                                 }
-                            for (int c = 0; c < 4 * mt; ++c)
+                            for (int c = 0; c < qmm_impl::skinny_rows(mt, ns, fmt.bits, M) / 4; ++c)
                                 for (int lane = 0; lane < 64; ++lane) {
                                     const int row = 4 * c + (lane >> 4);
                                     if (m_blk + 4 * c >= M) continue;  // copy not issued
@@ -102,8 +102,10 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int
     if (waves < 1 || waves > 16) abort();
     if (tw < 1 || tw > 16 * ns || (tw < 16 * ns && (ns != 1 || s != 1))) abort();  // narrowed: unsplit 16-column only
     if ((long long)(N + tw - 1) / tw > 65535) abort();  // grid x
-    if (M < 1 || skinny_lds_bytes(mt, ns, waves, gpw, fmt.sub()) > (size_t)kLdsPerCU) abort();
-    g_skinny_cfgs.insert(std::make_tuple(fmt.bits, mt, ns, gpw, waves));
+    const int rows = skinny_rows(mt, ns, fmt.bits, M);
+    if (M < 1 || (rows < 16 * mt && M > rows)) abort();
+    if (skinny_lds_bytes(mt, ns, waves, gpw, fmt.sub(), rows) > (size_t)kLdsPerCU) abort();
+    g_skinny_cfgs.insert(std::make_tuple(fmt.bits, mt, ns, gpw, waves, rows));
     check_skinny_offsets(fmt, mt, ns, tw, gpw, waves, M, N, K, s);
     ++g_launches;
     g_last_split = s;
@@ -353,8 +355,8 @@ int main()
                             EXPECT(rc == QMM_OK);
                         }
     for (const auto &c : g_skinny_cfgs)
-        printf("skinny config %d %d %d %d %d\n", std::get<0>(c), std::get<1>(c), std::get<2>(c), std::get<3>(c),
-               std::get<4>(c));
+        printf("skinny config %d %d %d %d %d %d\n", std::get<0>(c), std::get<1>(c), std::get<2>(c), std::get<3>(c),
+               std::get<4>(c), std::get<5>(c));
 
     if (failures) {
         fprintf(stderr, "%d host checks failed\n", failures);

@@ -787,6 +787,44 @@ def test_edge_shapes(M, N, K, s):
         check_tolerance(host_f64(C), ref, what="edge %dx%dx%d s=%d" % (M, N, K, ss))
 
 
+# Decode (up to 8 rows, 4-bit codes) stages 4 activation rows per group up to M = 4 and 8
+# rows up to M = 8 instead of 16, on 16-column tiles (narrowed when unsplit) and on 48-column
+# tiles (N above 8192 over more than 2^24 weights); every M from 1 to 9 (9: 16 rows again),
+# ragged N, splits with one, two and three groups per round, and near-equal partitions.
+DECODE_ROWS = [(M, 2560, 9728, (1, 4, 7)) for M in (1, 2, 3, 4, 5, 6, 7, 8, 9)] + \
+    [(M, 8200, 2560, (1, 3, 20)) for M in (1, 4, 5, 8)] + [(3, 1001, 1280, (1, 2, 10)), (6, 33, 384, (1, 3))]
+
+
+@pytest.mark.parametrize("M,N,K,splits", DECODE_ROWS)
+def test_decode_staged_rows(M, N, K, splits):
+    d = syn.w4a16_inputs(M, N, K, seed=7500 + M + N + K)
+    ref = oracle.qmm_w4a16(d["A"], d["Wq"], d["scale"], d["bias"], M, N, K)
+    dv = w4a16_device(d)
+    for ss in sorted(set(splits) | {0}):
+        say("decode rows M=%d N=%d K=%d s=%d" % (M, N, K, ss))
+        C = run_w4a16(dv, M, N, K, ss, guard=40)
+        check_tolerance(host_f64(C), ref, what="decode rows %dx%dx%d s=%d" % (M, N, K, ss))
+
+
+def test_decode_staged_rows_one_hot_exact():
+    """One-hot activation rows, A[m, k_m] = 1: C[m, n] = RNE_bf16(w[n, k_m]) exactly with 4 or
+    8 staged rows, on 16- and 48-column tiles (each output row reads only its own staged row)."""
+    for M, N, K in ((3, 2560, 2560), (8, 8200, 2560)):
+        d = syn.w4a16_inputs(M, N, K, seed=7600 + M)
+        ks = np.array([(37 * i + 5) % K for i in range(M)])
+        A = np.zeros((M, K), dtype=np.uint16)
+        A[np.arange(M), ks] = 0x3F80
+        d["A"] = A
+        say("decode rows one-hot M=%d N=%d" % (M, N))
+        C = run_w4a16(w4a16_device(d), M, N, K, 1, guard=40)
+        w = oracle.dequant_w4a16(d["Wq"], d["scale"], d["bias"], N, K)
+        expect = oracle.bf16_round_array(w[:, ks].T)
+        got = host_bits(C).copy()
+        got[got == 0x8000] = 0  # the sign of an exact zero is not part of the definition
+        expect[expect == 0x8000] = 0
+        assert np.array_equal(got, expect), (M, N)
+
+
 # Unsplit grids of 16-column small-M tiles with fewer tiles than CUs run narrower tiles of
 # ceil(N / (256 // row blocks)) columns: widths of 1 (one column per workgroup), 2, 4 (whole
 # 4-column stores), 10 and 12 (pairs), 11 (odd: pairs and single columns), ragged last tiles,

@@ -42,17 +42,22 @@ def test_host_code_under_sanitizers(tmp_path):
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "host checks ok" in r.stdout
     # every small-M configuration the host picked is one the kernel source instantiates
-    # (bits, mt, ns, gpw, at most MAXW waves)
+    # (bits, mt, ns, gpw, at most MAXW waves, staged rows: 16*mt for QMM_CFG)
     import re
     src = open(os.path.join(CSRC, "qmm_w4a16_skinny.hip")).read()
-    built = {tuple(int(x) for x in m) for m in re.findall(r"QMM_CFG\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+    built = {tuple(int(x) for x in m) + (16 * int(m[1]),)
+             for m in re.findall(r"QMM_CFG\((\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
+    built |= {tuple(int(x) for x in m)
+              for m in re.findall(r"QMM_CFGR\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)", src)}
     assert built
-    maxw = {c[:4]: c[4] for c in built}
+    maxw = {c[:4] + c[5:]: c[4] for c in built}
     picked = [tuple(int(x) for x in l.split()[2:]) for l in r.stdout.splitlines() if l.startswith("skinny config")]
     assert picked
-    for bits, mt, ns, gpw, waves in picked:
-        assert (bits, mt, ns, gpw) in maxw, ("no kernel instantiation for", bits, mt, ns, gpw)
-        assert waves <= maxw[(bits, mt, ns, gpw)], ("too many waves for", bits, mt, ns, gpw, waves)
+    assert any(rows < 16 * mt for _, mt, _, _, _, rows in picked)  # decode's compact staging is exercised
+    for bits, mt, ns, gpw, waves, rows in picked:
+        key = (bits, mt, ns, gpw, rows)
+        assert key in maxw, ("no kernel instantiation for", key)
+        assert waves <= maxw[key], ("too many waves for", key, waves)
 
 
 @needs_runtimes

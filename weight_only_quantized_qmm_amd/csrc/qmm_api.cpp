@@ -194,7 +194,9 @@ hipError_t dispatch_skinny(WFormat fmt, const W4A16Tile &tile, const void *A, co
                            hipStream_t st) {
     // the longest partition: ceil(G / s) blocks (near-equal partitions differ by at most one)
     const int G = K / kGroup;
-    const qmm_impl::SkinnyShape sh = qmm_impl::skinny_shape(tile.mt, tile.ns, (G + s - 1) / s, fmt.bits, fmt.sub());
+    const int rows = qmm_impl::skinny_rows(tile.mt, tile.ns, fmt.bits, M);
+    const qmm_impl::SkinnyShape sh =
+        qmm_impl::skinny_shape(tile.mt, tile.ns, (G + s - 1) / s, fmt.bits, fmt.sub(), rows);
     return qmm_impl::launch_w4a16_skinny(fmt, tile.mt, tile.ns, tile.tw, sh.gpw, sh.waves, A, Wq, scale, bias, out,
                                          f32_part, M, N, K, s, vec, st);
 }

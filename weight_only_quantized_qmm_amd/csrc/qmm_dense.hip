@@ -59,7 +59,11 @@ __device__ __forceinline__ void copy16(uint32_t lds_off, uint32_t voff, const vo
 }
 #pragma clang diagnostic pop
 
-constexpr int RING = 3;  // slots per operand: stage x in slot x % 3
+#ifndef QMM_DENSE_RING
+#define QMM_DENSE_RING 3
+#endif
+constexpr int RING = QMM_DENSE_RING;  // slots per operand: stage x in slot x % RING, RING - 1 stages ahead
+constexpr int AHEAD = RING - 1;
 
 struct DenseLds {
     char a[RING * SLOT];
@@ -192,20 +196,20 @@ dense_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, voi
     // the copies repeat it into a slot that is never read again, so every stage issues
     // NCOPY copies and the waits below are exact.
     const int nst = (c.k_end - c.k_begin + SK - 1) / SK;  // >= 1
-    issue(c, 0, 0);
-    issue(c, min(1, nst - 1), 1);
-    QMM_WAIT_VMCNT(GE::NCOPY);
+#pragma unroll
+    for (int x = 0; x < AHEAD; ++x) issue(c, min(x, nst - 1), x);
+    QMM_WAIT_VMCNT(GE::NCOPY * (AHEAD - 1));  // stage 0 landed
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    int slot = 0;  // st % 3
+    int slot = 0;  // st % RING
     for (int st = 0; st < nst; ++st) {
-        const int slot_issue = slot == 0 ? 2 : slot - 1;  // (st + 2) % 3: the slot stage st-1 used
-        issue(c, min(st + 2, nst - 1), slot_issue);
+        const int slot_issue = slot == 0 ? RING - 1 : slot - 1;  // (st + AHEAD) % RING: the slot stage st-1 used
+        issue(c, min(st + AHEAD, nst - 1), slot_issue);
         compute(c, L, slot, (c.k_end - (c.k_begin + SK * st)) < SK, acc);
-        QMM_WAIT_VMCNT(GE::NCOPY);  // the copies of stage st+1 landed; this stage's may remain
+        QMM_WAIT_VMCNT(GE::NCOPY * (AHEAD - 1));  // the copies of stage st+1 landed; later stages' may remain
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        slot = slot == 2 ? 0 : slot + 1;
+        slot = slot == RING - 1 ? 0 : slot + 1;
     }
     QMM_WAIT_VMCNT(0);  // no copy may still be writing LDS when the workgroup ends
 

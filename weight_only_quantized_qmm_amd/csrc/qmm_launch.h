@@ -45,35 +45,51 @@ inline bool format_supported(WFormat f)
 constexpr int kLdsPerCU = 160 * 1024;  // LDS bytes of one CU (and the most one workgroup may take)
 
 // Wave count and groups per load round of the SKINNY kernel for partitions of at most gpp groups
-// (128-value blocks). A wave stages a round's activations in LDS (4 KB per group and 16-row
-// tile) and its scale/bias entries (two dword arrays of 16*ns rows x gpw*sub entries, each
-// rounded up to 64); the workgroup's LDS is at most 160 KB.
+// (128-value blocks). A wave stages a round's activations in LDS (256 bytes per staged row and
+// group: 16 rows per 16-row tile, or only 4 or 8 with at most that many rows, see skinny_rows)
+// and its scale/bias entries (two dword arrays of 16*ns rows x gpw*sub entries, each rounded
+// up to 64); the workgroup's LDS is at most 160 KB.
 struct SkinnyShape {
     int waves;  // waves per workgroup, each taking every waves-th group of the partition
     int gpw;    // groups whose loads one wave issues together
 };
 
-inline size_t skinny_stage_bytes(int mt, int ns, int waves, int gpw, int sub)
+// Activation rows a wave stages per group. Decode (at most 8 rows, 4-bit codes, one 16-row
+// tile of 16 or 48 columns) stages only 4 or 8 rows, and the MFMA's 16 operand rows read
+// them cyclically (rows past M reach only output rows that are never stored): a quarter or
+// half of the LDS per group, which leaves room for the waves' fp32 tiles beside the staging
+// memory (A/B on MI355X, same waves and groups per round: down at M = 1 and 4, gate, up, q,
+// k, v and o at M = 1..8 3-4.5 % faster, down at M = 8 unchanged). More groups per round
+// in the freed LDS (4..8 on 16-column tiles, 3 on 48-column ones) were 2-7 % slower.
+inline int skinny_rows(int mt, int ns, int bits, int M)
 {
+    if (bits == 4 && mt == 1 && (ns == 1 || ns == 3) && M <= 8) return M <= 4 ? 4 : 8;
+    return 16 * mt;
+}
+
+inline size_t skinny_stage_bytes(int mt, int ns, int waves, int gpw, int sub, int rows)
+{
+    (void)mt;
     const size_t ew = (size_t)16 * ns * gpw * sub;
-    return (size_t)waves * gpw * mt * 4096 + (size_t)waves * 2 * ((ew + 63) & ~(size_t)63) * 4;
+    return (size_t)waves * gpw * rows * 256 + (size_t)waves * 2 * ((ew + 63) & ~(size_t)63) * 4;
 }
 inline size_t skinny_sum_bytes(int mt, int ns, int waves) { return (size_t)waves * mt * ns * 1024; }
 // The least LDS a configuration needs: the waves' fp32 tiles reuse the staging memory once
 // every wave has left it. (When staging and tiles fit side by side, the kernel keeps them
 // apart instead, so that a wave can store its tile without waiting for the others.)
-inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub)
+inline size_t skinny_lds_bytes(int mt, int ns, int waves, int gpw, int sub, int rows)
 {
-    const size_t stage = skinny_stage_bytes(mt, ns, waves, gpw, sub);
+    const size_t stage = skinny_stage_bytes(mt, ns, waves, gpw, sub, rows);
     const size_t sums = skinny_sum_bytes(mt, ns, waves);
     return stage > sums ? stage : sums;
 }
 
-inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4, int sub = 1)
+inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits, int sub, int rows)
 {
     // 16-column tiles: up to 12 waves; 32-column tiles of one 16-row block: 16; else 8.
     // Groups per round: up to 3, 2 for 48- and 64-column tiles of 16 or 32 rows, 1 for them
-    // with 64 rows (config sweeps of the Qwen3-4B projections at M = 16..64 on MI355X).
+    // with 64 rows (config sweeps of the Qwen3-4B projections at M = 16..64 on MI355X; the
+    // same limits with decode's fewer staged rows, see skinny_rows).
     const int max_waves = ns == 1 ? 12 : (mt == 1 && ns == 2) ? 16 : 8;
     int max_gpw = ns >= 3 ? (mt == 4 ? 1 : 2) : (mt == 4 ? 2 : 3);
     if (bits == 8 && max_gpw > 1) max_gpw -= 1;  // twice the weight registers per group
@@ -81,7 +97,7 @@ inline SkinnyShape skinny_shape(int mt, int ns, int gpp, int bits = 4, int sub =
     sh.waves = gpp < max_waves ? gpp : max_waves;
     const int per_wave = (gpp + sh.waves - 1) / sh.waves;
     sh.gpw = per_wave < max_gpw ? per_wave : max_gpw;
-    while (skinny_lds_bytes(mt, ns, sh.waves, sh.gpw, sub) > (size_t)kLdsPerCU) {
+    while (skinny_lds_bytes(mt, ns, sh.waves, sh.gpw, sub, rows) > (size_t)kLdsPerCU) {
         if (sh.gpw > 1) --sh.gpw;
         else --sh.waves;
     }

@@ -40,7 +40,8 @@
 // The 16x16x32 MFMA takes the weights as its first operand, so a lane's result is
 // four consecutive output columns of one row.
 //
-// LDS: wave w's staging slots are [GPW][16*MT rows][256 bytes] at w*GPW*MT*4 KB; chunk c
+// LDS: wave w's staging slots are [GPW][RS rows][256 bytes] at w*GPW*RS*256 (RS = 16*MT, or
+// 4 or 8 for decode, whose 16 operand rows then read the staged rows cyclically); chunk c
 // (16 bytes) of row r is stored at chunk c ^ (r % 16), so the 16 rows that one 16-lane
 // phase of an operand read touches fall on distinct banks. The waves' scale and bias
 // arrays follow the staging slots. The waves' fp32 tiles for the cross-wave sum follow
@@ -77,7 +78,7 @@ __device__ __forceinline__ void copy2(uint32_t lds_off, uint32_t voff, const voi
 }
 #pragma clang diagnostic pop
 
-template <int BITS, int MT, int NS, int GPW, int MAXW>
+template <int BITS, int MT, int NS, int GPW, int MAXW, int RS>
 __global__ void __launch_bounds__(64 * MAXW)
 w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__ Wq,
                     const uint16_t *__restrict__ scale, const uint16_t *__restrict__ bias,
@@ -85,7 +86,11 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
                     int f32_part, int sum_off)
 {
     constexpr int WV = BITS / 4;  // 16-byte weight loads per lane, group and 16-column subtile
-    constexpr int ABYTES = MT * 16 * 256;  // one staged group of activations: 16*MT rows x 128 values
+    // RS staged activation rows per group (16*MT, or 4 or 8 for decode: MT = 1, M <= RS); one
+    // staged group is RS rows x 128 values
+    static_assert(RS == 16 * MT || (MT == 1 && (RS == 4 || RS == 8)), "staged rows");
+    constexpr int ABYTES = RS * 256;
+    constexpr int NCPY = RS / 4;  // activation copies per group
     extern __shared__ __attribute__((aligned(1024))) char smem[];  // staging, then [WAVES][MT][NS][64] float4
     // Fetch every argument (and the grid's partition count and workgroup size) up front,
     // in one batch of scalar loads: left to itself the compiler loads the pointers after
@@ -130,9 +135,9 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     // past M is not issued at all, and its staging rows keep whatever they held. An MFMA
     // output row depends only on its own activation row, so such rows reach only output rows
     // past M, which are never stored (decode with M = 1..8 saves up to 15 of 16 copies).
-    uint32_t a_voff[4 * MT];
+    uint32_t a_voff[NCPY];
 #pragma unroll
-    for (int c = 0; c < 4 * MT; ++c) {
+    for (int c = 0; c < NCPY; ++c) {
         const int row = 4 * c + (lane >> 4);
         const int m = min(m_blk + row, M - 1);
         a_voff[c] = (uint32_t)m * (uint32_t)K * 2u + 16u * (uint32_t)((lane & 15) ^ (row & 15));
@@ -140,10 +145,13 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     char *stage = smem + (size_t)wave * GPW * ABYTES;
     const uint32_t stage_lds = lds_addr(stage);
     // Operand reads: lane (r, slot), step t, row tile i: staging row 16i + r, chunk 4*slot + t
-    // (values 32*slot + 8t .. +7 of the group).
+    // (values 32*slot + 8t .. +7 of the group). With fewer staged rows (RS < 16) operand row r
+    // reads staging row r % RS: rows from RS on are copies that reach only output rows past
+    // M, never stored.
+    const int rr = RS < 16 ? (r & (RS - 1)) : r;
     uint32_t a_rd[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) a_rd[t] = (uint32_t)(r * 256 + 16 * ((4 * slot + t) ^ r));
+    for (int t = 0; t < 4; ++t) a_rd[t] = (uint32_t)(rr * 256 + 16 * ((4 * slot + t) ^ rr));
 
     // Scale/bias: each round also copies, next to its activations, the scale and bias
     // entries its groups need into the wave's own dword arrays [16*NS rows][GPW*SUB] (SUB =
@@ -173,7 +181,7 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
             if (!has(base + q)) break;  // uniform across the wave
             const char *Ag = Abase + (size_t)(g0 + wave + waves * (base + q)) * 256;
 #pragma unroll
-            for (int c = 0; c < 4 * MT; ++c)
+            for (int c = 0; c < NCPY; ++c)
                 if (m_blk + 4 * c < M)  // a copy whose four rows all lie past M is skipped (see below)
                     copy16(stage_lds + (uint32_t)(q * ABYTES + 1024 * c), a_voff[c], Ag);
         }
@@ -356,24 +364,25 @@ w4a16_skinny_kernel(const uint16_t *__restrict__ A, const uint32_t *__restrict__
     }
 }
 
-template <int BITS, int MT, int NS, int GPW, int MAXW>
+template <int BITS, int MT, int NS, int GPW, int MAXW, int RS>
 hipError_t launch_cfg(const void *A, const void *Wq, const void *scale, const void *bias, void *out, bool f32_part,
                       int M, int N, int K, int tw, int s, int sub_shift, int waves, bool vec_store,
                       hipStream_t stream)
 {
     if (tw < 1 || tw > 16 * NS) return hipErrorInvalidValue;
     const dim3 grid((N + tw - 1) / tw, (M + 16 * MT - 1) / (16 * MT), s);
-    const size_t stage = qmm_impl::skinny_stage_bytes(MT, NS, waves, GPW, 1 << sub_shift);
+    const size_t stage = qmm_impl::skinny_stage_bytes(MT, NS, waves, GPW, 1 << sub_shift, RS);
     const size_t sums = qmm_impl::skinny_sum_bytes(MT, NS, waves);
     // the waves' tiles beside the staging memory when both fit (16-byte aligned: stage is a
     // multiple of 256), else over it
     const bool apart = stage + sums <= (size_t)qmm_impl::kLdsPerCU;
-    const size_t lds = apart ? stage + sums : qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift);
+    const size_t lds = apart ? stage + sums : qmm_impl::skinny_lds_bytes(MT, NS, waves, GPW, 1 << sub_shift, RS);
+    if (RS < 16 && M > RS) return hipErrorInvalidValue;
     if (waves > MAXW || lds > (size_t)qmm_impl::kLdsPerCU) return hipErrorInvalidValue;
     // the activation copies take 32-bit byte offsets into A
     if ((size_t)M * (size_t)K * 2 >= ((size_t)1 << 32)) return hipErrorInvalidValue;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW>), grid, dim3(64 * waves), lds, stream,
+    hipLaunchKernelGGL((w4a16_skinny_kernel<BITS, MT, NS, GPW, MAXW, RS>), grid, dim3(64 * waves), lds, stream,
                        static_cast<const uint16_t *>(A), static_cast<const uint32_t *>(Wq),
                        static_cast<const uint16_t *>(scale), static_cast<const uint16_t *>(bias),
                        out, M, N, K, tw, sub_shift, vec_store ? 1 : 0, f32_part ? 1 : 0, apart ? (int)stage : 0);
@@ -389,17 +398,20 @@ namespace qmm_impl {
 // 32-column tiles (ns 2) with up to 16 waves (mt 1) or 8 (mt 2, 4) and gpw <= 3, 3, 2;
 // 48- and 64-column tiles (ns 3, 4) with up to 8 waves and gpw <= 2, 2, 1 for mt 1, 2, 4 (register
 // budgets of 128 VGPRs per lane at 16 waves, 256 at 8). 8-bit codes take one group less per
-// round where the 4-bit limit is above one.
+// round where the 4-bit limit is above one. Decode with 4-bit codes on 16- and 48-column
+// tiles of one 16-row block stages 4 or 8 activation rows per group instead of 16 (skinny_rows).
 hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int waves, const void *A,
                                const void *Wq, const void *scale, const void *bias, void *out, bool f32_part, int M,
                                int N, int K, int s, bool vec_store, hipStream_t stream)
 {
     if (waves < 1 || waves > MAX_WAVES || !format_supported(fmt)) return hipErrorInvalidValue;
     const int sub_shift = fmt.group == 128 ? 0 : fmt.group == 64 ? 1 : 2;
-#define QMM_CFG(B_, MT_, NS_, GPW_, MAXW_)                                                                     \
-    if (fmt.bits == B_ && mt == MT_ && ns == NS_ && gpw == GPW_)                                               \
-        return launch_cfg<B_, MT_, NS_, GPW_, MAXW_>(A, Wq, scale, bias, out, f32_part, M, N, K, tw, s,         \
-                                                     sub_shift, waves, vec_store, stream);
+    const int rows = skinny_rows(mt, ns, fmt.bits, M);
+#define QMM_CFGR(B_, MT_, NS_, GPW_, MAXW_, RS_)                                                               \
+    if (fmt.bits == B_ && mt == MT_ && ns == NS_ && gpw == GPW_ && rows == RS_)                                \
+        return launch_cfg<B_, MT_, NS_, GPW_, MAXW_, RS_>(A, Wq, scale, bias, out, f32_part, M, N, K, tw, s,    \
+                                                          sub_shift, waves, vec_store, stream);
+#define QMM_CFG(B_, MT_, NS_, GPW_, MAXW_) QMM_CFGR(B_, MT_, NS_, GPW_, MAXW_, 16 * MT_)
     QMM_CFG(4, 1, 1, 1, 16) QMM_CFG(4, 1, 1, 2, 16) QMM_CFG(4, 1, 1, 3, 16)
     QMM_CFG(4, 1, 2, 1, 16) QMM_CFG(4, 1, 2, 2, 16) QMM_CFG(4, 1, 2, 3, 16)
     QMM_CFG(4, 2, 2, 1, 8) QMM_CFG(4, 2, 2, 2, 8) QMM_CFG(4, 2, 2, 3, 8)
@@ -420,7 +432,13 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int
     QMM_CFG(8, 2, 4, 1, 8)
     QMM_CFG(8, 4, 4, 1, 8)
     QMM_CFG(8, 1, 3, 1, 8) QMM_CFG(8, 2, 3, 1, 8) QMM_CFG(8, 4, 3, 1, 8)
+    // decode: 4 or 8 staged activation rows (skinny_rows)
+    QMM_CFGR(4, 1, 1, 1, 16, 4) QMM_CFGR(4, 1, 1, 2, 16, 4) QMM_CFGR(4, 1, 1, 3, 16, 4)
+    QMM_CFGR(4, 1, 1, 1, 16, 8) QMM_CFGR(4, 1, 1, 2, 16, 8) QMM_CFGR(4, 1, 1, 3, 16, 8)
+    QMM_CFGR(4, 1, 3, 1, 8, 4) QMM_CFGR(4, 1, 3, 2, 8, 4)
+    QMM_CFGR(4, 1, 3, 1, 8, 8) QMM_CFGR(4, 1, 3, 2, 8, 8)
 #undef QMM_CFG
+#undef QMM_CFGR
     return hipErrorInvalidValue;
 }
 

@@ -59,10 +59,9 @@ __device__ __forceinline__ void copy16(uint32_t lds_off, uint32_t voff, const vo
 }
 #pragma clang diagnostic pop
 
-#ifndef QMM_DENSE_RING
-#define QMM_DENSE_RING 3
-#endif
-constexpr int RING = QMM_DENSE_RING;  // slots per operand: stage x in slot x % RING, RING - 1 stages ahead
+// Slots per operand: stage x in slot x % RING, copied RING - 1 stages ahead. Four or five
+// slots (three or four stages in flight, 128 or 160 KB) were no faster on MI355X (cfg3, every s).
+constexpr int RING = 3;
 constexpr int AHEAD = RING - 1;
 
 struct DenseLds {

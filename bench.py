@@ -415,6 +415,9 @@ def formats_table(torch, syn, q):
 
 
 SMALL_KERNEL = "w4a16_skinny_kernel"
+GEMV_KERNEL = "gemv_kernel"
+DECODE_WORKLOAD = ("each decode shape (down, gate at M = 1, 4, 8) through the plan and through the matrix-vector "
+                   "entry point, second of two rounds")
 SMALL_WORKLOAD = ("the plan's call (matmul kernel, and the merge when split) of every sweep shape the small-M "
                   "kernel runs, second of two rounds")
 
@@ -439,6 +442,20 @@ def pmc_run(kind="large"):
         for sh in shapes:
             sh.call_pass1(0)
         what = "%d launches of %s" % (len(shapes), DOMINANT_KERNEL)
+    elif kind == "decode":
+        # two rounds over two buffer sets (the summary takes the second): each decode shape
+        # through the plan (the small-M kernel, unsplit) and through the matrix-vector kernel
+        shapes = [Shape(n, M, N, K, i + 100, 2, torch, syn, q) for n, M, N, K, i in syn.decode_sweep()]
+        for r in range(2):
+            for sh in shapes:
+                sh.call(r, 0)
+                torch.cuda.synchronize()
+                gs = q.qmm_gemv_min_split(sh.M, sh.K)
+                A, W, S, B = sh.sets[r]
+                ws = torch.empty(max(2 * gs * sh.M * sh.N, 256), dtype=torch.uint8, device="cuda")
+                q.qmm_w4a16_gemv(A, W, S, B, sh.C, sh.M, sh.N, sh.K, gs, ws if gs > 1 else None)
+                torch.cuda.synchronize()
+        what = "two rounds of %d decode shapes on %s and %s" % (len(shapes), SMALL_KERNEL, GEMV_KERNEL)
     else:
         # two rounds over two buffer sets: the second reads cold buffers with the clock up;
         # the summary takes its launches
@@ -524,6 +541,47 @@ def summarize_small_pmc(fetch_dir, write_dir, trace_dir, commands):
               "kernel source digest: %s" % source_digest([os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
                                                           for f in ("qmm_w4a16_skinny.hip", "qmm_api.cpp",
                                                                     "qmm_launch.h", "qmm_device.h")])]
+    print("\n".join(lines))
+
+
+def summarize_decode_pmc(fetch_dir, write_dir, trace_dir, commands):
+    """Text summary of the decode shapes' HBM traffic on both paths (the plan's small-M kernel
+    and the matrix-vector kernel): FETCH_SIZE and WRITE_SIZE per launch (scaled by the copy
+    kernel), the kernel-trace duration, the achieved HBM rate and the weight-read rate
+    (packed weights + scale/bias over the launch's duration) as a fraction of 8 TB/s."""
+    fetch = _counter_rows(fetch_dir, ["FETCH_SIZE"])["FETCH_SIZE"]
+    write = _counter_rows(write_dir, ["WRITE_SIZE"])["WRITE_SIZE"]
+    trace = _trace_durations(trace_dir)
+    pick = lambda rows, key: [(k, v) for _, k, v in rows if key(k)]
+    cf = [v for _, v in pick(fetch, lambda k: "calib_copy" in k)]
+    cw = [v for _, v in pick(write, lambda k: "calib_copy" in k)]
+    f_scale, w_scale = COPY_BYTES / (cf[0] * 1024.0), COPY_BYTES / (cw[0] * 1024.0)
+    import qmm_synth as syn
+    shapes = syn.decode_sweep()
+    mine = lambda k: SMALL_KERNEL in k or GEMV_KERNEL in k
+    # per shape and round: the plan's launch, then the matrix-vector launch (both unsplit here)
+    df, dw, dt = [pick(rows, mine)[2 * len(shapes):] for rows in (fetch, write, trace)]
+    lines = ["# HBM traffic of the decode shapes on %s and %s (%s) from rocprofv3 counters"
+             % (SMALL_KERNEL, GEMV_KERNEL, DECODE_WORKLOAD), "commands:"] + ["  " + c for c in commands] + [
+        "copy kernel: %d bytes read and written; FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB" % (COPY_BYTES, cf[0], cw[0]),
+        "fetch scale: %.4f" % f_scale, "write scale: %.4f" % w_scale,
+        "bytes = scaled FETCH + WRITE; algorithmic = packed weights + scale/bias + A + C; weight = packed weights +",
+        "scale/bias; us = kernel-trace duration of the same launch (the merge of a split matrix-vector call not",
+        "included); weight frac = weight bytes / us / 8 TB/s",
+        "%-5s %2s %5s %5s %-7s %10s %10s %10s %6s %7s %8s %8s" % ("proj", "M", "N", "K", "path", "fetch B", "write B",
+                                                                "algo B", "ratio", "us", "HBM GB/s", "wt frac")]
+    for i, (n, M, N, K, _) in enumerate(shapes):
+        wbytes = N * K // 2 + N * (K // 128) * 4
+        a = algorithmic_bytes(M, N, K)
+        for j, path in enumerate(("plan", "matvec")):
+            (kf, fv), (_, wv), (kt, ns) = df[2 * i + j], dw[2 * i + j], dt[2 * i + j]
+            assert (GEMV_KERNEL in kf) == (path == "matvec") and (GEMV_KERNEL in kt) == (path == "matvec"), (kf, kt)
+            fb, wb = fv * 1024 * f_scale, wv * 1024 * w_scale
+            lines.append("%-5s %2d %5d %5d %-7s %10.4g %10.4g %10.4g %6.2f %7.2f %8.1f %8.3f" % (
+                n, M, N, K, path, fb, wb, a, (fb + wb) / a, ns / 1e3, (fb + wb) / ns, wbytes / ns / (HBM_PEAK / 1e9)))
+    lines.append("kernel source digest: %s" % source_digest(
+        [os.path.join(ROOT, "weight_only_quantized_qmm_amd", "csrc", f)
+         for f in ("qmm_w4a16_skinny.hip", "qmm_gemv.hip", "qmm_api.cpp", "qmm_launch.h", "qmm_device.h")]))
     print("\n".join(lines))
 
 
@@ -712,11 +770,13 @@ def parse():
                     help="file that receives the per-shape and secondary tables (JSON)")
     ap.add_argument("--dominant-only", action="store_true",
                     help="only the dominant-kernel roofline measurement (the profiled command)")
-    ap.add_argument("--pmc-run", nargs="?", const="large", choices=("large", "small"),
+    ap.add_argument("--pmc-run", nargs="?", const="large", choices=("large", "small", "decode"),
                     help="only the workload of the profiler counter passes (large: the M = 2048 first passes; "
                          "small: the small-M kernel's shapes)")
     ap.add_argument("--summarize-small-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
                     help="print the small-M kernel's traffic summary of two --pmc passes and a kernel trace")
+    ap.add_argument("--summarize-decode-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR"),
+                    help="print the decode shapes' traffic summary (both paths) of two --pmc passes and a kernel trace")
     ap.add_argument("--summarize-lds", metavar="DIR",
                     help="print the LDS-activity summary of one --pmc pass (LDS_COUNTERS) over --dominant-only")
     ap.add_argument("--summarize-mix", nargs=2, metavar=("DIR1", "DIR2"),
@@ -884,6 +944,9 @@ def main():
         return
     if args.summarize_small_pmc:
         summarize_small_pmc(*args.summarize_small_pmc, args.pmc_commands)
+        return
+    if args.summarize_decode_pmc:
+        summarize_decode_pmc(*args.summarize_decode_pmc, args.pmc_commands)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], args.pmc_commands, args.summarize_trace[1], args.bench_avg_us)

@@ -61,3 +61,41 @@ def test_more_than_one_gpu_is_refused():
     import sys
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_decode_traffic_summary(tmp_path, capsys):
+    """The decode counter summary pairs each shape's second-round launches (plan, then
+    matrix-vector) with its counters and trace, scales the bytes by the copy kernel and
+    states the weight-read fraction: a synthetic run with known values."""
+    import qmm_synth as syn
+    shapes = syn.decode_sweep()
+    names = []
+    for _ in range(2):
+        for _ in shapes:
+            names += ["w4a16_skinny_kernel<4, 1, 1, 3, 16, 4>", "gemv_kernel<1, 2, 2, 2, 5>", "reduce_vec8"]
+    names.append("calib_copy_kernel")
+    kib = 1000.0  # every matmul launch: 1000 KiB fetched, 10 KiB written; the copy: half its bytes fetched
+    for d, counter, vals in (("f", "FETCH_SIZE", (kib, bench.COPY_BYTES / 2048.0)),
+                             ("w", "WRITE_SIZE", (10.0, bench.COPY_BYTES / 1024.0))):
+        (tmp_path / d).mkdir()
+        rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        for i, k in enumerate(names):
+            rows.append('%d,"%s",%s,%r' % (i + 1, k, counter, vals[1] if "calib_copy" in k else vals[0]))
+        (tmp_path / d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    (tmp_path / "t").mkdir()
+    rows = ["Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp"]
+    for i, k in enumerate(names):
+        rows.append('%d,"%s",%d,%d' % (i + 1, k, 1000 * i, 1000 * i + 5000))  # 5 us each
+    (tmp_path / "t" / "run_kernel_trace.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_decode_pmc(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "t"), ["cmd"])
+    out = capsys.readouterr().out.splitlines()
+    assert "fetch scale: 2.0000" in out and "write scale: 1.0000" in out
+    body = [l.split() for l in out if l.split() and l.split()[0] in ("down", "gate")]
+    assert len(body) == 2 * len(shapes)
+    for (name, M, N, K, _), plan, mv in zip(shapes, body[0::2], body[1::2]):
+        assert plan[4] == "plan" and mv[4] == "matvec" and plan[:4] == [name, str(M), str(N), str(K)]
+        b = 2 * kib * 1024 + 10 * 1024
+        assert abs(float(plan[5]) - 2 * kib * 1024) / b < 1e-3 and abs(float(plan[9]) - 5.0) < 1e-9
+        assert abs(float(plan[10]) - b / 5000) < 0.1  # GB/s = bytes per ns
+        wbytes = N * K // 2 + N * (K // 128) * 4
+        assert abs(float(plan[11]) - wbytes / 5000 / 8000) < 1e-3

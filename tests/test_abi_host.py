@@ -119,10 +119,10 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
     else:  # the page's rule over the kernel's tile without its divisor step (near-equal
         # partitions); partitions of at least 2048 values up to M = 32
         # 16-column tiles for up to 32 rows over at most 2^24 weights (and for up to 8 rows
-        # with at most 4096 columns); else 32 columns while
+        # with at most 4096 columns, and up to 4 rows at any width); else 32 columns while
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
         rows = -(-M // plan.block_m)
-        if M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096)):
+        if M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096) or M <= 4):
             assert plan.tile_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:
             assert plan.tile_n == 32

@@ -788,8 +788,9 @@ def test_edge_shapes(M, N, K, s):
 
 
 # Decode (up to 8 rows, 4-bit codes) stages 4 activation rows per group up to M = 4 and 8
-# rows up to M = 8 instead of 16, on 16-column tiles (narrowed when unsplit) and on 48-column
-# tiles (N above 8192 over more than 2^24 weights); every M from 1 to 9 (9: 16 rows again),
+# rows up to M = 8 instead of 16, on 16-column tiles (narrowed when unsplit; up to 4 rows at
+# any N) and on 48-column tiles (5 to 8 rows, N above 8192 over more than 2^24 weights);
+# every M from 1 to 9 (9: 16 rows again),
 # ragged N, splits with one, two and three groups per round, and near-equal partitions.
 DECODE_ROWS = [(M, 2560, 9728, (1, 4, 7)) for M in (1, 2, 3, 4, 5, 6, 7, 8, 9)] + \
     [(M, 8200, 2560, (1, 3, 20)) for M in (1, 4, 5, 8)] + [(3, 1001, 1280, (1, 2, 10)), (6, 33, 384, (1, 3))]

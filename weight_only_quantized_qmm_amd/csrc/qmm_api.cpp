@@ -153,8 +153,11 @@ W4A16Tile w4a16_tile(int M, int N, int K, int s) {
         // to 8 rows) also over more weights while those tiles fit one round of workgroups
         // (N <= 4096): the long reduction then runs unsplit instead of in split 48-column
         // tiles plus a second pass (down at M = 1, 4, 8 on MI355X: 8.6, 9.2, 10.2 us against
-        // 10.3, 10.6, 10.9).
-        if (M <= 32 && ((long long)N * K <= (1LL << 24) || (M <= 8 && N <= 16 * kCUs))) {
+        // 10.3, 10.6, 10.9). Up to 4 rows at any N: their staging (4 rows per group) is small
+        // enough for two or three workgroups per CU (gate at M = 1 and 4 on 608 16-column
+        // tiles: 6.67 and 6.65 us against 6.90 and 7.01 on 203 48-column tiles; at M = 8,
+        // with 8 staged rows, 7.95 against 7.18).
+        if (M <= 32 && ((long long)N * K <= (1LL << 24) || (M <= 8 && N <= 16 * kCUs) || M <= 4)) {
             t.ns = 1;
             return narrow_skinny(t, M, N, s);
         }

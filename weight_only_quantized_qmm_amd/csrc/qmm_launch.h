@@ -63,7 +63,8 @@ struct SkinnyShape {
 // in the freed LDS (4..8 on 16-column tiles, 3 on 48-column ones) were 2-7 % slower.
 inline int skinny_rows(int mt, int ns, int bits, int M)
 {
-    if (bits == 4 && mt == 1 && (ns == 1 || ns == 3) && M <= 8) return M <= 4 ? 4 : 8;
+    if (bits == 4 && mt == 1 && ns == 1 && M <= 8) return M <= 4 ? 4 : 8;
+    if (bits == 4 && mt == 1 && ns == 3 && M <= 8) return 8;  // 5..8 rows: up to 4 take 16-column tiles
     return 16 * mt;
 }
 

@@ -435,7 +435,6 @@ hipError_t launch_w4a16_skinny(WFormat fmt, int mt, int ns, int tw, int gpw, int
     // decode: 4 or 8 staged activation rows (skinny_rows)
     QMM_CFGR(4, 1, 1, 1, 16, 4) QMM_CFGR(4, 1, 1, 2, 16, 4) QMM_CFGR(4, 1, 1, 3, 16, 4)
     QMM_CFGR(4, 1, 1, 1, 16, 8) QMM_CFGR(4, 1, 1, 2, 16, 8) QMM_CFGR(4, 1, 1, 3, 16, 8)
-    QMM_CFGR(4, 1, 3, 1, 8, 4) QMM_CFGR(4, 1, 3, 2, 8, 4)
     QMM_CFGR(4, 1, 3, 1, 8, 8) QMM_CFGR(4, 1, 3, 2, 8, 8)
 #undef QMM_CFG
 #undef QMM_CFGR

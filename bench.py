@@ -873,6 +873,30 @@ def time_graph(torch, g, reps=5, warm_s=0.03):
     return ts[len(ts) // 2]
 
 
+def time_graphs_interleaved(torch, graphs, reps=7, warm_s=0.03):
+    """Median seconds of one replay of each graph, the graphs replayed in turn (A, B, A, B, ...)
+    after warm-up replays of all of them, so that a comparison between them sees the same
+    clock and thermal state (timed one after the other, a few-per-cent drift between the
+    two runs can reverse a few-per-cent difference)."""
+    t0 = time.perf_counter()
+    while True:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= warm_s:
+            break
+    ts = [[] for _ in graphs]
+    for _ in range(reps):
+        for i, g in enumerate(graphs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            ts[i].append(e0.elapsed_time(e1) / 1e3)
+    return [sorted(t)[len(t) // 2] for t in ts]
+
+
 def per_shape(torch, syn, q, name, M, N, K, idx, fmt=None, f32p=False, unsplit=True):
     """Per-call seconds of the policy split and of the unsplit control over >= 1 GiB of rotation."""
     probe = Shape(name, M, N, K, idx, 1, torch, syn, q, fmt, f32p)
@@ -880,10 +904,12 @@ def per_shape(torch, syn, q, name, M, N, K, idx, fmt=None, f32p=False, unsplit=T
     probe.free()
     sh = Shape(name, M, N, K, idx, R, torch, syn, q, fmt, f32p)
     out = {}
-    for s in ([0, 1] if sh.s > 1 and unsplit else [0] if sh.s > 1 else [1]):
-        g = graph_of(torch, lambda: [sh.call(r, s) for r in range(R)])
-        out[s] = time_graph(torch, g) / R
-        del g
+    splits = [0, 1] if sh.s > 1 and unsplit else [0] if sh.s > 1 else [1]
+    # the policy's split and the unsplit control replayed in turn (time_graphs_interleaved)
+    gs = [graph_of(torch, lambda s=s: [sh.call(r, s) for r in range(R)]) for s in splits]
+    for s, t in zip(splits, time_graphs_interleaved(torch, gs)):
+        out[s] = t / R
+    del gs
     if sh.s == 1:
         out[0] = out[1]
     out.setdefault(1, None)

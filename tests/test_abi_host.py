@@ -122,7 +122,10 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         # with at most 4096 columns, and up to 4 rows at any width); else 32 columns while
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
         rows = -(-M // plan.block_m)
-        if M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096) or M <= 4):
+        one_round_16 = M <= 64 and -(-M // 16) * -(-N // 16) <= 256 and N * K <= 1 << 24
+        if one_round_16:  # narrow projections: 16-row, 16-column tiles in one round
+            assert plan.block_m == 16 and plan.tile_n == 16
+        elif M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096) or M <= 4):
             assert plan.tile_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:
             assert plan.tile_n == 32

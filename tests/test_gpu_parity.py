@@ -828,9 +828,10 @@ def test_decode_staged_rows_one_hot_exact():
 
 # Unsplit grids of 16-column small-M tiles with fewer tiles than CUs run narrower tiles of
 # ceil(N / (256 // row blocks)) columns: widths of 1 (one column per workgroup), 2, 4 (whole
-# 4-column stores), 10 and 12 (pairs), 11 (odd: pairs and single columns), ragged last tiles,
-# and a 256-tile grid that is left as it is.
-NARROW = [(1, 1, 256, 1), (5, 40, 384, 1), (16, 300, 512, 2), (29, 1000, 640, 4), (7, 2500, 9728, 10),
+# 4-column stores), 8 (two 16-row blocks, the second ragged), 10 and 12 (pairs), 11 (odd:
+# pairs and single columns), ragged last tiles, and a 256-tile grid that is left as it is.
+NARROW = [(1, 1, 256, 1), (5, 40, 384, 1), (16, 300, 512, 2), (13, 1000, 640, 4), (29, 1000, 640, 8),
+          (7, 2500, 9728, 10),
           (32, 2561, 1024, 11), (3, 3000, 1280, 12), (20, 4095, 256, 16)]
 
 

@@ -145,6 +145,17 @@ W4A16Tile w4a16_tile(int M, int N, int K, int s) {
     t.tw = 0;
     if (M <= 64 || (M <= 128 && (long long)N * K <= (1LL << 24))) {
         t.kind = qmm_impl::W4A16_SKINNY;
+        // Narrow projections up to 64 rows whose 16-row, 16-column tiles fit one round of
+        // workgroups (k and v at M = 17..64): 16-row tiles, so that each workgroup reads 16
+        // rows of A instead of all M, unsplit (no second pass). A/B on MI355X: k and v at
+        // M = 24, 32, 48, 64 4.83, 5.10, 5.17, 5.07 us against 5.68, 6.07, 7.64, 7.96 on the
+        // 32- or 64-row tiles (split at M = 48 and 64); with two rounds of such tiles (q and
+        // o at M = 32, k at M = 128) 0-30 % slower, so only one round.
+        if (M <= 64 && ceil_div(M, 16) * ceil_div(N, 16) <= kCUs && (long long)N * K <= (1LL << 24)) {
+            t.mt = 1;
+            t.ns = 1;
+            return narrow_skinny(t, M, N, s);
+        }
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         // Up to 32 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
         // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o on MI355X:

@@ -123,8 +123,12 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         # they fit one workgroup per CU over K < 8192, else 48 when those fit, else 64
         rows = -(-M // plan.block_m)
         one_round_16 = M <= 64 and -(-M // 16) * -(-N // 16) <= 256 and N * K <= 1 << 24
+        t64 = -(-M // 16) * -(-N // 64)
+        one_round_64 = M <= 64 and N * K <= 1 << 24 and 3 * 256 <= 4 * t64 <= 4 * 256
         if one_round_16:  # narrow projections: 16-row, 16-column tiles in one round
             assert plan.block_m == 16 and plan.tile_n == 16
+        elif one_round_64:  # 16-row, 64-column tiles filling at least 3/4 of one round
+            assert plan.block_m == 16 and plan.tile_n == 64
         elif M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096) or M <= 4):
             assert plan.tile_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:

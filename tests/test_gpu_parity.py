@@ -773,7 +773,9 @@ EDGE = [(1, 1, 128, 1), (1, 17, 256, 2), (3, 33, 384, 3), (15, 100, 512, 4), (17
         (129, 70, 256, 2), (130, 1001, 640, 5), (2048, 16, 128, 1), (8, 4100, 1280, 10),
         # the decode tile rule's edges: up to 8 rows and 4096 columns over more than 2^24 weights
         # run 16-column tiles (one 256-workgroup round), 9 rows or 4097 columns do not; ragged N
-        (8, 4096, 8192, 2), (9, 4096, 8192, 2), (5, 4097, 8192, 3), (7, 2500, 9728, 4)]
+        (8, 4096, 8192, 2), (9, 4096, 8192, 2), (5, 4097, 8192, 3), (7, 2500, 9728, 4),
+        # 16-row tiles of 64 columns (at least three quarters of one round), ragged M and N
+        (50, 4000, 2560, 2), (33, 6000, 1280, 3)]
 
 
 @pytest.mark.parametrize("M,N,K,s", EDGE)

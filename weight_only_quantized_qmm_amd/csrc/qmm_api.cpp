@@ -156,6 +156,17 @@ W4A16Tile w4a16_tile(int M, int N, int K, int s) {
             t.ns = 1;
             return narrow_skinny(t, M, N, s);
         }
+        // Likewise 16-row tiles of 64 columns when those fill at least three quarters of one
+        // round (q at M = 48..64, N = 3072..4096): unsplit instead of 32- or 64-row tiles in
+        // two partitions plus the merge. A/B on MI355X: q at M = 48, 56, 64 8.36, 8.22, 8.33 us
+        // against 9.40, 9.73, 10.05, N = 3072 at M = 64 8.30 against 9.96. With 32 or 48
+        // columns, or filling fewer CUs (o at M = 32 and 64, q at M = 24 and 32), 0-7 % slower.
+        if (M <= 64 && (long long)N * K <= (1LL << 24) && ceil_div(M, 16) * ceil_div(N, 64) <= kCUs &&
+            4 * ceil_div(M, 16) * ceil_div(N, 64) >= 3 * kCUs) {
+            t.mt = 1;
+            t.ns = 4;
+            return narrow_skinny(t, M, N, s);
+        }
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         // Up to 32 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
         // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o on MI355X:

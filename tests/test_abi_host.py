@@ -564,3 +564,27 @@ def test_decode_tile_rule_edges():
     assert tiles[(9, 4096, 8192)][1] != 16 and tiles[(5, 4097, 8192)][1] != 16
     # 256 16-column tiles fill the CUs as they are; 157 of them run as 250 tiles of 10 columns
     assert tiles[(8, 4096, 8192)][3] == 16 and tiles[(7, 2500, 9728)][2:] == (1, 10)
+
+
+# Small-M tile choices around the 16-row rules, derived by hand (T16 = ceil(M/16) * ceil(N/16)
+# and T64 = ceil(M/16) * ceil(N/64) 16-row tiles; one round = 256 workgroups):
+#   (64, 1024, 2560): T16 = 4 * 64 = 256 <= 256          -> 16 x 16 tiles, unsplit, 256 workgroups
+#   (32, 1024, 2560): T16 = 2 * 64 = 128, narrowed to 256 // 2 = 128 tiles per row block of
+#                     ceil(1024 / 128) = 8 columns            -> 16 x 8, unsplit
+#   (65, 1024, 2560): M > 64                              -> not a 16-row tile
+#   (64, 4096, 2560): T16 = 1024; T64 = 4 * 64 = 256 >= 192 -> 16 x 64 tiles, unsplit
+#   (48, 4096, 2560): T64 = 3 * 64 = 192 = 3/4 of a round  -> 16 x 64 tiles, unsplit
+#   (32, 4096, 2560): T64 = 2 * 64 = 128 < 192             -> 32-row tiles of 16 columns (256 of them)
+#   (64, 4160, 2560): T64 = 4 * 65 = 260 > 256             -> not a 16-row tile
+#   (64, 9728, 2560): N*K > 2^24                           -> not a 16-row tile
+SMALL_HAND = [((64, 1024, 2560), (16, 16, 1, 64, 4)), ((32, 1024, 2560), (16, 8, 1, 128, 2)),
+              ((64, 4096, 2560), (16, 64, 1, 64, 4)), ((48, 4096, 2560), (16, 64, 1, 64, 3)),
+              ((32, 4096, 2560), (32, 16, 1, 256, 1))]
+
+
+def test_small_m_sixteen_row_tiles_hand_derived():
+    for (M, N, K), want in SMALL_HAND:
+        p = q.qmm_splitk_plan(M, N, K)
+        assert (p.block_m, p.block_n, p.s, p.grid_x, p.grid_y) == want, (M, N, K, p.as_dict())
+    for M, N, K in ((65, 1024, 2560), (64, 4160, 2560), (64, 9728, 2560)):
+        assert q.qmm_splitk_plan(M, N, K).block_m != 16, (M, N, K)

@@ -125,10 +125,13 @@ def test_plan_mi355x_preset_is_valid(M, N, K):
         one_round_16 = M <= 64 and -(-M // 16) * -(-N // 16) <= 256 and N * K <= 1 << 24
         t64 = -(-M // 16) * -(-N // 64)
         one_round_64 = M <= 64 and N * K <= 1 << 24 and 3 * 256 <= 4 * t64 <= 4 * 256
+        one_round_32 = 64 < M and -(-M // 32) * -(-N // 16) <= 256 and N * K <= 1 << 24
         if one_round_16:  # narrow projections: 16-row, 16-column tiles in one round
             assert plan.block_m == 16 and plan.tile_n == 16
         elif one_round_64:  # 16-row, 64-column tiles filling at least 3/4 of one round
             assert plan.block_m == 16 and plan.tile_n == 64
+        elif one_round_32:  # past 64 rows: 32-row, 16-column tiles in one round
+            assert plan.block_m == 32 and plan.tile_n == 16
         elif M <= 32 and (N * K <= 1 << 24 or (M <= 8 and N <= 4096) or M <= 4):
             assert plan.tile_n == 16
         elif rows * -(-N // 32) <= 256 and K < 8192:
@@ -208,7 +211,8 @@ def test_large_m_variant_on_the_sweep():
     assert big == {"q": (128, 256), "k": (128, 128), "v": (128, 128), "o": (256, 256), "gate": (256, 256),
                    "up": (256, 256), "down": (256, 256)}
     assert all(got[(n, 128)] == (128, 128) for n in ("gate", "up", "down"))
-    assert all(got[(n, 128)][0] == 64 for n in ("q", "k", "v", "o"))
+    assert all(got[(n, 128)][0] == 64 for n in ("q", "o"))
+    assert all(got[(n, 128)] == (32, 16) for n in ("k", "v"))  # 32-row tiles of 16 columns, one round
 
 
 def check_slot_filling(plan, M, K, slots, pol, what=""):
@@ -571,13 +575,17 @@ def test_decode_tile_rule_edges():
 #   (64, 1024, 2560): T16 = 4 * 64 = 256 <= 256          -> 16 x 16 tiles, unsplit, 256 workgroups
 #   (32, 1024, 2560): T16 = 2 * 64 = 128, narrowed to 256 // 2 = 128 tiles per row block of
 #                     ceil(1024 / 128) = 8 columns            -> 16 x 8, unsplit
-#   (65, 1024, 2560): M > 64                              -> not a 16-row tile
+#   (65, 1024, 2560): M > 64                              -> not a 16-row tile (32 x 16)
 #   (64, 4096, 2560): T16 = 1024; T64 = 4 * 64 = 256 >= 192 -> 16 x 64 tiles, unsplit
 #   (48, 4096, 2560): T64 = 3 * 64 = 192 = 3/4 of a round  -> 16 x 64 tiles, unsplit
 #   (32, 4096, 2560): T64 = 2 * 64 = 128 < 192             -> 32-row tiles of 16 columns (256 of them)
 #   (64, 4160, 2560): T64 = 4 * 65 = 260 > 256             -> not a 16-row tile
 #   (64, 9728, 2560): N*K > 2^24                           -> not a 16-row tile
-SMALL_HAND = [((64, 1024, 2560), (16, 16, 1, 64, 4)), ((32, 1024, 2560), (16, 8, 1, 128, 2)),
+#   (128, 1024, 2560): M > 64, ceil(128/32) * 64 = 256 <= 256  -> 32 x 16 tiles, unsplit
+#   (96, 1024, 2560): 3 * 64 = 192, narrowed to 256 // 3 = 85 tiles per row block of
+#                     ceil(1024 / 85) = 13 columns           -> 32 x 13, unsplit
+SMALL_HAND = [((128, 1024, 2560), (32, 16, 1, 64, 4)), ((96, 1024, 2560), (32, 13, 1, 79, 3)),
+              ((64, 1024, 2560), (16, 16, 1, 64, 4)), ((32, 1024, 2560), (16, 8, 1, 128, 2)),
               ((64, 4096, 2560), (16, 64, 1, 64, 4)), ((48, 4096, 2560), (16, 64, 1, 64, 3)),
               ((32, 4096, 2560), (32, 16, 1, 256, 1))]
 
@@ -588,3 +596,4 @@ def test_small_m_sixteen_row_tiles_hand_derived():
         assert (p.block_m, p.block_n, p.s, p.grid_x, p.grid_y) == want, (M, N, K, p.as_dict())
     for M, N, K in ((65, 1024, 2560), (64, 4160, 2560), (64, 9728, 2560)):
         assert q.qmm_splitk_plan(M, N, K).block_m != 16, (M, N, K)
+    assert q.qmm_splitk_plan(129, 1024, 2560).block_m >= 128  # past 128 rows: the large-M kernel

@@ -775,7 +775,10 @@ EDGE = [(1, 1, 128, 1), (1, 17, 256, 2), (3, 33, 384, 3), (15, 100, 512, 4), (17
         # run 16-column tiles (one 256-workgroup round), 9 rows or 4097 columns do not; ragged N
         (8, 4096, 8192, 2), (9, 4096, 8192, 2), (5, 4097, 8192, 3), (7, 2500, 9728, 4),
         # 16-row tiles of 64 columns (at least three quarters of one round), ragged M and N
-        (50, 4000, 2560, 2), (33, 6000, 1280, 3)]
+        (50, 4000, 2560, 2), (33, 6000, 1280, 3),
+        # past 64 rows, 32-row tiles of 16 columns in one round (narrowed to 13 at M = 80),
+        # ragged M and N
+        (100, 1000, 2560, 4), (80, 1024, 2560, 3)]
 
 
 @pytest.mark.parametrize("M,N,K,s", EDGE)

@@ -167,6 +167,15 @@ W4A16Tile w4a16_tile(int M, int N, int K, int s) {
             t.ns = 4;
             return narrow_skinny(t, M, N, s);
         }
+        // Past 64 rows the same holds with 32-row tiles of 16 columns (k and v at M = 65..128):
+        // unsplit, each workgroup reading 32 rows of A instead of 64 in split 64-row tiles.
+        // A/B on MI355X: k and v at M = 80, 96, 128 6.13, 6.25, 6.10 us against 8.28, 8.31,
+        // 8.43 (4 partitions plus the merge).
+        if (M > 64 && ceil_div(M, 32) * ceil_div(N, 16) <= kCUs && (long long)N * K <= (1LL << 24)) {
+            t.mt = 2;
+            t.ns = 1;
+            return narrow_skinny(t, M, N, s);
+        }
         t.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         // Up to 32 rows over at most 2^24 weights: 16-column tiles, so that the unsplit grid
         // has N/16 workgroups of up to 12 waves (config sweeps of q, k, v and o on MI355X:
